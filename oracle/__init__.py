@@ -1,0 +1,127 @@
+"""CPU oracle for the SSD layer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, links or calls anything here, and nothing
+here imports the product path: the two share only the seeded input
+generator (``ssd_inputs``), which holds none of the method's arithmetic.
+
+Contents
+--------
+* ``forward`` / ``decode_step``: the float64 sequential recurrence, in plain C
+  (``ssd_recurrence.c``), parallel over independent (batch, head) sequences.
+* ``chunked``: float64 numpy versions of each step of the chunked algorithm
+  (decay prefix, C B^T, intra-chunk masked product, chunk state, state
+  passing, output combine) used to check the GPU's intermediates.
+
+Every function is pinned by ``tests/test_oracle_pins.py`` against what the
+pages fix: the printed four-token example, the quadratic (masked attention)
+form, the closed forms for a = 1 and constant a, the rank bound, the split
+call and chunk-size invariance.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssd_recurrence.c")
+_LIB_PATH = os.path.join(_HERE, "_build", "libssd_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (plain -O2 + OpenMP, no fast-math)."""
+    os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        i64, dp = ctypes.c_int64, ctypes.c_void_p
+        lib.ssd_oracle_forward.argtypes = [i64] * 6 + [dp] * 9 + [i64, dp]
+        lib.ssd_oracle_forward.restype = ctypes.c_int
+        lib.ssd_oracle_decode_step.argtypes = [i64] * 5 + [dp] * 8
+        lib.ssd_oracle_decode_step.restype = ctypes.c_int
+        lib.ssd_oracle_num_threads.restype = ctypes.c_int
+        lib.ssd_oracle_set_num_threads.argtypes = [ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    return _load().ssd_oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    _load().ssd_oracle_set_num_threads(int(n))
+
+
+def _f64(a):
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor -> exact float64
+        import torch
+        a = a.detach().to("cpu").to(torch.float64).numpy()
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def forward(x, dt, A, B, C, D=None, init=None, chunk: int = 0):
+    """Sequential float64 recurrence.
+
+    Shapes: x [b, L, H, P], dt [b, L, H], A [H], B, C [b, L, G, N], D [H] or
+    None, init [b, H, P, N] or None.  Returns (y, final_state) and, when
+    ``chunk`` > 0, also the state entering every chunk, [b, nc, H, P, N].
+    """
+    x, dt, A, B, C, D, init = (_f64(v) for v in (x, dt, A, B, C, D, init))
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dt.shape == (b, L, H) and A.shape == (H,) and B.shape == (b, L, G, N)
+    assert C.shape == B.shape and (D is None or D.shape == (H,))
+    assert init is None or init.shape == (b, H, P, N)
+    y = np.empty((b, L, H, P))
+    final = np.empty((b, H, P, N))
+    bnd = None
+    if chunk > 0:
+        nc = (L + chunk - 1) // chunk
+        bnd = np.empty((b, nc, H, P, N))
+    rc = _load().ssd_oracle_forward(b, L, H, P, N, G, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                     _ptr(C), _ptr(D), _ptr(init), _ptr(y), _ptr(final),
+                                     int(chunk), _ptr(bnd))
+    if rc != 0:
+        raise ValueError("oracle: bad shape")
+    return (y, final, bnd) if chunk > 0 else (y, final)
+
+
+def decode_step(state, x, dt, A, B, C, D=None):
+    """One recurrence step on a carried state.
+
+    state [b, H, P, N] (float64, updated in place and returned), x [b, H, P],
+    dt [b, H], B, C [b, G, N].  Returns (y [b, H, P], state).
+    """
+    assert isinstance(state, np.ndarray) and state.dtype == np.float64 and state.flags.c_contiguous
+    x, dt, A, B, C, D = (_f64(v) for v in (x, dt, A, B, C, D))
+    b, H, P, N = state.shape
+    G = B.shape[1]
+    y = np.empty((b, H, P))
+    rc = _load().ssd_oracle_decode_step(b, H, P, N, G, _ptr(state), _ptr(x), _ptr(dt), _ptr(A),
+                                         _ptr(B), _ptr(C), _ptr(D), _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle: bad shape")
+    return y, state

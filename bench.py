@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Throughput of the SSD layer forward on one MI355X.
+
+Default workload: the 2.7B-layer shape (batch 4, L 4096, H 80, P 64, N 128,
+one B/C group, chunk 256, bfloat16 inputs, float32 accumulation), seeded
+synthetic inputs already resident in device memory.  A step is one full
+``ssd_forward`` call (all kernels of the chunked algorithm).  Before each
+timed step a 512 MiB buffer is overwritten so the 256 MB Infinity Cache does
+not hold the inputs; HIP events on the launch stream bracket the forward call
+alone.  Prints one JSON line.
+
+Other modes: ``--workload decode`` (512 single-token steps on a
+[256, 80, 64, 128] float32 state) and ``--workload copy`` (a plain
+device-to-device copy used to calibrate hardware byte counters).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "SSD fwd tokens/s at H=80,P=64,N=128,L=4096; % of MFMA/HBM roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=["forward", "decode", "copy"], default="forward")
+    ap.add_argument("--path", choices=["fused", "staged"], default="fused")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    return ap.parse_args()
+
+
+def forward_bytes(w) -> int:
+    """Compulsory bytes of one forward: read x, dt, B, C, A, D (+ init) once,
+    write y (+ final state) once."""
+    e = 2 if w.dtype == "bf16" else 4
+    b, L, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    n = 2 * b * L * H * P * e + b * L * H * e + 2 * b * L * G * N * e + 2 * H * 4
+    n += b * H * P * N * 4 * (2 if w.init_mode == "normal" else 1)
+    return n
+
+
+def forward_flops(w) -> int:
+    """Algorithmic flops of the chunked algorithm (lower-triangular blocks)."""
+    b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    tri = 0
+    for c in range((L + Q - 1) // Q):
+        q = min(Q, L - c * Q)
+        tri += q * (q + 1) // 2
+    nc = (L + Q - 1) // Q
+    per_bh = 2 * (P * tri + L * N * P + L * N * P) + 2 * nc * N * P
+    per_bg = 2 * N * tri
+    return b * H * per_bh + b * G * per_bg
+
+
+def kernel_bytes(w) -> dict:
+    """Algorithmic bytes of each kernel of the staged sequence, per launch
+    (what its own inputs and outputs must move at least once)."""
+    e = 2 if w.dtype == "bf16" else 4
+    b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    nc = (L + Q - 1) // Q
+    T16 = Q // 16
+    cs = b * H * nc * Q * 4
+    cb = b * nc * G * (T16 * (T16 + 1) // 2) * 256 * e
+    S = b * nc * H * P * N * 4
+    x = b * L * H * P * e
+    BC = b * L * G * N * e
+    st = b * H * P * N * 4
+    return {
+        "chunk_cumsum": b * L * H * e + H * 4 + cs,
+        "chunk_cb": 2 * BC + cb,
+        "chunk_state": x + BC + cs + S,
+        "state_passing": 2 * S + b * H * nc * 4 + st * (2 if w.init_mode == "normal" else 1),
+        "chunk_scan": x + BC + cb + cs + S + H * 4 + x,
+    }
+
+
+def kernel_flops(w) -> dict:
+    b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    tri = sum(min(Q, L - c * Q) * (min(Q, L - c * Q) + 1) // 2 for c in range((L + Q - 1) // Q))
+    return {"chunk_cb": 2 * N * tri * b * G, "chunk_state": 2 * L * N * P * b * H,
+            "chunk_scan": (2 * P * tri + 2 * L * N * P) * b * H}
+
+
+def run_forward_bench(args):
+    import torch
+
+    import selective_state_space_04_amd as ssd
+    import ssd_inputs as si
+
+    w = si.WORKLOADS[2]
+    dev = torch.device("cuda:0")
+    inp = si.make_forward_inputs(w)
+    g = lambda t: None if t is None else t.to(dev)
+    x, dt, A, B, C, D, init = (g(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "init"))
+    dims = ssd.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk,
+                         ssd.BF16 if w.dtype == "bf16" else ssd.F32)
+    ws = torch.empty(max(ssd.workspace_bytes(dims), 1), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
+    staged = args.path == "staged"
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def step():
+        ssd.forward(x, dt, A, B, C, D, init, chunk=w.chunk, staged=staged, y=y, final_state=fin,
+                    workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        if flush is not None:
+            flush.fill_(k & 0xFF)
+        starts[k].record()
+        step()
+        ends[k].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = statistics.mean(ms)
+    tokens = w.batch * w.seqlen
+    value = tokens / (ms_per_step * 1e-3)
+    t_roof_us = max(forward_bytes(w) / (HBM_PEAK_GBS * 1e3), forward_flops(w) / (BF16_PEAK_TFLOPS * 1e6))
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded; distributions of the workload)",
+        "config": {"workload": "2.7B-layer-shaped SSD forward", "batch": w.batch, "seqlen": w.seqlen,
+                   "nheads": w.nheads, "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
+                   "chunk": w.chunk, "inputs": "bf16", "accumulate": "fp32", "path": args.path,
+                   "mall_flushed": flush is not None},
+        "forward_roofline": {"bound": "hbm", "t_roof_us": t_roof_us, "frac": t_roof_us / (ms_per_step * 1e3),
+                             "alg_bytes": forward_bytes(w), "alg_flops": forward_flops(w)},
+        "ms_min": min(ms), "ms_median": statistics.median(ms), "wall_s": wall,
+    }
+
+    if not args.no_kernel_timing:
+        result["roofline"], result["kernels_us"] = kernel_roofline(ssd, w, x, dt, A, B, C, D, init, ws,
+                                                                  y, fin, flush, args)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inp)
+    return result
+
+
+def kernel_roofline(ssd, w, x, dt, A, B, C, D, init, ws, y, fin, flush, args):
+    """Average duration of each kernel of the forward, measured with HIP
+    events on the launch stream around the same kernels the forward runs,
+    and the roofline of the slowest one."""
+    import torch
+
+    Q, L = w.chunk, w.seqlen
+    nc = (L + Q - 1) // Q
+    e = 2 if w.dtype == "bf16" else 4
+    # carve the workspace exactly as the library does
+    al = lambda v: (v + 255) // 256 * 256
+    cs_b = w.batch * w.nheads * nc * Q * 4
+    cb_b = w.batch * nc * w.ngroups * Q * Q * e
+    S_b = w.batch * nc * w.nheads * w.headdim * w.dstate * 4
+    cs = ws[: cs_b].view(torch.float32).view(w.batch, w.nheads, nc, Q)
+    cb_off = al(cs_b)
+    cb = ws[cb_off: cb_off + cb_b].view(x.dtype).view(w.batch, nc, w.ngroups, Q, Q)
+    S_off = al(cb_off + cb_b)
+    S = ws[S_off: S_off + S_b].view(torch.float32).view(w.batch, nc, w.nheads, w.headdim, w.dstate)
+    stream = ssd._stream()
+    dims = ssd.make_dims(w.batch, L, w.nheads, w.headdim, w.dstate, w.ngroups, Q,
+                         ssd.BF16 if w.dtype == "bf16" else ssd.F32)
+    import ctypes
+    dp = ctypes.byref(dims)
+    p = ssd._p
+    seq = [
+        ("chunk_cumsum", lambda: ssd.lib.ssd_chunk_cumsum(dp, p(dt), p(A), p(cs), stream)),
+        ("chunk_cb", lambda: ssd.lib.ssd_chunk_cb(dp, p(B), p(C), p(cb), stream)),
+        ("chunk_state", lambda: ssd.lib.ssd_chunk_state(dp, p(x), p(B), p(cs), p(S), stream)),
+        ("state_passing", lambda: ssd.lib.ssd_state_passing(dp, p(S), p(cs), p(init), p(fin), stream)),
+        ("chunk_scan", lambda: ssd.lib.ssd_chunk_scan(dp, p(x), p(C), p(cb), p(cs), p(S), p(D), p(y), stream)),
+    ]
+    reps = max(args.steps, 5)
+    times = {n: [] for n, _ in seq}
+    for rep in range(reps + 2):
+        if flush is not None:
+            flush.fill_(rep & 0xFF)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)]
+        evs[0].record()
+        for i, (n, fn) in enumerate(seq):
+            st = fn()
+            if st != 0:
+                raise RuntimeError(f"{n}: status {st}")
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        if rep >= 2:
+            for i, (n, _) in enumerate(seq):
+                times[n].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)
+    avg = {n: statistics.mean(v) for n, v in times.items()}
+    dom = max(avg, key=avg.get)
+    kb = kernel_bytes(w)[dom]
+    achieved = kb / (avg[dom] * 1e-6) / 1e9
+    roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None, "alg_bytes_per_launch": kb,
+            "avg_launch_us": avg[dom]}
+    return roof, avg
+
+
+def cpu_baseline(w, inp):
+    import oracle
+
+    args = [inp[k] for k in ("x", "dt", "A", "B", "C", "D", "init")]
+    f = [oracle._f64(a) for a in args]
+    t0 = time.perf_counter()
+    oracle.forward(*f)
+    t = time.perf_counter() - t0
+    return {"value": w.batch * w.seqlen / t, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": f"the full workload ({w.batch}x{w.seqlen} tokens, {w.nheads} heads), "
+            f"float64 sequential recurrence, {t:.2f} s"}
+
+
+def run_decode_bench(args):
+    import torch
+
+    import selective_state_space_04_amd as ssd
+    import ssd_inputs as si
+
+    w = si.WORKLOADS[4]
+    dev = torch.device("cuda:0")
+    par = si.make_decode_params(w)
+    state = par["state"].to(dev)
+    A, D = par["A"].to(dev), par["D"].to(dev)
+    nsteps = w.steps
+    steps = [si.make_decode_step_inputs(w, s) for s in range(nsteps)]
+    xs = torch.stack([s["x"] for s in steps]).to(dev)
+    dts = torch.stack([s["dt"] for s in steps]).to(dev)
+    Bs = torch.stack([s["B"] for s in steps]).to(dev)
+    Cs = torch.stack([s["C"] for s in steps]).to(dev)
+    ys = torch.empty_like(xs)
+    for s in range(min(args.warmup, nsteps)):
+        ssd.decode_step(state, xs[s], dts[s], A, Bs[s], Cs[s], D, y=ys[s])
+    state.copy_(par["state"].to(dev))
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for s in range(nsteps):
+        ssd.decode_step(state, xs[s], dts[s], A, Bs[s], Cs[s], D, y=ys[s])
+        ev[s + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[s].elapsed_time(ev[s + 1]) * 1e3 for s in range(nsteps)]
+    total_ms = ev[0].elapsed_time(ev[-1])
+    bytes_step = 2 * w.batch * w.nheads * w.headdim * w.dstate * 4 + 2 * w.batch * w.nheads * w.headdim * 2 \
+        + w.batch * w.nheads * 2 + 2 * w.batch * w.ngroups * w.dstate * 2 + 2 * w.nheads * 4
+    avg_us = statistics.mean(per)
+    achieved = bytes_step / (avg_us * 1e-6) / 1e9
+    return {"metric": "SSD decode tokens/s, state [256,80,64,128] fp32, 512 steps", "value": w.batch * nsteps /
+            (total_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": nsteps, "warmup": args.warmup,
+            "ms_per_step": total_ms / nsteps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic", "config": {"workload": "decode step", "batch": w.batch,
+                                                              "nheads": w.nheads, "headdim": w.headdim,
+                                                              "dstate": w.dstate, "steps": nsteps},
+            "roofline": {"kernel": "decode", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "alg_bytes_per_launch": bytes_step, "avg_launch_us": avg_us},
+            "wall_s": wall}
+
+
+def run_copy(args):
+    """Device-to-device copy of 1 GiB, repeated: reference for byte counters."""
+    import torch
+
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(args.warmup):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    return {"metric": "device copy GB/s (1 GiB read + 1 GiB write)", "value": 2 * n / (ms * 1e-3) / 1e9,
+            "unit": "GB/s", "ms_per_step": ms, "steps": args.steps, "bytes_read_per_copy": n}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(each (batch, head) sequence is independent, so multi-GPU runs would shard batch/heads "
+              "with no communication -- not part of this build)", file=sys.stderr)
+        sys.exit(2)
+    if args.workload == "forward":
+        res = run_forward_bench(args)
+    elif args.workload == "decode":
+        res = run_decode_bench(args)
+    else:
+        res = run_copy(args)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

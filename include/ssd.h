@@ -1,0 +1,194 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) SSD layer library, libssd_mi355x.so.
+ *
+ * The SSD layer ("state space dual", the Mamba-2 core; docsaid.org review
+ * "Mamba-2", sections "SSM を一つの行列として書く" and "A を一つの数に簡略化する")
+ * computes, for every batch row b and head h (group g = h / (H / G)):
+ *
+ *   a_t    = exp(dt[b,t,h] * A[h])
+ *   h_t    = a_t * h_{t-1} + x[b,t,h,:] (outer) B[b,t,g,:]      state [P, N]
+ *   y[b,t,h,:] = h_t C[b,t,g,:] + D[h] * x[b,t,h,:]
+ *
+ * with h_{-1} = init_state (zeros when NULL).  ssd_forward evaluates it with
+ * the chunked algorithm (same review, section "2つのルートを半分ずつ"; SSD
+ * summary page, section "チャンク化アルゴリズム": the masked attention form
+ * inside blocks of `chunk` steps, the recurrence across blocks); the result
+ * does not depend on `chunk` except through rounding.  ssd_decode_step is
+ * one step of the recurrence on a carried state (review, section
+ * "4つのトークンで計算してみる": the recurrent route keeps a constant-size
+ * state and suits generation).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every array pointer is DEVICE memory owned by the caller; the
+ *   library never allocates, frees or retains them.  Scratch memory comes in
+ *   through `workspace`.  All arrays are dense, row-major and contiguous:
+ *     x, y  [batch, seqlen, nheads, headdim]     dtype
+ *     dt    [batch, seqlen, nheads]              dtype
+ *     B, C  [batch, seqlen, ngroups, dstate]     dtype
+ *     A, D  [nheads]                              float32
+ *     init_state, final_state, state  [batch, nheads, headdim, dstate]  float32
+ *   Decode uses the same layouts with seqlen = 1 (x, y [batch, nheads,
+ *   headdim]; dt [batch, nheads]; B, C [batch, ngroups, dstate]).
+ *   `dtype` (SSD_F32 or SSD_BF16) is the type of x, dt, B, C and y; states,
+ *   A and D are always float32.  Arrays must be 16-byte aligned and the
+ *   workspace 256-byte aligned.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
+ *   stream).  Calls only enqueue work on it; they never synchronise.
+ * Errors.  Argument errors are detected on the host before anything is
+ *   enqueued, and then nothing is written.  A failed launch returns
+ *   SSD_ERR_HIP.  Input VALUES are not checked: NaN/Inf propagate, and A > 0
+ *   or dt < 0 are evaluated as the defined recurrence (they may overflow).
+ * Aliasing.  y must not overlap any input.  final_state may be the same
+ *   array as init_state (in-place carry) but must not partially overlap it
+ *   or overlap anything else.
+ * Supported shapes.  headdim in {16, 32, 64, 128}; dstate in
+ *   {16, 32, 64, 128, 256}; chunk a multiple of 16 in [16, 256]; nheads a
+ *   multiple of ngroups; batch, seqlen >= 0 (seqlen may be any length: the
+ *   last chunk may be short).  Others return SSD_ERR_UNSUPPORTED.
+ */
+#ifndef SSD_MI355X_H
+#define SSD_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL = 1,        /* a required pointer is NULL */
+    SSD_ERR_SHAPE = 2,       /* a negative or inconsistent size */
+    SSD_ERR_DTYPE = 3,       /* dtype is not SSD_F32 / SSD_BF16 */
+    SSD_ERR_ALIGN = 4,       /* a pointer is not 16-byte (workspace: 256-byte) aligned */
+    SSD_ERR_WORKSPACE = 5,   /* workspace too small or NULL when needed */
+    SSD_ERR_UNSUPPORTED = 6, /* headdim / dstate / chunk outside the compiled set */
+    SSD_ERR_HIP = 7,         /* a HIP call or kernel launch failed */
+    SSD_ERR_ALIAS = 8        /* an output overlaps an input it must not overlap */
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+typedef struct {
+    int64_t batch;    /* b */
+    int64_t seqlen;   /* L (ignored by decode) */
+    int64_t nheads;   /* H */
+    int64_t headdim;  /* P */
+    int64_t dstate;   /* N */
+    int64_t ngroups;  /* G: heads h in [k*H/G, (k+1)*H/G) share B, C group k */
+    int64_t chunk;    /* Q: block length of the chunked algorithm (ignored by decode) */
+    int32_t dtype;    /* ssd_dtype of x, dt, B, C, y */
+} ssd_dims;
+
+/* Text for a status code (static storage; never NULL). */
+const char *ssd_status_string(ssd_status s);
+
+/* Text of the HIP error behind the calling thread's last SSD_ERR_HIP
+ * (static storage; "no error" when there was none). */
+const char *ssd_last_hip_error(void);
+
+/* Bytes of workspace ssd_forward / ssd_forward_staged need for these dims
+ * (0 for invalid dims).  Pure host computation. */
+size_t ssd_forward_workspace_bytes(const ssd_dims *dims);
+
+/*
+ * Layer forward over a whole sequence, chunked algorithm (review page,
+ * section "2つのルートを半分ずつ").
+ *   D           nullable: treated as zeros (the per-head skip term).
+ *   init_state  nullable: zeros.
+ *   final_state nullable: not written.  Receives h_{L-1}.
+ *   workspace   device scratch of at least ssd_forward_workspace_bytes(dims);
+ *               its contents on entry are ignored.
+ * y receives the outputs in dtype (bfloat16 rounded to nearest even).
+ */
+ssd_status ssd_forward(const ssd_dims *dims, const void *x, const void *dt, const float *A,
+                       const void *B, const void *C, const float *D, const float *init_state,
+                       void *y, float *final_state, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* Same contract and result as ssd_forward, computed by running the five step
+ * kernels below one after another with their intermediates in `workspace`
+ * (the unfused reference arrangement of the chunked algorithm). */
+ssd_status ssd_forward_staged(const ssd_dims *dims, const void *x, const void *dt,
+                              const float *A, const void *B, const void *C, const float *D,
+                              const float *init_state, void *y, float *final_state,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One recurrent step for `batch` sequences (review page, section
+ * "4つのトークンで計算してみる").  `state` [batch, H, P, N] float32 is read and
+ * overwritten in place with a_t * state + x B^T; y [batch, H, P] receives
+ * state C + D x.  dims->seqlen and dims->chunk are ignored.  D nullable.
+ */
+ssd_status ssd_decode_step(const ssd_dims *dims, float *state, const void *x, const void *dt,
+                           const float *A, const void *B, const void *C, const float *D,
+                           void *y, void *stream);
+
+/* ------------------------------------------------------------------------
+ * The steps of the chunked algorithm, one entry point each.  nc =
+ * ceil(seqlen / chunk); chunk c covers steps [c*chunk, min((c+1)*chunk, L)).
+ * Intermediates are float32 unless stated.
+ * ---------------------------------------------------------------------- */
+
+/* Decay prefix (review page, section "A を一つの数に簡略化する": the mask
+ * entries are products of per-step decays, so their logarithms are
+ * differences of a running sum).  cs [batch, H, nc, chunk]:
+ *   cs[b,h,c,i] = sum_{k = c*chunk .. c*chunk+i} dt[b,k,h] * A[h]
+ * computed by a log-depth wavefront scan in float32.  Entries past the end of
+ * a short last chunk repeat its last valid value. */
+ssd_status ssd_chunk_cumsum(const ssd_dims *dims, const void *dt, const float *A, float *cs,
+                            void *stream);
+
+/* C B^T inside each chunk (review page, section "A を一つの数に簡略化する":
+ * M = L o (C B^T); the same matrix for every head of a group).
+ * cb [batch, nc, G, chunk, chunk] in dtype:  cb[b,c,g,i,j] = C_{s+i} . B_{s+j}.
+ * Only 16 x 16 tiles on or below the diagonal are written (rows/columns past
+ * the sequence end are zero); tiles above the diagonal are left untouched. */
+ssd_status ssd_chunk_cb(const ssd_dims *dims, const void *B, const void *C, void *cb,
+                        void *stream);
+
+/* Each chunk's own end state, started from zero (review page, section
+ * "2つのルートを半分ずつ": the blocks below the diagonal are low rank and are
+ * carried as states).  states [batch, nc, H, P, N] float32:
+ *   S[b,c,h] = sum_j exp(cs_e - cs_j) x_{s+j} (outer) B_{s+j}, e = last step of c. */
+ssd_status ssd_chunk_state(const ssd_dims *dims, const void *x, const void *B, const float *cs,
+                           float *states, void *stream);
+
+/* Inter-chunk recurrence (state-space guide page, equation (3): affine maps
+ * compose).  In place on `states`: on entry S[b,c,h], on return the state
+ * entering chunk c, hprev[c] (hprev[0] = init or 0; hprev[c+1] =
+ * exp(cs_e(c)) hprev[c] + S[c]).  final_state (nullable) receives the state
+ * after the last chunk; it may alias init_state. */
+ssd_status ssd_state_passing(const ssd_dims *dims, float *states, const float *cs,
+                             const float *init_state, float *final_state, void *stream);
+
+/* Intra-chunk masked product plus output combine (SSD summary page,
+ * section "チャンク化アルゴリズム": per block (L o Q K^T) V, then the carried
+ * state's contribution is added):
+ *   y_{s+i} = sum_{j<=i} exp(cs_i - cs_j) cb[i,j] x_{s+j}
+ *             + exp(cs_i) hprev[c] C_{s+i} + D x_{s+i}.
+ * hprev nullable (zeros: y is then the intra-chunk part plus D x). D nullable. */
+ssd_status ssd_chunk_scan(const ssd_dims *dims, const void *x, const void *C, const void *cb,
+                          const float *cs, const float *hprev, const float *D, void *y,
+                          void *stream);
+
+/* ------------------------------------------------------------------------
+ * Host-only argument checks (no HIP call; usable without a GPU).  They
+ * return exactly the status the corresponding entry point would return
+ * before enqueuing anything.
+ * ---------------------------------------------------------------------- */
+ssd_status ssd_validate_forward(const ssd_dims *dims, const void *x, const void *dt,
+                                const float *A, const void *B, const void *C, const float *D,
+                                const float *init_state, const void *y,
+                                const float *final_state, const void *workspace,
+                                size_t workspace_bytes);
+ssd_status ssd_validate_decode(const ssd_dims *dims, const float *state, const void *x,
+                               const void *dt, const float *A, const void *B, const void *C,
+                               const float *D, const void *y);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSD_MI355X_H */

@@ -1,0 +1,245 @@
+"""MI355X (gfx950) SSD layer: Python binding of libssd_mi355x.so.
+
+This module only marshals arguments: it checks tensor devices, dtypes,
+shapes and contiguity, allocates outputs (and the workspace unless one is
+passed), and calls the C ABI declared in ``include/ssd.h`` on the current
+torch stream.  Every step of the computation runs in the library's HIP
+kernels; there is no fallback.  Importing fails loudly when the library has
+not been built (``python selective_state_space_04_amd/build.py``).
+
+Layouts: x, y [b, L, H, P]; dt [b, L, H]; B, C [b, L, G, N]; A, D [H] float32;
+states [b, H, P, N] float32.  x, dt, B, C share one dtype (float32 or
+bfloat16), which is also y's dtype.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssd_mi355x.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "ssd.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python selective_state_space_04_amd/build.py` (hipcc, gfx950)")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32)]
+
+
+F32, BF16 = 0, 1
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE", 4: "SSD_ERR_ALIGN",
+          5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_UNSUPPORTED", 7: "SSD_ERR_HIP", 8: "SSD_ERR_ALIAS"}
+
+_vp, _dp = ctypes.c_void_p, ctypes.POINTER(Dims)
+lib = ctypes.CDLL(LIB_PATH)
+_SIGS = {
+    "ssd_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "ssd_last_hip_error": (ctypes.c_char_p, []),
+    "ssd_forward_workspace_bytes": (ctypes.c_size_t, [_dp]),
+    "ssd_forward": (ctypes.c_int, [_dp] + [_vp] * 10 + [ctypes.c_size_t, _vp]),
+    "ssd_forward_staged": (ctypes.c_int, [_dp] + [_vp] * 10 + [ctypes.c_size_t, _vp]),
+    "ssd_decode_step": (ctypes.c_int, [_dp] + [_vp] * 9),
+    "ssd_chunk_cumsum": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp]),
+    "ssd_chunk_cb": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp]),
+    "ssd_chunk_state": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp, _vp]),
+    "ssd_state_passing": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp, _vp]),
+    "ssd_chunk_scan": (ctypes.c_int, [_dp] + [_vp] * 8),
+    "ssd_validate_forward": (ctypes.c_int, [_dp] + [_vp] * 10 + [ctypes.c_size_t]),
+    "ssd_validate_decode": (ctypes.c_int, [_dp] + [_vp] * 8),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.restype, _f.argtypes = _res, _args
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/ssd.h declares."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ssd_\w+)\s*\(", text, re.M)))
+
+
+class SSDError(RuntimeError):
+    def __init__(self, status: int):
+        msg = lib.ssd_status_string(status).decode()
+        if status == 7:
+            msg += f" ({lib.ssd_last_hip_error().decode()})"
+        super().__init__(msg)
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise SSDError(status)
+
+
+def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups=1, chunk=256, dtype=F32) -> Dims:
+    return Dims(int(batch), int(seqlen), int(nheads), int(headdim), int(dstate), int(ngroups),
+                int(chunk), int(dtype))
+
+
+def _p(t):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _stream():
+    return _vp(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, shape, dtype, dev):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _forward_dims(x, dt, A, B, C, D, init, chunk):
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [b, L, H, P] and B, C [b, L, G, N]")
+    if x.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    if x.device.type != "cuda":
+        raise ValueError("inputs must be on a HIP device")
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    _need(x, "x", (b, L, H, P), x.dtype, dev)
+    _need(dt, "dt", (b, L, H), x.dtype, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(B, "B", (b, L, G, N), x.dtype, dev)
+    _need(C, "C", (b, L, G, N), x.dtype, dev)
+    if D is not None:
+        _need(D, "D", (H,), torch.float32, dev)
+    if init is not None:
+        _need(init, "init_state", (b, H, P, N), torch.float32, dev)
+    return make_dims(b, L, H, P, N, G, chunk, _DT[x.dtype])
+
+
+def workspace_bytes(dims: Dims) -> int:
+    return int(lib.ssd_forward_workspace_bytes(ctypes.byref(dims)))
+
+
+def forward(x, dt, A, B, C, D=None, init_state=None, chunk: int = 256, *, staged: bool = False,
+            y=None, final_state=None, workspace=None, want_final: bool = True):
+    """Layer forward (chunked algorithm).  Returns (y, final_state).
+
+    ``y`` / ``final_state`` / ``workspace`` may be preallocated (the
+    workspace as a uint8 CUDA tensor of at least ``workspace_bytes``);
+    ``final_state`` may be ``init_state`` itself for an in-place carry.
+    """
+    dims = _forward_dims(x, dt, A, B, C, D, init_state, chunk)
+    b, L, H, P = x.shape
+    N = B.shape[3]
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", x.shape, x.dtype, x.device)
+    if final_state is None and want_final:
+        final_state = torch.empty((b, H, P, N), dtype=torch.float32, device=x.device)
+    elif final_state is not None:
+        _need(final_state, "final_state", (b, H, P, N), torch.float32, x.device)
+    nbytes = workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    fn = lib.ssd_forward_staged if staged else lib.ssd_forward
+    _check(fn(ctypes.byref(dims), _p(x), _p(dt), _p(A), _p(B), _p(C), _p(D), _p(init_state), _p(y),
+              _p(final_state), _p(workspace), workspace.numel(), _stream()))
+    return y, final_state
+
+
+def decode_step(state, x, dt, A, B, C, D=None, y=None):
+    """One recurrent step; ``state`` [b, H, P, N] float32 is updated in place.
+
+    x [b, H, P], dt [b, H], B, C [b, G, N].  Returns y [b, H, P]."""
+    if x.dim() != 3 or B.dim() != 3:
+        raise ValueError("x must be [b, H, P] and B, C [b, G, N]")
+    if x.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    dev = x.device
+    _need(state, "state", (b, H, P, N), torch.float32, dev)
+    _need(x, "x", (b, H, P), x.dtype, dev)
+    _need(dt, "dt", (b, H), x.dtype, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(B, "B", (b, G, N), x.dtype, dev)
+    _need(C, "C", (b, G, N), x.dtype, dev)
+    if D is not None:
+        _need(D, "D", (H,), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    dims = make_dims(b, 1, H, P, N, G, 16, _DT[x.dtype])
+    _check(lib.ssd_decode_step(ctypes.byref(dims), _p(state), _p(x), _p(dt), _p(A), _p(B), _p(C),
+                               _p(D), _p(y), _stream()))
+    return y
+
+
+# ---------------------------------------------------------------- the steps
+def _nc(L, Q):
+    return (L + Q - 1) // Q
+
+
+def chunk_cumsum(dt, A, chunk: int):
+    """cs [b, H, nc, chunk] float32 (decay prefix inside each chunk)."""
+    b, L, H = dt.shape
+    dims = make_dims(b, L, H, 16, 16, 1, chunk, _DT[dt.dtype])
+    cs = torch.empty((b, H, _nc(L, chunk), chunk), dtype=torch.float32, device=dt.device)
+    _check(lib.ssd_chunk_cumsum(ctypes.byref(dims), _p(dt.contiguous()), _p(A), _p(cs), _stream()))
+    return cs
+
+
+def chunk_cb(B, C, chunk: int, nheads: int | None = None):
+    """cb [b, nc, G, chunk, chunk] in B's dtype (lower tiles written)."""
+    b, L, G, N = B.shape
+    H = nheads or G
+    dims = make_dims(b, L, H, 16, N, G, chunk, _DT[B.dtype])
+    cb = torch.zeros((b, _nc(L, chunk), G, chunk, chunk), dtype=B.dtype, device=B.device)
+    _check(lib.ssd_chunk_cb(ctypes.byref(dims), _p(B), _p(C), _p(cb), _stream()))
+    return cb
+
+
+def chunk_state(x, B, cs, chunk: int):
+    """S [b, nc, H, P, N] float32 (each chunk's end state from zero)."""
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dims = make_dims(b, L, H, P, N, G, chunk, _DT[x.dtype])
+    S = torch.empty((b, _nc(L, chunk), H, P, N), dtype=torch.float32, device=x.device)
+    _check(lib.ssd_chunk_state(ctypes.byref(dims), _p(x), _p(B), _p(cs), _p(S), _stream()))
+    return S
+
+
+def state_passing(S, cs, L: int, chunk: int, init_state=None, final_state=None):
+    """In place: S -> hprev (state entering each chunk).  Returns (S, final)."""
+    b, nc, H, P, N = S.shape
+    dims = make_dims(b, L, H, P, N, 1, chunk, F32)
+    if final_state is None:
+        final_state = torch.empty((b, H, P, N), dtype=torch.float32, device=S.device)
+    _check(lib.ssd_state_passing(ctypes.byref(dims), _p(S), _p(cs), _p(init_state), _p(final_state),
+                                 _stream()))
+    return S, final_state
+
+
+def chunk_scan(x, C, cb, cs, hprev, D, chunk: int):
+    """y: intra-chunk masked product + exp(cs) hprev C + D x."""
+    b, L, H, P = x.shape
+    G, N = C.shape[2], C.shape[3]
+    dims = make_dims(b, L, H, P, N, G, chunk, _DT[x.dtype])
+    y = torch.empty_like(x)
+    _check(lib.ssd_chunk_scan(ctypes.byref(dims), _p(x), _p(C), _p(cb), _p(cs), _p(hprev), _p(D),
+                              _p(y), _stream()))
+    return y

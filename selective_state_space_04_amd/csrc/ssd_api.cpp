@@ -1,0 +1,350 @@
+// C ABI of libssd_mi355x.so: argument validation, workspace layout and the
+// launch sequence of each entry point.  The contract is documented in
+// include/ssd.h.  Validation is pure host code (no HIP call), so it can be
+// exercised on a machine without a GPU.
+#include "ssd.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "ssd_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxGridYZ = 65535;
+thread_local hipError_t g_last_hip = hipSuccess;
+
+struct Range {
+    uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+    bool empty() const { return lo == hi; }
+};
+
+Range range_of(const void *p, int64_t bytes) {
+    Range r;
+    if (p && bytes > 0) {
+        r.lo = (uintptr_t)p;
+        r.hi = r.lo + (uintptr_t)bytes;
+    }
+    return r;
+}
+
+bool overlap(const Range &a, const Range &b) {
+    return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool is_pow2_in(int64_t v, int64_t lo, int64_t hi) {
+    return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+// Multiplies with overflow detection; returns false past 2^62.
+bool mul_ok(int64_t &acc, int64_t v) {
+    if (v < 0) return false;
+    if (v != 0 && acc > ((int64_t)1 << 62) / v) return false;
+    acc *= v;
+    return true;
+}
+
+ssd_status check_dims(const ssd_dims *d, bool decode, ssd::Dims *out) {
+    if (!d) return SSD_ERR_NULL;
+    if (d->dtype != SSD_F32 && d->dtype != SSD_BF16) return SSD_ERR_DTYPE;
+    const int64_t L = decode ? 1 : d->seqlen;
+    if (d->batch < 0 || L < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
+        d->ngroups < 1 || (!decode && d->chunk < 1))
+        return SSD_ERR_SHAPE;
+    if (d->nheads % d->ngroups != 0) return SSD_ERR_SHAPE;
+    if (!is_pow2_in(d->headdim, 16, 128) || !is_pow2_in(d->dstate, 16, 256))
+        return SSD_ERR_UNSUPPORTED;
+    if (!decode && (d->chunk % 16 != 0 || d->chunk > 256)) return SSD_ERR_UNSUPPORTED;
+    if (d->batch > kMaxGridYZ || d->nheads > kMaxGridYZ) return SSD_ERR_UNSUPPORTED;
+    const int64_t Q = decode ? 16 : d->chunk;
+    const int64_t nc = (L + Q - 1) / Q;
+    int64_t n = d->batch;  // largest array: x / y, or the chunk states
+    if (!mul_ok(n, L) || !mul_ok(n, d->nheads) || !mul_ok(n, d->headdim))
+        return SSD_ERR_UNSUPPORTED;
+    int64_t ns = d->batch;
+    if (!mul_ok(ns, nc) || !mul_ok(ns, d->nheads) || !mul_ok(ns, d->headdim) ||
+        !mul_ok(ns, d->dstate))
+        return SSD_ERR_UNSUPPORTED;
+    int64_t grid = d->batch;  // one workgroup per (b, c, h)
+    if (!mul_ok(grid, nc) || !mul_ok(grid, d->nheads) || grid > INT32_MAX)
+        return SSD_ERR_UNSUPPORTED;
+    if (out) {
+        out->b = d->batch;
+        out->L = L;
+        out->H = d->nheads;
+        out->P = d->headdim;
+        out->N = d->dstate;
+        out->G = d->ngroups;
+        out->Q = Q;
+        out->nc = nc;
+        out->dtype = d->dtype;
+    }
+    return SSD_OK;
+}
+
+int64_t esize(const ssd::Dims &d) { return d.dtype == SSD_BF16 ? 2 : 4; }
+
+int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
+
+struct WsLayout {
+    int64_t cs = 0, cb = 0, S = 0, total = 0;
+};
+
+WsLayout ws_layout(const ssd::Dims &d) {
+    WsLayout w;
+    const int64_t cs_bytes = d.b * d.H * d.nc * d.Q * 4;
+    const int64_t cb_bytes = d.b * d.nc * d.G * d.Q * d.Q * esize(d);
+    const int64_t s_bytes = d.b * d.nc * d.H * d.P * d.N * 4;
+    w.cs = 0;
+    w.cb = align256(w.cs + cs_bytes);
+    w.S = align256(w.cb + cb_bytes);
+    w.total = align256(w.S + s_bytes);
+    if (d.b == 0 || d.nc == 0) w.total = 0;
+    return w;
+}
+
+ssd_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return SSD_OK;
+    g_last_hip = e;
+    return SSD_ERR_HIP;
+}
+
+ssd_status validate_forward(const ssd_dims *dims, const void *x, const void *dt, const float *A,
+                            const void *B, const void *C, const float *D, const float *init,
+                            const void *y, const float *fin, const void *ws, size_t ws_bytes,
+                            ssd::Dims *out) {
+    ssd::Dims d;
+    ssd_status st = check_dims(dims, false, &d);
+    if (st != SSD_OK) return st;
+    const bool tokens = d.b * d.L > 0;
+    if (!A) return SSD_ERR_NULL;
+    if (tokens && (!x || !dt || !B || !C || !y)) return SSD_ERR_NULL;
+    const void *ptrs[] = {x, dt, A, B, C, D, init, y, fin};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return SSD_ERR_ALIGN;
+    if (ws && !aligned(ws, 256)) return SSD_ERR_ALIGN;
+    const WsLayout w = ws_layout(d);
+    if (w.total > 0 && (!ws || (int64_t)ws_bytes < w.total)) return SSD_ERR_WORKSPACE;
+    const int64_t es = esize(d);
+    const int64_t state_bytes = d.b * d.H * d.P * d.N * 4;
+    const Range rx = range_of(x, d.b * d.L * d.H * d.P * es), rdt = range_of(dt, d.b * d.L * d.H * es),
+                rA = range_of(A, d.H * 4), rB = range_of(B, d.b * d.L * d.G * d.N * es),
+                rC = range_of(C, d.b * d.L * d.G * d.N * es), rD = range_of(D, d.H * 4),
+                ri = range_of(init, state_bytes), ry = range_of(y, d.b * d.L * d.H * d.P * es),
+                rf = range_of(fin, state_bytes), rw = range_of(ws, w.total);
+    const Range ins[] = {rx, rdt, rA, rB, rC, rD, ri};
+    for (const Range &r : ins)
+        if (overlap(ry, r) || overlap(rw, r)) return SSD_ERR_ALIAS;
+    if (overlap(ry, rf) || overlap(ry, rw) || overlap(rf, rw)) return SSD_ERR_ALIAS;
+    const Range ins_no_init[] = {rx, rdt, rA, rB, rC, rD};
+    for (const Range &r : ins_no_init)
+        if (overlap(rf, r)) return SSD_ERR_ALIAS;
+    if (overlap(rf, ri) && (const void *)fin != (const void *)init) return SSD_ERR_ALIAS;
+    if (out) *out = d;
+    return SSD_OK;
+}
+
+ssd_status validate_decode(const ssd_dims *dims, const float *state, const void *x,
+                           const void *dt, const float *A, const void *B, const void *C,
+                           const float *D, const void *y, ssd::Dims *out) {
+    ssd::Dims d;
+    ssd_status st = check_dims(dims, true, &d);
+    if (st != SSD_OK) return st;
+    if (!A) return SSD_ERR_NULL;
+    if (d.b > 0 && (!state || !x || !dt || !B || !C || !y)) return SSD_ERR_NULL;
+    const void *ptrs[] = {state, x, dt, A, B, C, D, y};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return SSD_ERR_ALIGN;
+    const int64_t es = esize(d);
+    const Range rs = range_of(state, d.b * d.H * d.P * d.N * 4), rx = range_of(x, d.b * d.H * d.P * es),
+                rdt = range_of(dt, d.b * d.H * es), rA = range_of(A, d.H * 4),
+                rB = range_of(B, d.b * d.G * d.N * es), rC = range_of(C, d.b * d.G * d.N * es),
+                rD = range_of(D, d.H * 4), ry = range_of(y, d.b * d.H * d.P * es);
+    const Range ins[] = {rx, rdt, rA, rB, rC, rD};
+    for (const Range &r : ins)
+        if (overlap(ry, r) || overlap(rs, r)) return SSD_ERR_ALIAS;
+    if (overlap(ry, rs)) return SSD_ERR_ALIAS;
+    if (out) *out = d;
+    return SSD_OK;
+}
+
+ssd_status validate_ptrs(const void *const *req, int nreq, const void *const *opt, int nopt) {
+    for (int i = 0; i < nreq; ++i)
+        if (!req[i]) return SSD_ERR_NULL;
+    for (int i = 0; i < nreq; ++i)
+        if (!aligned(req[i], 16)) return SSD_ERR_ALIGN;
+    for (int i = 0; i < nopt; ++i)
+        if (opt[i] && !aligned(opt[i], 16)) return SSD_ERR_ALIGN;
+    return SSD_OK;
+}
+
+// The five steps one after another, intermediates in the workspace.
+ssd_status run_staged(const ssd::Dims &d, const void *x, const void *dt, const float *A,
+                      const void *B, const void *C, const float *D, const float *init, void *y,
+                      float *fin, void *ws, hipStream_t st) {
+    if (d.b == 0) return SSD_OK;
+    if (d.nc == 0) return hip_status(ssd::launch_zero_state(d, init, fin, st));
+    const WsLayout w = ws_layout(d);
+    char *base = (char *)ws;
+    float *cs = (float *)(base + w.cs);
+    void *cb = base + w.cb;
+    float *S = (float *)(base + w.S);
+    hipError_t e;
+    if ((e = ssd::launch_chunk_cumsum(d, dt, A, cs, st)) != hipSuccess) return hip_status(e);
+    if ((e = ssd::launch_chunk_cb(d, B, C, cb, st)) != hipSuccess) return hip_status(e);
+    if ((e = ssd::launch_chunk_state(d, x, B, cs, S, st)) != hipSuccess) return hip_status(e);
+    if ((e = ssd::launch_state_passing(d, S, cs, init, fin, st)) != hipSuccess) return hip_status(e);
+    if ((e = ssd::launch_chunk_scan(d, x, C, cb, cs, S, D, y, st)) != hipSuccess) return hip_status(e);
+    return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ssd_status_string(ssd_status s) {
+    switch (s) {
+    case SSD_OK: return "SSD_OK";
+    case SSD_ERR_NULL: return "SSD_ERR_NULL: a required pointer is NULL";
+    case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE: negative or inconsistent sizes";
+    case SSD_ERR_DTYPE: return "SSD_ERR_DTYPE: dtype must be SSD_F32 or SSD_BF16";
+    case SSD_ERR_ALIGN: return "SSD_ERR_ALIGN: arrays must be 16-byte aligned (workspace 256-byte)";
+    case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing or too small";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: shape outside the compiled set";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP: a HIP call or kernel launch failed";
+    case SSD_ERR_ALIAS: return "SSD_ERR_ALIAS: an output overlaps an input";
+    }
+    return "SSD_ERR_UNKNOWN";
+}
+
+const char *ssd_last_hip_error(void) { return hipGetErrorString(g_last_hip); }
+
+size_t ssd_forward_workspace_bytes(const ssd_dims *dims) {
+    ssd::Dims d;
+    if (check_dims(dims, false, &d) != SSD_OK) return 0;
+    return (size_t)ws_layout(d).total;
+}
+
+ssd_status ssd_validate_forward(const ssd_dims *dims, const void *x, const void *dt,
+                                const float *A, const void *B, const void *C, const float *D,
+                                const float *init_state, const void *y, const float *final_state,
+                                const void *workspace, size_t workspace_bytes) {
+    return validate_forward(dims, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                            workspace_bytes, nullptr);
+}
+
+ssd_status ssd_validate_decode(const ssd_dims *dims, const float *state, const void *x,
+                               const void *dt, const float *A, const void *B, const void *C,
+                               const float *D, const void *y) {
+    return validate_decode(dims, state, x, dt, A, B, C, D, y, nullptr);
+}
+
+ssd_status ssd_forward_staged(const ssd_dims *dims, const void *x, const void *dt,
+                              const float *A, const void *B, const void *C, const float *D,
+                              const float *init_state, void *y, float *final_state,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+    ssd::Dims d;
+    ssd_status st = validate_forward(dims, x, dt, A, B, C, D, init_state, y, final_state,
+                                     workspace, workspace_bytes, &d);
+    if (st != SSD_OK) return st;
+    return run_staged(d, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                      (hipStream_t)stream);
+}
+
+ssd_status ssd_forward(const ssd_dims *dims, const void *x, const void *dt, const float *A,
+                       const void *B, const void *C, const float *D, const float *init_state,
+                       void *y, float *final_state, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    ssd::Dims d;
+    ssd_status st = validate_forward(dims, x, dt, A, B, C, D, init_state, y, final_state,
+                                     workspace, workspace_bytes, &d);
+    if (st != SSD_OK) return st;
+    return run_staged(d, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                      (hipStream_t)stream);
+}
+
+ssd_status ssd_decode_step(const ssd_dims *dims, float *state, const void *x, const void *dt,
+                           const float *A, const void *B, const void *C, const float *D, void *y,
+                           void *stream) {
+    ssd::Dims d;
+    ssd_status st = validate_decode(dims, state, x, dt, A, B, C, D, y, &d);
+    if (st != SSD_OK) return st;
+    return hip_status(ssd::launch_decode(d, state, x, dt, A, B, C, D, y, (hipStream_t)stream));
+}
+
+ssd_status ssd_chunk_cumsum(const ssd_dims *dims, const void *dt, const float *A, float *cs,
+                            void *stream) {
+    ssd::Dims d;
+    ssd_status st = check_dims(dims, false, &d);
+    if (st != SSD_OK) return st;
+    if (d.b * d.nc == 0) return SSD_OK;
+    const void *req[] = {dt, A, cs};
+    if ((st = validate_ptrs(req, 3, nullptr, 0)) != SSD_OK) return st;
+    return hip_status(ssd::launch_chunk_cumsum(d, dt, A, cs, (hipStream_t)stream));
+}
+
+ssd_status ssd_chunk_cb(const ssd_dims *dims, const void *B, const void *C, void *cb,
+                        void *stream) {
+    ssd::Dims d;
+    ssd_status st = check_dims(dims, false, &d);
+    if (st != SSD_OK) return st;
+    if (d.b * d.nc == 0) return SSD_OK;
+    const void *req[] = {B, C, cb};
+    if ((st = validate_ptrs(req, 3, nullptr, 0)) != SSD_OK) return st;
+    return hip_status(ssd::launch_chunk_cb(d, B, C, cb, (hipStream_t)stream));
+}
+
+ssd_status ssd_chunk_state(const ssd_dims *dims, const void *x, const void *B, const float *cs,
+                           float *states, void *stream) {
+    ssd::Dims d;
+    ssd_status st = check_dims(dims, false, &d);
+    if (st != SSD_OK) return st;
+    if (d.b * d.nc == 0) return SSD_OK;
+    const void *req[] = {x, B, cs, states};
+    if ((st = validate_ptrs(req, 4, nullptr, 0)) != SSD_OK) return st;
+    return hip_status(ssd::launch_chunk_state(d, x, B, cs, states, (hipStream_t)stream));
+}
+
+ssd_status ssd_state_passing(const ssd_dims *dims, float *states, const float *cs,
+                             const float *init_state, float *final_state, void *stream) {
+    ssd::Dims d;
+    ssd_status st = check_dims(dims, false, &d);
+    if (st != SSD_OK) return st;
+    if (d.b == 0) return SSD_OK;
+    if (d.nc > 0) {
+        const void *req[] = {states, cs};
+        const void *opt[] = {init_state, final_state};
+        if ((st = validate_ptrs(req, 2, opt, 2)) != SSD_OK) return st;
+    } else {
+        const void *opt[] = {init_state, final_state};
+        if ((st = validate_ptrs(nullptr, 0, opt, 2)) != SSD_OK) return st;
+    }
+    const int64_t sb = d.b * d.H * d.P * d.N * 4;
+    if (final_state && init_state != final_state &&
+        overlap(range_of(final_state, sb), range_of(init_state, sb)))
+        return SSD_ERR_ALIAS;
+    return hip_status(
+        ssd::launch_state_passing(d, states, cs, init_state, final_state, (hipStream_t)stream));
+}
+
+ssd_status ssd_chunk_scan(const ssd_dims *dims, const void *x, const void *C, const void *cb,
+                          const float *cs, const float *hprev, const float *D, void *y,
+                          void *stream) {
+    ssd::Dims d;
+    ssd_status st = check_dims(dims, false, &d);
+    if (st != SSD_OK) return st;
+    if (d.b * d.nc == 0) return SSD_OK;
+    const void *req[] = {x, C, cb, cs, y};
+    const void *opt[] = {hprev, D};
+    if ((st = validate_ptrs(req, 5, opt, 2)) != SSD_OK) return st;
+    const int64_t ybytes = d.b * d.L * d.H * d.P * esize(d);
+    if (overlap(range_of(y, ybytes), range_of(x, ybytes))) return SSD_ERR_ALIAS;
+    return hip_status(
+        ssd::launch_chunk_scan(d, x, C, cb, cs, hprev, D, y, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Device-side helpers shared by the SSD kernels (gfx950 / CDNA4 only).
+//
+// MFMA conventions used throughout (16 x 16 output tiles, wave64):
+//   lane l, r = l % 16, g = l / 16 (0..3)
+//   A operand: lane holds A[m = r][k in kset(g)]
+//   B operand: lane holds B[k in kset(g)][n = r]
+//   D (4 x f32 per lane): D[m = 4 g + e][n = r], e = 0..3
+// v_mfma_f32_16x16x32_bf16 takes 8 k-values per lane and v_mfma_f32_16x16x4_f32
+// one.  The order of k inside a lane group never matters for a contraction as
+// long as A and B use the same kset(g); the kernels pick contiguous sets
+// (bf16: k = 8 g .. 8 g + 7) so fragments load as one 16-byte vector.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
+
+// Blocks are dealt to the 8 XCDs round-robin (block k runs on XCD k % 8), and
+// each XCD has its own L2.  Work items that share operands (all heads of one
+// chunk share C, B and C B^T) should land on the same XCD, so map block k to
+// a contiguous slice of work items per XCD.  Identity when the count is not a
+// multiple of 8.
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t total) {
+    if (total % 8 != 0) return bid;
+    const int64_t per = total / 8;
+    return (bid % 8) * per + bid / 8;
+}
+
+// Copy a [rows x cols] bf16 tile from global memory (row stride `ld`
+// elements) into LDS transposed: dst[c * dstride + r] = src[r * ld + c],
+// optionally times scale[r] (rounded back to bf16).  Rows >= nvalid read as
+// zero.  rows % 4 == 0, cols % 8 == 0, dstride % 4 == 0.  Each thread moves
+// 4 x 8 blocks: four 16-byte loads, a register transpose with byte
+// permutes, eight 8-byte LDS stores.
+template <bool SCALE>
+__device__ __forceinline__ void stage_transposed_bf16(const bf16 *__restrict__ src, int64_t ld,
+                                                      int rows, int cols, int nvalid,
+                                                      bf16 *dst, int dstride,
+                                                      const float *scale) {
+    const int nbc = cols / 8, nbr = rows / 4;
+    for (int blk = threadIdx.x; blk < nbr * nbc; blk += blockDim.x) {
+        const int br = blk / nbc, bc = blk - br * nbc;
+        const int r0 = br * 4, c0 = bc * 8;
+        u32x4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = r0 + k;
+            if (r < nvalid) {
+                v[k] = *(const u32x4 *)(src + (int64_t)r * ld + c0);
+                if constexpr (SCALE) {
+                    bf16x8 t = as_bf16x8(v[k]);
+                    const float w = scale[r];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) t[e] = (bf16)((float)t[e] * w);
+                    v[k] = as_u32x4(t);
+                }
+            } else {
+                v[k] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            // dword m of each row holds columns c0 + 2m (low half) and c0 + 2m + 1 (high half)
+            const uint32_t lo01 = __builtin_amdgcn_perm(v[1][m], v[0][m], 0x05040100u);
+            const uint32_t lo23 = __builtin_amdgcn_perm(v[3][m], v[2][m], 0x05040100u);
+            const uint32_t hi01 = __builtin_amdgcn_perm(v[1][m], v[0][m], 0x07060302u);
+            const uint32_t hi23 = __builtin_amdgcn_perm(v[3][m], v[2][m], 0x07060302u);
+            *(u32x2 *)(dst + (c0 + 2 * m) * dstride + r0) = u32x2{lo01, lo23};
+            *(u32x2 *)(dst + (c0 + 2 * m + 1) * dstride + r0) = u32x2{hi01, hi23};
+        }
+    }
+}
+
+}  // namespace ssd

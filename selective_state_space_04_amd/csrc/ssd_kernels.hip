@@ -1,0 +1,644 @@
+// SSD layer kernels for gfx950 (MI355X): the steps of the chunked algorithm
+// and the single-token decode step.
+//
+// Notation (per batch row b, head h, group g = h / (H / G), chunk c covering
+// steps s = c Q .. s + q - 1 with q = min(Q, L - s)):
+//   cs_i      = sum_{k <= i} dt_{s+k} A_h            (decay prefix, log domain)
+//   G_ij      = C_{s+i} . B_{s+j}                      (shared by a group's heads)
+//   S_c       = sum_j exp(cs_{q-1} - cs_j) x_{s+j} B_{s+j}^T        [P, N]
+//   hprev_c   = state entering chunk c
+//   y_{s+i}   = sum_{j <= i} exp(cs_i - cs_j) G_ij x_{s+j}
+//               + exp(cs_i) hprev_c C_{s+i} + D_h x_{s+i}
+// (Mamba-2 review, docsaid.org: section "A を一つの数に簡略化する" for
+// M = L o (C B^T) with L_ij the product of decays; section "2つのルートを半分ずつ"
+// for the block split into a quadratic part inside blocks and states across
+// them.)  The within-chunk weights exp(cs_{q-1} - cs_j) on the chunk state are
+// what makes the split exact.
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+// ---------------------------------------------------------------------------
+// Decay prefix: one wave per (b, h, c).  Each lane sums up to 4 consecutive
+// steps serially, then a log-depth inclusive scan across the 64 lanes joins
+// them.  Entries past a short chunk's end repeat its last value (dt treated
+// as 0 there), so every consumer sees finite numbers.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(64) void k_chunk_cumsum(const T *__restrict__ dt,
+                                                     const float *__restrict__ A,
+                                                     float *__restrict__ cs, int64_t L, int H,
+                                                     int Q, int nc) {
+    const int c = blockIdx.x, h = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int64_t s = (int64_t)c * Q;
+    const int q = (int)min<int64_t>(Q, L - s);
+    const float Ah = A[h];
+    const int per = (Q + 63) / 64;  // <= 4
+    float v[4];
+    float run = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = lane * per + e;
+        float d = 0.f;
+        if (e < per && i < q) d = to_f32(dt[((b * L) + s + i) * H + h]) * Ah;
+        run += d;
+        v[e] = run;
+    }
+    float tot = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_up(tot, off, 64);
+        if (lane >= off) tot += o;
+    }
+    const float excl = tot - run;
+    float *out = cs + (((int64_t)b * H + h) * nc + c) * Q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = lane * per + e;
+        if (e < per && i < Q) out[i] = v[e] + excl;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// C B^T per (b, c, g): one wave per 16 x 16 tile on or below the diagonal,
+// K = N in MFMA steps.  A operand = C rows (m = i), B operand = B rows
+// (n = j); both are read straight from global memory with the contraction
+// index contiguous.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_chunk_cb(const T *__restrict__ B, const T *__restrict__ C,
+                                                  T *__restrict__ cb, int64_t L, int G, int N,
+                                                  int Q, int nc) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, grp = lane >> 4;
+    const int T16 = Q / 16;
+    const int ntiles = T16 * (T16 + 1) / 2;
+    const int tile = blockIdx.y * 4 + wave;
+    if (tile >= ntiles) return;
+    int ti = (int)((sqrtf(8.f * tile + 1.f) - 1.f) * 0.5f);
+    while ((ti + 1) * (ti + 2) / 2 <= tile) ++ti;
+    while (ti * (ti + 1) / 2 > tile) --ti;
+    const int tj = tile - ti * (ti + 1) / 2;
+    const int64_t bcg = blockIdx.x;
+    const int g = (int)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int c = (int)(bc % nc);
+    const int64_t b = bc / nc;
+    const int64_t s = (int64_t)c * Q;
+    const int64_t irow = s + ti * 16 + r, jrow = s + tj * 16 + r;
+    const bool vi = irow < L, vj = jrow < L;
+    const T *Crow = C + ((b * L + irow) * G + g) * N;
+    const T *Brow = B + ((b * L + jrow) * G + g) * N;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (sizeof(T) == 2) {
+        for (int k0 = 0; k0 < N; k0 += 32) {
+            const int k = k0 + grp * 8;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const u32x4 a = (vi && k < N) ? *(const u32x4 *)(Crow + k) : z;
+            const u32x4 bb = (vj && k < N) ? *(const u32x4 *)(Brow + k) : z;
+            acc = mfma_bf16(as_bf16x8(a), as_bf16x8(bb), acc);
+        }
+    } else {
+        for (int k0 = 0; k0 < N; k0 += 16) {
+            const int k = k0 + grp * 4;
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 a = vi ? *(const f32x4 *)(Crow + k) : z;
+            const f32x4 bb = vj ? *(const f32x4 *)(Brow + k) : z;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = mfma_f32(a[e], bb[e], acc);
+        }
+    }
+    T *out = cb + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        out[(int64_t)(ti * 16 + 4 * grp + e) * Q + tj * 16 + r] = from_f32<T>(acc[e]);
+}
+
+// ---------------------------------------------------------------------------
+// Chunk state S_c^T[n][p] = sum_j B_j[n] (w_j x_j[p]), one workgroup per
+// (b, c, h).  bf16: 64-step slabs of x (pre-scaled by w_j) and B are staged
+// in LDS transposed (step index contiguous) so each MFMA fragment is one
+// 16-byte LDS read.  f32: fragments come straight from global memory (one
+// element per lane per MFMA).  Wave w owns n-tiles w, w + 4, ...
+// ---------------------------------------------------------------------------
+template <typename T, int P, int N>
+__global__ __launch_bounds__(256) void k_chunk_state(const T *__restrict__ x,
+                                                     const T *__restrict__ B,
+                                                     const float *__restrict__ cs,
+                                                     float *__restrict__ S, int64_t L, int H,
+                                                     int G, int Q, int nc) {
+    constexpr int PT = P / 16, NT = N / 16, NTW = (NT + 3) / 4;
+    const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = (int)(wid % H);
+    const int64_t bc = wid / H;
+    const int c = (int)(bc % nc);
+    const int64_t b = bc / nc;
+    const int g = h / (H / G);
+    const int64_t s = (int64_t)c * Q;
+    const int q = (int)min<int64_t>(Q, L - s);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, grp = lane >> 4;
+
+    __shared__ float w_s[256];
+    const float *csc = cs + (((int64_t)b * H + h) * nc + c) * Q;
+    const float cs_last = csc[q - 1];
+    for (int j = threadIdx.x; j < Q; j += 256) w_s[j] = __expf(cs_last - csc[j]);
+    __syncthreads();
+
+    f32x4 acc[NTW][PT];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[t][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const T *xb = x + ((b * L + s) * H + h) * P;
+    const T *Bb = B + ((b * L + s) * G + g) * N;
+    if constexpr (sizeof(T) == 2) {
+        constexpr int SL = 64, LD = SL + 8;
+        __shared__ bf16 xs[P * LD];
+        __shared__ bf16 bs[N * LD];
+        for (int jb = 0; jb < q; jb += SL) {
+            const int nvalid = min(SL, q - jb);
+            stage_transposed_bf16<true>(xb + (int64_t)jb * H * P, (int64_t)H * P, SL, P, nvalid, xs,
+                                        LD, w_s + jb);
+            stage_transposed_bf16<false>(Bb + (int64_t)jb * G * N, (int64_t)G * N, SL, N, nvalid, bs,
+                                         LD, nullptr);
+            __syncthreads();
+#pragma unroll
+            for (int kk = 0; kk < SL; kk += 32) {
+                bf16x8 bx[PT];
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt)
+                    bx[pt] = *(const bf16x8 *)(xs + (pt * 16 + r) * LD + kk + grp * 8);
+#pragma unroll
+                for (int t = 0; t < NTW; ++t) {
+                    const int nt = wave + 4 * t;
+                    if (nt < NT) {
+                        const bf16x8 ab = *(const bf16x8 *)(bs + (nt * 16 + r) * LD + kk + grp * 8);
+#pragma unroll
+                        for (int pt = 0; pt < PT; ++pt) acc[t][pt] = mfma_bf16(ab, bx[pt], acc[t][pt]);
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    } else {
+        for (int j0 = 0; j0 < q; j0 += 16) {
+            float xv[PT][4];
+            bool valid[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = j0 + 4 * grp + e;
+                valid[e] = j < q;
+                const float w = valid[e] ? w_s[j] : 0.f;
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt)
+                    xv[pt][e] = valid[e] ? to_f32(xb[(int64_t)j * H * P + pt * 16 + r]) * w : 0.f;
+            }
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) {
+                const int nt = wave + 4 * t;
+                if (nt < NT) {
+                    float bv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = j0 + 4 * grp + e;
+                        bv[e] = valid[e] ? to_f32(Bb[(int64_t)j * G * N + nt * 16 + r]) : 0.f;
+                    }
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[t][pt] = mfma_f32(bv[e], xv[pt][e], acc[t][pt]);
+                }
+            }
+        }
+    }
+    // acc[t][pt][e] = S^T[n = nt*16 + 4 grp + e][p = pt*16 + r]
+    float *So = S + (((b * nc + c) * H + h) * (int64_t)P) * N;
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+        const int nt = wave + 4 * t;
+        if (nt < NT) {
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt)
+                *(f32x4 *)(So + (int64_t)(pt * 16 + r) * N + nt * 16 + 4 * grp) = acc[t][pt];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Inter-chunk recurrence, in place: S[c] -> hprev[c].  Each thread owns four
+// consecutive state elements of one (b, h) and walks the chunks in order,
+// with the next 8 chunk states loaded ahead (they do not depend on the
+// running state).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_state_passing(float *__restrict__ S,
+                                                       const float *__restrict__ cs,
+                                                       const float *init, float *fin, int64_t L,
+                                                       int H, int PN, int Q, int nc) {
+    const int h = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int e0 = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e0 >= PN) return;
+    const int64_t bh = b * H + h;
+    f32x4 hv = init ? *(const f32x4 *)(init + bh * PN + e0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const float *csb = cs + bh * (int64_t)nc * Q;
+    constexpr int U = 8;
+    for (int c0 = 0; c0 < nc; c0 += U) {
+        f32x4 sv[U];
+        float lam[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u;
+            if (c < nc) {
+                const int last = (int)min<int64_t>(Q, L - (int64_t)c * Q) - 1;
+                lam[u] = __expf(csb[(int64_t)c * Q + last]);
+                sv[u] = *(const f32x4 *)(S + (((b * nc + c) * H + h) * (int64_t)PN) + e0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u;
+            if (c < nc) {
+                *(f32x4 *)(S + (((b * nc + c) * H + h) * (int64_t)PN) + e0) = hv;
+                hv = lam[u] * hv + sv[u];
+            }
+        }
+    }
+    if (fin) *(f32x4 *)(fin + bh * PN + e0) = hv;
+}
+
+// final_state for an empty sequence: a copy of init (or zeros).
+__global__ __launch_bounds__(256) void k_copy_state(const float *init, float *fin, int64_t n) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    const f32x4 v = init ? *(const f32x4 *)(init + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+    *(f32x4 *)(fin + i) = v;
+}
+
+// ---------------------------------------------------------------------------
+// Intra-chunk masked product + output combine, one workgroup per (b, c, h).
+// Computed transposed, Y^T[p][i], so each lane ends up owning one output row
+// i and four consecutive channels p (one 8- or 16-byte store):
+//   off term:  Y^T += h[p][n] C[i][n]      (A = state rows, B = C rows)
+//   scale:     Y^T[:, i] *= exp(cs_i)
+//   intra:     Y^T += x^T[p][j] M^T[j][i], M^T[j][i] = exp(cs_i - cs_j) G[i][j] (j <= i)
+//   skip:      Y^T[p][i] += D_h x[i][p]
+// The 16-wide output tiles are dealt to the four waves in a snake order so
+// the triangular work is balanced.  bf16: x^T and the state (as bf16) are
+// staged in LDS; f32: operands come from global memory.
+// ---------------------------------------------------------------------------
+template <typename T, int P, int N>
+__global__ __launch_bounds__(256) void k_chunk_scan(const T *__restrict__ x, const T *__restrict__ C,
+                                                    const T *__restrict__ cb,
+                                                    const float *__restrict__ cs,
+                                                    const float *__restrict__ hprev,
+                                                    const float *__restrict__ D, T *__restrict__ y,
+                                                    int64_t L, int H, int G, int Q, int nc) {
+    constexpr int PT = P / 16;
+    const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = (int)(wid % H);
+    const int64_t bc = wid / H;
+    const int c = (int)(bc % nc);
+    const int64_t b = bc / nc;
+    const int g = h / (H / G);
+    const int64_t s = (int64_t)c * Q;
+    const int q = (int)min<int64_t>(Q, L - s);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, grp = lane >> 4;
+    const int Qp = (Q + 31) & ~31;
+
+    __shared__ float cs_s[256];
+    const float *csc = cs + (((int64_t)b * H + h) * nc + c) * Q;
+    for (int j = threadIdx.x; j < Qp; j += 256) cs_s[j] = csc[min(j, Q - 1)];
+
+    const T *cbc = cb + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
+    const float *hp = hprev ? hprev + (((b * nc + c) * H + h) * (int64_t)P) * N : nullptr;
+    const float Dh = D ? D[h] : 0.f;
+    const int64_t row0 = (b * L + s) * H + h;  // (row of step s, head h) in x / y
+    const T *Cb = C + ((b * L + s) * G + g) * N;
+
+    constexpr int XLD = 256 + 8, HLD = N + 8;
+    __shared__ bf16 xs[sizeof(T) == 2 ? P * XLD : 1];
+    __shared__ bf16 hs[sizeof(T) == 2 ? P * HLD : 1];
+    if constexpr (sizeof(T) == 2) {
+        stage_transposed_bf16<false>((const bf16 *)x + row0 * P, (int64_t)H * P, Qp, P, q, xs, XLD,
+                                     nullptr);
+        if (hp) {
+            for (int idx = threadIdx.x; idx < P * N / 8; idx += 256) {
+                const int p = idx / (N / 8), n0 = (idx - p * (N / 8)) * 8;
+                const f32x4 a0 = *(const f32x4 *)(hp + (int64_t)p * N + n0);
+                const f32x4 a1 = *(const f32x4 *)(hp + (int64_t)p * N + n0 + 4);
+                bf16x8 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = (bf16)a0[e];
+                    v[e + 4] = (bf16)a1[e];
+                }
+                *(bf16x8 *)(hs + p * HLD + n0) = v;
+            }
+        }
+    }
+    __syncthreads();
+
+    const int T16 = (q + 15) / 16;
+    for (int round = 0;; ++round) {
+        const int I = 4 * round + ((round & 1) ? 3 - wave : wave);
+        if (4 * round >= T16) break;
+        if (I >= T16) continue;
+        const int il = I * 16 + r;  // this lane's output row inside the chunk
+        const bool vi = il < q;
+        const float csi = cs_s[il];
+        f32x4 acc[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        const T *crow = Cb + (int64_t)il * G * N;
+        if (hp) {
+            if constexpr (sizeof(T) == 2) {
+                for (int k0 = 0; k0 < N; k0 += 32) {
+                    const int kk = k0 + grp * 8;
+                    const u32x4 z = {0u, 0u, 0u, 0u};
+                    const bf16x8 bcv = as_bf16x8((vi && kk < N) ? *(const u32x4 *)(crow + kk) : z);
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) {
+                        const bf16x8 ah =
+                            kk < N ? *(const bf16x8 *)(hs + (pt * 16 + r) * HLD + kk) : as_bf16x8(z);
+                        acc[pt] = mfma_bf16(ah, bcv, acc[pt]);
+                    }
+                }
+            } else {
+                for (int k0 = 0; k0 < N; k0 += 16) {
+                    const int kk = k0 + grp * 4;
+                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    const f32x4 c4 = vi ? *(const f32x4 *)(crow + kk) : z;
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) {
+                        const f32x4 h4 = *(const f32x4 *)(hp + (int64_t)(pt * 16 + r) * N + kk);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[pt] = mfma_f32(h4[e], c4[e], acc[pt]);
+                    }
+                }
+            }
+            const float ei = __expf(csi);
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) acc[pt] *= ei;
+        }
+
+        const T *grow = cbc + (int64_t)il * Q;
+        const int jend = I * 16 + 15;
+        if constexpr (sizeof(T) == 2) {
+            for (int j0 = 0; j0 <= jend; j0 += 32) {
+                const int jl = j0 + grp * 8;
+                bf16x8 bm;
+                if (jl <= il) {
+                    const bf16x8 gv = as_bf16x8(*(const u32x4 *)(grow + jl));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = jl + e;
+                        const float m = (j <= il) ? __expf(csi - cs_s[j]) * (float)gv[e] : 0.f;
+                        bm[e] = (bf16)m;
+                    }
+                } else {
+                    bm = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+                }
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const bf16x8 ax = *(const bf16x8 *)(xs + (pt * 16 + r) * XLD + jl);
+                    acc[pt] = mfma_bf16(ax, bm, acc[pt]);
+                }
+            }
+        } else {
+            for (int j0 = 0; j0 <= jend; j0 += 16) {
+                const int jl = j0 + grp * 4;
+                const f32x4 g4 = *(const f32x4 *)(grow + jl);
+                float m[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = jl + e;
+                    m[e] = (j <= il) ? __expf(csi - cs_s[j]) * g4[e] : 0.f;
+                }
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = jl + e;
+                        const float xa = j < q ? to_f32(x[(row0 + (int64_t)j * H) * P + pt * 16 + r]) : 0.f;
+                        acc[pt] = mfma_f32(xa, m[e], acc[pt]);
+                    }
+                }
+            }
+        }
+
+        if (vi) {
+            const T *xr = x + (row0 + (int64_t)il * H) * P;
+            T *yr = y + (row0 + (int64_t)il * H) * P;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const int p0 = pt * 16 + 4 * grp;
+                if constexpr (sizeof(T) == 2) {
+                    const u32x2 xw = *(const u32x2 *)(xr + p0);
+                    const bf16 *xe = (const bf16 *)&xw;
+                    bf16 o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc[pt][e] + Dh * (float)xe[e]);
+                    *(u32x2 *)(yr + p0) = *(const u32x2 *)o;
+                } else {
+                    const f32x4 xv = *(const f32x4 *)(xr + p0);
+                    *(f32x4 *)(yr + p0) = acc[pt] + Dh * xv;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode step: one workgroup per (b, h).  N / 4 lanes share a state row (one
+// float4 each); rows are processed 8 deep so 8 loads per lane are in flight.
+// The row dot product with C is a butterfly over the row's lanes.
+// ---------------------------------------------------------------------------
+template <typename T, int N>
+__global__ __launch_bounds__(256) void k_decode(float *__restrict__ state, const T *__restrict__ x,
+                                                const T *__restrict__ dt,
+                                                const float *__restrict__ A,
+                                                const T *__restrict__ B, const T *__restrict__ C,
+                                                const float *__restrict__ D, T *__restrict__ y,
+                                                int H, int G, int P) {
+    constexpr int NL = N / 4, RPI = 256 / NL, U = 8;
+    const int64_t bh = blockIdx.x;
+    const int h = (int)(bh % H);
+    const int64_t b = bh / H;
+    const int g = h / (H / G);
+    const int nl = threadIdx.x % NL, slot = threadIdx.x / NL;
+    const float a = __expf(to_f32(dt[bh]) * A[h]);
+    const float Dh = D ? D[h] : 0.f;
+    float bv[4], cv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bv[e] = to_f32(B[(b * G + g) * N + nl * 4 + e]);
+        cv[e] = to_f32(C[(b * G + g) * N + nl * 4 + e]);
+    }
+    float *st = state + bh * (int64_t)P * N;
+    const T *xp = x + bh * P;
+    T *yp = y + bh * P;
+    for (int p0 = 0; p0 < P; p0 += RPI * U) {
+        f32x4 hv[U];
+        float xv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 + u * RPI + slot;
+            if (p < P) {
+                hv[u] = *(const f32x4 *)(st + (int64_t)p * N + nl * 4);
+                xv[u] = to_f32(xp[p]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 + u * RPI + slot;
+            float part = 0.f;
+            if (p < P) {
+                f32x4 nh;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    nh[e] = a * hv[u][e] + xv[u] * bv[e];
+                    part += nh[e] * cv[e];
+                }
+                *(f32x4 *)(st + (int64_t)p * N + nl * 4) = nh;
+            }
+#pragma unroll
+            for (int off = NL / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+            if (nl == 0 && p < P) yp[p] = from_f32<T>(part + Dh * xv[u]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.
+// ---------------------------------------------------------------------------
+#define SSD_DISPATCH_PN(P_, N_, ...)                                              \
+    do {                                                                          \
+        switch (P_) {                                                             \
+        case 16: { constexpr int PP = 16; SSD_DISPATCH_N(N_, __VA_ARGS__); } break; \
+        case 32: { constexpr int PP = 32; SSD_DISPATCH_N(N_, __VA_ARGS__); } break; \
+        case 64: { constexpr int PP = 64; SSD_DISPATCH_N(N_, __VA_ARGS__); } break; \
+        case 128: { constexpr int PP = 128; SSD_DISPATCH_N(N_, __VA_ARGS__); } break; \
+        default: return hipErrorInvalidValue;                                     \
+        }                                                                         \
+    } while (0)
+#define SSD_DISPATCH_N(N_, ...)                                                   \
+    switch (N_) {                                                                 \
+    case 16: { constexpr int NN = 16; __VA_ARGS__; } break;                       \
+    case 32: { constexpr int NN = 32; __VA_ARGS__; } break;                       \
+    case 64: { constexpr int NN = 64; __VA_ARGS__; } break;                       \
+    case 128: { constexpr int NN = 128; __VA_ARGS__; } break;                     \
+    case 256: { constexpr int NN = 256; __VA_ARGS__; } break;                     \
+    default: return hipErrorInvalidValue;                                         \
+    }
+
+hipError_t launch_chunk_cumsum(const Dims &d, const void *dt, const float *A, float *cs,
+                               hipStream_t st) {
+    if (d.b == 0 || d.nc == 0) return hipSuccess;
+    dim3 grid((unsigned)d.nc, (unsigned)d.H, (unsigned)d.b);
+    if (d.dtype == 1)
+        k_chunk_cumsum<bf16><<<grid, 64, 0, st>>>((const bf16 *)dt, A, cs, d.L, (int)d.H, (int)d.Q,
+                                                  (int)d.nc);
+    else
+        k_chunk_cumsum<float><<<grid, 64, 0, st>>>((const float *)dt, A, cs, d.L, (int)d.H,
+                                                   (int)d.Q, (int)d.nc);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_cb(const Dims &d, const void *B, const void *C, void *cb, hipStream_t st) {
+    if (d.b == 0 || d.nc == 0) return hipSuccess;
+    const int T16 = (int)(d.Q / 16);
+    const int ntiles = T16 * (T16 + 1) / 2;
+    dim3 grid((unsigned)(d.b * d.nc * d.G), (unsigned)((ntiles + 3) / 4));
+    if (d.dtype == 1)
+        k_chunk_cb<bf16><<<grid, 256, 0, st>>>((const bf16 *)B, (const bf16 *)C, (bf16 *)cb, d.L,
+                                               (int)d.G, (int)d.N, (int)d.Q, (int)d.nc);
+    else
+        k_chunk_cb<float><<<grid, 256, 0, st>>>((const float *)B, (const float *)C, (float *)cb,
+                                                d.L, (int)d.G, (int)d.N, (int)d.Q, (int)d.nc);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_state(const Dims &d, const void *x, const void *B, const float *cs,
+                              float *S, hipStream_t st) {
+    if (d.b == 0 || d.nc == 0) return hipSuccess;
+    const unsigned grid = (unsigned)(d.b * d.nc * d.H);
+    SSD_DISPATCH_PN(d.P, d.N, {
+        if (d.dtype == 1)
+            k_chunk_state<bf16, PP, NN><<<grid, 256, 0, st>>>((const bf16 *)x, (const bf16 *)B, cs,
+                                                             S, d.L, (int)d.H, (int)d.G, (int)d.Q,
+                                                             (int)d.nc);
+        else
+            k_chunk_state<float, PP, NN><<<grid, 256, 0, st>>>((const float *)x, (const float *)B,
+                                                              cs, S, d.L, (int)d.H, (int)d.G,
+                                                              (int)d.Q, (int)d.nc);
+    });
+    return hipGetLastError();
+}
+
+hipError_t launch_state_passing(const Dims &d, float *S, const float *cs, const float *init,
+                                float *fin, hipStream_t st) {
+    if (d.b == 0) return hipSuccess;
+    const int PN = (int)(d.P * d.N);
+    if (d.nc == 0) {
+        if (!fin) return hipSuccess;
+        const int64_t n = d.b * d.H * PN;
+        k_copy_state<<<(unsigned)((n / 4 + 255) / 256), 256, 0, st>>>(init, fin, n);
+        return hipGetLastError();
+    }
+    dim3 grid((unsigned)((PN / 4 + 255) / 256), (unsigned)d.H, (unsigned)d.b);
+    k_state_passing<<<grid, 256, 0, st>>>(S, cs, init, fin, d.L, (int)d.H, PN, (int)d.Q,
+                                          (int)d.nc);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_state(const Dims &d, const float *init, float *fin, hipStream_t st) {
+    if (d.b == 0 || !fin) return hipSuccess;
+    const int64_t n = d.b * d.H * d.P * d.N;
+    k_copy_state<<<(unsigned)((n / 4 + 255) / 256), 256, 0, st>>>(init, fin, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_scan(const Dims &d, const void *x, const void *C, const void *cb,
+                             const float *cs, const float *hprev, const float *D, void *y,
+                             hipStream_t st) {
+    if (d.b == 0 || d.nc == 0) return hipSuccess;
+    const unsigned grid = (unsigned)(d.b * d.nc * d.H);
+    SSD_DISPATCH_PN(d.P, d.N, {
+        if (d.dtype == 1)
+            k_chunk_scan<bf16, PP, NN><<<grid, 256, 0, st>>>(
+                (const bf16 *)x, (const bf16 *)C, (const bf16 *)cb, cs, hprev, D, (bf16 *)y, d.L,
+                (int)d.H, (int)d.G, (int)d.Q, (int)d.nc);
+        else
+            k_chunk_scan<float, PP, NN><<<grid, 256, 0, st>>>(
+                (const float *)x, (const float *)C, (const float *)cb, cs, hprev, D, (float *)y,
+                d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc);
+    });
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const Dims &d, float *state, const void *x, const void *dt,
+                         const float *A, const void *B, const void *C, const float *D, void *y,
+                         hipStream_t st) {
+    if (d.b == 0) return hipSuccess;
+    const unsigned grid = (unsigned)(d.b * d.H);
+    SSD_DISPATCH_N(d.N, {
+        if (d.dtype == 1)
+            k_decode<bf16, NN><<<grid, 256, 0, st>>>(state, (const bf16 *)x, (const bf16 *)dt, A,
+                                                    (const bf16 *)B, (const bf16 *)C, D, (bf16 *)y,
+                                                    (int)d.H, (int)d.G, (int)d.P);
+        else
+            k_decode<float, NN><<<grid, 256, 0, st>>>(state, (const float *)x, (const float *)dt, A,
+                                                     (const float *)B, (const float *)C, D,
+                                                     (float *)y, (int)d.H, (int)d.G, (int)d.P);
+    });
+    return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -1,0 +1,30 @@
+// Host-side launchers of the SSD kernels (internal to libssd_mi355x.so).
+// Shapes are validated by the C-ABI layer before any launcher is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+struct Dims {
+    int64_t b, L, H, P, N, G, Q, nc;
+    int dtype;  // 0 = f32, 1 = bf16
+};
+
+hipError_t launch_chunk_cumsum(const Dims &d, const void *dt, const float *A, float *cs,
+                               hipStream_t st);
+hipError_t launch_chunk_cb(const Dims &d, const void *B, const void *C, void *cb, hipStream_t st);
+hipError_t launch_chunk_state(const Dims &d, const void *x, const void *B, const float *cs,
+                              float *S, hipStream_t st);
+hipError_t launch_state_passing(const Dims &d, float *S, const float *cs, const float *init,
+                                float *fin, hipStream_t st);
+hipError_t launch_chunk_scan(const Dims &d, const void *x, const void *C, const void *cb,
+                             const float *cs, const float *hprev, const float *D, void *y,
+                             hipStream_t st);
+hipError_t launch_decode(const Dims &d, float *state, const void *x, const void *dt,
+                         const float *A, const void *B, const void *C, const float *D, void *y,
+                         hipStream_t st);
+hipError_t launch_zero_state(const Dims &d, const float *init, float *fin, hipStream_t st);
+
+}  // namespace ssd

@@ -1,0 +1,183 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/ssd.h declares, and
+reject bad arguments on the host -- before any HIP call -- with the status
+the header documents.  The validators never dereference the pointers, so
+fake, suitably aligned addresses stand in for device buffers here.
+"""
+import ctypes
+import subprocess
+
+import pytest
+
+import selective_state_space_04_amd as ssd
+
+LIB = ssd.lib
+
+
+def dims(**kw):
+    base = dict(batch=2, seqlen=100, nheads=4, headdim=64, dstate=128, ngroups=2, chunk=64,
+                dtype=ssd.BF16)
+    base.update(kw)
+    return ssd.make_dims(**base)
+
+
+class Bufs:
+    """Disjoint fake device ranges, 4 KiB aligned, far apart."""
+
+    def __init__(self):
+        self.next = 1 << 40
+
+    def take(self, nbytes=0):
+        p = self.next
+        self.next += ((nbytes + (1 << 30)) >> 20) << 20
+        return p
+
+
+def fwd_args(d, **over):
+    b = Bufs()
+    ws = ssd.workspace_bytes(d)
+    args = dict(x=b.take(), dt=b.take(), A=b.take(), B=b.take(), C=b.take(), D=b.take(), init=b.take(),
+                y=b.take(), fin=b.take(), ws=b.take(), ws_bytes=ws)
+    args.update(over)
+    return args
+
+
+def vfwd(d, a):
+    return LIB.ssd_validate_forward(ctypes.byref(d), a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"],
+                                    a["init"], a["y"], a["fin"], a["ws"], a["ws_bytes"])
+
+
+def test_exports_every_declared_symbol():
+    names = ssd.header_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(LIB, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_status_strings():
+    for code, name in ssd.STATUS.items():
+        assert LIB.ssd_status_string(code).decode().startswith(name)
+    assert LIB.ssd_status_string(99).decode() == "SSD_ERR_UNKNOWN"
+
+
+def test_valid_forward_passes():
+    d = dims()
+    assert vfwd(d, fwd_args(d)) == 0
+    assert vfwd(d, fwd_args(d, D=None, init=None, fin=None)) == 0
+
+
+def test_workspace_bytes():
+    d = dims(batch=2, seqlen=100, nheads=4, headdim=64, dstate=128, ngroups=2, chunk=64)
+    nc = 2
+    cs = 2 * 4 * nc * 64 * 4
+    cb = 2 * nc * 2 * 64 * 64 * 2
+    S = 2 * nc * 4 * 64 * 128 * 4
+    al = lambda v: (v + 255) // 256 * 256
+    assert ssd.workspace_bytes(d) == al(al(al(cs) + cb) + S)
+    assert ssd.workspace_bytes(dims(seqlen=0)) == 0
+    assert ssd.workspace_bytes(dims(headdim=48)) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dtype", 2, "SSD_ERR_DTYPE"),
+    ("batch", -1, "SSD_ERR_SHAPE"),
+    ("seqlen", -5, "SSD_ERR_SHAPE"),
+    ("nheads", 0, "SSD_ERR_SHAPE"),
+    ("ngroups", 3, "SSD_ERR_SHAPE"),
+    ("chunk", 0, "SSD_ERR_SHAPE"),
+    ("headdim", 48, "SSD_ERR_UNSUPPORTED"),
+    ("headdim", 256, "SSD_ERR_UNSUPPORTED"),
+    ("dstate", 8, "SSD_ERR_UNSUPPORTED"),
+    ("dstate", 512, "SSD_ERR_UNSUPPORTED"),
+    ("chunk", 24, "SSD_ERR_UNSUPPORTED"),
+    ("chunk", 512, "SSD_ERR_UNSUPPORTED"),
+    ("batch", 70000, "SSD_ERR_UNSUPPORTED"),
+])
+def test_bad_dims(field, value, status):
+    d = dims(**{field: value})
+    good = dims()
+    a = fwd_args(good)
+    assert ssd.STATUS[vfwd(d, a)] == status
+
+
+def test_null_dims():
+    a = fwd_args(dims())
+    assert LIB.ssd_validate_forward(None, a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["init"],
+                                    a["y"], a["fin"], a["ws"], a["ws_bytes"]) == 1
+
+
+@pytest.mark.parametrize("name", ["x", "dt", "A", "B", "C", "y"])
+def test_null_required(name):
+    d = dims()
+    assert ssd.STATUS[vfwd(d, fwd_args(d, **{name: None}))] == "SSD_ERR_NULL"
+
+
+def test_empty_sequence_allows_null_arrays():
+    d = dims(seqlen=0)
+    assert vfwd(d, fwd_args(d, x=None, dt=None, B=None, C=None, y=None, ws=None, ws_bytes=0)) == 0
+
+
+@pytest.mark.parametrize("name", ["x", "dt", "A", "B", "C", "D", "init", "y", "fin"])
+def test_misaligned(name):
+    d = dims()
+    a = fwd_args(d)
+    a[name] += 8
+    assert ssd.STATUS[vfwd(d, a)] == "SSD_ERR_ALIGN"
+
+
+def test_workspace_checks():
+    d = dims()
+    a = fwd_args(d)
+    assert ssd.STATUS[vfwd(d, dict(a, ws_bytes=a["ws_bytes"] - 1))] == "SSD_ERR_WORKSPACE"
+    assert ssd.STATUS[vfwd(d, dict(a, ws=None))] == "SSD_ERR_WORKSPACE"
+    assert ssd.STATUS[vfwd(d, dict(a, ws=a["ws"] + 128))] == "SSD_ERR_ALIGN"
+
+
+def test_aliasing():
+    d = dims()
+    a = fwd_args(d)
+    assert ssd.STATUS[vfwd(d, dict(a, y=a["x"]))] == "SSD_ERR_ALIAS"
+    assert ssd.STATUS[vfwd(d, dict(a, y=a["C"] + 16))] == "SSD_ERR_ALIAS"
+    assert ssd.STATUS[vfwd(d, dict(a, fin=a["D"]))] == "SSD_ERR_ALIAS"
+    assert ssd.STATUS[vfwd(d, dict(a, ws=a["x"]))] == "SSD_ERR_ALIAS"
+    # final_state may be init_state itself, but not a shifted view of it
+    assert vfwd(d, dict(a, fin=a["init"])) == 0
+    assert ssd.STATUS[vfwd(d, dict(a, fin=a["init"] + 256))] == "SSD_ERR_ALIAS"
+
+
+def test_decode_validation():
+    d = dims(seqlen=1)
+    b = Bufs()
+    ptrs = [b.take() for _ in range(8)]   # state, x, dt, A, B, C, D, y
+    v = lambda dd, p: LIB.ssd_validate_decode(ctypes.byref(dd), *p)
+    assert v(d, ptrs) == 0
+    assert v(d, ptrs[:6] + [None] + ptrs[7:]) == 0          # D nullable
+    for i in [0, 1, 2, 3, 4, 5, 7]:
+        p = list(ptrs)
+        p[i] = None
+        assert ssd.STATUS[v(d, p)] == "SSD_ERR_NULL", i
+    p = list(ptrs)
+    p[7] = p[0]                                             # y aliases state
+    assert ssd.STATUS[v(d, p)] == "SSD_ERR_ALIAS"
+    p = list(ptrs)
+    p[1] += 2
+    assert ssd.STATUS[v(d, p)] == "SSD_ERR_ALIGN"
+    assert ssd.STATUS[v(dims(dstate=24), ptrs)] == "SSD_ERR_UNSUPPORTED"
+
+
+def test_entry_points_reject_before_launch():
+    """Errors come back from the real entry points without touching a device."""
+    d = dims(headdim=48)
+    a = fwd_args(dims())
+    st = LIB.ssd_forward(ctypes.byref(d), a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["init"],
+                         a["y"], a["fin"], a["ws"], a["ws_bytes"], None)
+    assert ssd.STATUS[st] == "SSD_ERR_UNSUPPORTED"
+    assert ssd.STATUS[LIB.ssd_chunk_cumsum(ctypes.byref(dims()), None, a["A"], a["ws"], None)] == "SSD_ERR_NULL"
+    assert ssd.STATUS[LIB.ssd_chunk_scan(ctypes.byref(dims()), a["x"], a["C"], a["ws"], a["ws"], None, None,
+                                         a["x"], None)] == "SSD_ERR_ALIAS"
+    assert ssd.STATUS[LIB.ssd_decode_step(ctypes.byref(dims(dtype=5)), *([a["x"]] * 8), None, None)] == \
+        "SSD_ERR_DTYPE"

@@ -1,0 +1,309 @@
+"""GPU parity: every kernel of the HIP path, called through the C ABI, against
+the float64 CPU oracle on the same seeded inputs.
+
+Error metric: relative L2 error ||gpu - oracle|| / ||oracle|| per
+(batch, head) slice (y: the [L, P] slice; states: the [P, N] slice); a test
+passes when the worst slice is within the tolerance.  Tolerances: 1e-5 for
+float32 inputs, 2e-2 for bfloat16 inputs with float32 accumulation (the same
+bound for y and for the final state).  Intermediates use the tolerances
+stated at each test.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ssd_inputs as si
+from oracle import chunked
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def ssd():
+    import selective_state_space_04_amd as m
+    return m
+
+
+DEV = "cuda:0"
+
+
+def dev(t):
+    return None if t is None else t.to(DEV)
+
+
+def f64(t):
+    return None if t is None else t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def worst_rel(a, r, kind):
+    a, r = np.asarray(a, np.float64), np.asarray(r, np.float64)
+    if kind == "y":        # [b, L, H, P] -> slices (b, h)
+        b, L, H, P = r.shape
+        a = a.transpose(0, 2, 1, 3).reshape(b * H, -1)
+        r = r.transpose(0, 2, 1, 3).reshape(b * H, -1)
+    else:                  # [..., P, N] -> slices over the leading axes
+        a = a.reshape(-1, a.shape[-2] * a.shape[-1])
+        r = r.reshape(-1, r.shape[-2] * r.shape[-1])
+    num = np.linalg.norm(a - r, axis=1)
+    den = np.maximum(np.linalg.norm(r, axis=1), 1e-30)
+    return float(np.max(num / den)) if len(num) else 0.0
+
+
+def small(dtype="f32", **kw):
+    base = dict(name="small", batch=2, seqlen=300, nheads=4, headdim=32, dstate=64, ngroups=2,
+                chunk=64, dtype=dtype, d_mode="normal", init_mode="normal", seed=7)
+    base.update(kw)
+    return si.Workload(**base)
+
+
+def run_forward(ssd, inp, chunk, staged=False, **kw):
+    out = ssd.forward(dev(inp["x"]), dev(inp["dt"]), dev(inp["A"]), dev(inp["B"]), dev(inp["C"]),
+                      dev(inp["D"]), dev(inp["init"]), chunk=chunk, staged=staged, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_forward(inp, chunk=0):
+    return oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["init"],
+                          chunk=chunk)
+
+
+# ------------------------------------------------------------------ the steps
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_cumsum(ssd, dtype):
+    w = small(dtype)
+    inp = si.make_forward_inputs(w)
+    cs = ssd.chunk_cumsum(dev(inp["dt"]), dev(inp["A"]), w.chunk).cpu().numpy()
+    ref = chunked.chunk_cumsum(inp["dt"], inp["A"], w.chunk)
+    valid = ~np.isnan(ref)
+    err = np.abs(cs[valid] - ref[valid]) / np.maximum(np.abs(ref[valid]), 1e-3)
+    assert err.max() < 1e-5
+    last = ref[:, :, -1, (w.seqlen - 1) % w.chunk]
+    assert np.allclose(cs[:, :, -1, (w.seqlen % w.chunk):], last[..., None], rtol=1e-6)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_cb(ssd, dtype):
+    w = small(dtype)
+    inp = si.make_forward_inputs(w)
+    cb = ssd.chunk_cb(dev(inp["B"]), dev(inp["C"]), w.chunk, nheads=w.nheads).float().cpu().numpy()
+    ref = chunked.chunk_cb(inp["C"], inp["B"], w.chunk)
+    low = np.tril(np.ones((w.chunk, w.chunk), bool))
+    a, r = cb[..., low], ref[..., low]
+    tol = 1e-5 if dtype == "f32" else 8e-3   # bf16 output rounding of each entry
+    assert np.linalg.norm(a - r) / np.linalg.norm(r) < tol
+    assert np.all(np.abs(a - r) <= tol * 4 * np.abs(r) + 1e-6)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_state(ssd, dtype):
+    w = small(dtype)
+    inp = si.make_forward_inputs(w)
+    cs_gpu = ssd.chunk_cumsum(dev(inp["dt"]), dev(inp["A"]), w.chunk)
+    S = ssd.chunk_state(dev(inp["x"]), dev(inp["B"]), cs_gpu, w.chunk).cpu().numpy()
+    cs = chunked.chunk_cumsum(inp["dt"], inp["A"], w.chunk)
+    ref = chunked.chunk_state(inp["x"], inp["B"], cs, w.chunk)
+    assert worst_rel(S, ref, "state") < TOL[dtype]
+
+
+def test_state_passing(ssd):
+    """Fed the oracle's chunk states and prefix (as float32), the kernel must
+    reproduce the oracle's boundary states and final state."""
+    w = small("f32")
+    inp = si.make_forward_inputs(w)
+    cs = chunked.chunk_cumsum(inp["dt"], inp["A"], w.chunk)
+    S = chunked.chunk_state(inp["x"], inp["B"], cs, w.chunk)
+    cs32 = np.where(np.isnan(cs), 0.0, cs)
+    for c in range(cs.shape[2]):   # padded entries repeat the last valid one
+        q = min(w.chunk, w.seqlen - c * w.chunk)
+        cs32[:, :, c, q:] = cs[:, :, c, q - 1 : q]
+    hprev, fin = ssd.state_passing(dev(torch.tensor(S, dtype=torch.float32)),
+                                   dev(torch.tensor(cs32, dtype=torch.float32)), w.seqlen, w.chunk,
+                                   init_state=dev(inp["init"]))
+    _, final, bnd = oracle_forward(inp, chunk=w.chunk)
+    assert worst_rel(hprev.cpu().numpy(), bnd, "state") < 1e-5
+    assert worst_rel(fin.cpu().numpy(), final, "state") < 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_scan_intra_only(ssd, dtype):
+    """With no carried state and no skip term the scan is the masked
+    quadratic form inside each chunk."""
+    w = small(dtype)
+    inp = si.make_forward_inputs(w)
+    cs_gpu = ssd.chunk_cumsum(dev(inp["dt"]), dev(inp["A"]), w.chunk)
+    cb_gpu = ssd.chunk_cb(dev(inp["B"]), dev(inp["C"]), w.chunk, nheads=w.nheads)
+    y = ssd.chunk_scan(dev(inp["x"]), dev(inp["C"]), cb_gpu, cs_gpu, None, None, w.chunk)
+    cs = chunked.chunk_cumsum(inp["dt"], inp["A"], w.chunk)
+    ref = chunked.chunk_scan_intra(chunked.chunk_cb(inp["C"], inp["B"], w.chunk), cs, inp["x"], w.chunk)
+    assert worst_rel(f64(y), ref, "y") < TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_scan_with_state(ssd, dtype):
+    """Given the oracle's boundary states, intra + state term + skip = y."""
+    w = small(dtype)
+    inp = si.make_forward_inputs(w)
+    y_ref, _, bnd = oracle_forward(inp, chunk=w.chunk)
+    cs_gpu = ssd.chunk_cumsum(dev(inp["dt"]), dev(inp["A"]), w.chunk)
+    cb_gpu = ssd.chunk_cb(dev(inp["B"]), dev(inp["C"]), w.chunk, nheads=w.nheads)
+    y = ssd.chunk_scan(dev(inp["x"]), dev(inp["C"]), cb_gpu, cs_gpu,
+                       dev(torch.tensor(bnd, dtype=torch.float32)), dev(inp["D"]), w.chunk)
+    assert worst_rel(f64(y), y_ref, "y") < TOL[dtype]
+
+
+# ------------------------------------------------------------------ forward
+@pytest.mark.parametrize("staged", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [16, 48, 64, 128, 256])
+def test_forward_small(ssd, dtype, chunk, staged):
+    w = small(dtype, chunk=chunk)
+    inp = si.make_forward_inputs(w)
+    y, fin = run_forward(ssd, inp, chunk, staged=staged)
+    y_ref, f_ref = oracle_forward(inp)
+    assert worst_rel(f64(y), y_ref, "y") < TOL[dtype]
+    assert worst_rel(f64(fin), f_ref, "state") < TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("P", [16, 32, 64, 128])
+@pytest.mark.parametrize("N", [16, 32, 64, 128, 256])
+def test_forward_shapes(ssd, dtype, P, N):
+    w = small(dtype, batch=1, seqlen=77, nheads=2, headdim=P, dstate=N, ngroups=1, chunk=32, seed=P * 1000 + N)
+    inp = si.make_forward_inputs(w)
+    y, fin = run_forward(ssd, inp, w.chunk)
+    y_ref, f_ref = oracle_forward(inp)
+    assert worst_rel(f64(y), y_ref, "y") < TOL[dtype]
+    assert worst_rel(f64(fin), f_ref, "state") < TOL[dtype]
+
+
+@pytest.mark.parametrize("L", [1, 10, 16, 63, 64, 65])
+def test_forward_short_and_ragged(ssd, L):
+    w = small("f32", seqlen=L, chunk=64)
+    inp = si.make_forward_inputs(w)
+    y, fin = run_forward(ssd, inp, 64)
+    y_ref, f_ref = oracle_forward(inp)
+    assert worst_rel(f64(y), y_ref, "y") < 1e-5
+    assert worst_rel(f64(fin), f_ref, "state") < 1e-5
+
+
+def test_forward_empty(ssd):
+    w = small("f32", seqlen=0)
+    inp = si.make_forward_inputs(w)
+    y, fin = run_forward(ssd, inp, 64)
+    assert y.shape[1] == 0
+    assert torch.equal(fin.cpu(), inp["init"])
+    w = small("f32", seqlen=0, init_mode="zero")
+    y, fin = run_forward(ssd, si.make_forward_inputs(w), 64)
+    assert torch.count_nonzero(fin) == 0
+    w = small("f32", batch=0)
+    y, fin = run_forward(ssd, si.make_forward_inputs(w), 64)
+    assert y.numel() == 0 and fin.numel() == 0
+
+
+def test_worked_example_on_gpu(ssd):
+    """The four-token example printed on the Mamba-2 review page, embedded in
+    the smallest compiled shape (P = N = 16) by zero padding."""
+    import json, os
+    ex = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")))
+    x = torch.zeros(1, 4, 1, 16)
+    x[0, :, 0, 0] = torch.tensor(ex["x"])
+    B = torch.zeros(1, 4, 1, 16)
+    C = torch.zeros(1, 4, 1, 16)
+    B[0, :, 0, :2] = torch.tensor(ex["B"], dtype=torch.float32)
+    C[0, :, 0, :2] = torch.tensor(ex["C"], dtype=torch.float32)
+    dt = -torch.log(torch.tensor(ex["a"], dtype=torch.float32)).reshape(1, 4, 1)
+    A = torch.tensor([-1.0])
+    for chunk in (16, 32):
+        y, fin = ssd.forward(dev(x), dev(dt), dev(A), dev(B), dev(C), chunk=chunk)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(y[0, :, 0, 0].cpu().numpy(), ex["y_printed"], atol=1e-6, rtol=0)
+        np.testing.assert_allclose(fin[0, 0, 0, :2].cpu().numpy(), ex["final_state_derived"], atol=1e-6)
+        assert torch.count_nonzero(y[0, :, 0, 1:]) == 0
+
+
+def test_split_call_and_inplace_carry(ssd):
+    """forward(0:L) == forward(0:k) then forward(k:L, init = previous final),
+    with the carry done in place (final_state is init_state)."""
+    w = small("f32", seqlen=333)
+    inp = si.make_forward_inputs(w)
+    y_ref, f_ref = oracle_forward(inp)
+    k = 150
+    part = lambda a, b_: {kk: (v[:, a:b_].contiguous() if kk in ("x", "dt", "B", "C") else v)
+                          for kk, v in inp.items() if kk != "workload"}
+    state = dev(inp["init"]).clone()
+    p1 = part(0, k)
+    y1, _ = ssd.forward(dev(p1["x"]), dev(p1["dt"]), dev(p1["A"]), dev(p1["B"]), dev(p1["C"]), dev(p1["D"]),
+                        state, chunk=64, final_state=state)
+    p2 = part(k, 333)
+    y2, _ = ssd.forward(dev(p2["x"]), dev(p2["dt"]), dev(p2["A"]), dev(p2["B"]), dev(p2["C"]), dev(p2["D"]),
+                        state, chunk=64, final_state=state)
+    torch.cuda.synchronize()
+    y = torch.cat([y1, y2], dim=1)
+    assert worst_rel(f64(y), y_ref, "y") < 1e-5
+    assert worst_rel(f64(state), f_ref, "state") < 1e-5
+
+
+def test_deterministic(ssd):
+    w = small("bf16", seqlen=1000, chunk=128)
+    inp = si.make_forward_inputs(w)
+    y1, f1 = run_forward(ssd, inp, 128)
+    y2, f2 = run_forward(ssd, inp, 128)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [16, 64, 128, 256])
+def test_decode_steps_equal_forward(ssd, dtype, N):
+    w = small(dtype, seqlen=20, dstate=N, headdim=64 if N != 16 else 16)
+    inp = si.make_forward_inputs(w)
+    y_ref, f_ref = oracle_forward(inp)
+    state = dev(inp["init"]).clone()
+    ys = []
+    for t in range(w.seqlen):
+        ys.append(ssd.decode_step(state, dev(inp["x"][:, t].contiguous()), dev(inp["dt"][:, t].contiguous()),
+                                  dev(inp["A"]), dev(inp["B"][:, t].contiguous()),
+                                  dev(inp["C"][:, t].contiguous()), dev(inp["D"])))
+    torch.cuda.synchronize()
+    y = torch.stack(ys, dim=1)
+    assert worst_rel(f64(y), y_ref, "y") < TOL[dtype]
+    assert worst_rel(f64(state), f_ref, "state") < TOL[dtype]
+
+
+# ------------------------------------------------------------------ full-size workloads
+@pytest.mark.parametrize("idx", [0, 1, 2, 3])
+def test_workload_forward_full(ssd, idx):
+    w = si.WORKLOADS[idx]
+    inp = si.make_forward_inputs(w)
+    print(f"workload {idx} {w.name}: gpu forward", flush=True)
+    y, fin = run_forward(ssd, inp, w.chunk)
+    y, fin = f64(y), f64(fin)
+    print(f"workload {idx}: oracle ({oracle.num_threads()} threads)", flush=True)
+    y_ref, f_ref = oracle_forward(inp)
+    ey, ef = worst_rel(y, y_ref, "y"), worst_rel(fin, f_ref, "state")
+    print(f"workload {idx}: worst rel err y={ey:.3e} final={ef:.3e}", flush=True)
+    assert ey < TOL[w.dtype]
+    assert ef < TOL[w.dtype]
+
+
+def test_workload_decode_full(ssd):
+    """Decode workload at its full state size ([256, 80, 64, 128] fp32), 8 steps."""
+    w = si.WORKLOADS[4]
+    par = si.make_decode_params(w)
+    state = dev(par["state"]).clone()
+    ref_state = f64(par["state"]).copy()
+    A, D = dev(par["A"]), dev(par["D"])
+    for s in range(8):
+        st = si.make_decode_step_inputs(w, s)
+        y = ssd.decode_step(state, dev(st["x"]), dev(st["dt"]), A, dev(st["B"]), dev(st["C"]), D)
+        y_ref, ref_state = oracle.decode_step(ref_state, st["x"], st["dt"], par["A"], st["B"], st["C"], par["D"])
+        torch.cuda.synchronize()
+        ey = worst_rel(f64(y)[:, None], y_ref[:, None], "y")
+        assert ey < TOL[w.dtype], (s, ey)
+    assert worst_rel(f64(state), ref_state, "state") < TOL[w.dtype]

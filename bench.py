@@ -79,7 +79,14 @@ def kernel_bytes(w) -> dict:
     x = b * L * H * P * e
     BC = b * L * G * N * e
     st = b * H * P * N * 4
+    init_b = st if w.init_mode == "normal" else 0
     return {
+        # single-pass arrangement: prep reads B, C and writes the lower C B^T
+        # tiles and B^T; main reads x, dt, C, the tiles, B^T, A, D (+ init)
+        # and writes y and the final state (the state hand-off between chunks
+        # is not algorithmic traffic)
+        "forward_prep": 2 * BC + cb + b * nc * G * N * Q * e,
+        "forward_main": x + b * L * H * e + BC + cb + b * nc * G * N * Q * e + 2 * H * 4 + init_b + x + st,
         "chunk_cumsum": b * L * H * e + H * 4 + cs,
         "chunk_cb": 2 * BC + cb,
         "chunk_state": x + BC + cs + S,
@@ -161,37 +168,47 @@ def run_forward_bench(args):
 
 
 def kernel_roofline(ssd, w, x, dt, A, B, C, D, init, ws, y, fin, flush, args):
-    """Average duration of each kernel of the forward, measured with HIP
-    events on the launch stream around the same kernels the forward runs,
-    and the roofline of the slowest one."""
+    """Average duration of each kernel launch of the forward, measured with
+    HIP events on the launch stream around the same launches the forward
+    makes (through the per-launch entry points), and the roofline of the
+    slowest one."""
+    import ctypes
+
     import torch
 
     Q, L = w.chunk, w.seqlen
     nc = (L + Q - 1) // Q
     e = 2 if w.dtype == "bf16" else 4
-    # carve the workspace exactly as the library does
-    al = lambda v: (v + 255) // 256 * 256
-    cs_b = w.batch * w.nheads * nc * Q * 4
-    cb_b = w.batch * nc * w.ngroups * Q * Q * e
-    S_b = w.batch * nc * w.nheads * w.headdim * w.dstate * 4
-    cs = ws[: cs_b].view(torch.float32).view(w.batch, w.nheads, nc, Q)
-    cb_off = al(cs_b)
-    cb = ws[cb_off: cb_off + cb_b].view(x.dtype).view(w.batch, nc, w.ngroups, Q, Q)
-    S_off = al(cb_off + cb_b)
-    S = ws[S_off: S_off + S_b].view(torch.float32).view(w.batch, nc, w.nheads, w.headdim, w.dstate)
     stream = ssd._stream()
     dims = ssd.make_dims(w.batch, L, w.nheads, w.headdim, w.dstate, w.ngroups, Q,
                          ssd.BF16 if w.dtype == "bf16" else ssd.F32)
-    import ctypes
     dp = ctypes.byref(dims)
     p = ssd._p
-    seq = [
-        ("chunk_cumsum", lambda: ssd.lib.ssd_chunk_cumsum(dp, p(dt), p(A), p(cs), stream)),
-        ("chunk_cb", lambda: ssd.lib.ssd_chunk_cb(dp, p(B), p(C), p(cb), stream)),
-        ("chunk_state", lambda: ssd.lib.ssd_chunk_state(dp, p(x), p(B), p(cs), p(S), stream)),
-        ("state_passing", lambda: ssd.lib.ssd_state_passing(dp, p(S), p(cs), p(init), p(fin), stream)),
-        ("chunk_scan", lambda: ssd.lib.ssd_chunk_scan(dp, p(x), p(C), p(cb), p(cs), p(S), p(D), p(y), stream)),
-    ]
+    nbytes = ws.numel()
+    single = args.path == "fused" and ssd.lib.ssd_forward_is_single_pass(dp)
+    if single:
+        seq = [
+            ("forward_prep", lambda: ssd.lib.ssd_forward_prep(dp, p(B), p(C), p(ws), nbytes, stream)),
+            ("forward_main", lambda: ssd.lib.ssd_forward_main(dp, p(x), p(dt), p(A), p(B), p(C), p(D), p(init),
+                                                             p(y), p(fin), p(ws), nbytes, stream)),
+        ]
+    else:
+        # carve the workspace exactly as the staged arrangement does
+        al = lambda v: (v + 255) // 256 * 256
+        cs_b = w.batch * w.nheads * nc * Q * 4
+        cb_b = w.batch * nc * w.ngroups * Q * Q * e
+        S_b = w.batch * nc * w.nheads * w.headdim * w.dstate * 4
+        cs = ws[:cs_b]
+        cb = ws[al(cs_b): al(cs_b) + cb_b]
+        S = ws[al(al(cs_b) + cb_b):]
+        seq = [
+            ("chunk_cumsum", lambda: ssd.lib.ssd_chunk_cumsum(dp, p(dt), p(A), p(cs), stream)),
+            ("chunk_cb", lambda: ssd.lib.ssd_chunk_cb(dp, p(B), p(C), p(cb), stream)),
+            ("chunk_state", lambda: ssd.lib.ssd_chunk_state(dp, p(x), p(B), p(cs), p(S), stream)),
+            ("state_passing", lambda: ssd.lib.ssd_state_passing(dp, p(S), p(cs), p(init), p(fin), stream)),
+            ("chunk_scan", lambda: ssd.lib.ssd_chunk_scan(dp, p(x), p(C), p(cb), p(cs), p(S), p(D), p(y),
+                                                          stream)),
+        ]
     reps = max(args.steps, 5)
     times = {n: [] for n, _ in seq}
     for rep in range(reps + 2):

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 
 #include "ssd_launch.h"
@@ -90,6 +91,7 @@ int64_t esize(const ssd::Dims &d) { return d.dtype == SSD_BF16 ? 2 : 4; }
 
 int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
 
+// Workspace of the staged arrangement: cs | C B^T | chunk states.
 struct WsLayout {
     int64_t cs = 0, cb = 0, S = 0, total = 0;
 };
@@ -105,6 +107,29 @@ WsLayout ws_layout(const ssd::Dims &d) {
     w.total = align256(w.S + s_bytes);
     if (d.b == 0 || d.nc == 0) w.total = 0;
     return w;
+}
+
+// Workspace of the single-pass arrangement: C B^T | B^T | state ring (2
+// slots) | hand-off flags + ticket counter.
+struct FusedLayout {
+    int64_t cb = 0, Bt = 0, ring = 0, flags = 0, total = 0;
+};
+
+FusedLayout fused_layout(const ssd::Dims &d) {
+    FusedLayout f;
+    f.cb = 0;
+    f.Bt = align256(f.cb + d.b * d.nc * d.G * d.Q * d.Q * 2);
+    f.ring = align256(f.Bt + d.b * d.nc * d.G * d.N * d.Q * 2);
+    f.flags = align256(f.ring + 2 * d.b * d.H * d.P * d.N * 4);
+    f.total = align256(f.flags + (d.b * d.H + 1) * 4);
+    if (d.b == 0 || d.nc == 0) f.total = 0;
+    return f;
+}
+
+int64_t ws_total(const ssd::Dims &d) {
+    int64_t t = ws_layout(d).total;
+    if (ssd::fused_supported(d)) t = std::max(t, fused_layout(d).total);
+    return t;
 }
 
 ssd_status hip_status(hipError_t e) {
@@ -127,15 +152,15 @@ ssd_status validate_forward(const ssd_dims *dims, const void *x, const void *dt,
     for (const void *p : ptrs)
         if (p && !aligned(p, 16)) return SSD_ERR_ALIGN;
     if (ws && !aligned(ws, 256)) return SSD_ERR_ALIGN;
-    const WsLayout w = ws_layout(d);
-    if (w.total > 0 && (!ws || (int64_t)ws_bytes < w.total)) return SSD_ERR_WORKSPACE;
+    const int64_t wtotal = ws_total(d);
+    if (wtotal > 0 && (!ws || (int64_t)ws_bytes < wtotal)) return SSD_ERR_WORKSPACE;
     const int64_t es = esize(d);
     const int64_t state_bytes = d.b * d.H * d.P * d.N * 4;
     const Range rx = range_of(x, d.b * d.L * d.H * d.P * es), rdt = range_of(dt, d.b * d.L * d.H * es),
                 rA = range_of(A, d.H * 4), rB = range_of(B, d.b * d.L * d.G * d.N * es),
                 rC = range_of(C, d.b * d.L * d.G * d.N * es), rD = range_of(D, d.H * 4),
                 ri = range_of(init, state_bytes), ry = range_of(y, d.b * d.L * d.H * d.P * es),
-                rf = range_of(fin, state_bytes), rw = range_of(ws, w.total);
+                rf = range_of(fin, state_bytes), rw = range_of(ws, wtotal);
     const Range ins[] = {rx, rdt, rA, rB, rC, rD, ri};
     for (const Range &r : ins)
         if (overlap(ry, r) || overlap(rw, r)) return SSD_ERR_ALIAS;
@@ -202,6 +227,24 @@ ssd_status run_staged(const ssd::Dims &d, const void *x, const void *dt, const f
     return SSD_OK;
 }
 
+ssd_status run_fused_prep(const ssd::Dims &d, const void *B, const void *C, void *ws,
+                          hipStream_t st) {
+    const FusedLayout f = fused_layout(d);
+    char *base = (char *)ws;
+    return hip_status(ssd::launch_fused_prep(d, B, C, base + f.cb, base + f.Bt,
+                                             (int *)(base + f.flags), st));
+}
+
+ssd_status run_fused_main(const ssd::Dims &d, const void *x, const void *dt, const float *A,
+                          const void *C, const float *D, const float *init, void *y, float *fin,
+                          void *ws, hipStream_t st) {
+    const FusedLayout f = fused_layout(d);
+    char *base = (char *)ws;
+    return hip_status(ssd::launch_fused_main(d, x, dt, A, base + f.Bt, C, base + f.cb, D, init, y,
+                                             fin, (float *)(base + f.ring),
+                                             (int *)(base + f.flags), st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -226,7 +269,7 @@ const char *ssd_last_hip_error(void) { return hipGetErrorString(g_last_hip); }
 size_t ssd_forward_workspace_bytes(const ssd_dims *dims) {
     ssd::Dims d;
     if (check_dims(dims, false, &d) != SSD_OK) return 0;
-    return (size_t)ws_layout(d).total;
+    return (size_t)ws_total(d);
 }
 
 ssd_status ssd_validate_forward(const ssd_dims *dims, const void *x, const void *dt,
@@ -263,8 +306,47 @@ ssd_status ssd_forward(const ssd_dims *dims, const void *x, const void *dt, cons
     ssd_status st = validate_forward(dims, x, dt, A, B, C, D, init_state, y, final_state,
                                      workspace, workspace_bytes, &d);
     if (st != SSD_OK) return st;
+    if (d.b > 0 && d.nc > 0 && ssd::fused_supported(d)) {
+        hipStream_t s = (hipStream_t)stream;
+        if ((st = run_fused_prep(d, B, C, workspace, s)) != SSD_OK) return st;
+        return run_fused_main(d, x, dt, A, C, D, init_state, y, final_state, workspace, s);
+    }
     return run_staged(d, x, dt, A, B, C, D, init_state, y, final_state, workspace,
                       (hipStream_t)stream);
+}
+
+int ssd_forward_is_single_pass(const ssd_dims *dims) {
+    ssd::Dims d;
+    if (check_dims(dims, false, &d) != SSD_OK) return 0;
+    return (d.b > 0 && d.nc > 0 && ssd::fused_supported(d)) ? 1 : 0;
+}
+
+ssd_status ssd_forward_prep(const ssd_dims *dims, const void *B, const void *C, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    ssd::Dims d;
+    ssd_status st = check_dims(dims, false, &d);
+    if (st != SSD_OK) return st;
+    if (!ssd::fused_supported(d)) return SSD_ERR_UNSUPPORTED;
+    if (d.b == 0 || d.nc == 0) return SSD_OK;
+    const void *req[] = {B, C, workspace};
+    if ((st = validate_ptrs(req, 3, nullptr, 0)) != SSD_OK) return st;
+    if (!aligned(workspace, 256)) return SSD_ERR_ALIGN;
+    if ((int64_t)workspace_bytes < ws_total(d)) return SSD_ERR_WORKSPACE;
+    return run_fused_prep(d, B, C, workspace, (hipStream_t)stream);
+}
+
+ssd_status ssd_forward_main(const ssd_dims *dims, const void *x, const void *dt, const float *A,
+                            const void *B, const void *C, const float *D, const float *init_state,
+                            void *y, float *final_state, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    ssd::Dims d;
+    ssd_status st = validate_forward(dims, x, dt, A, B, C, D, init_state, y, final_state,
+                                     workspace, workspace_bytes, &d);
+    if (st != SSD_OK) return st;
+    if (!ssd::fused_supported(d)) return SSD_ERR_UNSUPPORTED;
+    if (d.b == 0 || d.nc == 0) return SSD_OK;
+    return run_fused_main(d, x, dt, A, C, D, init_state, y, final_state, workspace,
+                          (hipStream_t)stream);
 }
 
 ssd_status ssd_decode_step(const ssd_dims *dims, float *state, const void *x, const void *dt,

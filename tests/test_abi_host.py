@@ -71,13 +71,25 @@ def test_valid_forward_passes():
 
 
 def test_workspace_bytes():
-    d = dims(batch=2, seqlen=100, nheads=4, headdim=64, dstate=128, ngroups=2, chunk=64)
+    al = lambda v: (v + 255) // 256 * 256
+    # staged layout: cs | C B^T | chunk states
+    d = dims(batch=2, seqlen=100, nheads=4, headdim=32, dstate=128, ngroups=2, chunk=64)
     nc = 2
     cs = 2 * 4 * nc * 64 * 4
     cb = 2 * nc * 2 * 64 * 64 * 2
+    S = 2 * nc * 4 * 32 * 128 * 4
+    staged = al(al(al(cs) + cb) + S)
+    assert LIB.ssd_forward_is_single_pass(ctypes.byref(d)) == 0
+    assert ssd.workspace_bytes(d) == staged
+    # single-pass layout (bf16, P=64, N=128): C B^T | B^T | ring | flags; the
+    # workspace covers both arrangements
+    d = dims(batch=2, seqlen=100, nheads=4, headdim=64, dstate=128, ngroups=2, chunk=64)
+    assert LIB.ssd_forward_is_single_pass(ctypes.byref(d)) == 1
     S = 2 * nc * 4 * 64 * 128 * 4
-    al = lambda v: (v + 255) // 256 * 256
-    assert ssd.workspace_bytes(d) == al(al(al(cs) + cb) + S)
+    staged = al(al(al(cs) + cb) + S)
+    fused = al(al(al(al(cb) + 2 * nc * 2 * 128 * 64 * 2) + 2 * 2 * 4 * 64 * 128 * 4) + (2 * 4 + 1) * 4)
+    assert ssd.workspace_bytes(d) == max(staged, fused)
+    assert LIB.ssd_forward_is_single_pass(ctypes.byref(dims(dtype=ssd.F32))) == 0
     assert ssd.workspace_bytes(dims(seqlen=0)) == 0
     assert ssd.workspace_bytes(dims(headdim=48)) == 0
 

@@ -307,3 +307,78 @@ def test_workload_decode_full(ssd):
         ey = worst_rel(f64(y)[:, None], y_ref[:, None], "y")
         assert ey < TOL[w.dtype], (s, ey)
     assert worst_rel(f64(state), ref_state, "state") < TOL[w.dtype]
+
+
+# ------------------------------------------------------------------ single-pass route
+def single_pass(ssd, w):
+    import ctypes
+    d = ssd.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk, ssd.BF16)
+    return bool(ssd.lib.ssd_forward_is_single_pass(ctypes.byref(d)))
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 48, 64, 112, 128, 256])
+@pytest.mark.parametrize("L", [1, 37, 256, 700])
+def test_single_pass_forward(ssd, chunk, L):
+    w = small("bf16", batch=2, seqlen=L, nheads=6, headdim=64, dstate=128, ngroups=2, chunk=chunk,
+              seed=L * 7 + chunk)
+    assert single_pass(ssd, w)
+    inp = si.make_forward_inputs(w)
+    y, fin = run_forward(ssd, inp, chunk)
+    y_ref, f_ref = oracle_forward(inp)
+    assert worst_rel(f64(y), y_ref, "y") < 2e-2
+    assert worst_rel(f64(fin), f_ref, "state") < 2e-2
+
+
+def test_single_pass_long_chain(ssd):
+    """256 chunks of 16 steps per (b, h): a long hand-off chain, with the
+    fast/slow decay split of the long workload."""
+    w = small("bf16", batch=1, seqlen=4096, nheads=8, headdim=64, dstate=128, ngroups=1, chunk=16,
+              dt_mode="split", seed=11)
+    assert single_pass(ssd, w)
+    inp = si.make_forward_inputs(w)
+    y, fin = run_forward(ssd, inp, 16)
+    y_ref, f_ref = oracle_forward(inp)
+    assert worst_rel(f64(y), y_ref, "y") < 2e-2
+    assert worst_rel(f64(fin), f_ref, "state") < 2e-2
+
+
+def test_single_pass_matches_staged_and_repeats(ssd):
+    w = small("bf16", batch=3, seqlen=1500, nheads=16, headdim=64, dstate=128, ngroups=1, chunk=256, seed=5)
+    inp = si.make_forward_inputs(w)
+    y1, f1 = run_forward(ssd, inp, 256)
+    y2, f2 = run_forward(ssd, inp, 256, staged=True)
+    assert worst_rel(f64(y1), f64(y2), "y") < 2e-2
+    assert worst_rel(f64(f1), f64(f2), "state") < 1e-2
+    for _ in range(3):   # the hand-off must give the same bits every time
+        y3, f3 = run_forward(ssd, inp, 256)
+        assert torch.equal(y1, y3) and torch.equal(f1, f3)
+
+
+def test_single_pass_inplace_carry(ssd):
+    w = small("bf16", batch=2, seqlen=600, nheads=4, headdim=64, dstate=128, ngroups=1, chunk=128, seed=9)
+    inp = si.make_forward_inputs(w)
+    y_ref, f_ref = oracle_forward(inp)
+    state = dev(inp["init"]).clone()
+    y, _ = ssd.forward(dev(inp["x"]), dev(inp["dt"]), dev(inp["A"]), dev(inp["B"]), dev(inp["C"]),
+                       dev(inp["D"]), state, chunk=128, final_state=state)
+    torch.cuda.synchronize()
+    assert worst_rel(f64(y), y_ref, "y") < 2e-2
+    assert worst_rel(f64(state), f_ref, "state") < 2e-2
+
+
+def test_single_pass_launches_compose(ssd):
+    """ssd_forward == ssd_forward_prep then ssd_forward_main (bit for bit)."""
+    import ctypes
+    w = small("bf16", batch=2, seqlen=900, nheads=8, headdim=64, dstate=128, ngroups=2, chunk=128, seed=3)
+    inp = si.make_forward_inputs(w)
+    t = {k: dev(v) for k, v in inp.items() if k != "workload"}
+    y1, f1 = ssd.forward(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["init"], chunk=128)
+    d = ssd.make_dims(2, 900, 8, 64, 128, 2, 128, ssd.BF16)
+    ws = torch.empty(ssd.workspace_bytes(d), dtype=torch.uint8, device=DEV)
+    y2, f2 = torch.empty_like(y1), torch.empty_like(f1)
+    p, s = ssd._p, ssd._stream()
+    assert ssd.lib.ssd_forward_prep(ctypes.byref(d), p(t["B"]), p(t["C"]), p(ws), ws.numel(), s) == 0
+    assert ssd.lib.ssd_forward_main(ctypes.byref(d), p(t["x"]), p(t["dt"]), p(t["A"]), p(t["B"]), p(t["C"]),
+                                    p(t["D"]), p(t["init"]), p(y2), p(f2), p(ws), ws.numel(), s) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)

@@ -80,13 +80,14 @@ def kernel_bytes(w) -> dict:
     BC = b * L * G * N * e
     st = b * H * P * N * 4
     init_b = st if w.init_mode == "normal" else 0
+    Bt = b * nc * G * N * ((Q + 31) // 32 * 32) * e
     return {
         # single-pass arrangement: prep reads B, C and writes the lower C B^T
         # tiles and B^T; main reads x, dt, C, the tiles, B^T, A, D (+ init)
         # and writes y and the final state (the state hand-off between chunks
         # is not algorithmic traffic)
-        "forward_prep": 2 * BC + cb + b * nc * G * N * Q * e,
-        "forward_main": x + b * L * H * e + BC + cb + b * nc * G * N * Q * e + 2 * H * 4 + init_b + x + st,
+        "forward_prep": 2 * BC + cb + Bt,
+        "forward_main": x + b * L * H * e + BC + cb + Bt + 2 * H * 4 + init_b + x + st,
         "chunk_cumsum": b * L * H * e + H * 4 + cs,
         "chunk_cb": 2 * BC + cb,
         "chunk_state": x + BC + cs + S,

@@ -109,8 +109,8 @@ WsLayout ws_layout(const ssd::Dims &d) {
     return w;
 }
 
-// Workspace of the single-pass arrangement: C B^T | B^T | state ring (2
-// slots) | hand-off flags + ticket counter.
+// Workspace of the single-pass arrangement: C B^T | B^T (rows padded to a
+// multiple of 32 steps) | state ring (2 slots) | hand-off flags.
 struct FusedLayout {
     int64_t cb = 0, Bt = 0, ring = 0, flags = 0, total = 0;
 };
@@ -119,7 +119,8 @@ FusedLayout fused_layout(const ssd::Dims &d) {
     FusedLayout f;
     f.cb = 0;
     f.Bt = align256(f.cb + d.b * d.nc * d.G * d.Q * d.Q * 2);
-    f.ring = align256(f.Bt + d.b * d.nc * d.G * d.N * d.Q * 2);
+    const int64_t Qp = (d.Q + 31) & ~(int64_t)31;  // B^T rows padded to 32 steps
+    f.ring = align256(f.Bt + d.b * d.nc * d.G * d.N * Qp * 2);
     f.flags = align256(f.ring + 2 * d.b * d.H * d.P * d.N * 4);
     f.total = align256(f.flags + (d.b * d.H + 1) * 4);
     if (d.b == 0 || d.nc == 0) f.total = 0;

@@ -24,13 +24,15 @@
 // non-increasing for dt >= 0, A <= 0), so nothing overflows; a factor that
 // underflows multiplies a contribution that is itself below the float range.
 //
-// Ordering: workgroups take a ticket from an atomic counter and map it to
-// (c, b, h) chunk-major, so the workgroup chunk c waits on has a smaller
-// ticket, i.e. it has already started and never waits on a later one: the
-// chain always drains.  The wait is also bounded (it gives up after ~0.2 s
-// and the result is then wrong, never hung).  The flag is written with a
-// release at agent scope after the state (L2 written back), and read with an
-// acquire at agent scope (L2 invalidated) so the state is seen across XCDs.
+// Ordering: block ids map to (c, b, h) so that the workgroup chunk c waits
+// on always has a smaller id in the same dispatch stream; with in-order
+// dispatch it is already resident or done, so the chain always drains.  The
+// wait is also bounded (it gives up after ~0.2 s and the result is then
+// wrong, never hung).  The handed-off state is written and read with
+// agent-scope atomic accesses, which are coherent across the XCDs' separate
+// L2 caches; the writer raises the flag at its very end, after waiting for
+// its stores to complete (s_waitcnt), and the reader issues its state loads
+// only after it has seen the flag.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -40,31 +42,65 @@ namespace {
 
 constexpr int kSpinLimit = 1 << 21;
 
-// Stage rows [0, Q) of x (row stride ld) transposed into two LDS copies:
-// plain (xs) and scaled by scale[r] (xt).  Rows >= nvalid are zero.
-__device__ __forceinline__ void stage_x_pair(const bf16 *__restrict__ src, int64_t ld, int rows,
-                                             int cols, int nvalid, bf16 *xs, bf16 *xt, int dstride,
-                                             const float *scale) {
-    const int nbc = cols / 8, nbr = rows / 4;
-    for (int blk = threadIdx.x; blk < nbr * nbc; blk += blockDim.x) {
-        const int br = blk / nbc, bc = blk - br * nbc;
-        const int r0 = br * 4, c0 = bc * 8;
-        u32x4 v[4], w[4];
+// 16-byte load / store as two 64-bit agent-scope relaxed atomics: coherent
+// across the XCDs' separate L2 caches with no cache write-back/invalidate.
+__device__ __forceinline__ f32x4 ld_agent_f32x4(const float *p) {
+    const uint64_t a = __hip_atomic_load((const uint64_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t b = __hip_atomic_load((const uint64_t *)p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return f32x4{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
+                 __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32))};
+}
+__device__ __forceinline__ void st_agent_f32x4(float *p, f32x4 v) {
+    const uint64_t a = ((uint64_t)__float_as_uint(v[1]) << 32) | __float_as_uint(v[0]);
+    const uint64_t b = ((uint64_t)__float_as_uint(v[3]) << 32) | __float_as_uint(v[2]);
+    __hip_atomic_store((uint64_t *)p, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store((uint64_t *)p + 1, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// x staging, split so the loads can be issued long before the LDS writes.
+// A thread owns up to XB blocks of 4 rows x 8 columns: blocks tid, tid + 256.
+template <int P>
+struct XStage {
+    static constexpr int NBC = P / 8;                  // 8-column blocks per row group
+    static constexpr int XB = (256 / 4) * NBC / 256;   // blocks per thread for 256 rows
+    u32x4 v[XB][4];
+};
+
+template <int P>
+__device__ __forceinline__ void stage_x_load(XStage<P> &st, const bf16 *__restrict__ src, int64_t ld,
+                                             int nvalid) {
+#pragma unroll
+    for (int i = 0; i < XStage<P>::XB; ++i) {
+        const int blk = threadIdx.x + 256 * i;
+        const int br = blk / XStage<P>::NBC, bc = blk - br * XStage<P>::NBC;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int rr = r0 + k;
-            if (rr < nvalid) {
-                v[k] = *(const u32x4 *)(src + (int64_t)rr * ld + c0);
-                bf16x8 t = as_bf16x8(v[k]);
-                const float s = scale[rr];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) t[e] = (bf16)((float)t[e] * s);
-                w[k] = as_u32x4(t);
-            } else {
-                v[k] = u32x4{0u, 0u, 0u, 0u};
-                w[k] = v[k];
-            }
+            const int rr = br * 4 + k;
+            st.v[i][k] = rr < nvalid ? *(const u32x4 *)(src + (int64_t)rr * ld + bc * 8) : u32x4{0u, 0u, 0u, 0u};
         }
+    }
+}
+
+// Write the loaded blocks transposed into LDS: xs plain, xt scaled by
+// scale[row] (rows >= nvalid were loaded as zero and stay zero).
+template <int P>
+__device__ __forceinline__ void stage_x_write(const XStage<P> &st, bf16 *xs, bf16 *xt, int dstride,
+                                              const float *scale) {
+#pragma unroll
+    for (int i = 0; i < XStage<P>::XB; ++i) {
+        const int blk = threadIdx.x + 256 * i;
+        const int br = blk / XStage<P>::NBC, bc = blk - br * XStage<P>::NBC;
+        const int r0 = br * 4, c0 = bc * 8;
+        u32x4 w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            bf16x8 t = as_bf16x8(st.v[i][k]);
+            const float sc = scale[r0 + k];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t[e] = (bf16)((float)t[e] * sc);
+            w[k] = as_u32x4(t);
+        }
+        const u32x4 *v = st.v[i];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             *(u32x2 *)(xs + (c0 + 2 * m) * dstride + r0) =
@@ -88,9 +124,9 @@ __device__ __forceinline__ void stage_x_pair(const bf16 *__restrict__ src, int64
 // ---------------------------------------------------------------------------
 // Preparation for the single-pass kernel, one launch:
 //   grid.y <  ntg : C B^T lower tiles (as k_chunk_cb), four per workgroup
-//   grid.y == ntg : B^T of the chunk ([N][Q], steps contiguous, zero past
-//                   the sequence end); workgroup (0, ntg) also clears the
-//                   hand-off flags and the ticket counter.
+//   grid.y == ntg : B^T of the chunk ([N][Qp], steps contiguous, Qp = Q
+//                   rounded up to 32, zero past the sequence end and past Q);
+//                   workgroup (0, ntg) also clears the hand-off flags.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_fused_prep(const bf16 *__restrict__ B,
                                                     const bf16 *__restrict__ C,
@@ -110,8 +146,9 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16 *__restrict__ B,
         if (bcg == 0)
             for (int64_t i = threadIdx.x; i < nflags; i += blockDim.x) flags[i] = 0;
         const int q = (int)min<int64_t>(Q, L - s);
-        stage_transposed_bf16<false>(B + ((b * L + s) * G + g) * N, (int64_t)G * N, Q, N, q,
-                                     Bt + bcg * (int64_t)N * Q, Q, nullptr);
+        const int Qp = (Q + 31) & ~31;
+        stage_transposed_bf16<false>(B + ((b * L + s) * G + g) * N, (int64_t)G * N, Qp, N, q,
+                                     Bt + bcg * (int64_t)N * Qp, Qp, nullptr);
         return;
     }
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -141,22 +178,26 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16 *__restrict__ B,
 
 // ---------------------------------------------------------------------------
 // The single-pass kernel.  256 threads (4 waves).  Wave w owns state n-tiles
-// {w, w + 4, ...} and output tiles {w, 7 - w, 8 + w, 15 - w} (balanced over
-// the triangle).
+// {w, w + 4} and output tiles {w, 7 - w, 8 + w, 15 - w} (balanced over the
+// triangle).  Global operands are loaded into registers ahead of the phase
+// that uses them (B^T before the x staging, the C B^T rows of the next tile
+// while the current tile computes, C before the hand-off wait), so each phase
+// pays one memory latency, not one per MFMA step.
 // ---------------------------------------------------------------------------
 template <int P, int N>
-__global__ __launch_bounds__(256) void k_ssd_fused(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ssd_fused(
     const bf16 *__restrict__ x, const bf16 *__restrict__ dt, const float *__restrict__ A,
     const bf16 *__restrict__ Bt, const bf16 *__restrict__ C, const bf16 *__restrict__ cb,
     const float *__restrict__ D, const float *init, bf16 *__restrict__ y, float *fin,
     float *ring, int *flags, int64_t L, int H, int G, int Q, int nc, int64_t nbh) {
-    constexpr int PT = P / 16, NT = N / 16, NTW = (NT + 3) / 4;
+    constexpr int PT = P / 16, NT = N / 16, NTW = NT / 4, NKN = N / 32;
+    static_assert(NT % 4 == 0 && N % 32 == 0, "N must be a multiple of 64");
     constexpr int XLD = 256 + 8, HLD = N + 8;
     static_assert(P * HLD <= P * XLD, "state staging reuses the scaled-x buffer");
-    __shared__ int tk_s;
     __shared__ float cs_s[256];
     __shared__ float wsum_s[4];
     __shared__ float ref_s[8];   // r_J: cs at the last step of 32-block J
+    __shared__ float lam_s[8];   // exp(r_J - r_{J-1}): decay across 32-block J
     __shared__ float vsc_s[256]; // v_j = exp(r_J(j) - cs_j)
     __shared__ bf16 xs[P * XLD];
     __shared__ bf16 xt[P * XLD];
@@ -164,19 +205,51 @@ __global__ __launch_bounds__(256) void k_ssd_fused(
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, grp = lane >> 4;
-    int *ticket = flags + nbh;
-    if (tid == 0) tk_s = atomicAdd(ticket, 1);
-    __syncthreads();
-    const int64_t t = tk_s;
-    if (t >= (int64_t)nc * nbh) return;   // cannot happen when the counter was cleared
-    const int c = (int)(t / nbh);
-    const int64_t bh = t - (int64_t)c * nbh;
+    // Work item of this workgroup.  Workgroups are dealt round-robin to 8
+    // streams (block k -> stream k % 8, the XCD round-robin); stream x walks
+    // chunk-columns c = 0, 1, ... over its own eighth of the (b, h) pairs.
+    // So the predecessor (c - 1, b, h) of every item is block k - nbh: same
+    // stream, smaller id.  With in-order dispatch inside a stream, the
+    // lowest unfinished block is always resident and its predecessor is done,
+    // so the chain drains; the bounded wait below is a backstop.
+    int c;
+    int64_t bh;
+    {
+        const int64_t k = blockIdx.x;
+        if (nbh % 8 == 0) {
+            const int64_t per = nbh / 8, m = k >> 3;
+            c = (int)(m / per);
+            bh = (k & 7) * per + (m - (int64_t)c * per);
+        } else {
+            c = (int)(k / nbh);
+            bh = k - (int64_t)c * nbh;
+        }
+    }
     const int64_t b = bh / H;
     const int h = (int)(bh - b * H);
     const int g = h / (H / G);
     const int64_t s = (int64_t)c * Q;
     const int q = (int)min<int64_t>(Q, L - s);
     const int nb = (q + 31) / 32;          // 32-step blocks holding data
+    const int T16 = (q + 15) / 16;
+    const int Qp = (Q + 31) & ~31;         // row length of B^T
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+
+    // B^T fragments of the chunk-state MFMAs, in flight during steps 1-2
+    const bf16 *Btc = Bt + ((b * nc + c) * G + g) * (int64_t)N * Qp;
+    bf16x8 bfr[8][NTW];
+#pragma unroll
+    for (int J = 0; J < 8; ++J)
+#pragma unroll
+        for (int tt = 0; tt < NTW; ++tt)
+            bfr[J][tt] = as_bf16x8(J < nb ? *(const u32x4 *)(Btc + (int64_t)((wave + 4 * tt) * 16 + r) * Qp +
+                                                             32 * J + grp * 8)
+                                          : z4);
+
+    // this chunk of x, loaded in one round together with B^T and dt
+    const int64_t row0 = (b * L + s) * H + h;
+    XStage<P> xst;
+    stage_x_load<P>(xst, x + row0 * P, (int64_t)H * P, q);
 
     // 1. decay prefix
     {
@@ -193,70 +266,91 @@ __global__ __launch_bounds__(256) void k_ssd_fused(
         __syncthreads();
         if (tid < 8) ref_s[tid] = cs_s[min(32 * tid + 31, q - 1)];
         __syncthreads();
+        if (tid < 8) lam_s[tid] = tid ? __expf(ref_s[tid] - ref_s[tid - 1]) : 1.f;
         vsc_s[tid] = __expf(ref_s[tid >> 5] - v);
         __syncthreads();
     }
     const float cs_last = cs_s[q - 1];
 
-    // 2. stage x^T and x~^T
-    const int64_t row0 = (b * L + s) * H + h;
-    stage_x_pair(x + row0 * P, (int64_t)H * P, (q + 31) & ~31, P, q, xs, xt, XLD, vsc_s);
+    // C B^T rows of the intra-chunk product, two output tiles ahead (a slot is
+    // refilled as soon as its tile has been consumed)
+    const bf16 *cbc = cb + ((b * nc + c) * G + g) * (int64_t)Q * Q;
+    auto tile_of = [&](int k) { return (k & 1) ? (8 * (k >> 1) + 7 - wave) : (8 * (k >> 1) + wave); };
+    bf16x8 gbuf[2][7], gdiag[2];
+    auto load_tile = [&](int k, int slot) {
+        const int I = tile_of(k);
+        if (I >= T16) return;
+        const int il = I * 16 + r;
+        const bf16 *grow = cbc + (int64_t)il * Q;
+        const int Jd = I >> 1;
+#pragma unroll
+        for (int J = 0; J < 7; ++J)
+            if (J < Jd) gbuf[slot][J] = as_bf16x8(*(const u32x4 *)(grow + 32 * J + grp * 8));
+        const int jl = 32 * Jd + grp * 8;
+        gdiag[slot] = as_bf16x8(jl <= il ? *(const u32x4 *)(grow + jl) : z4);
+    };
+    load_tile(0, 0);
+    load_tile(1, 1);
+
+    // 2. stage x^T and x~^T (rows past q were loaded as zero)
+    stage_x_write<P>(xst, xs, xt, XLD, vsc_s);
     __syncthreads();
 
-    // 3. chunk state: acc_s[t][pt] = S^T[n = 16 (wave + 4 t) + 4 grp + e][p = 16 pt + r]
-    const bf16 *Btc = Bt + ((b * nc + c) * G + g) * (int64_t)N * Q;
+    // 3. chunk state: acc_s[tt][pt] = S^T[n = 16 (wave + 4 tt) + 4 grp + e][p = 16 pt + r]
     f32x4 acc_s[NTW][PT];
 #pragma unroll
     for (int tt = 0; tt < NTW; ++tt)
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc_s[tt][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int J = 0; J < nb; ++J) {
-        if (J > 0) {
-            const float lam = __expf(ref_s[J] - ref_s[J - 1]);
+#pragma unroll
+    for (int J = 0; J < 8; ++J) {
+        if (J < nb) {
+            if (J > 0) {
+                const float lam = lam_s[J];
+#pragma unroll
+                for (int tt = 0; tt < NTW; ++tt)
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) acc_s[tt][pt] *= lam;
+            }
+            bf16x8 bx[PT];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt)
+                bx[pt] = *(const bf16x8 *)(xt + (pt * 16 + r) * XLD + 32 * J + grp * 8);
 #pragma unroll
             for (int tt = 0; tt < NTW; ++tt)
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt) acc_s[tt][pt] *= lam;
-        }
-        bf16x8 bx[PT];
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) bx[pt] = *(const bf16x8 *)(xt + (pt * 16 + r) * XLD + 32 * J + grp * 8);
-#pragma unroll
-        for (int tt = 0; tt < NTW; ++tt) {
-            const int nt = wave + 4 * tt;
-            if (nt < NT) {
-                const bf16x8 a = as_bf16x8(*(const u32x4 *)(Btc + (int64_t)(nt * 16 + r) * Q + 32 * J + grp * 8));
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) acc_s[tt][pt] = mfma_bf16(a, bx[pt], acc_s[tt][pt]);
-            }
+                for (int pt = 0; pt < PT; ++pt) acc_s[tt][pt] = mfma_bf16(bfr[J][tt], bx[pt], acc_s[tt][pt]);
         }
     }
 
     // 4. intra-chunk product for this wave's output tiles
-    const bf16 *cbc = cb + ((b * nc + c) * G + g) * (int64_t)Q * Q;
-    const int T16 = (q + 15) / 16;
     f32x4 acc_y[4][PT];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int I = (k & 1) ? (8 * (k >> 1) + 7 - wave) : (8 * (k >> 1) + wave);
+        const int cur = k & 1;
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc_y[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (I >= T16) continue;
+        const int I = tile_of(k);
+        if (I >= T16) {
+            if (k < 2) load_tile(k + 2, cur);
+            continue;
+        }
         const int il = I * 16 + r;
         const float csi = cs_s[il];
-        const bf16 *grow = cbc + (int64_t)il * Q;
         const int Jd = I >> 1;
-        for (int J = 0; J < Jd; ++J) {
-            if (J > 0) {
-                const float lam = __expf(ref_s[J] - ref_s[J - 1]);
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt) acc_y[k][pt] *= lam;
-            }
-            const bf16x8 gf = as_bf16x8(*(const u32x4 *)(grow + 32 * J + grp * 8));
+        for (int J = 0; J < 7; ++J) {
+            if (J < Jd) {
+                if (J > 0) {
+                    const float lam = lam_s[J];
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                const bf16x8 ax = *(const bf16x8 *)(xt + (pt * 16 + r) * XLD + 32 * J + grp * 8);
-                acc_y[k][pt] = mfma_bf16(ax, gf, acc_y[k][pt]);
+                    for (int pt = 0; pt < PT; ++pt) acc_y[k][pt] *= lam;
+                }
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const bf16x8 ax = *(const bf16x8 *)(xt + (pt * 16 + r) * XLD + 32 * J + grp * 8);
+                    acc_y[k][pt] = mfma_bf16(ax, gbuf[cur][J], acc_y[k][pt]);
+                }
             }
         }
         if (Jd > 0) {
@@ -266,35 +360,43 @@ __global__ __launch_bounds__(256) void k_ssd_fused(
         }
         const int jl = 32 * Jd + grp * 8;
         bf16x8 bm;
-        if (jl <= il) {
-            const bf16x8 gv = as_bf16x8(*(const u32x4 *)(grow + jl));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int j = jl + e;
-                bm[e] = (bf16)((j <= il) ? __expf(csi - cs_s[j]) * (float)gv[e] : 0.f);
-            }
-        } else {
-            bm = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+        for (int e = 0; e < 8; ++e) {
+            const int j = jl + e;
+            bm[e] = (bf16)((j <= il) ? __expf(csi - cs_s[j]) * (float)gdiag[cur][e] : 0.f);
         }
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
             const bf16x8 ax = *(const bf16x8 *)(xs + (pt * 16 + r) * XLD + jl);
             acc_y[k][pt] = mfma_bf16(ax, bm, acc_y[k][pt]);
         }
+        if (k < 2) load_tile(k + 2, cur);
     }
 
-    // 5. state hand-off
+    // C fragments of the state term, in flight across the hand-off
+    const bf16 *Cb = C + ((b * L + s) * G + g) * N;
+    bf16x8 cfr[4][NKN];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int il = tile_of(k) * 16 + r;
+        const bool ok = tile_of(k) < T16 && il < q;
+#pragma unroll
+        for (int kn = 0; kn < NKN; ++kn)
+            cfr[k][kn] = as_bf16x8(ok ? *(const u32x4 *)(Cb + (int64_t)il * G * N + kn * 32 + grp * 8) : z4);
+    }
+
+    // 5. state hand-off.  The ring is read and written with agent-scope
+    // atomic accesses (coherent across XCDs without cache maintenance); the
+    // flag goes up only after every wave's ring stores have completed.
     const int64_t PN = (int64_t)P * N;
     const float *hp = nullptr;
     if (c > 0) {
-        // every thread observes the flag itself, then acquires at agent scope
         int n = 0;
         while (__hip_atomic_load(flags + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < c &&
                n < kSpinLimit) {
             __builtin_amdgcn_s_sleep(2);
             ++n;
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         hp = ring + (int64_t)((c - 1) & 1) * nbh * PN + bh * PN;
     } else {
         hp = init ? init + bh * PN : nullptr;
@@ -302,76 +404,82 @@ __global__ __launch_bounds__(256) void k_ssd_fused(
     __syncthreads();  // every wave is done with x~ before hs overwrites it
     const bool have_h = hp != nullptr;
     const float lam_c = __expf(cs_last);
-    float *hout = (c == nc - 1) ? (fin ? fin + bh * PN : nullptr)
-                                : ring + (int64_t)(c & 1) * nbh * PN + bh * PN;
+    const bool last = c == nc - 1;
+    float *hout = last ? (fin ? fin + bh * PN : nullptr) : ring + (int64_t)(c & 1) * nbh * PN + bh * PN;
 #pragma unroll
     for (int tt = 0; tt < NTW; ++tt) {
-        const int nt = wave + 4 * tt;
-        if (nt < NT) {
+        f32x4 hv[PT];
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                const int p = pt * 16 + r, n0 = nt * 16 + 4 * grp;
-                const f32x4 hv = have_h ? *(const f32x4 *)(hp + (int64_t)p * N + n0) : f32x4{0.f, 0.f, 0.f, 0.f};
-                if (hout) *(f32x4 *)(hout + (int64_t)p * N + n0) = lam_c * hv + acc_s[tt][pt];
-                bf16 hb[4];
+        for (int pt = 0; pt < PT; ++pt) {
+            const int64_t off = (int64_t)(pt * 16 + r) * N + (wave + 4 * tt) * 16 + 4 * grp;
+            if (!have_h)
+                hv[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            else if (c > 0)
+                hv[pt] = ld_agent_f32x4(hp + off);
+            else
+                hv[pt] = *(const f32x4 *)(hp + off);
+        }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) hb[e] = (bf16)hv[e];
-                *(u32x2 *)(hs + p * HLD + n0) = *(const u32x2 *)hb;
+        for (int pt = 0; pt < PT; ++pt) {
+            const int p = pt * 16 + r, n0 = (wave + 4 * tt) * 16 + 4 * grp;
+            const f32x4 hn = lam_c * hv[pt] + acc_s[tt][pt];
+            if (hout) {
+                if (last)
+                    *(f32x4 *)(hout + (int64_t)p * N + n0) = hn;
+                else
+                    st_agent_f32x4(hout + (int64_t)p * N + n0, hn);
             }
+            bf16 hb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hb[e] = (bf16)hv[pt][e];
+            *(u32x2 *)(hs + p * HLD + n0) = *(const u32x2 *)hb;
         }
     }
-    if (c < nc - 1) {
-        // each wave releases its own ring stores (L2 write-back at agent
-        // scope, completion awaited) before the flag goes up
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __syncthreads();
-        if (tid == 0) __hip_atomic_store(flags + bh, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-        __syncthreads();
-    }
+    __syncthreads();  // hs complete
 
     // 6. state term, skip term, store
-    const bf16 *Cb = C + ((b * L + s) * G + g) * N;
     const float Dh = D ? D[h] : 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int I = (k & 1) ? (8 * (k >> 1) + 7 - wave) : (8 * (k >> 1) + wave);
+        const int I = tile_of(k);
         if (I >= T16) continue;
         const int il = I * 16 + r;
-        const bool vi = il < q;
         if (have_h) {
             f32x4 tmp[PT];
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) tmp[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const bf16 *crow = Cb + (int64_t)il * G * N;
 #pragma unroll
-            for (int k0 = 0; k0 < N; k0 += 32) {
-                const int kk = k0 + grp * 8;
-                const bf16x8 cf = as_bf16x8(vi ? *(const u32x4 *)(crow + kk) : u32x4{0u, 0u, 0u, 0u});
+            for (int kn = 0; kn < NKN; ++kn) {
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) {
-                    const bf16x8 ah = *(const bf16x8 *)(hs + (pt * 16 + r) * HLD + kk);
-                    tmp[pt] = mfma_bf16(ah, cf, tmp[pt]);
+                    const bf16x8 ah = *(const bf16x8 *)(hs + (pt * 16 + r) * HLD + kn * 32 + grp * 8);
+                    tmp[pt] = mfma_bf16(ah, cfr[k][kn], tmp[pt]);
                 }
             }
             const float ei = __expf(cs_s[il]);
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) acc_y[k][pt] += ei * tmp[pt];
         }
-        if (vi) {
-            const bf16 *xr = x + (row0 + (int64_t)il * H) * P;
+        if (il < q) {
             bf16 *yr = y + (row0 + (int64_t)il * H) * P;
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
                 const int p0 = pt * 16 + 4 * grp;
-                const u32x2 xw = *(const u32x2 *)(xr + p0);
-                const bf16 *xe = (const bf16 *)&xw;
                 bf16 o[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc_y[k][pt][e] + Dh * (float)xe[e]);
+                for (int e = 0; e < 4; ++e)
+                    o[e] = (bf16)(acc_y[k][pt][e] + Dh * (float)xs[(p0 + e) * XLD + il]);
                 *(u32x2 *)(yr + p0) = *(const u32x2 *)o;
             }
         }
+    }
+    // publish h_c last: by now this wave's ring stores have long completed,
+    // so waiting for them costs little, and the flag goes up only after
+    // every wave's stores are done
+    if (!last) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(flags + bh, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -109,20 +109,21 @@ WsLayout ws_layout(const ssd::Dims &d) {
     return w;
 }
 
-// Workspace of the single-pass arrangement: C B^T | B^T (rows padded to a
-// multiple of 32 steps) | state ring (2 slots) | hand-off flags.
+// Workspace of the single-pass arrangement: fragment-ordered C B^T, B^T and
+// C of every chunk | state ring (2 slots) | hand-off flags.
 struct FusedLayout {
-    int64_t cb = 0, Bt = 0, ring = 0, flags = 0, total = 0;
+    int64_t Gf = 0, Btf = 0, Cf = 0, ring = 0, flags = 0, total = 0;
 };
 
 FusedLayout fused_layout(const ssd::Dims &d) {
     FusedLayout f;
-    f.cb = 0;
-    f.Bt = align256(f.cb + d.b * d.nc * d.G * d.Q * d.Q * 2);
-    const int64_t Qp = (d.Q + 31) & ~(int64_t)31;  // B^T rows padded to 32 steps
-    f.ring = align256(f.Bt + d.b * d.nc * d.G * d.N * Qp * 2);
+    const int64_t nbcg = d.b * d.nc * d.G, T16 = d.Q / 16, NJ = (d.Q + 31) / 32;
+    f.Gf = 0;
+    f.Btf = align256(f.Gf + nbcg * T16 * NJ * 1024);
+    f.Cf = align256(f.Btf + nbcg * d.N * NJ * 64);
+    f.ring = align256(f.Cf + nbcg * T16 * (d.N / 32) * 1024);
     f.flags = align256(f.ring + 2 * d.b * d.H * d.P * d.N * 4);
-    f.total = align256(f.flags + (d.b * d.H + 1) * 4);
+    f.total = align256(f.flags + d.b * d.H * 4);
     if (d.b == 0 || d.nc == 0) f.total = 0;
     return f;
 }
@@ -232,7 +233,7 @@ ssd_status run_fused_prep(const ssd::Dims &d, const void *B, const void *C, void
                           hipStream_t st) {
     const FusedLayout f = fused_layout(d);
     char *base = (char *)ws;
-    return hip_status(ssd::launch_fused_prep(d, B, C, base + f.cb, base + f.Bt,
+    return hip_status(ssd::launch_fused_prep(d, B, C, base + f.Gf, base + f.Btf, base + f.Cf,
                                              (int *)(base + f.flags), st));
 }
 
@@ -241,8 +242,8 @@ ssd_status run_fused_main(const ssd::Dims &d, const void *x, const void *dt, con
                           void *ws, hipStream_t st) {
     const FusedLayout f = fused_layout(d);
     char *base = (char *)ws;
-    return hip_status(ssd::launch_fused_main(d, x, dt, A, base + f.Bt, C, base + f.cb, D, init, y,
-                                             fin, (float *)(base + f.ring),
+    return hip_status(ssd::launch_fused_main(d, x, dt, A, base + f.Btf, base + f.Cf, base + f.Gf, D,
+                                             init, y, fin, (float *)(base + f.ring),
                                              (int *)(base + f.flags), st));
 }
 

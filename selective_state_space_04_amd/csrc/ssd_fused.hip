@@ -42,19 +42,16 @@ namespace {
 
 constexpr int kSpinLimit = 1 << 21;
 
-// 16-byte load / store as two 64-bit agent-scope relaxed atomics: coherent
+// 8-byte load / store as a 64-bit agent-scope relaxed atomic: coherent
 // across the XCDs' separate L2 caches with no cache write-back/invalidate.
-__device__ __forceinline__ f32x4 ld_agent_f32x4(const float *p) {
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x2 ld_agent_f32x2(const float *p) {
     const uint64_t a = __hip_atomic_load((const uint64_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t b = __hip_atomic_load((const uint64_t *)p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return f32x4{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
-                 __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32))};
+    return f32x2{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32))};
 }
-__device__ __forceinline__ void st_agent_f32x4(float *p, f32x4 v) {
+__device__ __forceinline__ void st_agent_f32x2(float *p, f32x2 v) {
     const uint64_t a = ((uint64_t)__float_as_uint(v[1]) << 32) | __float_as_uint(v[0]);
-    const uint64_t b = ((uint64_t)__float_as_uint(v[3]) << 32) | __float_as_uint(v[2]);
     __hip_atomic_store((uint64_t *)p, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store((uint64_t *)p + 1, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // x staging, split so the loads can be issued long before the LDS writes.
@@ -66,13 +63,23 @@ struct XStage {
     u32x4 v[XB][4];
 };
 
+// Block blk -> (row group br, column block bc).  Each 32-lane half-wave
+// covers 16 consecutive row groups and two adjacent column blocks, so its
+// transposed 8-byte LDS stores hit 64 distinct banks.
+template <int P>
+__device__ __forceinline__ void xstage_block(int blk, int &br, int &bc) {
+    constexpr int NBC = XStage<P>::NBC;
+    bc = (blk >> 4) % NBC;
+    br = (blk & 15) + 16 * ((blk >> 4) / NBC);
+}
+
 template <int P>
 __device__ __forceinline__ void stage_x_load(XStage<P> &st, const bf16 *__restrict__ src, int64_t ld,
                                              int nvalid) {
 #pragma unroll
     for (int i = 0; i < XStage<P>::XB; ++i) {
-        const int blk = threadIdx.x + 256 * i;
-        const int br = blk / XStage<P>::NBC, bc = blk - br * XStage<P>::NBC;
+        int br, bc;
+        xstage_block<P>(threadIdx.x + 256 * i, br, bc);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int rr = br * 4 + k;
@@ -88,8 +95,8 @@ __device__ __forceinline__ void stage_x_write(const XStage<P> &st, bf16 *xs, bf1
                                               const float *scale) {
 #pragma unroll
     for (int i = 0; i < XStage<P>::XB; ++i) {
-        const int blk = threadIdx.x + 256 * i;
-        const int br = blk / XStage<P>::NBC, bc = blk - br * XStage<P>::NBC;
+        int br, bc;
+        xstage_block<P>(threadIdx.x + 256 * i, br, bc);
         const int r0 = br * 4, c0 = bc * 8;
         u32x4 w[4];
 #pragma unroll
@@ -122,19 +129,30 @@ __device__ __forceinline__ void stage_x_write(const XStage<P> &st, bf16 *xs, bf1
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Preparation for the single-pass kernel, one launch:
-//   grid.y <  ntg : C B^T lower tiles (as k_chunk_cb), four per workgroup
-//   grid.y == ntg : B^T of the chunk ([N][Qp], steps contiguous, Qp = Q
-//                   rounded up to 32, zero past the sequence end and past Q);
-//                   workgroup (0, ntg) also clears the hand-off flags.
+// Preparation for the single-pass kernel.  It writes the operands shared by
+// all heads of a group in MFMA-fragment order, so the single-pass kernel
+// loads each fragment of a wave as one contiguous 1 KiB block (lane l of the
+// fragment at byte 16 l).  For chunk (b, c, g), with r = l % 16, q4 = l / 16:
+//   Gf [I][J][l]  = C B^T rows 16 I + r, columns 32 J + 8 q4 .. + 7
+//                   (I < Q/16, J <= I/2; the diagonal 32-block is complete)
+//   Btf[t][J][l]  = B rows 32 J + 8 q4 .. + 7 at column 16 t + r  (B^T)
+//   Cf [I][k][l]  = C row 16 I + r, columns 32 k + 8 q4 .. + 7
+// Rows past the sequence end are zero.  grid.y: [0, ntg) C B^T tiles (four
+// 16 x 16 tiles per workgroup), ntg: B^T, ntg + 1: C and the flag reset.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int prep_tiles(int T16) {
+    int n = 0;
+    for (int ti = 0; ti < T16; ++ti) n += (ti | 1) + 1;
+    return n;
+}
+
 __global__ __launch_bounds__(256) void k_fused_prep(const bf16 *__restrict__ B,
                                                     const bf16 *__restrict__ C,
-                                                    bf16 *__restrict__ cb, bf16 *__restrict__ Bt,
-                                                    int *flags, int64_t nflags, int64_t L, int G,
-                                                    int N, int Q, int nc) {
-    const int T16 = Q / 16;
-    const int ntiles = T16 * (T16 + 1) / 2;
+                                                    bf16 *__restrict__ Gf, bf16 *__restrict__ Btf,
+                                                    bf16 *__restrict__ Cf, int *flags, int64_t nflags,
+                                                    int64_t L, int G, int N, int Q, int nc) {
+    const int T16 = Q / 16, NJ = (Q + 31) / 32, NKN = N / 32;
+    const int ntiles = prep_tiles(T16);
     const int ntg = (ntiles + 3) / 4;
     const int64_t bcg = blockIdx.x;
     const int g = (int)(bcg % G);
@@ -142,38 +160,67 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16 *__restrict__ B,
     const int c = (int)(bc % nc);
     const int64_t b = bc / nc;
     const int64_t s = (int64_t)c * Q;
-    if ((int)blockIdx.y == ntg) {
-        if (bcg == 0)
-            for (int64_t i = threadIdx.x; i < nflags; i += blockDim.x) flags[i] = 0;
-        const int q = (int)min<int64_t>(Q, L - s);
-        const int Qp = (Q + 31) & ~31;
-        stage_transposed_bf16<false>(B + ((b * L + s) * G + g) * N, (int64_t)G * N, Qp, N, q,
-                                     Bt + bcg * (int64_t)N * Qp, Qp, nullptr);
+    const int q = (int)min<int64_t>(Q, L - s);
+    const bf16 *Bc = B + ((b * L + s) * G + g) * N;
+    const bf16 *Cc = C + ((b * L + s) * G + g) * N;
+    const int64_t ld = (int64_t)G * N;
+    const int y = blockIdx.y;
+    if (y == ntg) {
+        // B^T fragments: thread item = (row block of 4, column n); 4 rows x 1 column
+        bf16 *dst = Btf + bcg * (int64_t)N * NJ * 32;
+        for (int it = threadIdx.x; it < (NJ * 32 / 4) * N; it += blockDim.x) {
+            const int n = it % N, r0 = (it / N) * 4;
+            bf16 v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] = (r0 + k < q) ? Bc[(int64_t)(r0 + k) * ld + n] : (bf16)0.f;
+            const int J = r0 / 32, q4 = (r0 % 32) / 8, e0 = r0 % 8;
+            const int lane = (n % 16) + 16 * q4;
+            *(u32x2 *)(dst + (((int64_t)(n / 16) * NJ + J) * 64 + lane) * 8 + e0) = *(const u32x2 *)v;
+        }
         return;
     }
+    if (y == ntg + 1) {
+        if (bcg == 0)
+            for (int64_t i = threadIdx.x; i < nflags; i += blockDim.x) flags[i] = 0;
+        bf16 *dst = Cf + bcg * (int64_t)T16 * NKN * 64 * 8;
+        for (int it = threadIdx.x; it < Q * (N / 8); it += blockDim.x) {
+            const int row = it / (N / 8), cb8 = it % (N / 8);
+            const u32x4 v = row < q ? *(const u32x4 *)(Cc + (int64_t)row * ld + cb8 * 8) : u32x4{0u, 0u, 0u, 0u};
+            const int I = row / 16, kn = cb8 / 4, q4 = cb8 % 4;
+            *(u32x4 *)(dst + (((int64_t)I * NKN + kn) * 64 + (row % 16) + 16 * q4) * 8) = v;
+        }
+        return;
+    }
+    // C B^T tile (ti, tj), computed transposed so each lane holds four
+    // consecutive columns j of one row i: D[m = j][n = i] = sum_k B_j C_i
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, grp = lane >> 4;
-    const int tile = blockIdx.y * 4 + wave;
+    int tile = y * 4 + wave;
     if (tile >= ntiles) return;
-    int ti = (int)((sqrtf(8.f * tile + 1.f) - 1.f) * 0.5f);
-    while ((ti + 1) * (ti + 2) / 2 <= tile) ++ti;
-    while (ti * (ti + 1) / 2 > tile) --ti;
-    const int tj = tile - ti * (ti + 1) / 2;
-    const int64_t irow = s + ti * 16 + r, jrow = s + tj * 16 + r;
-    const bool vi = irow < L, vj = jrow < L;
-    const bf16 *Crow = C + ((b * L + irow) * G + g) * N;
-    const bf16 *Brow = B + ((b * L + jrow) * G + g) * N;
+    int ti = 0;
+    while (tile >= (ti | 1) + 1) {
+        tile -= (ti | 1) + 1;
+        ++ti;
+    }
+    const int tj = tile;
+    const int irow = ti * 16 + r, jrow = tj * 16 + r;
+    const bool vi = irow < q, vj = jrow < q;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < N; k0 += 32) {
         const int k = k0 + grp * 8;
         const u32x4 z = {0u, 0u, 0u, 0u};
-        const u32x4 a = (vi && k < N) ? *(const u32x4 *)(Crow + k) : z;
-        const u32x4 bb = (vj && k < N) ? *(const u32x4 *)(Brow + k) : z;
-        acc = mfma_bf16(as_bf16x8(a), as_bf16x8(bb), acc);
+        const u32x4 bj = vj ? *(const u32x4 *)(Bc + (int64_t)jrow * ld + k) : z;
+        const u32x4 ci = vi ? *(const u32x4 *)(Cc + (int64_t)irow * ld + k) : z;
+        acc = mfma_bf16(as_bf16x8(bj), as_bf16x8(ci), acc);
     }
-    bf16 *out = cb + bcg * (int64_t)Q * Q;
+    // acc[e] = G[i = 16 ti + r][j = 16 tj + 4 grp + e]
+    const int i = ti * 16 + r, j0 = tj * 16 + 4 * grp;
+    const int J = j0 / 32, q4 = (j0 % 32) / 8, e0 = j0 % 8;
+    bf16 o[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[(int64_t)(ti * 16 + 4 * grp + e) * Q + tj * 16 + r] = (bf16)acc[e];
+    for (int e = 0; e < 4; ++e) o[e] = (bf16)acc[e];
+    bf16 *dst = Gf + bcg * (int64_t)T16 * NJ * 64 * 8;
+    *(u32x2 *)(dst + (((int64_t)(i / 16) * NJ + J) * 64 + (i % 16) + 16 * q4) * 8 + e0) = *(const u32x2 *)o;
 }
 
 // ---------------------------------------------------------------------------
@@ -187,7 +234,7 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16 *__restrict__ B,
 template <int P, int N>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ssd_fused(
     const bf16 *__restrict__ x, const bf16 *__restrict__ dt, const float *__restrict__ A,
-    const bf16 *__restrict__ Bt, const bf16 *__restrict__ C, const bf16 *__restrict__ cb,
+    const bf16 *__restrict__ Btf, const bf16 *__restrict__ Cf, const bf16 *__restrict__ Gf,
     const float *__restrict__ D, const float *init, bf16 *__restrict__ y, float *fin,
     float *ring, int *flags, int64_t L, int H, int G, int Q, int nc, int64_t nbh) {
     constexpr int PT = P / 16, NT = N / 16, NTW = NT / 4, NKN = N / 32;
@@ -232,18 +279,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int q = (int)min<int64_t>(Q, L - s);
     const int nb = (q + 31) / 32;          // 32-step blocks holding data
     const int T16 = (q + 15) / 16;
-    const int Qp = (Q + 31) & ~31;         // row length of B^T
+    const int NJ = (Q + 31) / 32, T16Q = Q / 16;
     const u32x4 z4 = {0u, 0u, 0u, 0u};
+    const int64_t bcg = (b * nc + c) * G + g;
+    const bf16 *Btc = Btf + bcg * (int64_t)N * NJ * 32;
+    const bf16 *Gfc = Gf + bcg * (int64_t)T16Q * NJ * 512;
+    const bf16 *Cfc = Cf + bcg * (int64_t)T16Q * NKN * 512;
 
     // B^T fragments of the chunk-state MFMAs, in flight during steps 1-2
-    const bf16 *Btc = Bt + ((b * nc + c) * G + g) * (int64_t)N * Qp;
     bf16x8 bfr[8][NTW];
 #pragma unroll
     for (int J = 0; J < 8; ++J)
 #pragma unroll
         for (int tt = 0; tt < NTW; ++tt)
-            bfr[J][tt] = as_bf16x8(J < nb ? *(const u32x4 *)(Btc + (int64_t)((wave + 4 * tt) * 16 + r) * Qp +
-                                                             32 * J + grp * 8)
+            bfr[J][tt] = as_bf16x8(J < nb ? *(const u32x4 *)(Btc + (((int64_t)(wave + 4 * tt) * NJ + J) * 64 + lane) * 8)
                                           : z4);
 
     // this chunk of x, loaded in one round together with B^T and dt
@@ -274,20 +323,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     // C B^T rows of the intra-chunk product, two output tiles ahead (a slot is
     // refilled as soon as its tile has been consumed)
-    const bf16 *cbc = cb + ((b * nc + c) * G + g) * (int64_t)Q * Q;
     auto tile_of = [&](int k) { return (k & 1) ? (8 * (k >> 1) + 7 - wave) : (8 * (k >> 1) + wave); };
     bf16x8 gbuf[2][7], gdiag[2];
     auto load_tile = [&](int k, int slot) {
         const int I = tile_of(k);
         if (I >= T16) return;
-        const int il = I * 16 + r;
-        const bf16 *grow = cbc + (int64_t)il * Q;
+        const bf16 *gt = Gfc + (int64_t)I * NJ * 512 + lane * 8;
         const int Jd = I >> 1;
 #pragma unroll
         for (int J = 0; J < 7; ++J)
-            if (J < Jd) gbuf[slot][J] = as_bf16x8(*(const u32x4 *)(grow + 32 * J + grp * 8));
-        const int jl = 32 * Jd + grp * 8;
-        gdiag[slot] = as_bf16x8(jl <= il ? *(const u32x4 *)(grow + jl) : z4);
+            if (J < Jd) gbuf[slot][J] = as_bf16x8(*(const u32x4 *)(gt + J * 512));
+        gdiag[slot] = as_bf16x8(*(const u32x4 *)(gt + Jd * 512));
     };
     load_tile(0, 0);
     load_tile(1, 1);
@@ -321,6 +367,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) acc_s[tt][pt] = mfma_bf16(bfr[J][tt], bx[pt], acc_s[tt][pt]);
         }
+    }
+
+    // If chunk c - 1 has already published h_{c-1}, start loading it now so
+    // the loads overlap the intra-chunk product (the flag read is uniform
+    // across the wave; otherwise the loads wait for the flag after step 4).
+    // Ring layout: lane-major, so each wave moves one contiguous 512-byte
+    // block per 8-byte access; init / final_state use the [P][N] layout.
+    const int64_t PN = (int64_t)P * N;
+    auto ring_off = [&](int tt, int pt, int half) -> int64_t {
+        return ((((int64_t)(wave * NTW + tt) * PT + pt) * 2 + half) * 64 + lane) * 2;
+    };
+    const float *hring = c > 0 ? ring + (int64_t)((c - 1) & 1) * nbh * PN + bh * PN : nullptr;
+    f32x2 hpre[NTW][PT][2];
+    bool early = false;
+    if (c > 0 && __hip_atomic_load(flags + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= c) {
+        early = true;
+#pragma unroll
+        for (int tt = 0; tt < NTW; ++tt)
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) hpre[tt][pt][half] = ld_agent_f32x2(hring + ring_off(tt, pt, half));
     }
 
     // 4. intra-chunk product for this wave's output tiles
@@ -374,30 +442,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 
     // C fragments of the state term, in flight across the hand-off
-    const bf16 *Cb = C + ((b * L + s) * G + g) * N;
     bf16x8 cfr[4][NKN];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int il = tile_of(k) * 16 + r;
-        const bool ok = tile_of(k) < T16 && il < q;
+        const bool ok = tile_of(k) < T16;
 #pragma unroll
         for (int kn = 0; kn < NKN; ++kn)
-            cfr[k][kn] = as_bf16x8(ok ? *(const u32x4 *)(Cb + (int64_t)il * G * N + kn * 32 + grp * 8) : z4);
+            cfr[k][kn] = as_bf16x8(ok ? *(const u32x4 *)(Cfc + (((int64_t)tile_of(k) * NKN + kn) * 64 + lane) * 8) : z4);
     }
 
     // 5. state hand-off.  The ring is read and written with agent-scope
-    // atomic accesses (coherent across XCDs without cache maintenance); the
-    // flag goes up only after every wave's ring stores have completed.
-    const int64_t PN = (int64_t)P * N;
+    // atomic accesses (coherent across XCDs without cache maintenance).
     const float *hp = nullptr;
     if (c > 0) {
-        int n = 0;
-        while (__hip_atomic_load(flags + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < c &&
-               n < kSpinLimit) {
-            __builtin_amdgcn_s_sleep(2);
-            ++n;
+        if (!early) {
+            int n = 0;
+            while (__hip_atomic_load(flags + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < c &&
+                   n < kSpinLimit) {
+                __builtin_amdgcn_s_sleep(2);
+                ++n;
+            }
         }
-        hp = ring + (int64_t)((c - 1) & 1) * nbh * PN + bh * PN;
+        hp = hring;
     } else {
         hp = init ? init + bh * PN : nullptr;
     }
@@ -412,22 +478,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
             const int64_t off = (int64_t)(pt * 16 + r) * N + (wave + 4 * tt) * 16 + 4 * grp;
-            if (!have_h)
+            if (!have_h) {
                 hv[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            else if (c > 0)
-                hv[pt] = ld_agent_f32x4(hp + off);
-            else
+            } else if (c > 0) {
+                const f32x2 lo = early ? hpre[tt][pt][0] : ld_agent_f32x2(hp + ring_off(tt, pt, 0));
+                const f32x2 hi = early ? hpre[tt][pt][1] : ld_agent_f32x2(hp + ring_off(tt, pt, 1));
+                hv[pt] = f32x4{lo[0], lo[1], hi[0], hi[1]};
+            } else {
                 hv[pt] = *(const f32x4 *)(hp + off);
+            }
         }
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
             const int p = pt * 16 + r, n0 = (wave + 4 * tt) * 16 + 4 * grp;
             const f32x4 hn = lam_c * hv[pt] + acc_s[tt][pt];
             if (hout) {
-                if (last)
+                if (last) {
                     *(f32x4 *)(hout + (int64_t)p * N + n0) = hn;
-                else
-                    st_agent_f32x4(hout + (int64_t)p * N + n0, hn);
+                } else {
+                    st_agent_f32x2(hout + ring_off(tt, pt, 0), f32x2{hn[0], hn[1]});
+                    st_agent_f32x2(hout + ring_off(tt, pt, 1), f32x2{hn[2], hn[3]});
+                }
             }
             bf16 hb[4];
 #pragma unroll
@@ -487,23 +558,26 @@ bool fused_supported(const Dims &d) {
     return d.dtype == 1 && d.P == 64 && d.N == 128 && d.Q <= 256 && d.nc >= 1;
 }
 
-hipError_t launch_fused_prep(const Dims &d, const void *B, const void *C, void *cb, void *Bt,
-                             int *flags, hipStream_t st) {
+hipError_t launch_fused_prep(const Dims &d, const void *B, const void *C, void *Gf, void *Btf,
+                             void *Cf, int *flags, hipStream_t st) {
     const int T16 = (int)(d.Q / 16);
-    const int ntg = (T16 * (T16 + 1) / 2 + 3) / 4;
-    dim3 grid((unsigned)(d.b * d.nc * d.G), (unsigned)(ntg + 1));
-    k_fused_prep<<<grid, 256, 0, st>>>((const bf16 *)B, (const bf16 *)C, (bf16 *)cb, (bf16 *)Bt, flags,
-                                       d.b * d.H + 1, d.L, (int)d.G, (int)d.N, (int)d.Q, (int)d.nc);
+    int ntiles = 0;
+    for (int ti = 0; ti < T16; ++ti) ntiles += (ti | 1) + 1;
+    const int ntg = (ntiles + 3) / 4;
+    dim3 grid((unsigned)(d.b * d.nc * d.G), (unsigned)(ntg + 2));
+    k_fused_prep<<<grid, 256, 0, st>>>((const bf16 *)B, (const bf16 *)C, (bf16 *)Gf, (bf16 *)Btf,
+                                       (bf16 *)Cf, flags, d.b * d.H, d.L, (int)d.G, (int)d.N,
+                                       (int)d.Q, (int)d.nc);
     return hipGetLastError();
 }
 
 hipError_t launch_fused_main(const Dims &d, const void *x, const void *dt, const float *A,
-                             const void *Bt, const void *C, const void *cb, const float *D,
+                             const void *Btf, const void *Cf, const void *Gf, const float *D,
                              const float *init, void *y, float *fin, float *ring, int *flags,
                              hipStream_t st) {
     const unsigned grid = (unsigned)(d.b * d.nc * d.H);
     k_ssd_fused<64, 128><<<grid, 256, 0, st>>>(
-        (const bf16 *)x, (const bf16 *)dt, A, (const bf16 *)Bt, (const bf16 *)C, (const bf16 *)cb, D,
+        (const bf16 *)x, (const bf16 *)dt, A, (const bf16 *)Btf, (const bf16 *)Cf, (const bf16 *)Gf, D,
         init, (bf16 *)y, fin, ring, flags, d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc, d.b * d.H);
     return hipGetLastError();
 }

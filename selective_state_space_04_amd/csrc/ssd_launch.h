@@ -26,10 +26,10 @@ hipError_t launch_decode(const Dims &d, float *state, const void *x, const void 
                          const float *A, const void *B, const void *C, const float *D, void *y,
                          hipStream_t st);
 bool fused_supported(const Dims &d);
-hipError_t launch_fused_prep(const Dims &d, const void *B, const void *C, void *cb, void *Bt,
-                             int *flags, hipStream_t st);
+hipError_t launch_fused_prep(const Dims &d, const void *B, const void *C, void *Gf, void *Btf,
+                             void *Cf, int *flags, hipStream_t st);
 hipError_t launch_fused_main(const Dims &d, const void *x, const void *dt, const float *A,
-                             const void *Bt, const void *C, const void *cb, const float *D,
+                             const void *Btf, const void *Cf, const void *Gf, const float *D,
                              const float *init, void *y, float *fin, float *ring, int *flags,
                              hipStream_t st);
 hipError_t launch_zero_state(const Dims &d, const float *init, float *fin, hipStream_t st);

@@ -88,6 +88,27 @@ __device__ __forceinline__ void stage_x_load(XStage<P> &st, const bf16 *__restri
     }
 }
 
+// Write the loaded blocks transposed into LDS (plain copy only).
+template <int P>
+__device__ __forceinline__ void stage_x_write_plain(const XStage<P> &st, bf16 *xs, int dstride) {
+#pragma unroll
+    for (int i = 0; i < XStage<P>::XB; ++i) {
+        int br, bc;
+        xstage_block<P>(threadIdx.x + 256 * i, br, bc);
+        const int r0 = br * 4, c0 = bc * 8;
+        const u32x4 *v = st.v[i];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            *(u32x2 *)(xs + (c0 + 2 * m) * dstride + r0) =
+                u32x2{__builtin_amdgcn_perm(v[1][m], v[0][m], 0x05040100u),
+                      __builtin_amdgcn_perm(v[3][m], v[2][m], 0x05040100u)};
+            *(u32x2 *)(xs + (c0 + 2 * m + 1) * dstride + r0) =
+                u32x2{__builtin_amdgcn_perm(v[1][m], v[0][m], 0x07060302u),
+                      __builtin_amdgcn_perm(v[3][m], v[2][m], 0x07060302u)};
+        }
+    }
+}
+
 // Write the loaded blocks transposed into LDS: xs plain, xt scaled by
 // scale[row] (rows >= nvalid were loaded as zero and stay zero).
 template <int P>
@@ -224,15 +245,26 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16 *__restrict__ B,
 }
 
 // ---------------------------------------------------------------------------
-// The single-pass kernel.  256 threads (4 waves).  Wave w owns state n-tiles
-// {w, w + 4} and output tiles {w, 7 - w, 8 + w, 15 - w} (balanced over the
-// triangle).  Global operands are loaded into registers ahead of the phase
-// that uses them (B^T before the x staging, the C B^T rows of the next tile
-// while the current tile computes, C before the hand-off wait), so each phase
-// pays one memory latency, not one per MFMA step.
+// The single-pass kernel.  256 threads (4 waves); sized for three workgroups
+// per CU (<= 53 KB LDS, <= 168 VGPRs).  Wave w owns state n-tiles {w, w + 4}
+// and output tiles {w, 7 - w, 8 + w, 15 - w} (balanced over the triangle).
+//   1. decay prefix of the chunk (wave scans); weights w_j = exp(cs_last -
+//      cs_j) for the chunk state
+//   2. x^T staged in LDS (loaded in one round at entry, with B^T and dt)
+//   3. chunk state S_c^T = sum_j (w_j B_j)^T x_j (w folded into the B^T
+//      fragments)
+//   4. hand-off: wait for h_{c-1} (ring slot of chunk c - 1, or init), write
+//      h_c = exp(cs_last) h_{c-1} + S_c to the ring (or final_state) and raise
+//      the flag; h_{c-1} (bf16) goes to LDS for step 5
+//   5. per output tile: intra-chunk product (off-diagonal 32-blocks J use
+//      exp(cs_i - cs_j) = exp(cs_i - r_J) exp(r_J - cs_j), both factors <= 1,
+//      folded into the C B^T fragment; the diagonal 32-block takes the mask
+//      exp(cs_i - cs_j) [j <= i] element by element), + exp(cs_i) h_{c-1} C_i
+//      + D x_i, stored as bf16.  The next tile's C B^T and C fragments load
+//      while the current tile computes.
 // ---------------------------------------------------------------------------
 template <int P, int N>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ssd_fused(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_ssd_fused(
     const bf16 *__restrict__ x, const bf16 *__restrict__ dt, const float *__restrict__ A,
     const bf16 *__restrict__ Btf, const bf16 *__restrict__ Cf, const bf16 *__restrict__ Gf,
     const float *__restrict__ D, const float *init, bf16 *__restrict__ y, float *fin,
@@ -240,25 +272,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int PT = P / 16, NT = N / 16, NTW = NT / 4, NKN = N / 32;
     static_assert(NT % 4 == 0 && N % 32 == 0, "N must be a multiple of 64");
     constexpr int XLD = 256 + 8, HLD = N + 8;
-    static_assert(P * HLD <= P * XLD, "state staging reuses the scaled-x buffer");
     __shared__ float cs_s[256];
+    __shared__ float wv_s[256];  // w_j during step 3, then v_j = exp(r_J(j) - cs_j)
     __shared__ float wsum_s[4];
     __shared__ float ref_s[8];   // r_J: cs at the last step of 32-block J
-    __shared__ float lam_s[8];   // exp(r_J - r_{J-1}): decay across 32-block J
-    __shared__ float vsc_s[256]; // v_j = exp(r_J(j) - cs_j)
     __shared__ bf16 xs[P * XLD];
-    __shared__ bf16 xt[P * XLD];
-    bf16 *hs = xt;               // reused for h_{c-1} (bf16) once x~ is consumed
+    __shared__ bf16 hs[P * HLD];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, grp = lane >> 4;
-    // Work item of this workgroup.  Workgroups are dealt round-robin to 8
-    // streams (block k -> stream k % 8, the XCD round-robin); stream x walks
-    // chunk-columns c = 0, 1, ... over its own eighth of the (b, h) pairs.
-    // So the predecessor (c - 1, b, h) of every item is block k - nbh: same
-    // stream, smaller id.  With in-order dispatch inside a stream, the
-    // lowest unfinished block is always resident and its predecessor is done,
-    // so the chain drains; the bounded wait below is a backstop.
+    // Work item.  Workgroups are dealt round-robin to 8 streams (block k ->
+    // stream k % 8, the XCD round-robin); stream x walks chunk-columns
+    // c = 0, 1, ... over its own eighth of the (b, h) pairs, so the
+    // predecessor (c - 1, b, h) of every item is block k - nbh: same stream,
+    // smaller id.  With in-order dispatch inside a stream, the lowest
+    // unfinished block is always resident and its predecessor is done, so
+    // the chain drains; the bounded wait below is a backstop.
     int c;
     int64_t bh;
     {
@@ -285,8 +314,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bf16 *Btc = Btf + bcg * (int64_t)N * NJ * 32;
     const bf16 *Gfc = Gf + bcg * (int64_t)T16Q * NJ * 512;
     const bf16 *Cfc = Cf + bcg * (int64_t)T16Q * NKN * 512;
+    const int64_t PN = (int64_t)P * N;
 
-    // B^T fragments of the chunk-state MFMAs, in flight during steps 1-2
+    // x, B^T and dt in one round
+    const int64_t row0 = (b * L + s) * H + h;
+    XStage<P> xst;
+    stage_x_load<P>(xst, x + row0 * P, (int64_t)H * P, q);
     bf16x8 bfr[8][NTW];
 #pragma unroll
     for (int J = 0; J < 8; ++J)
@@ -294,11 +327,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int tt = 0; tt < NTW; ++tt)
             bfr[J][tt] = as_bf16x8(J < nb ? *(const u32x4 *)(Btc + (((int64_t)(wave + 4 * tt) * NJ + J) * 64 + lane) * 8)
                                           : z4);
-
-    // this chunk of x, loaded in one round together with B^T and dt
-    const int64_t row0 = (b * L + s) * H + h;
-    XStage<P> xst;
-    stage_x_load<P>(xst, x + row0 * P, (int64_t)H * P, q);
 
     // 1. decay prefix
     {
@@ -314,32 +342,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         cs_s[tid] = v;  // past q: repeats the last valid value
         __syncthreads();
         if (tid < 8) ref_s[tid] = cs_s[min(32 * tid + 31, q - 1)];
-        __syncthreads();
-        if (tid < 8) lam_s[tid] = tid ? __expf(ref_s[tid] - ref_s[tid - 1]) : 1.f;
-        vsc_s[tid] = __expf(ref_s[tid >> 5] - v);
-        __syncthreads();
+        wv_s[tid] = __expf(cs_s[q - 1] - v);
     }
     const float cs_last = cs_s[q - 1];
 
-    // C B^T rows of the intra-chunk product, two output tiles ahead (a slot is
-    // refilled as soon as its tile has been consumed)
-    auto tile_of = [&](int k) { return (k & 1) ? (8 * (k >> 1) + 7 - wave) : (8 * (k >> 1) + wave); };
-    bf16x8 gbuf[2][7], gdiag[2];
-    auto load_tile = [&](int k, int slot) {
-        const int I = tile_of(k);
-        if (I >= T16) return;
-        const bf16 *gt = Gfc + (int64_t)I * NJ * 512 + lane * 8;
-        const int Jd = I >> 1;
-#pragma unroll
-        for (int J = 0; J < 7; ++J)
-            if (J < Jd) gbuf[slot][J] = as_bf16x8(*(const u32x4 *)(gt + J * 512));
-        gdiag[slot] = as_bf16x8(*(const u32x4 *)(gt + Jd * 512));
-    };
-    load_tile(0, 0);
-    load_tile(1, 1);
-
-    // 2. stage x^T and x~^T (rows past q were loaded as zero)
-    stage_x_write<P>(xst, xs, xt, XLD, vsc_s);
+    // 2. stage x^T (rows past q were loaded as zero)
+    stage_x_write_plain<P>(xst, xs, XLD);
     __syncthreads();
 
     // 3. chunk state: acc_s[tt][pt] = S^T[n = 16 (wave + 4 tt) + 4 grp + e][p = 16 pt + r]
@@ -351,123 +359,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int J = 0; J < 8; ++J) {
         if (J < nb) {
-            if (J > 0) {
-                const float lam = lam_s[J];
-#pragma unroll
-                for (int tt = 0; tt < NTW; ++tt)
-#pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) acc_s[tt][pt] *= lam;
-            }
+            const f32x4 w0 = *(const f32x4 *)(wv_s + 32 * J + grp * 8);
+            const f32x4 w1 = *(const f32x4 *)(wv_s + 32 * J + grp * 8 + 4);
             bf16x8 bx[PT];
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt)
-                bx[pt] = *(const bf16x8 *)(xt + (pt * 16 + r) * XLD + 32 * J + grp * 8);
+                bx[pt] = *(const bf16x8 *)(xs + (pt * 16 + r) * XLD + 32 * J + grp * 8);
 #pragma unroll
-            for (int tt = 0; tt < NTW; ++tt)
+            for (int tt = 0; tt < NTW; ++tt) {
+                bf16x8 a = bfr[J][tt];
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt) acc_s[tt][pt] = mfma_bf16(bfr[J][tt], bx[pt], acc_s[tt][pt]);
+                for (int e = 0; e < 4; ++e) {
+                    a[e] = (bf16)((float)a[e] * w0[e]);
+                    a[e + 4] = (bf16)((float)a[e + 4] * w1[e]);
+                }
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) acc_s[tt][pt] = mfma_bf16(a, bx[pt], acc_s[tt][pt]);
+            }
         }
     }
 
-    // If chunk c - 1 has already published h_{c-1}, start loading it now so
-    // the loads overlap the intra-chunk product (the flag read is uniform
-    // across the wave; otherwise the loads wait for the flag after step 4).
-    // Ring layout: lane-major, so each wave moves one contiguous 512-byte
-    // block per 8-byte access; init / final_state use the [P][N] layout.
-    const int64_t PN = (int64_t)P * N;
+    // fragments of the first output tile, in flight across the hand-off
+    auto tile_of = [&](int k) { return (k & 1) ? (8 * (k >> 1) + 7 - wave) : (8 * (k >> 1) + wave); };
+    bf16x8 gbuf[2][7], gdiag[2], cbuf[2][NKN];
+    auto load_tile = [&](int k, int slot) {
+        const int I = tile_of(k);
+        if (I >= T16) return;
+        const bf16 *gt = Gfc + (int64_t)I * NJ * 512 + lane * 8;
+        const int Jd = I >> 1;
+#pragma unroll
+        for (int J = 0; J < 7; ++J)
+            if (J < Jd) gbuf[slot][J] = as_bf16x8(*(const u32x4 *)(gt + J * 512));
+        gdiag[slot] = as_bf16x8(*(const u32x4 *)(gt + Jd * 512));
+#pragma unroll
+        for (int kn = 0; kn < NKN; ++kn)
+            cbuf[slot][kn] = as_bf16x8(*(const u32x4 *)(Cfc + (((int64_t)I * NKN + kn) * 64 + lane) * 8));
+    };
+    load_tile(0, 0);
+
+    // 4. state hand-off.  The ring is read and written with agent-scope
+    // atomic accesses (coherent across XCDs without cache maintenance), in a
+    // lane-major layout so each wave moves one contiguous 512-byte block per
+    // access; init / final_state use the [P][N] layout.
     auto ring_off = [&](int tt, int pt, int half) -> int64_t {
         return ((((int64_t)(wave * NTW + tt) * PT + pt) * 2 + half) * 64 + lane) * 2;
     };
-    const float *hring = c > 0 ? ring + (int64_t)((c - 1) & 1) * nbh * PN + bh * PN : nullptr;
-    f32x2 hpre[NTW][PT][2];
-    bool early = false;
-    if (c > 0 && __hip_atomic_load(flags + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= c) {
-        early = true;
-#pragma unroll
-        for (int tt = 0; tt < NTW; ++tt)
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                for (int half = 0; half < 2; ++half) hpre[tt][pt][half] = ld_agent_f32x2(hring + ring_off(tt, pt, half));
-    }
-
-    // 4. intra-chunk product for this wave's output tiles
-    f32x4 acc_y[4][PT];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int cur = k & 1;
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) acc_y[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int I = tile_of(k);
-        if (I >= T16) {
-            if (k < 2) load_tile(k + 2, cur);
-            continue;
-        }
-        const int il = I * 16 + r;
-        const float csi = cs_s[il];
-        const int Jd = I >> 1;
-#pragma unroll
-        for (int J = 0; J < 7; ++J) {
-            if (J < Jd) {
-                if (J > 0) {
-                    const float lam = lam_s[J];
-#pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) acc_y[k][pt] *= lam;
-                }
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    const bf16x8 ax = *(const bf16x8 *)(xt + (pt * 16 + r) * XLD + 32 * J + grp * 8);
-                    acc_y[k][pt] = mfma_bf16(ax, gbuf[cur][J], acc_y[k][pt]);
-                }
-            }
-        }
-        if (Jd > 0) {
-            const float u = __expf(csi - ref_s[Jd - 1]);
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) acc_y[k][pt] *= u;
-        }
-        const int jl = 32 * Jd + grp * 8;
-        bf16x8 bm;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int j = jl + e;
-            bm[e] = (bf16)((j <= il) ? __expf(csi - cs_s[j]) * (float)gdiag[cur][e] : 0.f);
-        }
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            const bf16x8 ax = *(const bf16x8 *)(xs + (pt * 16 + r) * XLD + jl);
-            acc_y[k][pt] = mfma_bf16(ax, bm, acc_y[k][pt]);
-        }
-        if (k < 2) load_tile(k + 2, cur);
-    }
-
-    // C fragments of the state term, in flight across the hand-off
-    bf16x8 cfr[4][NKN];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const bool ok = tile_of(k) < T16;
-#pragma unroll
-        for (int kn = 0; kn < NKN; ++kn)
-            cfr[k][kn] = as_bf16x8(ok ? *(const u32x4 *)(Cfc + (((int64_t)tile_of(k) * NKN + kn) * 64 + lane) * 8) : z4);
-    }
-
-    // 5. state hand-off.  The ring is read and written with agent-scope
-    // atomic accesses (coherent across XCDs without cache maintenance).
     const float *hp = nullptr;
     if (c > 0) {
-        if (!early) {
-            int n = 0;
-            while (__hip_atomic_load(flags + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < c &&
-                   n < kSpinLimit) {
-                __builtin_amdgcn_s_sleep(2);
-                ++n;
-            }
+        int n = 0;
+        while (__hip_atomic_load(flags + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < c &&
+               n < kSpinLimit) {
+            __builtin_amdgcn_s_sleep(1);
+            ++n;
         }
-        hp = hring;
+        hp = ring + (int64_t)((c - 1) & 1) * nbh * PN + bh * PN;
     } else {
         hp = init ? init + bh * PN : nullptr;
     }
-    __syncthreads();  // every wave is done with x~ before hs overwrites it
+    __syncthreads();  // step 3 is done in every wave: wv_s may be rewritten
+    {
+        const int J = tid >> 5;   // v_j relative to the end of j's own 32-block
+        wv_s[tid] = __expf(ref_s[J] - cs_s[tid]);
+    }
     const bool have_h = hp != nullptr;
     const float lam_c = __expf(cs_last);
     const bool last = c == nc - 1;
@@ -481,8 +434,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (!have_h) {
                 hv[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
             } else if (c > 0) {
-                const f32x2 lo = early ? hpre[tt][pt][0] : ld_agent_f32x2(hp + ring_off(tt, pt, 0));
-                const f32x2 hi = early ? hpre[tt][pt][1] : ld_agent_f32x2(hp + ring_off(tt, pt, 1));
+                const f32x2 lo = ld_agent_f32x2(hp + ring_off(tt, pt, 0));
+                const f32x2 hi = ld_agent_f32x2(hp + ring_off(tt, pt, 1));
                 hv[pt] = f32x4{lo[0], lo[1], hi[0], hi[1]};
             } else {
                 hv[pt] = *(const f32x4 *)(hp + off);
@@ -506,15 +459,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             *(u32x2 *)(hs + p * HLD + n0) = *(const u32x2 *)hb;
         }
     }
-    __syncthreads();  // hs complete
+    if (!last) __builtin_amdgcn_s_waitcnt(0);  // this wave's ring stores are complete
+    __syncthreads();                            // ... in every wave; hs and wv_s complete
+    if (!last && tid == 0) __hip_atomic_store(flags + bh, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-    // 6. state term, skip term, store
+    // 5. output tiles
     const float Dh = D ? D[h] : 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
+        const int cur = k & 1;
+        if (k < 3) load_tile(k + 1, cur ^ 1);
         const int I = tile_of(k);
         if (I >= T16) continue;
         const int il = I * 16 + r;
+        const float csi = cs_s[il];
+        const int Jd = I >> 1;
+        f32x4 acc[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int J = 0; J < 7; ++J) {
+            if (J < Jd) {
+                const float u = __expf(csi - ref_s[J]);
+                const f32x4 v0 = *(const f32x4 *)(wv_s + 32 * J + grp * 8);
+                const f32x4 v1 = *(const f32x4 *)(wv_s + 32 * J + grp * 8 + 4);
+                bf16x8 gm = gbuf[cur][J];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    gm[e] = (bf16)((float)gm[e] * (u * v0[e]));
+                    gm[e + 4] = (bf16)((float)gm[e + 4] * (u * v1[e]));
+                }
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const bf16x8 ax = *(const bf16x8 *)(xs + (pt * 16 + r) * XLD + 32 * J + grp * 8);
+                    acc[pt] = mfma_bf16(ax, gm, acc[pt]);
+                }
+            }
+        }
+        {
+            const int jl = 32 * Jd + grp * 8;
+            const bf16x8 gd = gdiag[cur];
+            bf16x8 bm;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = jl + e;
+                bm[e] = (bf16)((j <= il) ? __expf(csi - cs_s[j]) * (float)gd[e] : 0.f);
+            }
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const bf16x8 ax = *(const bf16x8 *)(xs + (pt * 16 + r) * XLD + jl);
+                acc[pt] = mfma_bf16(ax, bm, acc[pt]);
+            }
+        }
         if (have_h) {
             f32x4 tmp[PT];
 #pragma unroll
@@ -524,12 +520,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) {
                     const bf16x8 ah = *(const bf16x8 *)(hs + (pt * 16 + r) * HLD + kn * 32 + grp * 8);
-                    tmp[pt] = mfma_bf16(ah, cfr[k][kn], tmp[pt]);
+                    tmp[pt] = mfma_bf16(ah, cbuf[cur][kn], tmp[pt]);
                 }
             }
-            const float ei = __expf(cs_s[il]);
+            const float ei = __expf(csi);
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) acc_y[k][pt] += ei * tmp[pt];
+            for (int pt = 0; pt < PT; ++pt) acc[pt] += ei * tmp[pt];
         }
         if (il < q) {
             bf16 *yr = y + (row0 + (int64_t)il * H) * P;
@@ -538,19 +534,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const int p0 = pt * 16 + 4 * grp;
                 bf16 o[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    o[e] = (bf16)(acc_y[k][pt][e] + Dh * (float)xs[(p0 + e) * XLD + il]);
+                for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc[pt][e] + Dh * (float)xs[(p0 + e) * XLD + il]);
                 *(u32x2 *)(yr + p0) = *(const u32x2 *)o;
             }
         }
-    }
-    // publish h_c last: by now this wave's ring stores have long completed,
-    // so waiting for them costs little, and the flag goes up only after
-    // every wave's stores are done
-    if (!last) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0) __hip_atomic_store(flags + bh, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -231,9 +231,28 @@ def kernel_roofline(ssd, w, x, dt, A, B, C, D, init, ws, y, fin, flush, args):
     kb = kernel_bytes(w)[dom]
     achieved = kb / (avg[dom] * 1e-6) / 1e9
     roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None, "alg_bytes_per_launch": kb,
+            "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(dom), "alg_bytes_per_launch": kb,
             "avg_launch_us": avg[dom]}
     return roof, avg
+
+
+def measured_traffic(key: str):
+    """HBM bytes per launch from the committed rocprofv3 counters
+    (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE, scaled by the copy
+    calibration), or None once the kernel source has changed since they were
+    taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(key)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != rec["source_sha256_16"]:
+        return None
+    return rec["bytes"]
 
 
 def cpu_baseline(w, inp):
@@ -292,7 +311,7 @@ def run_decode_bench(args):
                                                               "nheads": w.nheads, "headdim": w.headdim,
                                                               "dstate": w.dstate, "steps": nsteps},
             "roofline": {"kernel": "decode", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("decode"),
                          "alg_bytes_per_launch": bytes_step, "avg_launch_us": avg_us},
             "wall_s": wall}
 

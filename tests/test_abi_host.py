@@ -81,13 +81,19 @@ def test_workspace_bytes():
     staged = al(al(al(cs) + cb) + S)
     assert LIB.ssd_forward_is_single_pass(ctypes.byref(d)) == 0
     assert ssd.workspace_bytes(d) == staged
-    # single-pass layout (bf16, P=64, N=128): C B^T | B^T | ring | flags; the
-    # workspace covers both arrangements
+    # single-pass layout (bf16, P=64, N=128): C B^T fragments | B^T fragments |
+    # C fragments | state ring (2 slots) | flags; the workspace covers both
+    # arrangements
     d = dims(batch=2, seqlen=100, nheads=4, headdim=64, dstate=128, ngroups=2, chunk=64)
     assert LIB.ssd_forward_is_single_pass(ctypes.byref(d)) == 1
     S = 2 * nc * 4 * 64 * 128 * 4
     staged = al(al(al(cs) + cb) + S)
-    fused = al(al(al(al(cb) + 2 * nc * 2 * 128 * 64 * 2) + 2 * 2 * 4 * 64 * 128 * 4) + (2 * 4 + 1) * 4)
+    nbcg, t16, nj = 2 * nc * 2, 64 // 16, 64 // 32
+    gf = nbcg * t16 * nj * 1024
+    btf = nbcg * 128 * nj * 64
+    cf = nbcg * t16 * (128 // 32) * 1024
+    ring = 2 * 2 * 4 * 64 * 128 * 4
+    fused = al(al(al(al(al(gf) + btf) + cf) + ring) + 2 * 4 * 4)
     assert ssd.workspace_bytes(d) == max(staged, fused)
     assert LIB.ssd_forward_is_single_pass(ctypes.byref(dims(dtype=ssd.F32))) == 0
     assert ssd.workspace_bytes(dims(seqlen=0)) == 0

@@ -74,7 +74,7 @@ __device__ __forceinline__ void xstage_block(int blk, int &br, int &bc) {
 }
 
 template <int P>
-__device__ __forceinline__ void stage_x_load(XStage<P> &st, const bf16 *__restrict__ src, int64_t ld,
+__device__ __forceinline__ void stage_x_load(XStage<P> &st, const bf16 *__restrict__ src, int ld,
                                              int nvalid) {
 #pragma unroll
     for (int i = 0; i < XStage<P>::XB; ++i) {
@@ -83,7 +83,7 @@ __device__ __forceinline__ void stage_x_load(XStage<P> &st, const bf16 *__restri
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int rr = br * 4 + k;
-            st.v[i][k] = rr < nvalid ? *(const u32x4 *)(src + (int64_t)rr * ld + bc * 8) : u32x4{0u, 0u, 0u, 0u};
+            st.v[i][k] = rr < nvalid ? *(const u32x4 *)(src + rr * ld + bc * 8) : u32x4{0u, 0u, 0u, 0u};
         }
     }
 }
@@ -159,7 +159,9 @@ __device__ __forceinline__ void stage_x_write(const XStage<P> &st, bf16 *xs, bf1
 //   Btf[t][J][l]  = B rows 32 J + 8 q4 .. + 7 at column 16 t + r  (B^T)
 //   Cf [I][k][l]  = C row 16 I + r, columns 32 k + 8 q4 .. + 7
 // Rows past the sequence end are zero.  grid.y: [0, ntg) C B^T tiles (four
-// 16 x 16 tiles per workgroup), ntg: B^T, ntg + 1: C and the flag reset.
+// 16 x 16 tiles per workgroup); ntg + t (t < N/16): B^T fragments of state
+// column tile t, staged through LDS; ntg + N/16 + u (u < 8): C fragments of
+// row tiles I with I % 8 == u (u = 0 also clears the flags).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int prep_tiles(int T16) {
     int n = 0;
@@ -167,55 +169,69 @@ __device__ __forceinline__ int prep_tiles(int T16) {
     return n;
 }
 
+template <int N>
 __global__ __launch_bounds__(256) void k_fused_prep(const bf16 *__restrict__ B,
                                                     const bf16 *__restrict__ C,
                                                     bf16 *__restrict__ Gf, bf16 *__restrict__ Btf,
-                                                    bf16 *__restrict__ Cf, int *flags, int64_t nflags,
-                                                    int64_t L, int G, int N, int Q, int nc) {
-    const int T16 = Q / 16, NJ = (Q + 31) / 32, NKN = N / 32;
+                                                    bf16 *__restrict__ Cf, int *flags, int nflags,
+                                                    int L, int G, int Q, int nc) {
+    constexpr int NKN = N / 32, NTT = N / 16;
+    const int T16 = Q / 16, NJ = (Q + 31) / 32;
     const int ntiles = prep_tiles(T16);
     const int ntg = (ntiles + 3) / 4;
-    const int64_t bcg = blockIdx.x;
-    const int g = (int)(bcg % G);
-    const int64_t bc = bcg / G;
-    const int c = (int)(bc % nc);
-    const int64_t b = bc / nc;
-    const int64_t s = (int64_t)c * Q;
-    const int q = (int)min<int64_t>(Q, L - s);
-    const bf16 *Bc = B + ((b * L + s) * G + g) * N;
-    const bf16 *Cc = C + ((b * L + s) * G + g) * N;
-    const int64_t ld = (int64_t)G * N;
+    const int bcg = blockIdx.x;
+    const int g = bcg % G;
+    const int bc = bcg / G;
+    const int c = bc % nc;
+    const int b = bc / nc;
+    const int s = c * Q;
+    const int q = min(Q, L - s);
+    const bf16 *Bc = B + ((int64_t)(b * L + s) * G + g) * N;
+    const bf16 *Cc = C + ((int64_t)(b * L + s) * G + g) * N;
+    const int ld = G * N;
     const int y = blockIdx.y;
-    if (y == ntg) {
-        // B^T fragments: thread item = (row block of 4, column n); 4 rows x 1 column
-        bf16 *dst = Btf + bcg * (int64_t)N * NJ * 32;
-        for (int it = threadIdx.x; it < (NJ * 32 / 4) * N; it += blockDim.x) {
-            const int n = it % N, r0 = (it / N) * 4;
-            bf16 v[4];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r = lane & 15, grp = lane >> 4;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    if (y >= ntg && y < ntg + NTT) {
+        // B^T fragments of column tile t: B[0 .. Q-1][16 t .. 16 t + 15] into LDS
+        // (two 16-byte pieces per row), then 8 rows x 1 column per lane.
+        constexpr int BLD = 20;  // row stride: 10 dwords, 8-byte aligned; 8-row groups fall on distinct banks
+        __shared__ bf16 bt_s[256 * BLD];
+        const int t = y - ntg;
+        for (int it = threadIdx.x; it < NJ * 64; it += 256) {  // rows up to 32 NJ; past q zero
+            const int row = it >> 1, half = it & 1;
+            const u32x4 v = row < q ? *(const u32x4 *)(Bc + (int64_t)row * ld + t * 16 + half * 8) : z;
+            u32x2 *d = (u32x2 *)(bt_s + row * BLD + half * 8);  // 8-byte aligned: two 8-byte stores
+            d[0] = u32x2{v[0], v[1]};
+            d[1] = u32x2{v[2], v[3]};
+        }
+        __syncthreads();
+        bf16 *dst = Btf + (int64_t)bcg * (N * NJ * 32) + (int64_t)t * (NJ * 512) + lane * 8;
+        for (int J = wave; J < NJ; J += 4) {
+            bf16x8 v;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) v[k] = (r0 + k < q) ? Bc[(int64_t)(r0 + k) * ld + n] : (bf16)0.f;
-            const int J = r0 / 32, q4 = (r0 % 32) / 8, e0 = r0 % 8;
-            const int lane = (n % 16) + 16 * q4;
-            *(u32x2 *)(dst + (((int64_t)(n / 16) * NJ + J) * 64 + lane) * 8 + e0) = *(const u32x2 *)v;
+            for (int e = 0; e < 8; ++e) v[e] = bt_s[(32 * J + 8 * grp + e) * BLD + r];
+            *(bf16x8 *)(dst + J * 512) = v;
         }
         return;
     }
-    if (y == ntg + 1) {
-        if (bcg == 0)
-            for (int64_t i = threadIdx.x; i < nflags; i += blockDim.x) flags[i] = 0;
-        bf16 *dst = Cf + bcg * (int64_t)T16 * NKN * 64 * 8;
-        for (int it = threadIdx.x; it < Q * (N / 8); it += blockDim.x) {
-            const int row = it / (N / 8), cb8 = it % (N / 8);
-            const u32x4 v = row < q ? *(const u32x4 *)(Cc + (int64_t)row * ld + cb8 * 8) : u32x4{0u, 0u, 0u, 0u};
-            const int I = row / 16, kn = cb8 / 4, q4 = cb8 % 4;
-            *(u32x4 *)(dst + (((int64_t)I * NKN + kn) * 64 + (row % 16) + 16 * q4) * 8) = v;
+    if (y >= ntg + NTT) {
+        const int u = y - ntg - NTT;
+        if (u == 0 && bcg == 0)
+            for (int i = threadIdx.x; i < nflags; i += 256) flags[i] = 0;
+        bf16 *dst = Cf + (int64_t)bcg * (T16 * NKN * 512) + lane * 8;
+        // fragments (I, kn) with I % 8 == u: one per wave per step
+        for (int f = wave; f < ((T16 - u + 7) / 8) * NKN; f += 4) {
+            const int I = u + 8 * (f / NKN), kn = f % NKN;
+            const int row = I * 16 + r;
+            const u32x4 v = row < q ? *(const u32x4 *)(Cc + (int64_t)row * ld + kn * 32 + grp * 8) : z;
+            *(u32x4 *)(dst + (I * NKN + kn) * 512) = v;
         }
         return;
     }
     // C B^T tile (ti, tj), computed transposed so each lane holds four
     // consecutive columns j of one row i: D[m = j][n = i] = sum_k B_j C_i
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int r = lane & 15, grp = lane >> 4;
     int tile = y * 4 + wave;
     if (tile >= ntiles) return;
     int ti = 0;
@@ -226,22 +242,24 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16 *__restrict__ B,
     const int tj = tile;
     const int irow = ti * 16 + r, jrow = tj * 16 + r;
     const bool vi = irow < q, vj = jrow < q;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < N; k0 += 32) {
-        const int k = k0 + grp * 8;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        const u32x4 bj = vj ? *(const u32x4 *)(Bc + (int64_t)jrow * ld + k) : z;
-        const u32x4 ci = vi ? *(const u32x4 *)(Cc + (int64_t)irow * ld + k) : z;
-        acc = mfma_bf16(as_bf16x8(bj), as_bf16x8(ci), acc);
+    u32x4 bj[NKN], ci[NKN];
+#pragma unroll
+    for (int k0 = 0; k0 < NKN; ++k0) {
+        const int k = k0 * 32 + grp * 8;
+        bj[k0] = vj ? *(const u32x4 *)(Bc + (int64_t)jrow * ld + k) : z;
+        ci[k0] = vi ? *(const u32x4 *)(Cc + (int64_t)irow * ld + k) : z;
     }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < NKN; ++k0) acc = mfma_bf16(as_bf16x8(bj[k0]), as_bf16x8(ci[k0]), acc);
     // acc[e] = G[i = 16 ti + r][j = 16 tj + 4 grp + e]
     const int i = ti * 16 + r, j0 = tj * 16 + 4 * grp;
     const int J = j0 / 32, q4 = (j0 % 32) / 8, e0 = j0 % 8;
     bf16 o[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = (bf16)acc[e];
-    bf16 *dst = Gf + bcg * (int64_t)T16 * NJ * 64 * 8;
-    *(u32x2 *)(dst + (((int64_t)(i / 16) * NJ + J) * 64 + (i % 16) + 16 * q4) * 8 + e0) = *(const u32x2 *)o;
+    bf16 *dst = Gf + (int64_t)bcg * (T16 * NJ * 512);
+    *(u32x2 *)(dst + ((i / 16) * NJ + J) * 512 + ((i % 16) + 16 * q4) * 8 + e0) = *(const u32x2 *)o;
 }
 
 // ---------------------------------------------------------------------------
@@ -268,7 +286,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const bf16 *__restrict__ x, const bf16 *__restrict__ dt, const float *__restrict__ A,
     const bf16 *__restrict__ Btf, const bf16 *__restrict__ Cf, const bf16 *__restrict__ Gf,
     const float *__restrict__ D, const float *init, bf16 *__restrict__ y, float *fin,
-    float *ring, int *flags, int64_t L, int H, int G, int Q, int nc, int64_t nbh) {
+    float *ring, int *flags, int L, int H, int G, int Q, int nc, int nbh) {
     constexpr int PT = P / 16, NT = N / 16, NTW = NT / 4, NKN = N / 32;
     static_assert(NT % 4 == 0 && N % 32 == 0, "N must be a multiple of 64");
     constexpr int XLD = 256 + 8, HLD = N + 8;
@@ -279,7 +297,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     __shared__ bf16 xs[P * XLD];
     __shared__ bf16 hs[P * HLD];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar offsets
     const int r = lane & 15, grp = lane >> 4;
     // Work item.  Workgroups are dealt round-robin to 8 streams (block k ->
     // stream k % 8, the XCD round-robin); stream x walks chunk-columns
@@ -288,44 +307,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     // smaller id.  With in-order dispatch inside a stream, the lowest
     // unfinished block is always resident and its predecessor is done, so
     // the chain drains; the bounded wait below is a backstop.
-    int c;
-    int64_t bh;
+    int c, bh;
     {
-        const int64_t k = blockIdx.x;
+        const int k = blockIdx.x;
         if (nbh % 8 == 0) {
-            const int64_t per = nbh / 8, m = k >> 3;
-            c = (int)(m / per);
-            bh = (k & 7) * per + (m - (int64_t)c * per);
+            const int per = nbh / 8, m = k >> 3;
+            c = m / per;
+            bh = (k & 7) * per + (m - c * per);
         } else {
-            c = (int)(k / nbh);
-            bh = k - (int64_t)c * nbh;
+            c = k / nbh;
+            bh = k - c * nbh;
         }
     }
-    const int64_t b = bh / H;
-    const int h = (int)(bh - b * H);
+    const int b = bh / H;
+    const int h = bh - b * H;
     const int g = h / (H / G);
-    const int64_t s = (int64_t)c * Q;
-    const int q = (int)min<int64_t>(Q, L - s);
+    const int s = c * Q;
+    const int q = min(Q, L - s);
     const int nb = (q + 31) / 32;          // 32-step blocks holding data
     const int T16 = (q + 15) / 16;
     const int NJ = (Q + 31) / 32, T16Q = Q / 16;
     const u32x4 z4 = {0u, 0u, 0u, 0u};
-    const int64_t bcg = (b * nc + c) * G + g;
-    const bf16 *Btc = Btf + bcg * (int64_t)N * NJ * 32;
-    const bf16 *Gfc = Gf + bcg * (int64_t)T16Q * NJ * 512;
-    const bf16 *Cfc = Cf + bcg * (int64_t)T16Q * NKN * 512;
-    const int64_t PN = (int64_t)P * N;
+    const int bcg = (b * nc + c) * G + g;
+    const bf16 *Btc = Btf + bcg * (N * NJ * 32);
+    const bf16 *Gfc = Gf + bcg * (T16Q * NJ * 512);
+    const bf16 *Cfc = Cf + bcg * (T16Q * NKN * 512);
+    constexpr int PN = P * N;
 
     // x, B^T and dt in one round
-    const int64_t row0 = (b * L + s) * H + h;
+    const int row0 = (b * L + s) * H + h;
     XStage<P> xst;
-    stage_x_load<P>(xst, x + row0 * P, (int64_t)H * P, q);
+    stage_x_load<P>(xst, x + row0 * P, H * P, q);
     bf16x8 bfr[8][NTW];
 #pragma unroll
     for (int J = 0; J < 8; ++J)
 #pragma unroll
         for (int tt = 0; tt < NTW; ++tt)
-            bfr[J][tt] = as_bf16x8(J < nb ? *(const u32x4 *)(Btc + (((int64_t)(wave + 4 * tt) * NJ + J) * 64 + lane) * 8)
+            bfr[J][tt] = as_bf16x8(J < nb ? *(const u32x4 *)(Btc + (((wave + 4 * tt) * NJ + J) * 64 + lane) * 8)
                                           : z4);
 
     // 1. decay prefix
@@ -385,7 +403,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     auto load_tile = [&](int k, int slot) {
         const int I = tile_of(k);
         if (I >= T16) return;
-        const bf16 *gt = Gfc + (int64_t)I * NJ * 512 + lane * 8;
+        const bf16 *gt = Gfc + I * NJ * 512 + lane * 8;
         const int Jd = I >> 1;
 #pragma unroll
         for (int J = 0; J < 7; ++J)
@@ -393,7 +411,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         gdiag[slot] = as_bf16x8(*(const u32x4 *)(gt + Jd * 512));
 #pragma unroll
         for (int kn = 0; kn < NKN; ++kn)
-            cbuf[slot][kn] = as_bf16x8(*(const u32x4 *)(Cfc + (((int64_t)I * NKN + kn) * 64 + lane) * 8));
+            cbuf[slot][kn] = as_bf16x8(*(const u32x4 *)(Cfc + ((I * NKN + kn) * 64 + lane) * 8));
     };
     load_tile(0, 0);
 
@@ -401,8 +419,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     // atomic accesses (coherent across XCDs without cache maintenance), in a
     // lane-major layout so each wave moves one contiguous 512-byte block per
     // access; init / final_state use the [P][N] layout.
-    auto ring_off = [&](int tt, int pt, int half) -> int64_t {
-        return ((((int64_t)(wave * NTW + tt) * PT + pt) * 2 + half) * 64 + lane) * 2;
+    auto ring_off = [&](int tt, int pt, int half) -> int {
+        return ((((wave * NTW + tt) * PT + pt) * 2 + half) * 64 + lane) * 2;
     };
     const float *hp = nullptr;
     if (c > 0) {
@@ -412,7 +430,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             __builtin_amdgcn_s_sleep(1);
             ++n;
         }
-        hp = ring + (int64_t)((c - 1) & 1) * nbh * PN + bh * PN;
+        hp = ring + ((c - 1) & 1) * nbh * PN + bh * PN;
     } else {
         hp = init ? init + bh * PN : nullptr;
     }
@@ -424,13 +442,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const bool have_h = hp != nullptr;
     const float lam_c = __expf(cs_last);
     const bool last = c == nc - 1;
-    float *hout = last ? (fin ? fin + bh * PN : nullptr) : ring + (int64_t)(c & 1) * nbh * PN + bh * PN;
+    float *hout = last ? (fin ? fin + bh * PN : nullptr) : ring + (c & 1) * nbh * PN + bh * PN;
 #pragma unroll
     for (int tt = 0; tt < NTW; ++tt) {
         f32x4 hv[PT];
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
-            const int64_t off = (int64_t)(pt * 16 + r) * N + (wave + 4 * tt) * 16 + 4 * grp;
+            const int off = (pt * 16 + r) * N + (wave + 4 * tt) * 16 + 4 * grp;
             if (!have_h) {
                 hv[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
             } else if (c > 0) {
@@ -447,7 +465,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             const f32x4 hn = lam_c * hv[pt] + acc_s[tt][pt];
             if (hout) {
                 if (last) {
-                    *(f32x4 *)(hout + (int64_t)p * N + n0) = hn;
+                    *(f32x4 *)(hout + p * N + n0) = hn;
                 } else {
                     st_agent_f32x2(hout + ring_off(tt, pt, 0), f32x2{hn[0], hn[1]});
                     st_agent_f32x2(hout + ring_off(tt, pt, 1), f32x2{hn[2], hn[3]});
@@ -528,7 +546,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             for (int pt = 0; pt < PT; ++pt) acc[pt] += ei * tmp[pt];
         }
         if (il < q) {
-            bf16 *yr = y + (row0 + (int64_t)il * H) * P;
+            bf16 *yr = y + (row0 + il * H) * P;
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
                 const int p0 = pt * 16 + 4 * grp;
@@ -542,7 +560,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 }
 
 bool fused_supported(const Dims &d) {
-    return d.dtype == 1 && d.P == 64 && d.N == 128 && d.Q <= 256 && d.nc >= 1;
+    if (!(d.dtype == 1 && d.P == 64 && d.N == 128 && d.Q <= 256 && d.nc >= 1)) return false;
+    // element offsets inside the single-pass kernel are 32-bit
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t nbh = d.b * d.H, T16 = d.Q / 16, NJ = (d.Q + 31) / 32, nbcg = d.b * d.nc * d.G;
+    return d.b * d.L * d.H * d.P < lim && d.nc * nbh < lim && 2 * nbh * d.P * d.N < lim &&
+           nbcg * T16 * NJ * 512 < lim && nbcg * d.N * NJ * 32 < lim && nbcg * T16 * (d.N / 32) * 512 < lim;
 }
 
 hipError_t launch_fused_prep(const Dims &d, const void *B, const void *C, void *Gf, void *Btf,
@@ -551,10 +574,10 @@ hipError_t launch_fused_prep(const Dims &d, const void *B, const void *C, void *
     int ntiles = 0;
     for (int ti = 0; ti < T16; ++ti) ntiles += (ti | 1) + 1;
     const int ntg = (ntiles + 3) / 4;
-    dim3 grid((unsigned)(d.b * d.nc * d.G), (unsigned)(ntg + 2));
-    k_fused_prep<<<grid, 256, 0, st>>>((const bf16 *)B, (const bf16 *)C, (bf16 *)Gf, (bf16 *)Btf,
-                                       (bf16 *)Cf, flags, d.b * d.H, d.L, (int)d.G, (int)d.N,
-                                       (int)d.Q, (int)d.nc);
+    dim3 grid((unsigned)(d.b * d.nc * d.G), (unsigned)(ntg + d.N / 16 + 8));
+    k_fused_prep<128><<<grid, 256, 0, st>>>((const bf16 *)B, (const bf16 *)C, (bf16 *)Gf, (bf16 *)Btf,
+                                            (bf16 *)Cf, flags, (int)(d.b * d.H), (int)d.L, (int)d.G,
+                                            (int)d.Q, (int)d.nc);
     return hipGetLastError();
 }
 
@@ -565,7 +588,8 @@ hipError_t launch_fused_main(const Dims &d, const void *x, const void *dt, const
     const unsigned grid = (unsigned)(d.b * d.nc * d.H);
     k_ssd_fused<64, 128><<<grid, 256, 0, st>>>(
         (const bf16 *)x, (const bf16 *)dt, A, (const bf16 *)Btf, (const bf16 *)Cf, (const bf16 *)Gf, D,
-        init, (bf16 *)y, fin, ring, flags, d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc, d.b * d.H);
+        init, (bf16 *)y, fin, ring, flags, (int)d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc,
+        (int)(d.b * d.H));
     return hipGetLastError();
 }
 

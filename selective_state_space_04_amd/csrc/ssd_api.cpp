@@ -123,7 +123,7 @@ FusedLayout fused_layout(const ssd::Dims &d) {
     f.Cf = align256(f.Btf + nbcg * d.N * NJ * 64);
     f.ring = align256(f.Cf + nbcg * T16 * (d.N / 32) * 1024);
     f.flags = align256(f.ring + 2 * d.b * d.H * d.P * d.N * 4);
-    f.total = align256(f.flags + d.b * d.H * 4);
+    f.total = align256(f.flags + d.b * d.H * 4 * 4);  // one flag per (b, h, wave)
     if (d.b == 0 || d.nc == 0) f.total = 0;
     return f;
 }

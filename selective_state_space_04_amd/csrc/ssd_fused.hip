@@ -63,14 +63,14 @@ struct XStage {
     u32x4 v[XB][4];
 };
 
-// Block blk -> (row group br, column block bc).  Each 32-lane half-wave
-// covers 16 consecutive row groups and two adjacent column blocks, so its
-// transposed 8-byte LDS stores hit 64 distinct banks.
+// Block blk -> (row group br, column block bc).  The eight column blocks of
+// a row group are eight adjacent lanes, so each load instruction reads whole
+// 128-byte rows (P = 64: one cache line per row).
 template <int P>
 __device__ __forceinline__ void xstage_block(int blk, int &br, int &bc) {
     constexpr int NBC = XStage<P>::NBC;
-    bc = (blk >> 4) % NBC;
-    br = (blk & 15) + 16 * ((blk >> 4) / NBC);
+    bc = blk % NBC;
+    br = blk / NBC;
 }
 
 template <int P>
@@ -291,7 +291,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     static_assert(NT % 4 == 0 && N % 32 == 0, "N must be a multiple of 64");
     constexpr int XLD = 256 + 8, HLD = N + 8;
     __shared__ float cs_s[256];
-    __shared__ float wv_s[256];  // w_j during step 3, then v_j = exp(r_J(j) - cs_j)
+    __shared__ float wv_s[256];  // w_j = exp(cs_last - cs_j), chunk-state weights
+    __shared__ float v_s[256];   // v_j = exp(r_J(j) - cs_j), intra-chunk mask factor
     __shared__ float wsum_s[4];
     __shared__ float ref_s[8];   // r_J: cs at the last step of 32-block J
     __shared__ bf16 xs[P * XLD];
@@ -361,6 +362,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         __syncthreads();
         if (tid < 8) ref_s[tid] = cs_s[min(32 * tid + 31, q - 1)];
         wv_s[tid] = __expf(cs_s[q - 1] - v);
+        // v_j relative to the end of j's own 32-block (cs past q repeats)
+        v_s[tid] = __expf(cs_s[min(32 * (tid >> 5) + 31, q - 1)] - v);
     }
     const float cs_last = cs_s[q - 1];
 
@@ -368,7 +371,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     stage_x_write_plain<P>(xst, xs, XLD);
     __syncthreads();
 
-    // 3. chunk state: acc_s[tt][pt] = S^T[n = 16 (wave + 4 tt) + 4 grp + e][p = 16 pt + r]
+    // 3. hand-off, first half: wait until wave `wave` of chunk c - 1 of this
+    // (b, h) has published its slice of h_{c-1}, then load the slice (it
+    // arrives while the chunk state is computed).  The ring is read and
+    // written with agent-scope atomic accesses (coherent across XCDs without
+    // cache maintenance), in a lane-major layout so each wave moves one
+    // contiguous 512-byte block per access; init / final_state use the
+    // [P][N] layout.  hv[tt][pt][e] = h_{c-1}[p = 16 pt + r][n = 16 (wave + 4 tt) + 4 grp + e]
+    auto ring_off = [&](int tt, int pt, int half) -> int {
+        return ((((wave * NTW + tt) * PT + pt) * 2 + half) * 64 + lane) * 2;
+    };
+    int *myflag = flags + bh * 4 + wave;
+    const bool have_h = c > 0 || init != nullptr;
+    f32x4 hv[NTW][PT];
+    if (c > 0) {
+        int n = 0;
+        while (__hip_atomic_load(myflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < c && n < kSpinLimit) {
+            __builtin_amdgcn_s_sleep(1);
+            ++n;
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const float *hp = ring + ((c - 1) & 1) * nbh * PN + bh * PN;
+#pragma unroll
+        for (int tt = 0; tt < NTW; ++tt)
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const f32x2 lo = ld_agent_f32x2(hp + ring_off(tt, pt, 0));
+                const f32x2 hi = ld_agent_f32x2(hp + ring_off(tt, pt, 1));
+                hv[tt][pt] = f32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+    } else {
+#pragma unroll
+        for (int tt = 0; tt < NTW; ++tt)
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt)
+                hv[tt][pt] = init ? *(const f32x4 *)(init + bh * PN + (pt * 16 + r) * N + (wave + 4 * tt) * 16 + 4 * grp)
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // 4. chunk state: acc_s[tt][pt] = S^T[n = 16 (wave + 4 tt) + 4 grp + e][p = 16 pt + r]
     f32x4 acc_s[NTW][PT];
 #pragma unroll
     for (int tt = 0; tt < NTW; ++tt)
@@ -415,54 +456,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     };
     load_tile(0, 0);
 
-    // 4. state hand-off.  The ring is read and written with agent-scope
-    // atomic accesses (coherent across XCDs without cache maintenance), in a
-    // lane-major layout so each wave moves one contiguous 512-byte block per
-    // access; init / final_state use the [P][N] layout.
-    auto ring_off = [&](int tt, int pt, int half) -> int {
-        return ((((wave * NTW + tt) * PT + pt) * 2 + half) * 64 + lane) * 2;
-    };
-    const float *hp = nullptr;
-    if (c > 0) {
-        int n = 0;
-        while (__hip_atomic_load(flags + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < c &&
-               n < kSpinLimit) {
-            __builtin_amdgcn_s_sleep(1);
-            ++n;
-        }
-        hp = ring + ((c - 1) & 1) * nbh * PN + bh * PN;
-    } else {
-        hp = init ? init + bh * PN : nullptr;
-    }
-    __syncthreads();  // step 3 is done in every wave: wv_s may be rewritten
-    {
-        const int J = tid >> 5;   // v_j relative to the end of j's own 32-block
-        wv_s[tid] = __expf(ref_s[J] - cs_s[tid]);
-    }
-    const bool have_h = hp != nullptr;
+    // 5. hand-off, second half: h_c = exp(cs_last) h_{c-1} + S_c to this
+    // wave's ring slice (or final_state); h_{c-1} as bf16 to LDS.  The wave
+    // raises its flag after its first output tile, once these stores have
+    // completed.
     const float lam_c = __expf(cs_last);
     const bool last = c == nc - 1;
     float *hout = last ? (fin ? fin + bh * PN : nullptr) : ring + (c & 1) * nbh * PN + bh * PN;
 #pragma unroll
     for (int tt = 0; tt < NTW; ++tt) {
-        f32x4 hv[PT];
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            const int off = (pt * 16 + r) * N + (wave + 4 * tt) * 16 + 4 * grp;
-            if (!have_h) {
-                hv[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            } else if (c > 0) {
-                const f32x2 lo = ld_agent_f32x2(hp + ring_off(tt, pt, 0));
-                const f32x2 hi = ld_agent_f32x2(hp + ring_off(tt, pt, 1));
-                hv[pt] = f32x4{lo[0], lo[1], hi[0], hi[1]};
-            } else {
-                hv[pt] = *(const f32x4 *)(hp + off);
-            }
-        }
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
             const int p = pt * 16 + r, n0 = (wave + 4 * tt) * 16 + 4 * grp;
-            const f32x4 hn = lam_c * hv[pt] + acc_s[tt][pt];
+            const f32x4 hn = lam_c * hv[tt][pt] + acc_s[tt][pt];
             if (hout) {
                 if (last) {
                     *(f32x4 *)(hout + p * N + n0) = hn;
@@ -473,87 +479,118 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             }
             bf16 hb[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) hb[e] = (bf16)hv[pt][e];
+            for (int e = 0; e < 4; ++e) hb[e] = (bf16)hv[tt][pt][e];
             *(u32x2 *)(hs + p * HLD + n0) = *(const u32x2 *)hb;
         }
     }
-    if (!last) __builtin_amdgcn_s_waitcnt(0);  // this wave's ring stores are complete
-    __syncthreads();                            // ... in every wave; hs and wv_s complete
-    if (!last && tid == 0) __hip_atomic_store(flags + bh, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();  // hs complete in every wave
 
     // 5. output tiles
     const float Dh = D ? D[h] : 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int cur = k & 1;
-        if (k < 3) load_tile(k + 1, cur ^ 1);
+        if (k > 0 && k < 3) load_tile(k + 1, cur ^ 1);
         const int I = tile_of(k);
-        if (I >= T16) continue;
+        const bool valid = I < T16;
         const int il = I * 16 + r;
-        const float csi = cs_s[il];
-        const int Jd = I >> 1;
         f32x4 acc[PT];
+        if (valid) {
+            const float csi = cs_s[il];
+            const int Jd = I >> 1;
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int J = 0; J < 7; ++J) {
-            if (J < Jd) {
-                const float u = __expf(csi - ref_s[J]);
-                const f32x4 v0 = *(const f32x4 *)(wv_s + 32 * J + grp * 8);
-                const f32x4 v1 = *(const f32x4 *)(wv_s + 32 * J + grp * 8 + 4);
-                bf16x8 gm = gbuf[cur][J];
+            for (int J = 0; J < 7; ++J) {
+                if (J < Jd) {
+                    const float u = __expf(csi - ref_s[J]);
+                    const f32x4 v0 = *(const f32x4 *)(v_s + 32 * J + grp * 8);
+                    const f32x4 v1 = *(const f32x4 *)(v_s + 32 * J + grp * 8 + 4);
+                    bf16x8 gm = gbuf[cur][J];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    gm[e] = (bf16)((float)gm[e] * (u * v0[e]));
-                    gm[e + 4] = (bf16)((float)gm[e + 4] * (u * v1[e]));
+                    for (int e = 0; e < 4; ++e) {
+                        gm[e] = (bf16)((float)gm[e] * (u * v0[e]));
+                        gm[e + 4] = (bf16)((float)gm[e + 4] * (u * v1[e]));
+                    }
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) {
+                        const bf16x8 ax = *(const bf16x8 *)(xs + (pt * 16 + r) * XLD + 32 * J + grp * 8);
+                        acc[pt] = mfma_bf16(ax, gm, acc[pt]);
+                    }
+                }
+            }
+            {
+                const int jl = 32 * Jd + grp * 8;
+                const bf16x8 gd = gdiag[cur];
+                bf16x8 bm;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = jl + e;
+                    bm[e] = (bf16)((j <= il) ? __expf(csi - cs_s[j]) * (float)gd[e] : 0.f);
                 }
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) {
-                    const bf16x8 ax = *(const bf16x8 *)(xs + (pt * 16 + r) * XLD + 32 * J + grp * 8);
-                    acc[pt] = mfma_bf16(ax, gm, acc[pt]);
+                    const bf16x8 ax = *(const bf16x8 *)(xs + (pt * 16 + r) * XLD + jl);
+                    acc[pt] = mfma_bf16(ax, bm, acc[pt]);
                 }
             }
-        }
-        {
-            const int jl = 32 * Jd + grp * 8;
-            const bf16x8 gd = gdiag[cur];
-            bf16x8 bm;
+            if (have_h) {
+                f32x4 tmp[PT];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int j = jl + e;
-                bm[e] = (bf16)((j <= il) ? __expf(csi - cs_s[j]) * (float)gd[e] : 0.f);
-            }
+                for (int pt = 0; pt < PT; ++pt) tmp[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                const bf16x8 ax = *(const bf16x8 *)(xs + (pt * 16 + r) * XLD + jl);
-                acc[pt] = mfma_bf16(ax, bm, acc[pt]);
-            }
-        }
-        if (have_h) {
-            f32x4 tmp[PT];
+                for (int kn = 0; kn < NKN; ++kn) {
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) tmp[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kn = 0; kn < NKN; ++kn) {
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    const bf16x8 ah = *(const bf16x8 *)(hs + (pt * 16 + r) * HLD + kn * 32 + grp * 8);
-                    tmp[pt] = mfma_bf16(ah, cbuf[cur][kn], tmp[pt]);
+                    for (int pt = 0; pt < PT; ++pt) {
+                        const bf16x8 ah = *(const bf16x8 *)(hs + (pt * 16 + r) * HLD + kn * 32 + grp * 8);
+                        tmp[pt] = mfma_bf16(ah, cbuf[cur][kn], tmp[pt]);
+                    }
                 }
-            }
-            const float ei = __expf(csi);
+                const float ei = __expf(csi);
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) acc[pt] += ei * tmp[pt];
+                for (int pt = 0; pt < PT; ++pt) acc[pt] += ei * tmp[pt];
+            }
         }
-        if (il < q) {
-            bf16 *yr = y + (row0 + il * H) * P;
+        if (k == 0) {
+            // this wave's ring slice is complete: raise its flag, then fetch tile 1
+            if (!last) {
+                __builtin_amdgcn_s_waitcnt(0);
+                if (lane == 0) __hip_atomic_store(myflag, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            load_tile(1, 1);
+        }
+        if (valid) {
+            // Lane (r, grp) holds row i = 16 I + r, columns 16 pt + 4 grp .. + 3
+            // (block M[grp][pt]).  Transpose the 4 x 4 block grid across the
+            // lane groups (butterfly over lane ^ 16, lane ^ 32) so lane group g
+            // holds M[0..3][g] = columns 16 g .. 16 g + 15: two 16-byte stores
+            // per lane instead of four 8-byte ones.
+            u32x2 m[PT];
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
                 const int p0 = pt * 16 + 4 * grp;
                 bf16 o[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc[pt][e] + Dh * (float)xs[(p0 + e) * XLD + il]);
-                *(u32x2 *)(yr + p0) = *(const u32x2 *)o;
+                m[pt] = *(const u32x2 *)o;
+            }
+            auto xchg = [](u32x2 v, int mask) {
+                return u32x2{(uint32_t)__shfl_xor((int)v[0], mask, 64), (uint32_t)__shfl_xor((int)v[1], mask, 64)};
+            };
+            const bool g1 = grp & 1, g2 = grp & 2;
+            // stage 1: keep the columns of this lane's parity, swap the rest with g ^ 1
+            const u32x2 c0 = g1 ? m[1] : m[0], c2 = g1 ? m[3] : m[2];          // M[g][g&1], M[g][2+(g&1)]
+            const u32x2 c1 = xchg(g1 ? m[0] : m[1], 16), c3 = xchg(g1 ? m[2] : m[3], 16);  // M[g^1][..]
+            // stage 2: keep column g, swap column g ^ 2 with g ^ 2
+            const u32x2 t0 = g2 ? c2 : c0, t1 = g2 ? c3 : c1;                 // M[g][g], M[g^1][g]
+            const u32x2 t2 = xchg(g2 ? c0 : c2, 32), t3 = xchg(g2 ? c1 : c3, 32);  // M[g^2][g], M[g^3][g]
+            // order by source row: out[s] = t[s ^ g]
+            const u32x2 a0 = g1 ? t1 : t0, a1 = g1 ? t0 : t1, a2 = g1 ? t3 : t2, a3 = g1 ? t2 : t3;
+            const u32x2 o0 = g2 ? a2 : a0, o1 = g2 ? a3 : a1, o2 = g2 ? a0 : a2, o3 = g2 ? a1 : a3;
+            if (il < q) {
+                bf16 *yr = y + (row0 + il * H) * P + 16 * grp;
+                *(u32x4 *)yr = u32x4{o0[0], o0[1], o1[0], o1[1]};
+                *(u32x4 *)(yr + 8) = u32x4{o2[0], o2[1], o3[0], o3[1]};
             }
         }
     }
@@ -576,7 +613,7 @@ hipError_t launch_fused_prep(const Dims &d, const void *B, const void *C, void *
     const int ntg = (ntiles + 3) / 4;
     dim3 grid((unsigned)(d.b * d.nc * d.G), (unsigned)(ntg + d.N / 16 + 8));
     k_fused_prep<128><<<grid, 256, 0, st>>>((const bf16 *)B, (const bf16 *)C, (bf16 *)Gf, (bf16 *)Btf,
-                                            (bf16 *)Cf, flags, (int)(d.b * d.H), (int)d.L, (int)d.G,
+                                            (bf16 *)Cf, flags, (int)(d.b * d.H * 4), (int)d.L, (int)d.G,
                                             (int)d.Q, (int)d.nc);
     return hipGetLastError();
 }

@@ -291,8 +291,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     static_assert(NT % 4 == 0 && N % 32 == 0, "N must be a multiple of 64");
     constexpr int XLD = 256 + 8, HLD = N + 8;
     __shared__ float cs_s[256];
-    __shared__ float wv_s[256];  // w_j = exp(cs_last - cs_j), chunk-state weights
-    __shared__ float v_s[256];   // v_j = exp(r_J(j) - cs_j), intra-chunk mask factor
+    // w_j = exp(cs_last - cs_j) (chunk-state weights) until step 4 is done in
+    // every wave, then v_j = exp(r_J(j) - cs_j) (intra-chunk mask factor).
+    // One array keeps the workgroup within a third of the CU's LDS.
+    __shared__ float wv_s[256];
     __shared__ float wsum_s[4];
     __shared__ float ref_s[8];   // r_J: cs at the last step of 32-block J
     __shared__ bf16 xs[P * XLD];
@@ -362,8 +364,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         __syncthreads();
         if (tid < 8) ref_s[tid] = cs_s[min(32 * tid + 31, q - 1)];
         wv_s[tid] = __expf(cs_s[q - 1] - v);
-        // v_j relative to the end of j's own 32-block (cs past q repeats)
-        v_s[tid] = __expf(cs_s[min(32 * (tid >> 5) + 31, q - 1)] - v);
     }
     const float cs_last = cs_s[q - 1];
 
@@ -456,6 +456,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     };
     load_tile(0, 0);
 
+    __syncthreads();  // step 4 is done in every wave: w may be replaced by v
+    // v_j relative to the end of j's own 32-block (cs past q repeats)
+    wv_s[tid] = __expf(ref_s[tid >> 5] - cs_s[tid]);
+
     // 5. hand-off, second half: h_c = exp(cs_last) h_{c-1} + S_c to this
     // wave's ring slice (or final_state); h_{c-1} as bf16 to LDS.  The wave
     // raises its flag after its first output tile, once these stores have
@@ -483,7 +487,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             *(u32x2 *)(hs + p * HLD + n0) = *(const u32x2 *)hb;
         }
     }
-    __syncthreads();  // hs complete in every wave
+    __syncthreads();  // hs and v complete in every wave
 
     // 5. output tiles
     const float Dh = D ? D[h] : 0.f;
@@ -504,8 +508,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             for (int J = 0; J < 7; ++J) {
                 if (J < Jd) {
                     const float u = __expf(csi - ref_s[J]);
-                    const f32x4 v0 = *(const f32x4 *)(v_s + 32 * J + grp * 8);
-                    const f32x4 v1 = *(const f32x4 *)(v_s + 32 * J + grp * 8 + 4);
+                    const f32x4 v0 = *(const f32x4 *)(wv_s + 32 * J + grp * 8);
+                    const f32x4 v1 = *(const f32x4 *)(wv_s + 32 * J + grp * 8 + 4);
                     bf16x8 gm = gbuf[cur][J];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {

@@ -158,17 +158,12 @@ __device__ __forceinline__ void stage_x_write(const XStage<P> &st, bf16 *xs, bf1
 //                   (I < Q/16, J <= I/2; the diagonal 32-block is complete)
 //   Btf[t][J][l]  = B rows 32 J + 8 q4 .. + 7 at column 16 t + r  (B^T)
 //   Cf [I][k][l]  = C row 16 I + r, columns 32 k + 8 q4 .. + 7
-// Rows past the sequence end are zero.  grid.y: [0, ntg) C B^T tiles (four
-// 16 x 16 tiles per workgroup); ntg + t (t < N/16): B^T fragments of state
-// column tile t, staged through LDS; ntg + N/16 + u (u < 8): C fragments of
-// row tiles I with I % 8 == u (u = 0 also clears the flags).
+// Rows past the sequence end are zero.  One workgroup per 64 x 64 block
+// (bi, bj), bj <= bi, of C B^T: it stages C rows 64 bi .. + 63 and B rows
+// 64 bj .. + 63 in LDS (whole-row loads) and wave w computes row tile
+// 4 bi + w.  Diagonal blocks also write the C fragments of their rows and
+// the B^T fragments of their 32-blocks; block (0, 0) clears the flags.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int prep_tiles(int T16) {
-    int n = 0;
-    for (int ti = 0; ti < T16; ++ti) n += (ti | 1) + 1;
-    return n;
-}
-
 template <int N>
 __global__ __launch_bounds__(256) void k_fused_prep(const bf16 *__restrict__ B,
                                                     const bf16 *__restrict__ C,
@@ -176,9 +171,11 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16 *__restrict__ B,
                                                     bf16 *__restrict__ Cf, int *flags, int nflags,
                                                     int L, int G, int Q, int nc) {
     constexpr int NKN = N / 32, NTT = N / 16;
+    constexpr int RLD = N + 8;            // LDS row stride (elements): 16-byte reads spread over banks
+    constexpr int RCH = N / 8;            // 16-byte pieces per row
+    __shared__ bf16 cs_rows[64 * RLD];
+    __shared__ bf16 bs_rows[64 * RLD];
     const int T16 = Q / 16, NJ = (Q + 31) / 32;
-    const int ntiles = prep_tiles(T16);
-    const int ntg = (ntiles + 3) / 4;
     const int bcg = blockIdx.x;
     const int g = bcg % G;
     const int bc = bcg / G;
@@ -186,80 +183,81 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16 *__restrict__ B,
     const int b = bc / nc;
     const int s = c * Q;
     const int q = min(Q, L - s);
+    // block (bi, bj) from the lower-triangular index
+    int bi = 0, bj = blockIdx.y;
+    while (bj > bi) {
+        bj -= bi + 1;
+        ++bi;
+    }
+    const bool diag = bi == bj;
     const bf16 *Bc = B + ((int64_t)(b * L + s) * G + g) * N;
     const bf16 *Cc = C + ((int64_t)(b * L + s) * G + g) * N;
     const int ld = G * N;
-    const int y = blockIdx.y;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int r = lane & 15, grp = lane >> 4;
     const u32x4 z = {0u, 0u, 0u, 0u};
-    if (y >= ntg && y < ntg + NTT) {
-        // B^T fragments of column tile t: B[0 .. Q-1][16 t .. 16 t + 15] into LDS
-        // (two 16-byte pieces per row), then 8 rows x 1 column per lane.
-        constexpr int BLD = 20;  // row stride: 10 dwords, 8-byte aligned; 8-row groups fall on distinct banks
-        __shared__ bf16 bt_s[256 * BLD];
-        const int t = y - ntg;
-        for (int it = threadIdx.x; it < NJ * 64; it += 256) {  // rows up to 32 NJ; past q zero
-            const int row = it >> 1, half = it & 1;
-            const u32x4 v = row < q ? *(const u32x4 *)(Bc + (int64_t)row * ld + t * 16 + half * 8) : z;
-            u32x2 *d = (u32x2 *)(bt_s + row * BLD + half * 8);  // 8-byte aligned: two 8-byte stores
-            d[0] = u32x2{v[0], v[1]};
-            d[1] = u32x2{v[2], v[3]};
+    if (diag && bi == 0 && bcg == 0)
+        for (int i = tid; i < nflags; i += 256) flags[i] = 0;
+
+    // stage: 64 C rows and 64 B rows, RCH adjacent lanes per row (rows past q: zero)
+    for (int it = tid; it < 64 * RCH; it += 256) {
+        const int row = it / RCH, ch = it % RCH;
+        const int ci = 64 * bi + row, bj_row = 64 * bj + row;
+        const u32x4 vc = ci < q ? *(const u32x4 *)(Cc + (int64_t)ci * ld + ch * 8) : z;
+        const u32x4 vb = bj_row < q ? *(const u32x4 *)(Bc + (int64_t)bj_row * ld + ch * 8) : z;
+        *(u32x4 *)(cs_rows + row * RLD + ch * 8) = vc;
+        *(u32x4 *)(bs_rows + row * RLD + ch * 8) = vb;
+    }
+    __syncthreads();
+
+    const int I = 4 * bi + wave;  // row tile of this wave
+    if (I < T16) {
+        // C B^T tiles (I, jt), jt = 4 bj .. 4 bj + 3, computed transposed so each
+        // lane holds four consecutive columns j of one row i:
+        // D[m = j][n = i] = sum_k B_j C_i
+        bf16x8 cf[NKN];
+#pragma unroll
+        for (int k = 0; k < NKN; ++k)
+            cf[k] = *(const bf16x8 *)(cs_rows + (wave * 16 + r) * RLD + k * 32 + grp * 8);
+        bf16 *dstg = Gf + (int64_t)bcg * (T16 * NJ * 512);
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+            const int jt = 4 * bj + jq;
+            if (jt * 16 >= Q) break;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < NKN; ++k) {
+                const bf16x8 bv = *(const bf16x8 *)(bs_rows + (jq * 16 + r) * RLD + k * 32 + grp * 8);
+                acc = mfma_bf16(bv, cf[k], acc);
+            }
+            // acc[e] = G[i = 16 I + r][j = 16 jt + 4 grp + e]
+            const int j0 = jt * 16 + 4 * grp;
+            const int J = j0 / 32, q4 = (j0 % 32) / 8, e0 = j0 % 8;
+            bf16 o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = (bf16)acc[e];
+            *(u32x2 *)(dstg + (I * NJ + J) * 512 + (r + 16 * q4) * 8 + e0) = *(const u32x2 *)o;
         }
-        __syncthreads();
-        bf16 *dst = Btf + (int64_t)bcg * (N * NJ * 32) + (int64_t)t * (NJ * 512) + lane * 8;
-        for (int J = wave; J < NJ; J += 4) {
+        if (diag) {
+            // C fragments of row tile I
+            bf16 *dstc = Cf + (int64_t)bcg * (T16 * NKN * 512) + lane * 8;
+#pragma unroll
+            for (int k = 0; k < NKN; ++k) *(bf16x8 *)(dstc + (I * NKN + k) * 512) = cf[k];
+        }
+    }
+    if (diag) {
+        // B^T fragments of 32-blocks J = 2 bi, 2 bi + 1: (t, J) pairs, 2 NTT per block
+        bf16 *dstb = Btf + (int64_t)bcg * (N * NJ * 32) + lane * 8;
+        for (int f = wave; f < 2 * NTT; f += 4) {
+            const int J = 2 * bi + (f & 1), t = f >> 1;
+            if (J >= NJ) continue;
             bf16x8 v;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = bt_s[(32 * J + 8 * grp + e) * BLD + r];
-            *(bf16x8 *)(dst + J * 512) = v;
+            for (int e = 0; e < 8; ++e) v[e] = bs_rows[((f & 1) * 32 + 8 * grp + e) * RLD + t * 16 + r];
+            *(bf16x8 *)(dstb + (t * NJ + J) * 512) = v;
         }
-        return;
     }
-    if (y >= ntg + NTT) {
-        const int u = y - ntg - NTT;
-        if (u == 0 && bcg == 0)
-            for (int i = threadIdx.x; i < nflags; i += 256) flags[i] = 0;
-        bf16 *dst = Cf + (int64_t)bcg * (T16 * NKN * 512) + lane * 8;
-        // fragments (I, kn) with I % 8 == u: one per wave per step
-        for (int f = wave; f < ((T16 - u + 7) / 8) * NKN; f += 4) {
-            const int I = u + 8 * (f / NKN), kn = f % NKN;
-            const int row = I * 16 + r;
-            const u32x4 v = row < q ? *(const u32x4 *)(Cc + (int64_t)row * ld + kn * 32 + grp * 8) : z;
-            *(u32x4 *)(dst + (I * NKN + kn) * 512) = v;
-        }
-        return;
-    }
-    // C B^T tile (ti, tj), computed transposed so each lane holds four
-    // consecutive columns j of one row i: D[m = j][n = i] = sum_k B_j C_i
-    int tile = y * 4 + wave;
-    if (tile >= ntiles) return;
-    int ti = 0;
-    while (tile >= (ti | 1) + 1) {
-        tile -= (ti | 1) + 1;
-        ++ti;
-    }
-    const int tj = tile;
-    const int irow = ti * 16 + r, jrow = tj * 16 + r;
-    const bool vi = irow < q, vj = jrow < q;
-    u32x4 bj[NKN], ci[NKN];
-#pragma unroll
-    for (int k0 = 0; k0 < NKN; ++k0) {
-        const int k = k0 * 32 + grp * 8;
-        bj[k0] = vj ? *(const u32x4 *)(Bc + (int64_t)jrow * ld + k) : z;
-        ci[k0] = vi ? *(const u32x4 *)(Cc + (int64_t)irow * ld + k) : z;
-    }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k0 = 0; k0 < NKN; ++k0) acc = mfma_bf16(as_bf16x8(bj[k0]), as_bf16x8(ci[k0]), acc);
-    // acc[e] = G[i = 16 ti + r][j = 16 tj + 4 grp + e]
-    const int i = ti * 16 + r, j0 = tj * 16 + 4 * grp;
-    const int J = j0 / 32, q4 = (j0 % 32) / 8, e0 = j0 % 8;
-    bf16 o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = (bf16)acc[e];
-    bf16 *dst = Gf + (int64_t)bcg * (T16 * NJ * 512);
-    *(u32x2 *)(dst + ((i / 16) * NJ + J) * 512 + ((i % 16) + 16 * q4) * 8 + e0) = *(const u32x2 *)o;
 }
 
 // ---------------------------------------------------------------------------
@@ -611,11 +609,8 @@ bool fused_supported(const Dims &d) {
 
 hipError_t launch_fused_prep(const Dims &d, const void *B, const void *C, void *Gf, void *Btf,
                              void *Cf, int *flags, hipStream_t st) {
-    const int T16 = (int)(d.Q / 16);
-    int ntiles = 0;
-    for (int ti = 0; ti < T16; ++ti) ntiles += (ti | 1) + 1;
-    const int ntg = (ntiles + 3) / 4;
-    dim3 grid((unsigned)(d.b * d.nc * d.G), (unsigned)(ntg + d.N / 16 + 8));
+    const int T64 = (int)((d.Q + 63) / 64);
+    dim3 grid((unsigned)(d.b * d.nc * d.G), (unsigned)(T64 * (T64 + 1) / 2));
     k_fused_prep<128><<<grid, 256, 0, st>>>((const bf16 *)B, (const bf16 *)C, (bf16 *)Gf, (bf16 *)Btf,
                                             (bf16 *)Cf, flags, (int)(d.b * d.H * 4), (int)d.L, (int)d.G,
                                             (int)d.Q, (int)d.nc);

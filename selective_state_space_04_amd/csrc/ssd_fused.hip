@@ -33,6 +33,8 @@
 // L2 caches; the writer raises the flag at its very end, after waiting for
 // its stores to complete (s_waitcnt), and the reader issues its state loads
 // only after it has seen the flag.
+#include <type_traits>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -83,7 +85,10 @@ __device__ __forceinline__ void stage_x_load(XStage<P> &st, const bf16 *__restri
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int rr = br * 4 + k;
-            st.v[i][k] = rr < nvalid ? *(const u32x4 *)(src + rr * ld + bc * 8) : u32x4{0u, 0u, 0u, 0u};
+            // x is read once: a non-temporal load keeps it from displacing the
+            // per-chunk operands every head of the chunk re-reads
+            st.v[i][k] = rr < nvalid ? __builtin_nontemporal_load((const u32x4 *)(src + rr * ld + bc * 8))
+                                     : u32x4{0u, 0u, 0u, 0u};
         }
     }
 }
@@ -279,6 +284,31 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16 *__restrict__ B,
 //      + D x_i, stored as bf16.  The next tile's C B^T and C fragments load
 //      while the current tile computes.
 // ---------------------------------------------------------------------------
+// Operands of one 16-row output tile I: its off-diagonal C B^T fragments
+// (32-blocks J < I / 2; NG is the most a tile in this slot can have), the
+// diagonal one and the four C fragments.  With `all` every off-diagonal slot
+// is loaded (in bounds, possibly unused), so the number of loads is fixed.
+template <int NG>
+struct TileOps {
+    static constexpr int kNG = NG;
+    u32x4 g[NG];
+    u32x4 gd;
+    u32x4 cf[4];
+};
+
+template <int NG>
+__device__ __forceinline__ void tile_load(TileOps<NG> &t, const bf16 *Gfc, const bf16 *Cfc, int I, int NJ,
+                                          int lane, bool all) {
+    const bf16 *gt = Gfc + I * NJ * 512 + lane * 8;
+    const int Jd = I >> 1;
+#pragma unroll
+    for (int J = 0; J < NG; ++J)
+        if (all || J < Jd) t.g[J] = *(const u32x4 *)(gt + J * 512);
+    t.gd = *(const u32x4 *)(gt + Jd * 512);
+#pragma unroll
+    for (int kn = 0; kn < 4; ++kn) t.cf[kn] = *(const u32x4 *)(Cfc + ((I * 4 + kn) * 64 + lane) * 8);
+}
+
 template <int P, int N>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_ssd_fused(
     const bf16 *__restrict__ x, const bf16 *__restrict__ dt, const float *__restrict__ A,
@@ -436,23 +466,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         }
     }
 
-    // fragments of the first output tile, in flight across the hand-off
-    auto tile_of = [&](int k) { return (k & 1) ? (8 * (k >> 1) + 7 - wave) : (8 * (k >> 1) + wave); };
-    bf16x8 gbuf[2][7], gdiag[2], cbuf[2][NKN];
-    auto load_tile = [&](int k, int slot) {
-        const int I = tile_of(k);
-        if (I >= T16) return;
-        const bf16 *gt = Gfc + I * NJ * 512 + lane * 8;
-        const int Jd = I >> 1;
-#pragma unroll
-        for (int J = 0; J < 7; ++J)
-            if (J < Jd) gbuf[slot][J] = as_bf16x8(*(const u32x4 *)(gt + J * 512));
-        gdiag[slot] = as_bf16x8(*(const u32x4 *)(gt + Jd * 512));
-#pragma unroll
-        for (int kn = 0; kn < NKN; ++kn)
-            cbuf[slot][kn] = as_bf16x8(*(const u32x4 *)(Cfc + ((I * NKN + kn) * 64 + lane) * 8));
-    };
-    load_tile(0, 0);
+    // Output tiles of this wave: T_k = {w, 7 - w, 8 + w, 15 - w}; tile T_k has
+    // at most 2k + 1 off-diagonal 32-blocks.  Tile 0's operands load now (they
+    // land during the hand-off), tiles 1 and 2 after it, tile 3 after tile 0.
+    // With every tile of a full chunk valid, each load count is fixed, so the
+    // wait before raising the flag can leave the later tiles' loads in flight.
+    const int tI[4] = {wave, 7 - wave, 8 + wave, 15 - wave};
+    const bool full = T16 == 16 && T16Q == 16;
+    TileOps<1> t0;
+    TileOps<3> t1;
+    TileOps<5> t2;
+    TileOps<7> t3;
+    if (tI[0] < T16) tile_load(t0, Gfc, Cfc, tI[0], NJ, lane, full);
 
     __syncthreads();  // step 4 is done in every wave: w may be replaced by v
     // v_j relative to the end of j's own 32-block (cs past q repeats)
@@ -487,114 +512,122 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     }
     __syncthreads();  // hs and v complete in every wave
 
-    // 5. output tiles
+    // 6. output tiles
     const float Dh = D ? D[h] : 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int cur = k & 1;
-        if (k > 0 && k < 3) load_tile(k + 1, cur ^ 1);
-        const int I = tile_of(k);
-        const bool valid = I < T16;
+    if (tI[1] < T16) tile_load(t1, Gfc, Cfc, tI[1], NJ, lane, full);
+    if (tI[2] < T16) tile_load(t2, Gfc, Cfc, tI[2], NJ, lane, full);
+
+    // acc[pt][e] = y[i = 16 I + r][p = 16 pt + 4 grp + e] (D[m = p][n = i] of the MFMAs):
+    // the state term exp(cs_i) C_i h_{c-1} first (scaled once), then the intra product
+    auto compute_tile = [&](const auto &t, int I, f32x4(&acc)[PT]) {
+        constexpr int NG = std::decay_t<decltype(t)>::kNG;
         const int il = I * 16 + r;
-        f32x4 acc[PT];
-        if (valid) {
-            const float csi = cs_s[il];
-            const int Jd = I >> 1;
+        const float csi = cs_s[il];
+        const int Jd = I >> 1;
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (have_h) {
 #pragma unroll
-            for (int J = 0; J < 7; ++J) {
-                if (J < Jd) {
-                    const float u = __expf(csi - ref_s[J]);
-                    const f32x4 v0 = *(const f32x4 *)(wv_s + 32 * J + grp * 8);
-                    const f32x4 v1 = *(const f32x4 *)(wv_s + 32 * J + grp * 8 + 4);
-                    bf16x8 gm = gbuf[cur][J];
+            for (int kn = 0; kn < NKN; ++kn) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        gm[e] = (bf16)((float)gm[e] * (u * v0[e]));
-                        gm[e + 4] = (bf16)((float)gm[e + 4] * (u * v1[e]));
-                    }
-#pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) {
-                        const bf16x8 ax = *(const bf16x8 *)(xs + (pt * 16 + r) * XLD + 32 * J + grp * 8);
-                        acc[pt] = mfma_bf16(ax, gm, acc[pt]);
-                    }
+                for (int pt = 0; pt < PT; ++pt) {
+                    const bf16x8 ah = *(const bf16x8 *)(hs + (pt * 16 + r) * HLD + kn * 32 + grp * 8);
+                    acc[pt] = mfma_bf16(ah, as_bf16x8(t.cf[kn]), acc[pt]);
                 }
             }
-            {
-                const int jl = 32 * Jd + grp * 8;
-                const bf16x8 gd = gdiag[cur];
-                bf16x8 bm;
+            const float ei = __expf(csi);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int j = jl + e;
-                    bm[e] = (bf16)((j <= il) ? __expf(csi - cs_s[j]) * (float)gd[e] : 0.f);
+            for (int pt = 0; pt < PT; ++pt) acc[pt] *= ei;
+        }
+#pragma unroll
+        for (int J = 0; J < NG; ++J) {
+            if (J < Jd) {
+                const float u = __expf(csi - ref_s[J]);
+                const f32x4 v0 = *(const f32x4 *)(wv_s + 32 * J + grp * 8);
+                const f32x4 v1 = *(const f32x4 *)(wv_s + 32 * J + grp * 8 + 4);
+                bf16x8 gm = as_bf16x8(t.g[J]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    gm[e] = (bf16)((float)gm[e] * (u * v0[e]));
+                    gm[e + 4] = (bf16)((float)gm[e + 4] * (u * v1[e]));
                 }
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) {
-                    const bf16x8 ax = *(const bf16x8 *)(xs + (pt * 16 + r) * XLD + jl);
-                    acc[pt] = mfma_bf16(ax, bm, acc[pt]);
+                    const bf16x8 ax = *(const bf16x8 *)(xs + (pt * 16 + r) * XLD + 32 * J + grp * 8);
+                    acc[pt] = mfma_bf16(ax, gm, acc[pt]);
                 }
             }
-            if (have_h) {
-                f32x4 tmp[PT];
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) tmp[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kn = 0; kn < NKN; ++kn) {
-#pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) {
-                        const bf16x8 ah = *(const bf16x8 *)(hs + (pt * 16 + r) * HLD + kn * 32 + grp * 8);
-                        tmp[pt] = mfma_bf16(ah, cbuf[cur][kn], tmp[pt]);
-                    }
-                }
-                const float ei = __expf(csi);
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) acc[pt] += ei * tmp[pt];
-            }
         }
-        if (k == 0) {
-            // this wave's ring slice is complete: raise its flag, then fetch tile 1
-            if (!last) {
-                __builtin_amdgcn_s_waitcnt(0);
-                if (lane == 0) __hip_atomic_store(myflag, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            load_tile(1, 1);
-        }
-        if (valid) {
-            // Lane (r, grp) holds row i = 16 I + r, columns 16 pt + 4 grp .. + 3
-            // (block M[grp][pt]).  Transpose the 4 x 4 block grid across the
-            // lane groups (butterfly over lane ^ 16, lane ^ 32) so lane group g
-            // holds M[0..3][g] = columns 16 g .. 16 g + 15: two 16-byte stores
-            // per lane instead of four 8-byte ones.
-            u32x2 m[PT];
+        const int jl = 32 * Jd + grp * 8;
+        const bf16x8 gd = as_bf16x8(t.gd);
+        bf16x8 bm;
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                const int p0 = pt * 16 + 4 * grp;
-                bf16 o[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc[pt][e] + Dh * (float)xs[(p0 + e) * XLD + il]);
-                m[pt] = *(const u32x2 *)o;
-            }
-            auto xchg = [](u32x2 v, int mask) {
-                return u32x2{(uint32_t)__shfl_xor((int)v[0], mask, 64), (uint32_t)__shfl_xor((int)v[1], mask, 64)};
-            };
-            const bool g1 = grp & 1, g2 = grp & 2;
-            // stage 1: keep the columns of this lane's parity, swap the rest with g ^ 1
-            const u32x2 c0 = g1 ? m[1] : m[0], c2 = g1 ? m[3] : m[2];          // M[g][g&1], M[g][2+(g&1)]
-            const u32x2 c1 = xchg(g1 ? m[0] : m[1], 16), c3 = xchg(g1 ? m[2] : m[3], 16);  // M[g^1][..]
-            // stage 2: keep column g, swap column g ^ 2 with g ^ 2
-            const u32x2 t0 = g2 ? c2 : c0, t1 = g2 ? c3 : c1;                 // M[g][g], M[g^1][g]
-            const u32x2 t2 = xchg(g2 ? c0 : c2, 32), t3 = xchg(g2 ? c1 : c3, 32);  // M[g^2][g], M[g^3][g]
-            // order by source row: out[s] = t[s ^ g]
-            const u32x2 a0 = g1 ? t1 : t0, a1 = g1 ? t0 : t1, a2 = g1 ? t3 : t2, a3 = g1 ? t2 : t3;
-            const u32x2 o0 = g2 ? a2 : a0, o1 = g2 ? a3 : a1, o2 = g2 ? a0 : a2, o3 = g2 ? a1 : a3;
-            if (il < q) {
-                bf16 *yr = y + (row0 + il * H) * P + 16 * grp;
-                *(u32x4 *)yr = u32x4{o0[0], o0[1], o1[0], o1[1]};
-                *(u32x4 *)(yr + 8) = u32x4{o2[0], o2[1], o3[0], o3[1]};
-            }
+        for (int e = 0; e < 8; ++e) {
+            const int j = jl + e;
+            bm[e] = (bf16)((j <= il) ? __expf(csi - cs_s[j]) * (float)gd[e] : 0.f);
         }
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const bf16x8 ax = *(const bf16x8 *)(xs + (pt * 16 + r) * XLD + jl);
+            acc[pt] = mfma_bf16(ax, bm, acc[pt]);
+        }
+    };
+    // + D x_i, to bf16.  Lane (r, grp) holds row i = 16 I + r, columns 16 pt +
+    // 4 grp .. + 3 (block M[grp][pt]).  A butterfly over lane ^ 16, lane ^ 32
+    // transposes the 4 x 4 block grid so lane group g holds M[0..3][g] =
+    // columns 16 g .. 16 g + 15: two 16-byte stores per lane.
+    auto store_tile = [&](int I, const f32x4(&acc)[PT]) {
+        const int il = I * 16 + r;
+        u32x2 m[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const int p0 = pt * 16 + 4 * grp;
+            bf16 o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc[pt][e] + Dh * (float)xs[(p0 + e) * XLD + il]);
+            m[pt] = *(const u32x2 *)o;
+        }
+        auto xchg = [](u32x2 v, int mask) {
+            return u32x2{(uint32_t)__shfl_xor((int)v[0], mask, 64), (uint32_t)__shfl_xor((int)v[1], mask, 64)};
+        };
+        const bool g1 = grp & 1, g2 = grp & 2;
+        // stage 1: keep the columns of this lane's parity, swap the rest with g ^ 1
+        const u32x2 c0 = g1 ? m[1] : m[0], c2 = g1 ? m[3] : m[2];                      // M[g][g&1], M[g][2+(g&1)]
+        const u32x2 c1 = xchg(g1 ? m[0] : m[1], 16), c3 = xchg(g1 ? m[2] : m[3], 16);  // M[g^1][..]
+        // stage 2: keep column g, swap column g ^ 2 with g ^ 2
+        const u32x2 t0v = g2 ? c2 : c0, t1v = g2 ? c3 : c1;                              // M[g][g], M[g^1][g]
+        const u32x2 t2v = xchg(g2 ? c0 : c2, 32), t3v = xchg(g2 ? c1 : c3, 32);          // M[g^2][g], M[g^3][g]
+        // order by source row: out[s] = t[s ^ g]
+        const u32x2 a0 = g1 ? t1v : t0v, a1 = g1 ? t0v : t1v, a2 = g1 ? t3v : t2v, a3 = g1 ? t2v : t3v;
+        const u32x2 o0 = g2 ? a2 : a0, o1 = g2 ? a3 : a1, o2 = g2 ? a0 : a2, o3 = g2 ? a1 : a3;
+        if (il < q) {
+            bf16 *yr = y + (row0 + il * H) * P + 16 * grp;
+            *(u32x4 *)yr = u32x4{o0[0], o0[1], o1[0], o1[1]};
+            *(u32x4 *)(yr + 8) = u32x4{o2[0], o2[1], o3[0], o3[1]};
+        }
+    };
+
+    f32x4 acc[PT];
+    if (tI[0] < T16) compute_tile(t0, tI[0], acc);
+    if (!last) {
+        // this wave's ring slice is complete: raise its flag (the loads of
+        // tiles 1 and 2, issued above, are waited for here too)
+        __builtin_amdgcn_s_waitcnt(0);
+        if (lane == 0) __hip_atomic_store(myflag, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tI[0] < T16) store_tile(tI[0], acc);
+    if (tI[3] < T16) tile_load(t3, Gfc, Cfc, tI[3], NJ, lane, full);
+    if (tI[1] < T16) {
+        compute_tile(t1, tI[1], acc);
+        store_tile(tI[1], acc);
+    }
+    if (tI[2] < T16) {
+        compute_tile(t2, tI[2], acc);
+        store_tile(tI[2], acc);
+    }
+    if (tI[3] < T16) {
+        compute_tile(t3, tI[3], acc);
+        store_tile(tI[3], acc);
     }
 }
 

@@ -65,14 +65,25 @@ struct XStage {
     u32x4 v[XB][4];
 };
 
-// Block blk -> (row group br, column block bc).  The eight column blocks of
-// a row group are eight adjacent lanes, so each load instruction reads whole
-// 128-byte rows (P = 64: one cache line per row).
+// Block blk -> (row group br, column block bc).  Each 32-lane half-wave
+// covers 16 consecutive row groups and two adjacent column blocks, so its
+// transposed 8-byte LDS stores hit distinct banks.  (Eight adjacent lanes
+// per row would read whole rows, but their transposed stores then collide
+// eight ways, which costs more.)
 template <int P>
 __device__ __forceinline__ void xstage_block(int blk, int &br, int &bc) {
     constexpr int NBC = XStage<P>::NBC;
-    bc = blk % NBC;
-    br = blk / NBC;
+    bc = (blk >> 4) % NBC;
+    br = (blk & 15) + 16 * ((blk >> 4) / NBC);
+}
+
+// LDS tiles with rows of 16-byte chunks, unpadded; chunk k of row `row` is
+// stored at k ^ (row & 15).  A 16-byte operand read by lanes r = 0..15
+// (rows 16 pt + r) at chunk 4 J + grp then covers all banks once, and so do
+// the transposed staging stores.  Offsets in elements; W = row length.
+template <int W>
+__device__ __forceinline__ int swz(int row, int col) {
+    return row * W + ((((col >> 3) ^ row) & 15) | ((col >> 3) & ~15)) * 8 + (col & 7);
 }
 
 template <int P>
@@ -82,20 +93,28 @@ __device__ __forceinline__ void stage_x_load(XStage<P> &st, const bf16 *__restri
     for (int i = 0; i < XStage<P>::XB; ++i) {
         int br, bc;
         xstage_block<P>(threadIdx.x + 256 * i, br, bc);
+        // x is read once: a non-temporal load keeps it from displacing the
+        // per-chunk operands every head of the chunk re-reads.  Rows past
+        // nvalid are zero (a full 256-row chunk needs no test).
+        if (nvalid >= 256) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int rr = br * 4 + k;
-            // x is read once: a non-temporal load keeps it from displacing the
-            // per-chunk operands every head of the chunk re-reads
-            st.v[i][k] = rr < nvalid ? __builtin_nontemporal_load((const u32x4 *)(src + rr * ld + bc * 8))
-                                     : u32x4{0u, 0u, 0u, 0u};
+            for (int k = 0; k < 4; ++k)
+                st.v[i][k] = __builtin_nontemporal_load((const u32x4 *)(src + (br * 4 + k) * ld + bc * 8));
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int rr = br * 4 + k;
+                st.v[i][k] = rr < nvalid ? __builtin_nontemporal_load((const u32x4 *)(src + rr * ld + bc * 8))
+                                         : u32x4{0u, 0u, 0u, 0u};
+            }
         }
     }
 }
 
-// Write the loaded blocks transposed into LDS (plain copy only).
+// Write the loaded blocks transposed into the chunk-swizzled x^T tile
+// (row = column of x, 256 steps per row); rows past q were loaded as zero.
 template <int P>
-__device__ __forceinline__ void stage_x_write_plain(const XStage<P> &st, bf16 *xs, int dstride) {
+__device__ __forceinline__ void stage_x_write_swz(const XStage<P> &st, bf16 *xs) {
 #pragma unroll
     for (int i = 0; i < XStage<P>::XB; ++i) {
         int br, bc;
@@ -104,50 +123,12 @@ __device__ __forceinline__ void stage_x_write_plain(const XStage<P> &st, bf16 *x
         const u32x4 *v = st.v[i];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            *(u32x2 *)(xs + (c0 + 2 * m) * dstride + r0) =
+            *(u32x2 *)(xs + swz<256>(c0 + 2 * m, r0)) =
                 u32x2{__builtin_amdgcn_perm(v[1][m], v[0][m], 0x05040100u),
                       __builtin_amdgcn_perm(v[3][m], v[2][m], 0x05040100u)};
-            *(u32x2 *)(xs + (c0 + 2 * m + 1) * dstride + r0) =
+            *(u32x2 *)(xs + swz<256>(c0 + 2 * m + 1, r0)) =
                 u32x2{__builtin_amdgcn_perm(v[1][m], v[0][m], 0x07060302u),
                       __builtin_amdgcn_perm(v[3][m], v[2][m], 0x07060302u)};
-        }
-    }
-}
-
-// Write the loaded blocks transposed into LDS: xs plain, xt scaled by
-// scale[row] (rows >= nvalid were loaded as zero and stay zero).
-template <int P>
-__device__ __forceinline__ void stage_x_write(const XStage<P> &st, bf16 *xs, bf16 *xt, int dstride,
-                                              const float *scale) {
-#pragma unroll
-    for (int i = 0; i < XStage<P>::XB; ++i) {
-        int br, bc;
-        xstage_block<P>(threadIdx.x + 256 * i, br, bc);
-        const int r0 = br * 4, c0 = bc * 8;
-        u32x4 w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            bf16x8 t = as_bf16x8(st.v[i][k]);
-            const float sc = scale[r0 + k];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) t[e] = (bf16)((float)t[e] * sc);
-            w[k] = as_u32x4(t);
-        }
-        const u32x4 *v = st.v[i];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            *(u32x2 *)(xs + (c0 + 2 * m) * dstride + r0) =
-                u32x2{__builtin_amdgcn_perm(v[1][m], v[0][m], 0x05040100u),
-                      __builtin_amdgcn_perm(v[3][m], v[2][m], 0x05040100u)};
-            *(u32x2 *)(xs + (c0 + 2 * m + 1) * dstride + r0) =
-                u32x2{__builtin_amdgcn_perm(v[1][m], v[0][m], 0x07060302u),
-                      __builtin_amdgcn_perm(v[3][m], v[2][m], 0x07060302u)};
-            *(u32x2 *)(xt + (c0 + 2 * m) * dstride + r0) =
-                u32x2{__builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u),
-                      __builtin_amdgcn_perm(w[3][m], w[2][m], 0x05040100u)};
-            *(u32x2 *)(xt + (c0 + 2 * m + 1) * dstride + r0) =
-                u32x2{__builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u),
-                      __builtin_amdgcn_perm(w[3][m], w[2][m], 0x07060302u)};
         }
     }
 }
@@ -317,7 +298,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     float *ring, int *flags, int L, int H, int G, int Q, int nc, int nbh) {
     constexpr int PT = P / 16, NT = N / 16, NTW = NT / 4, NKN = N / 32;
     static_assert(NT % 4 == 0 && N % 32 == 0, "N must be a multiple of 64");
-    constexpr int XLD = 256 + 8, HLD = N + 8;
+    constexpr int XW = 256, HW = N;   // unpadded rows, chunk-swizzled (swz)
     __shared__ float cs_s[256];
     // w_j = exp(cs_last - cs_j) (chunk-state weights) until step 4 is done in
     // every wave, then v_j = exp(r_J(j) - cs_j) (intra-chunk mask factor).
@@ -325,8 +306,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     __shared__ float wv_s[256];
     __shared__ float wsum_s[4];
     __shared__ float ref_s[8];   // r_J: cs at the last step of 32-block J
-    __shared__ bf16 xs[P * XLD];
-    __shared__ bf16 hs[P * HLD];
+    __shared__ bf16 xs[P * XW];
+    __shared__ bf16 hs[P * HW];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar offsets
@@ -369,13 +350,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const int row0 = (b * L + s) * H + h;
     XStage<P> xst;
     stage_x_load<P>(xst, x + row0 * P, H * P, q);
+    // B^T fragments (rows past q are stored as zero; blocks past NJ are not read)
     bf16x8 bfr[8][NTW];
+    if (NJ == 8) {
 #pragma unroll
-    for (int J = 0; J < 8; ++J)
+        for (int J = 0; J < 8; ++J)
 #pragma unroll
-        for (int tt = 0; tt < NTW; ++tt)
-            bfr[J][tt] = as_bf16x8(J < nb ? *(const u32x4 *)(Btc + (((wave + 4 * tt) * NJ + J) * 64 + lane) * 8)
-                                          : z4);
+            for (int tt = 0; tt < NTW; ++tt)
+                bfr[J][tt] = as_bf16x8(*(const u32x4 *)(Btc + (((wave + 4 * tt) * 8 + J) * 64 + lane) * 8));
+    } else {
+#pragma unroll
+        for (int J = 0; J < 8; ++J)
+#pragma unroll
+            for (int tt = 0; tt < NTW; ++tt)
+                bfr[J][tt] = as_bf16x8(J < NJ ? *(const u32x4 *)(Btc + (((wave + 4 * tt) * NJ + J) * 64 + lane) * 8)
+                                              : z4);
+    }
 
     // 1. decay prefix
     {
@@ -396,7 +386,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const float cs_last = cs_s[q - 1];
 
     // 2. stage x^T (rows past q were loaded as zero)
-    stage_x_write_plain<P>(xst, xs, XLD);
+    stage_x_write_swz<P>(xst, xs);
     __syncthreads();
 
     // 3. hand-off, first half: wait until wave `wave` of chunk c - 1 of this
@@ -406,9 +396,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     // cache maintenance), in a lane-major layout so each wave moves one
     // contiguous 512-byte block per access; init / final_state use the
     // [P][N] layout.  hv[tt][pt][e] = h_{c-1}[p = 16 pt + r][n = 16 (wave + 4 tt) + 4 grp + e]
-    auto ring_off = [&](int tt, int pt, int half) -> int {
-        return ((((wave * NTW + tt) * PT + pt) * 2 + half) * 64 + lane) * 2;
-    };
+    // ring_off(tt, pt, half) = ring_base(tt) + (pt * 2 + half) * 128: the
+    // per-(pt, half) part folds into the access's immediate offset
+    auto ring_base = [&](int tt) -> int { return ((wave * NTW + tt) * PT * 2 * 64 + lane) * 2; };
+    auto ring_off = [&](int tt, int pt, int half) -> int { return ring_base(tt) + (pt * 2 + half) * 128; };
     int *myflag = flags + bh * 4 + wave;
     const bool have_h = c > 0 || init != nullptr;
     f32x4 hv[NTW][PT];
@@ -421,13 +412,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         const float *hp = ring + ((c - 1) & 1) * nbh * PN + bh * PN;
 #pragma unroll
-        for (int tt = 0; tt < NTW; ++tt)
+        for (int tt = 0; tt < NTW; ++tt) {
+            const float *hb = hp + ring_base(tt);
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
-                const f32x2 lo = ld_agent_f32x2(hp + ring_off(tt, pt, 0));
-                const f32x2 hi = ld_agent_f32x2(hp + ring_off(tt, pt, 1));
+                const f32x2 lo = ld_agent_f32x2(hb + (pt * 2) * 128);
+                const f32x2 hi = ld_agent_f32x2(hb + (pt * 2 + 1) * 128);
                 hv[tt][pt] = f32x4{lo[0], lo[1], hi[0], hi[1]};
             }
+        }
     } else {
 #pragma unroll
         for (int tt = 0; tt < NTW; ++tt)
@@ -451,7 +444,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             bf16x8 bx[PT];
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt)
-                bx[pt] = *(const bf16x8 *)(xs + (pt * 16 + r) * XLD + 32 * J + grp * 8);
+                bx[pt] = *(const bf16x8 *)(xs + swz<XW>(pt * 16 + r, 32 * J + grp * 8));
 #pragma unroll
             for (int tt = 0; tt < NTW; ++tt) {
                 bf16x8 a = bfr[J][tt];
@@ -500,14 +493,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 if (last) {
                     *(f32x4 *)(hout + p * N + n0) = hn;
                 } else {
-                    st_agent_f32x2(hout + ring_off(tt, pt, 0), f32x2{hn[0], hn[1]});
-                    st_agent_f32x2(hout + ring_off(tt, pt, 1), f32x2{hn[2], hn[3]});
+                    float *hb = hout + ring_base(tt);
+                    st_agent_f32x2(hb + (pt * 2) * 128, f32x2{hn[0], hn[1]});
+                    st_agent_f32x2(hb + (pt * 2 + 1) * 128, f32x2{hn[2], hn[3]});
                 }
             }
             bf16 hb[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) hb[e] = (bf16)hv[tt][pt][e];
-            *(u32x2 *)(hs + p * HLD + n0) = *(const u32x2 *)hb;
+            *(u32x2 *)(hs + swz<HW>(p, n0)) = *(const u32x2 *)hb;
         }
     }
     __syncthreads();  // hs and v complete in every wave
@@ -531,7 +525,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             for (int kn = 0; kn < NKN; ++kn) {
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) {
-                    const bf16x8 ah = *(const bf16x8 *)(hs + (pt * 16 + r) * HLD + kn * 32 + grp * 8);
+                    const bf16x8 ah = *(const bf16x8 *)(hs + swz<HW>(pt * 16 + r, kn * 32 + grp * 8));
                     acc[pt] = mfma_bf16(ah, as_bf16x8(t.cf[kn]), acc[pt]);
                 }
             }
@@ -553,7 +547,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 }
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) {
-                    const bf16x8 ax = *(const bf16x8 *)(xs + (pt * 16 + r) * XLD + 32 * J + grp * 8);
+                    const bf16x8 ax = *(const bf16x8 *)(xs + swz<XW>(pt * 16 + r, 32 * J + grp * 8));
                     acc[pt] = mfma_bf16(ax, gm, acc[pt]);
                 }
             }
@@ -568,7 +562,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         }
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
-            const bf16x8 ax = *(const bf16x8 *)(xs + (pt * 16 + r) * XLD + jl);
+            const bf16x8 ax = *(const bf16x8 *)(xs + swz<XW>(pt * 16 + r, jl));
             acc[pt] = mfma_bf16(ax, bm, acc[pt]);
         }
     };
@@ -578,13 +572,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     // columns 16 g .. 16 g + 15: two 16-byte stores per lane.
     auto store_tile = [&](int I, const f32x4(&acc)[PT]) {
         const int il = I * 16 + r;
+        // x[i][16 pt + 4 grp + e] = xs[swz(16 pt + 4 grp + e, il)]; row & 15 = 4 grp + e,
+        // so the swizzled column offset depends on e only
+        int xoff[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xoff[e] = (4 * grp + e) * XW + swz<XW>(4 * grp + e, il) - (4 * grp + e) * XW;
         u32x2 m[PT];
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
-            const int p0 = pt * 16 + 4 * grp;
             bf16 o[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc[pt][e] + Dh * (float)xs[(p0 + e) * XLD + il]);
+            for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc[pt][e] + Dh * (float)xs[pt * 16 * XW + xoff[e]]);
             m[pt] = *(const u32x2 *)o;
         }
         auto xchg = [](u32x2 v, int mask) {

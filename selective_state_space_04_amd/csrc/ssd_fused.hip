@@ -2,23 +2,18 @@
 //
 // One workgroup per (b, c, h) does every step of the chunked algorithm for
 // its chunk (Mamba-2 review, docsaid.org, section "2つのルートを半分ずつ":
-// quadratic form inside the block, only the end-of-block state handed to the
-// next block), so x is read from HBM once and y written once:
-//
+// the quadratic form inside the block, only the end-of-block state handed to
+// the next block), so x is read from HBM once and y is written once:
 //   1. decay prefix cs of the chunk (wave scans over dt * A_h)
-//   2. x^T staged in LDS twice: as is, and scaled per 32-step block by
-//      v_j = exp(r_J - cs_j), r_J = cs at the block's last step
-//   3. chunk state S_c^T = sum_J exp(cs_last - r_J) B_J^T x~_J (MFMA; the
-//      block factors are applied Horner-style between blocks)
-//   4. intra-chunk product: for output tile I, blocks J strictly before the
-//      tile's own 32-block use the unmodified C B^T tile (MFMA B operand
-//      straight from memory) against x~, Horner-rescaled, then one row
-//      factor exp(cs_i - r); only the diagonal 32-block needs a per-element
-//      mask exp(cs_i - cs_j) [j <= i]
-//   5. state hand-off: wait until chunk c-1 of this (b, h) has published
-//      h_{c-1}, publish h_c = exp(cs_last) h_{c-1} + S_c (2-slot ring), or
-//      write final_state for the last chunk
-//   6. y = intra + exp(cs_i) h_{c-1} C_i + D x_i
+//   2. x^T staged in LDS
+//   3. wait for the state entering the chunk and start loading it
+//   4. chunk state S_c^T = sum_j (w_j B_j)^T x_j, w_j = exp(cs_last - cs_j)
+//   5. h_c = exp(cs_last) h_{c-1} + S_c handed to chunk c + 1 (or written as
+//      final_state); h_{c-1} kept in LDS for step 6
+//   6. y = (C B^T masked by exp(cs_i - cs_j) [j <= i]) x + exp(cs_i) C_i h_{c-1}
+//      + D x_i, per 16-row output tile
+// A preparation kernel writes C B^T, B^T and C of every chunk in MFMA-fragment
+// order beforehand (they are shared by all heads of a group).
 //
 // Every factor exp(a) used in the factorised mask has a <= 0 (cs is
 // non-increasing for dt >= 0, A <= 0), so nothing overflows; a factor that
@@ -27,12 +22,12 @@
 // Ordering: block ids map to (c, b, h) so that the workgroup chunk c waits
 // on always has a smaller id in the same dispatch stream; with in-order
 // dispatch it is already resident or done, so the chain always drains.  The
-// wait is also bounded (it gives up after ~0.2 s and the result is then
+// wait is also bounded (it gives up after ~0.1 s and the result is then
 // wrong, never hung).  The handed-off state is written and read with
 // agent-scope atomic accesses, which are coherent across the XCDs' separate
-// L2 caches; the writer raises the flag at its very end, after waiting for
-// its stores to complete (s_waitcnt), and the reader issues its state loads
-// only after it has seen the flag.
+// L2 caches.  Each wave hands off its own slice of the state: it raises its
+// flag only after its slice's stores have completed (s_waitcnt), and the
+// reading wave issues its loads only after it has seen that flag.
 #include <type_traits>
 
 #include "ssd_device.h"
@@ -248,22 +243,23 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16 *__restrict__ B,
 
 // ---------------------------------------------------------------------------
 // The single-pass kernel.  256 threads (4 waves); sized for three workgroups
-// per CU (<= 53 KB LDS, <= 168 VGPRs).  Wave w owns state n-tiles {w, w + 4}
+// per CU (51,248 B LDS, <= 168 VGPRs).  Wave w owns state n-tiles {w, w + 4}
 // and output tiles {w, 7 - w, 8 + w, 15 - w} (balanced over the triangle).
-//   1. decay prefix of the chunk (wave scans); weights w_j = exp(cs_last -
-//      cs_j) for the chunk state
-//   2. x^T staged in LDS (loaded in one round at entry, with B^T and dt)
-//   3. chunk state S_c^T = sum_j (w_j B_j)^T x_j (w folded into the B^T
-//      fragments)
-//   4. hand-off: wait for h_{c-1} (ring slot of chunk c - 1, or init), write
-//      h_c = exp(cs_last) h_{c-1} + S_c to the ring (or final_state) and raise
-//      the flag; h_{c-1} (bf16) goes to LDS for step 5
-//   5. per output tile: intra-chunk product (off-diagonal 32-blocks J use
-//      exp(cs_i - cs_j) = exp(cs_i - r_J) exp(r_J - cs_j), both factors <= 1,
-//      folded into the C B^T fragment; the diagonal 32-block takes the mask
-//      exp(cs_i - cs_j) [j <= i] element by element), + exp(cs_i) h_{c-1} C_i
-//      + D x_i, stored as bf16.  The next tile's C B^T and C fragments load
-//      while the current tile computes.
+//   1. loads x, dt and the B^T fragments in one round; decay prefix (wave
+//      scans); w_j = exp(cs_last - cs_j)
+//   2. x^T staged in LDS (unpadded, chunk-swizzled rows)
+//   3. wait for wave w's slice of h_{c-1} (flag of chunk c - 1, or init);
+//      issue its loads
+//   4. chunk state S_c^T for n-tiles {w, w + 4} (w folded into the B^T
+//      fragments); the state slice lands meanwhile
+//   5. w replaced by v_j = exp(r_J - cs_j) in LDS; h_c = exp(cs_last) h_{c-1}
+//      + S_c to the ring slice (or final_state); h_{c-1} (bf16) to LDS
+//   6. output tiles: exp(cs_i) C_i h_{c-1} + intra-chunk product (off-diagonal
+//      32-blocks J use exp(cs_i - cs_j) = exp(cs_i - r_J) exp(r_J - cs_j),
+//      both factors <= 1, folded into the C B^T fragment; the diagonal
+//      32-block takes exp(cs_i - cs_j) [j <= i] element by element) + D x_i,
+//      stored as bf16.  The flag is raised after the first tile, once the
+//      ring stores have completed.
 // ---------------------------------------------------------------------------
 // Operands of one 16-row output tile I: its off-diagonal C B^T fragments
 // (32-blocks J < I / 2; NG is the most a tile in this slot can have), the

@@ -10,6 +10,8 @@ Contents
 --------
 * ``forward`` / ``decode_step``: the float64 sequential recurrence, in plain C
   (``ssd_recurrence.c``), parallel over independent (batch, head) sequences.
+* ``backward``: reverse-mode differentiation of that recurrence, step by
+  step in reverse order (``ssd_backward.c``), float64.
 * ``chunked``: float64 numpy versions of each step of the chunked algorithm
   (decay prefix, C B^T, intra-chunk masked product, chunk state, state
   passing, output combine) used to check the GPU's intermediates.
@@ -29,6 +31,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_recurrence.c")
+_SRC_BWD = os.path.join(_HERE, "ssd_backward.c")
 _LIB_PATH = os.path.join(_HERE, "_build", "libssd_oracle.so")
 _lib = None
 
@@ -39,7 +42,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-                               _SRC, "-o", tmp, "-lm"])
+                               _SRC, _SRC_BWD, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -53,6 +56,8 @@ def _load():
         i64, dp = ctypes.c_int64, ctypes.c_void_p
         lib.ssd_oracle_forward.argtypes = [i64] * 6 + [dp] * 9 + [i64, dp]
         lib.ssd_oracle_forward.restype = ctypes.c_int
+        lib.ssd_oracle_backward.argtypes = [i64] * 6 + [dp] * 16
+        lib.ssd_oracle_backward.restype = ctypes.c_int
         lib.ssd_oracle_decode_step.argtypes = [i64] * 5 + [dp] * 8
         lib.ssd_oracle_decode_step.restype = ctypes.c_int
         lib.ssd_oracle_num_threads.restype = ctypes.c_int
@@ -107,6 +112,37 @@ def forward(x, dt, A, B, C, D=None, init=None, chunk: int = 0):
     if rc != 0:
         raise ValueError("oracle: bad shape")
     return (y, final, bnd) if chunk > 0 else (y, final)
+
+
+def backward(x, dt, A, B, C, D, init, dy, dfinal=None):
+    """Gradient of the forward map by reverse-mode differentiation of the
+    sequential recurrence (float64).
+
+    With loss = sum(dy * y) + sum(dfinal * final_state), returns a dict with
+    dx [b, L, H, P], ddt [b, L, H], dA [H], dB and dC [b, L, G, N], dD [H]
+    (zero-filled when D is None) and dinit [b, H, P, N] (the gradient of the
+    initial state, also when init is None, i.e. zero).
+    """
+    x, dt, A, B, C, D, init, dy, dfinal = (_f64(v) for v in (x, dt, A, B, C, D, init, dy, dfinal))
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dy.shape == x.shape and (dfinal is None or dfinal.shape == (b, H, P, N))
+    dx = np.empty_like(x)
+    ddt = np.empty((b, L, H))
+    dB_h = np.empty((b, L, H, N))
+    dC_h = np.empty((b, L, H, N))
+    dA_bh = np.empty((b, H))
+    dD_bh = np.empty((b, H))
+    dinit = np.empty((b, H, P, N))
+    rc = _load().ssd_oracle_backward(b, L, H, P, N, G, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                      _ptr(D), _ptr(init), _ptr(dy), _ptr(dfinal), _ptr(dx), _ptr(ddt),
+                                      _ptr(dB_h), _ptr(dC_h), _ptr(dA_bh), _ptr(dD_bh), _ptr(dinit))
+    if rc != 0:
+        raise ValueError("oracle backward: bad shape or out of memory")
+    hg = H // G
+    return {"dx": dx, "ddt": ddt, "dA": dA_bh.sum(axis=0),
+            "dB": dB_h.reshape(b, L, G, hg, N).sum(axis=3), "dC": dC_h.reshape(b, L, G, hg, N).sum(axis=3),
+            "dD": dD_bh.sum(axis=0), "dinit": dinit}
 
 
 def decode_step(state, x, dt, A, B, C, D=None):

@@ -152,6 +152,41 @@ ssd_status ssd_decode_step(const ssd_dims *dims, float *state, const void *x, co
                            void *y, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Gradient of the layer (reverse-mode differentiation of the map that
+ * ssd_forward evaluates; the pages define the forward map, in the review
+ * page's sections "SSM を一つの行列として書く" and "2つのルートを半分ずつ", and the
+ * gradient is its chain rule, organised by the same chunks).  With
+ *   Loss = sum(dy * y) + sum(dfinal_state * final_state)
+ * for the y and final_state that ssd_forward returns on the same inputs,
+ * it writes
+ *   dx  [batch, L, H, P]  dtype     dLoss/dx
+ *   ddt [batch, L, H]     dtype     dLoss/ddt
+ *   dA  [H]               float32   dLoss/dA (summed over batch and steps)
+ *   dB, dC [batch, L, G, N] dtype   dLoss/dB, dLoss/dC (summed over the
+ *                                   heads of each group)
+ *   dD  [H]               float32   dLoss/dD = sum of dy . x per head
+ *   dinit_state [batch, H, P, N] float32  dLoss/dinit_state
+ * Inputs are those of ssd_forward plus dy [batch, L, H, P] (dtype) and
+ * dfinal_state [batch, H, P, N] (float32).  Nullable: D (zeros),
+ * init_state (zeros), dfinal_state (zeros), dD and dinit_state (not
+ * written).  Every output must not overlap any input, another output or
+ * the workspace.  The forward is recomputed inside (nothing is kept from a
+ * forward call); the gradients do not depend on `chunk` except through
+ * rounding.  Gradients in dtype are rounded to nearest even from float32
+ * accumulators.  Same shape support, alignment, stream and error rules as
+ * ssd_forward; argument errors write nothing.  For batch = 0 or L = 0, dA
+ * and dD are zero and dinit_state = dfinal_state.
+ * ssd_backward_workspace_bytes: bytes of workspace needed (0 for invalid
+ * dims; pure host computation).
+ */
+size_t ssd_backward_workspace_bytes(const ssd_dims *dims);
+ssd_status ssd_backward(const ssd_dims *dims, const void *x, const void *dt, const float *A,
+                        const void *B, const void *C, const float *D, const float *init_state,
+                        const void *dy, const float *dfinal_state, void *dx, void *ddt, float *dA,
+                        void *dB, void *dC, float *dD, float *dinit_state, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * The steps of the chunked algorithm, one entry point each.  nc =
  * ceil(seqlen / chunk); chunk c covers steps [c*chunk, min((c+1)*chunk, L)).
  * Intermediates are float32 unless stated.
@@ -212,6 +247,13 @@ ssd_status ssd_validate_forward(const ssd_dims *dims, const void *x, const void 
 ssd_status ssd_validate_decode(const ssd_dims *dims, const float *state, const void *x,
                                const void *dt, const float *A, const void *B, const void *C,
                                const float *D, const void *y);
+ssd_status ssd_validate_backward(const ssd_dims *dims, const void *x, const void *dt,
+                                 const float *A, const void *B, const void *C, const float *D,
+                                 const float *init_state, const void *dy,
+                                 const float *dfinal_state, const void *dx, const void *ddt,
+                                 const float *dA, const void *dB, const void *dC, const float *dD,
+                                 const float *dinit_state, const void *workspace,
+                                 size_t workspace_bytes);
 
 #ifdef __cplusplus
 }

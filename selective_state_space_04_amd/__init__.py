@@ -58,6 +58,9 @@ _SIGS = {
     "ssd_chunk_scan": (ctypes.c_int, [_dp] + [_vp] * 8),
     "ssd_validate_forward": (ctypes.c_int, [_dp] + [_vp] * 10 + [ctypes.c_size_t]),
     "ssd_validate_decode": (ctypes.c_int, [_dp] + [_vp] * 8),
+    "ssd_backward_workspace_bytes": (ctypes.c_size_t, [_dp]),
+    "ssd_backward": (ctypes.c_int, [_dp] + [_vp] * 17 + [ctypes.c_size_t, _vp]),
+    "ssd_validate_backward": (ctypes.c_int, [_dp] + [_vp] * 17 + [ctypes.c_size_t]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -163,6 +166,46 @@ def forward(x, dt, A, B, C, D=None, init_state=None, chunk: int = 256, *, staged
     _check(fn(ctypes.byref(dims), _p(x), _p(dt), _p(A), _p(B), _p(C), _p(D), _p(init_state), _p(y),
               _p(final_state), _p(workspace), workspace.numel(), _stream()))
     return y, final_state
+
+
+def backward_workspace_bytes(dims: Dims) -> int:
+    return int(lib.ssd_backward_workspace_bytes(ctypes.byref(dims)))
+
+
+def backward(x, dt, A, B, C, dy, D=None, init_state=None, dfinal_state=None, chunk: int = 256, *,
+             out=None, workspace=None, want_dD: bool = True, want_dinit: bool = True):
+    """Gradient of sum(dy * y) + sum(dfinal_state * final_state) for the
+    forward on the same inputs.  Returns a dict with dx, ddt, dA, dB, dC and
+    (when wanted) dD and dinit (dx, ddt, dB, dC in the input dtype; dA, dD,
+    dinit float32).  ``out`` may hold preallocated outputs under those names.
+    """
+    dims = _forward_dims(x, dt, A, B, C, D, init_state, chunk)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    _need(dy, "dy", x.shape, x.dtype, dev)
+    if dfinal_state is not None:
+        _need(dfinal_state, "dfinal_state", (b, H, P, N), torch.float32, dev)
+    shapes = {"dx": (x.shape, x.dtype), "ddt": (dt.shape, x.dtype), "dA": ((H,), torch.float32),
+              "dB": (B.shape, x.dtype), "dC": (C.shape, x.dtype)}
+    if want_dD:
+        shapes["dD"] = ((H,), torch.float32)
+    if want_dinit:
+        shapes["dinit"] = ((b, H, P, N), torch.float32)
+    out = dict(out or {})
+    for k, (shp, dty) in shapes.items():
+        if k in out:
+            _need(out[k], k, shp, dty, dev)
+        else:
+            out[k] = torch.empty(tuple(shp), dtype=dty, device=dev)
+    nbytes = backward_workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib.ssd_backward(ctypes.byref(dims), _p(x), _p(dt), _p(A), _p(B), _p(C), _p(D),
+                            _p(init_state), _p(dy), _p(dfinal_state), _p(out["dx"]), _p(out["ddt"]),
+                            _p(out["dA"]), _p(out["dB"]), _p(out["dC"]), _p(out.get("dD")),
+                            _p(out.get("dinit")), _p(workspace), workspace.numel(), _stream()))
+    return out
 
 
 def decode_step(state, x, dt, A, B, C, D=None, y=None):

@@ -134,6 +134,36 @@ int64_t ws_total(const ssd::Dims &d) {
     return t;
 }
 
+// Workspace of the gradient: cs | C B^T | (C B^T)^T | forward states H_c |
+// state gradients R_c | dCB | dCB^T | state terms of dC and dB | per-chunk
+// partials of dA and dD | float64 prefix (float32 inputs only).
+struct BwdLayout {
+    int64_t cs = 0, cb = 0, cbT = 0, Hs = 0, Rs = 0, dcb = 0, dcbT = 0, dCs = 0, dBs = 0,
+            part = 0, cs64 = 0, total = 0;
+};
+
+BwdLayout bwd_layout(const ssd::Dims &d) {
+    BwdLayout w;
+    const int64_t cb_bytes = d.b * d.nc * d.G * d.Q * d.Q * esize(d);
+    const int64_t s_bytes = d.b * d.nc * d.H * d.P * d.N * 4;
+    const int64_t dcb_bytes = d.b * d.nc * d.G * d.Q * d.Q * 4;
+    const int64_t g_bytes = d.b * d.L * d.G * d.N * 4;
+    w.cs = 0;
+    w.cb = align256(w.cs + d.b * d.H * d.nc * d.Q * 4);
+    w.cbT = align256(w.cb + cb_bytes);
+    w.Hs = align256(w.cbT + cb_bytes);
+    w.Rs = align256(w.Hs + s_bytes);
+    w.dcb = align256(w.Rs + s_bytes);
+    w.dcbT = align256(w.dcb + dcb_bytes);
+    w.dCs = align256(w.dcbT + dcb_bytes);
+    w.dBs = align256(w.dCs + g_bytes);
+    w.part = align256(w.dBs + g_bytes);
+    w.cs64 = align256(w.part + d.b * d.nc * d.H * 2 * 4);
+    w.total = align256(w.cs64 + (d.dtype == SSD_F32 ? d.b * d.H * d.nc * d.Q * 8 : 0));
+    if (d.b == 0 || d.nc == 0) w.total = 0;
+    return w;
+}
+
 ssd_status hip_status(hipError_t e) {
     if (e == hipSuccess) return SSD_OK;
     g_last_hip = e;
@@ -199,6 +229,45 @@ ssd_status validate_decode(const ssd_dims *dims, const float *state, const void 
     return SSD_OK;
 }
 
+ssd_status validate_backward(const ssd_dims *dims, const void *x, const void *dt, const float *A,
+                             const void *B, const void *C, const float *D, const float *init,
+                             const void *dy, const float *dfinal, const void *dx, const void *ddt,
+                             const float *dA, const void *dB, const void *dC, const float *dD,
+                             const float *dinit, const void *ws, size_t ws_bytes, ssd::Dims *out) {
+    ssd::Dims d;
+    ssd_status st = check_dims(dims, false, &d);
+    if (st != SSD_OK) return st;
+    const bool tokens = d.b * d.L > 0;
+    if (!A || !dA) return SSD_ERR_NULL;
+    if (tokens && (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC)) return SSD_ERR_NULL;
+    const void *ptrs[] = {x, dt, A, B, C, D, init, dy, dfinal, dx, ddt, dA, dB, dC, dD, dinit};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return SSD_ERR_ALIGN;
+    if (ws && !aligned(ws, 256)) return SSD_ERR_ALIGN;
+    const int64_t wtotal = bwd_layout(d).total;
+    if (wtotal > 0 && (!ws || (int64_t)ws_bytes < wtotal)) return SSD_ERR_WORKSPACE;
+    const int64_t es = esize(d);
+    const int64_t tok = d.b * d.L, state_bytes = d.b * d.H * d.P * d.N * 4;
+    const Range ins[] = {range_of(x, tok * d.H * d.P * es), range_of(dt, tok * d.H * es),
+                         range_of(A, d.H * 4),           range_of(B, tok * d.G * d.N * es),
+                         range_of(C, tok * d.G * d.N * es), range_of(D, d.H * 4),
+                         range_of(init, state_bytes),    range_of(dy, tok * d.H * d.P * es),
+                         range_of(dfinal, state_bytes)};
+    const Range outs[] = {range_of(dx, tok * d.H * d.P * es), range_of(ddt, tok * d.H * es),
+                          range_of(dA, d.H * 4),           range_of(dB, tok * d.G * d.N * es),
+                          range_of(dC, tok * d.G * d.N * es), range_of(dD, d.H * 4),
+                          range_of(dinit, state_bytes),    range_of(ws, wtotal)};
+    constexpr int nout = sizeof(outs) / sizeof(outs[0]);
+    for (int i = 0; i < nout; ++i) {
+        for (const Range &r : ins)
+            if (overlap(outs[i], r)) return SSD_ERR_ALIAS;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(outs[i], outs[j])) return SSD_ERR_ALIAS;
+    }
+    if (out) *out = d;
+    return SSD_OK;
+}
+
 ssd_status validate_ptrs(const void *const *req, int nreq, const void *const *opt, int nopt) {
     for (int i = 0; i < nreq; ++i)
         if (!req[i]) return SSD_ERR_NULL;
@@ -222,11 +291,51 @@ ssd_status run_staged(const ssd::Dims &d, const void *x, const void *dt, const f
     float *S = (float *)(base + w.S);
     hipError_t e;
     if ((e = ssd::launch_chunk_cumsum(d, dt, A, cs, st)) != hipSuccess) return hip_status(e);
-    if ((e = ssd::launch_chunk_cb(d, B, C, cb, st)) != hipSuccess) return hip_status(e);
-    if ((e = ssd::launch_chunk_state(d, x, B, cs, S, st)) != hipSuccess) return hip_status(e);
+    if ((e = ssd::launch_chunk_cb(d, B, C, cb, nullptr, st)) != hipSuccess) return hip_status(e);
+    if ((e = ssd::launch_chunk_state(d, x, B, cs, S, false, st)) != hipSuccess) return hip_status(e);
     if ((e = ssd::launch_state_passing(d, S, cs, init, fin, st)) != hipSuccess) return hip_status(e);
     if ((e = ssd::launch_chunk_scan(d, x, C, cb, cs, S, D, y, st)) != hipSuccess) return hip_status(e);
     return SSD_OK;
+}
+
+// The gradient: forward states recomputed, state gradients passed backwards,
+// then the per-chunk and per-group gradient kernels.
+ssd_status run_backward(const ssd::Dims &d, const void *x, const void *dt, const float *A,
+                        const void *B, const void *C, const float *D, const float *init,
+                        const void *dy, const float *dfinal, void *dx, void *ddt, float *dA,
+                        void *dB, void *dC, float *dD, float *dinit, void *ws, hipStream_t st) {
+    hipError_t e;
+    if (d.b == 0 || d.nc == 0) {
+        if ((e = ssd::launch_zero_state(d, dfinal, dinit, st)) != hipSuccess) return hip_status(e);
+        return hip_status(ssd::launch_head_reduce(d, nullptr, dA, dD, st));
+    }
+    const BwdLayout w = bwd_layout(d);
+    char *base = (char *)ws;
+    float *cs = (float *)(base + w.cs), *Hs = (float *)(base + w.Hs), *Rs = (float *)(base + w.Rs);
+    float *dcb = (float *)(base + w.dcb), *dcbT = (float *)(base + w.dcbT);
+    float *dCs = (float *)(base + w.dCs), *dBs = (float *)(base + w.dBs);
+    float *part = (float *)(base + w.part);
+    double *cs64 = d.dtype == SSD_F32 ? (double *)(base + w.cs64) : nullptr;
+    void *cb = base + w.cb, *cbT = base + w.cbT;
+    if ((e = ssd::launch_chunk_cumsum(d, dt, A, cs, st)) != hipSuccess) return hip_status(e);
+    if (cs64 && (e = ssd::launch_chunk_cumsum64(d, dt, A, cs64, st)) != hipSuccess)
+        return hip_status(e);
+    if ((e = ssd::launch_chunk_cb(d, B, C, cb, cbT, st)) != hipSuccess) return hip_status(e);
+    if ((e = ssd::launch_chunk_state(d, x, B, cs, Hs, false, st)) != hipSuccess) return hip_status(e);
+    if ((e = ssd::launch_state_passing(d, Hs, cs, init, nullptr, st)) != hipSuccess)
+        return hip_status(e);
+    if ((e = ssd::launch_chunk_state(d, dy, C, cs, Rs, true, st)) != hipSuccess) return hip_status(e);
+    if ((e = ssd::launch_state_passing_rev(d, Rs, cs, dfinal, dinit, st)) != hipSuccess)
+        return hip_status(e);
+    if ((e = ssd::launch_chunk_bwd(d, x, dy, dt, A, B, C, cb, cbT, cs, cs64, Hs, Rs, D, dx, ddt,
+                                   part, st)) != hipSuccess)
+        return hip_status(e);
+    if ((e = ssd::launch_group_bwd(d, x, dy, cs, cs64, Hs, Rs, dcb, dcbT, dCs, dBs, st)) !=
+        hipSuccess)
+        return hip_status(e);
+    if ((e = ssd::launch_group_combine(d, B, C, dcb, dcbT, dCs, dBs, dB, dC, st)) != hipSuccess)
+        return hip_status(e);
+    return hip_status(ssd::launch_head_reduce(d, part, dA, dD, st));
 }
 
 ssd_status run_fused_prep(const ssd::Dims &d, const void *B, const void *C, void *ws,
@@ -351,6 +460,37 @@ ssd_status ssd_forward_main(const ssd_dims *dims, const void *x, const void *dt,
                           (hipStream_t)stream);
 }
 
+size_t ssd_backward_workspace_bytes(const ssd_dims *dims) {
+    ssd::Dims d;
+    if (check_dims(dims, false, &d) != SSD_OK) return 0;
+    return (size_t)bwd_layout(d).total;
+}
+
+ssd_status ssd_validate_backward(const ssd_dims *dims, const void *x, const void *dt,
+                                 const float *A, const void *B, const void *C, const float *D,
+                                 const float *init_state, const void *dy,
+                                 const float *dfinal_state, const void *dx, const void *ddt,
+                                 const float *dA, const void *dB, const void *dC, const float *dD,
+                                 const float *dinit_state, const void *workspace,
+                                 size_t workspace_bytes) {
+    return validate_backward(dims, x, dt, A, B, C, D, init_state, dy, dfinal_state, dx, ddt, dA,
+                             dB, dC, dD, dinit_state, workspace, workspace_bytes, nullptr);
+}
+
+ssd_status ssd_backward(const ssd_dims *dims, const void *x, const void *dt, const float *A,
+                        const void *B, const void *C, const float *D, const float *init_state,
+                        const void *dy, const float *dfinal_state, void *dx, void *ddt, float *dA,
+                        void *dB, void *dC, float *dD, float *dinit_state, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    ssd::Dims d;
+    ssd_status st = validate_backward(dims, x, dt, A, B, C, D, init_state, dy, dfinal_state, dx,
+                                      ddt, dA, dB, dC, dD, dinit_state, workspace, workspace_bytes,
+                                      &d);
+    if (st != SSD_OK) return st;
+    return run_backward(d, x, dt, A, B, C, D, init_state, dy, dfinal_state, dx, ddt, dA, dB, dC,
+                        dD, dinit_state, workspace, (hipStream_t)stream);
+}
+
 ssd_status ssd_decode_step(const ssd_dims *dims, float *state, const void *x, const void *dt,
                            const float *A, const void *B, const void *C, const float *D, void *y,
                            void *stream) {
@@ -379,7 +519,7 @@ ssd_status ssd_chunk_cb(const ssd_dims *dims, const void *B, const void *C, void
     if (d.b * d.nc == 0) return SSD_OK;
     const void *req[] = {B, C, cb};
     if ((st = validate_ptrs(req, 3, nullptr, 0)) != SSD_OK) return st;
-    return hip_status(ssd::launch_chunk_cb(d, B, C, cb, (hipStream_t)stream));
+    return hip_status(ssd::launch_chunk_cb(d, B, C, cb, nullptr, (hipStream_t)stream));
 }
 
 ssd_status ssd_chunk_state(const ssd_dims *dims, const void *x, const void *B, const float *cs,
@@ -390,7 +530,7 @@ ssd_status ssd_chunk_state(const ssd_dims *dims, const void *x, const void *B, c
     if (d.b * d.nc == 0) return SSD_OK;
     const void *req[] = {x, B, cs, states};
     if ((st = validate_ptrs(req, 4, nullptr, 0)) != SSD_OK) return st;
-    return hip_status(ssd::launch_chunk_state(d, x, B, cs, states, (hipStream_t)stream));
+    return hip_status(ssd::launch_chunk_state(d, x, B, cs, states, false, (hipStream_t)stream));
 }
 
 ssd_status ssd_state_passing(const ssd_dims *dims, float *states, const float *cs,

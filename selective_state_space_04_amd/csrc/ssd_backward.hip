@@ -1,0 +1,853 @@
+// Gradient of the SSD layer (gfx950 / MI355X), by the chunked algorithm.
+//
+// Forward map per batch row b, head h (group g), chunk c of q steps starting
+// at s, with cs_i the decay prefix inside the chunk and H_c the state entering
+// it (Mamba-2 review, docsaid.org, sections "A を一つの数に簡略化する" and
+// "2つのルートを半分ずつ"):
+//   y_i      = sum_{j<=i} M_ij x_j + exp(cs_i) H_c C_i + D x_i,   M_ij = exp(cs_i - cs_j) C_i.B_j
+//   H_{c+1}  = exp(cs_e) H_c + sum_j exp(cs_e - cs_j) x_j B_j^T     (e = q - 1)
+// Given dy and dfinal = dLoss/dH_nc, the chain rule gives, with
+// R_c = dLoss/dH_{c+1} (the gradient of the state leaving chunk c):
+//   R_{nc-1} = dfinal,  R_{c-1} = exp(cs_e(c)) R_c + sum_i exp(cs_i) dy_i C_i^T,  dinit = R_{-1}
+//   dx_j = sum_{i>=j} M_ij dy_i + exp(cs_e - cs_j) R_c B_j + D dy_j
+//   dC_i = sum_h [ sum_{j<=i} exp(cs_i - cs_j)(dy_i.x_j) B_j + exp(cs_i) H_c^T dy_i ]
+//   dB_j = sum_h [ sum_{i>=j} exp(cs_i - cs_j)(dy_i.x_j) C_i + exp(cs_e - cs_j) R_c^T x_j ]
+// and for the log-decays, with y'_k = y_k - D x_k and dx'_k = dx_k - D dy_k,
+//   dLoss/dcs_k = dy_k.y'_k - x_k.dx'_k + [k = e] <R_c, H_{c+1}>
+// (differentiate each exponent: the terms in which cs_k appears with a plus
+// sign sum to dy_k.y'_k plus the end-of-chunk state, those with a minus sign
+// to x_k.dx'_k), so the gradient of dA_t = dt_t A_h, which enters every cs_k
+// with k >= t, is the suffix sum ddA_t = sum_{k>=t} dLoss/dcs_k, and
+// ddt_t = A_h ddA_t, dA_h = sum dt_t ddA_t, dD_h = sum dy.x.
+//
+// Two choices keep the decay gradients accurate where a head forgets fast
+// (|cs| in the thousands, neighbouring decays ~1e-3): the diagonal terms
+// M_kk x_k and M_kk dy_k, which cancel exactly between dy_k.y'_k and
+// x_k.dx'_k, are left out of both (strict masks; M_kk dy_k is added to dx on
+// its own); and for float32 inputs the prefix is kept in float64 (dt A is
+// exact there), so cs_i - cs_j is exact before it is rounded for exp.
+//
+// Kernels (the forward states H_c and the state gradients R_c are produced
+// first by the step kernels of ssd_kernels.hip and k_state_passing_rev):
+//   k_chunk_bwd     per (b, c, h): recomputes y'_i, computes dx and the
+//                   decay gradients of the chunk; per-chunk partial sums of
+//                   dA_h and dD_h.
+//   k_group_bwd     per (b, c, g, 64 rows): loops over the heads of the group
+//                   and sums exp(cs_i - cs_j)(dy_i.x_j) (dCB, both
+//                   orientations) and the state terms of dC and dB.
+//   k_group_combine per (b, c, g, 16 rows): dC = dC_state + dCB B,
+//                   dB = dB_state + dCB^T C, rounded to the input dtype.
+//   k_head_reduce   per h: sums the per-chunk partials of dA_h and dD_h.
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+// ---------------------------------------------------------------------------
+// Reverse inter-chunk recurrence, in place: on entry S[c] = sum_i exp(cs_i)
+// dy_i C_i^T of chunk c; on return S[c] = R_c.  Mirror image of
+// k_state_passing: each thread owns four state elements of one (b, h) and
+// walks the chunks from the last to the first, 8 chunk inputs loaded ahead.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_state_passing_rev(float *__restrict__ S,
+                                                           const float *__restrict__ cs,
+                                                           const float *dfinal, float *dinit,
+                                                           int64_t L, int H, int PN, int Q,
+                                                           int nc) {
+    const int h = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int e0 = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e0 >= PN) return;
+    const int64_t bh = b * H + h;
+    f32x4 gv = dfinal ? *(const f32x4 *)(dfinal + bh * PN + e0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const float *csb = cs + bh * (int64_t)nc * Q;
+    constexpr int U = 8;
+    for (int c1 = nc - 1; c1 >= 0; c1 -= U) {
+        f32x4 sv[U];
+        float lam[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c1 - u;
+            if (c >= 0) {
+                const int last = (int)min<int64_t>(Q, L - (int64_t)c * Q) - 1;
+                lam[u] = __expf(csb[(int64_t)c * Q + last]);
+                sv[u] = *(const f32x4 *)(S + (((b * nc + c) * H + h) * (int64_t)PN) + e0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c1 - u;
+            if (c >= 0) {
+                *(f32x4 *)(S + (((b * nc + c) * H + h) * (int64_t)PN) + e0) = gv;
+                gv = lam[u] * gv + sv[u];
+            }
+        }
+    }
+    if (dinit) *(f32x4 *)(dinit + bh * PN + e0) = gv;
+}
+
+// ---------------------------------------------------------------------------
+// Decay prefix in float64, one wave per (b, h, c): the same sums as
+// k_chunk_cumsum, with dt A formed exactly (a float32 product fits in a
+// float64 significand) and accumulated in float64.  Entries past a short
+// chunk's end repeat its last value.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(64) void k_chunk_cumsum64(const T *__restrict__ dt,
+                                                       const float *__restrict__ A,
+                                                       double *__restrict__ cs, int64_t L, int H,
+                                                       int Q, int nc) {
+    const int c = blockIdx.x, h = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int64_t s = (int64_t)c * Q;
+    const int q = (int)min<int64_t>(Q, L - s);
+    const double Ah = A[h];
+    const int per = (Q + 63) / 64;  // <= 4
+    double v[4];
+    double run = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = lane * per + e;
+        double d = 0.0;
+        if (e < per && i < q) d = (double)to_f32(dt[((b * L) + s + i) * H + h]) * Ah;
+        run += d;
+        v[e] = run;
+    }
+    double tot = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double o = __shfl_up(tot, off, 64);
+        if (lane >= off) tot += o;
+    }
+    const double excl = tot - run;
+    double *out = cs + (((int64_t)b * H + h) * nc + c) * Q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = lane * per + e;
+        if (e < per && i < Q) out[i] = v[e] + excl;
+    }
+}
+
+// exp(a - b) with the difference formed in the prefix's own precision.
+template <typename CsT>
+__device__ __forceinline__ float exp_diff(CsT a, CsT b) {
+    return __expf((float)(a - b));
+}
+
+// fp32 [P][N] state -> bf16 [P][ld] in LDS.
+template <int P, int N>
+__device__ __forceinline__ void stage_state_bf16(const float *__restrict__ src, bf16 *dst, int ld) {
+    for (int idx = threadIdx.x; idx < P * N / 8; idx += blockDim.x) {
+        const int p = idx / (N / 8), n0 = (idx - p * (N / 8)) * 8;
+        const f32x4 a0 = *(const f32x4 *)(src + (int64_t)p * N + n0);
+        const f32x4 a1 = *(const f32x4 *)(src + (int64_t)p * N + n0 + 4);
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[e] = (bf16)a0[e];
+            v[e + 4] = (bf16)a1[e];
+        }
+        *(bf16x8 *)(dst + p * ld + n0) = v;
+    }
+}
+
+// Four consecutive channels p0..p0+3 of one row, as float.
+template <typename T>
+__device__ __forceinline__ f32x4 load4(const T *p) {
+    if constexpr (sizeof(T) == 2) {
+        const u32x2 w = *(const u32x2 *)p;
+        const bf16 *e = (const bf16 *)&w;
+        return f32x4{(float)e[0], (float)e[1], (float)e[2], (float)e[3]};
+    } else {
+        return *(const f32x4 *)p;
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T *p, f32x4 v) {
+    if constexpr (sizeof(T) == 2) {
+        bf16 o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+        *(u32x2 *)p = *(const u32x2 *)o;
+    } else {
+        *(f32x4 *)p = v;
+    }
+}
+
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) {
+    return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+}
+
+// Sum over the four lane groups that share r = lane % 16.
+__device__ __forceinline__ float sum_groups(float v) {
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Per (b, c, h): dx, ddt and the chunk's partials of dA_h and dD_h.
+// Two phases over the same LDS (bf16: one [P][Q] operand tile and one
+// [P][N] state tile; f32: operands straight from global memory):
+//   Y: x^T and H_c staged; per 16-row tile, Y''^T[p][i] = (H_c C_i) e^{cs_i}
+//      + sum_{j<i} x^T[p][j] M_ij  (the forward's output without D and
+//      without its diagonal term), then yy_i = dy_i . y''_i.
+//   X: dy^T and R_c staged; per 16-column tile, dX''^T[p][j] =
+//      e^{cs_e - cs_j} (R_c B_j) + sum_{i>j} dy^T[p][i] M_ij, with M read
+//      from cbT so the step index i is contiguous; xdx_j = x_j . dx''_j and the
+//      state part x_j . (e^{cs_e - cs_j} R_c B_j) summed for <R_c, H_{c+1}>;
+//      dx = dx'' + (M_jj + D) dy stored.
+// Then one wave forms dLoss/dcs_k, its suffix sums ddA, and writes ddt.
+// Output tiles go to the waves in a snake order (triangular work balanced).
+// ---------------------------------------------------------------------------
+template <typename T, int P, int N, typename CsT>
+__global__ __launch_bounds__(256) void k_chunk_bwd(
+    const T *__restrict__ x, const T *__restrict__ dy, const T *__restrict__ dt,
+    const float *__restrict__ A, const T *__restrict__ B, const T *__restrict__ C,
+    const T *__restrict__ cb, const T *__restrict__ cbT, const CsT *__restrict__ cs,
+    const float *__restrict__ Hs, const float *__restrict__ Rs, const float *__restrict__ D,
+    T *__restrict__ dx, T *__restrict__ ddt, float *__restrict__ part, int64_t L, int H, int G,
+    int Q, int nc) {
+    constexpr bool BF = sizeof(T) == 2;
+    constexpr int PT = P / 16;
+    const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = (int)(wid % H);
+    const int64_t bc = wid / H;
+    const int c = (int)(bc % nc);
+    const int64_t b = bc / nc;
+    const int g = h / (H / G);
+    const int64_t s = (int64_t)c * Q;
+    const int q = (int)min<int64_t>(Q, L - s);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, grp = lane >> 4;
+    const int Qp = (Q + 31) & ~31;
+
+    __shared__ CsT cs_s[256];
+    __shared__ float yy_s[256], xdx_s[256], red_s[4][3];
+    const CsT *csc = cs + (((int64_t)b * H + h) * nc + c) * Q;
+    for (int j = threadIdx.x; j < 256; j += 256) {
+        cs_s[j] = csc[min(j, Q - 1)];
+        yy_s[j] = 0.f;
+        xdx_s[j] = 0.f;
+    }
+
+    const int64_t row0 = (b * L + s) * H + h;  // (row of step s, head h) in x / dy / dx
+    const T *Cb = C + ((b * L + s) * G + g) * N;
+    const T *Bb = B + ((b * L + s) * G + g) * N;
+    const int64_t cboff = (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
+    const T *cbc = cb + cboff, *cbTc = cbT + cboff;
+    const int64_t soff = (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+    const float *hp = Hs + soff, *rp = Rs + soff;
+    const float Dh = D ? D[h] : 0.f;
+
+    constexpr int XLD = 256 + 8, HLD = N + 8;
+    __shared__ bf16 ops_s[BF ? P * XLD : 1];
+    __shared__ bf16 st_s[BF ? P * HLD : 1];
+
+    // State term of one 16-row (or column) tile: acc[pt][e] += sum_n S[p][n] V_row[n],
+    // p = pt*16 + 4 grp + e, S = H_c or R_c, V_row the lane's row of C or B.
+    auto state_term = [&](f32x4 *acc, const T *vrow, bool valid, const float *sg) {
+        if constexpr (BF) {
+#pragma unroll
+            for (int k0 = 0; k0 < N; k0 += 32) {
+                const int kk = k0 + grp * 8;
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                const u32x4 bv = (valid && kk < N) ? *(const u32x4 *)(vrow + kk) : z;
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const u32x4 av = kk < N ? *(const u32x4 *)(st_s + (pt * 16 + r) * HLD + kk) : z;
+                    acc[pt] = mfma_bf16(as_bf16x8(av), as_bf16x8(bv), acc[pt]);
+                }
+            }
+        } else {
+#pragma unroll 4
+            for (int k0 = 0; k0 < N; k0 += 16) {
+                const int kk = k0 + grp * 4;
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 c4 = valid ? *(const f32x4 *)(vrow + kk) : z;
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const f32x4 h4 = *(const f32x4 *)(sg + (int64_t)(pt * 16 + r) * N + kk);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[pt] = mfma_f32(h4[e], c4[e], acc[pt]);
+                }
+            }
+        }
+    };
+
+    // ---------------- phase Y ----------------
+    if constexpr (BF) {
+        stage_transposed_bf16<false>((const bf16 *)x + row0 * P, (int64_t)H * P, Qp, P, q, ops_s,
+                                     XLD, nullptr);
+        stage_state_bf16<P, N>(hp, st_s, HLD);
+    }
+    __syncthreads();
+
+    const int T16 = (q + 15) / 16;
+    for (int round = 0; 4 * round < T16; ++round) {
+        const int I = 4 * round + ((round & 1) ? 3 - wave : wave);
+        if (I >= T16) continue;
+        const int il = I * 16 + r;
+        const bool vi = il < q;
+        const CsT csi = cs_s[il];
+        f32x4 acc[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        state_term(acc, Cb + (int64_t)il * G * N, vi, hp);
+        const float ei = __expf((float)csi);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[pt] *= ei;
+
+        const T *grow = cbc + (int64_t)il * Q;
+        const int jend = I * 16 + 15;
+        if constexpr (BF) {
+            for (int j0 = 0; j0 <= jend; j0 += 32) {
+                const int jl = j0 + grp * 8;
+                bf16x8 bm;
+                if (jl < il) {
+                    const bf16x8 gv = as_bf16x8(*(const u32x4 *)(grow + jl));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = jl + e;
+                        bm[e] = (bf16)((j < il) ? exp_diff(csi, cs_s[j]) * (float)gv[e] : 0.f);
+                    }
+                } else {
+                    bm = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+                }
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const bf16x8 ax = *(const bf16x8 *)(ops_s + (pt * 16 + r) * XLD + jl);
+                    acc[pt] = mfma_bf16(ax, bm, acc[pt]);
+                }
+            }
+        } else {
+            for (int j0 = 0; j0 <= jend; j0 += 16) {
+                const int jl = j0 + grp * 4;
+                const f32x4 g4 = *(const f32x4 *)(grow + jl);
+                float m[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = jl + e;
+                    m[e] = (j < il) ? exp_diff(csi, cs_s[j]) * g4[e] : 0.f;
+                }
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = jl + e;
+                        const float xa =
+                            j < q ? to_f32(x[(row0 + (int64_t)j * H) * P + pt * 16 + r]) : 0.f;
+                        acc[pt] = mfma_f32(xa, m[e], acc[pt]);
+                    }
+                }
+            }
+        }
+        float yy = 0.f;
+        if (vi) {
+            const T *dyr = dy + (row0 + (int64_t)il * H) * P;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) yy += dot4(acc[pt], load4(dyr + pt * 16 + 4 * grp));
+        }
+        yy = sum_groups(yy);
+        if (grp == 0 && vi) yy_s[il] = yy;
+    }
+    __syncthreads();
+
+    // ---------------- phase X ----------------
+    if constexpr (BF) {
+        stage_transposed_bf16<false>((const bf16 *)dy + row0 * P, (int64_t)H * P, Qp, P, q, ops_s,
+                                     XLD, nullptr);
+        stage_state_bf16<P, N>(rp, st_s, HLD);
+    }
+    float rh = 0.f;  // <R_c, H_c>
+    for (int idx = threadIdx.x; idx < P * N / 4; idx += 256)
+        rh += dot4(*(const f32x4 *)(rp + 4 * idx), *(const f32x4 *)(hp + 4 * idx));
+    __syncthreads();
+
+    const CsT csE = cs_s[q - 1];
+    float vsum = 0.f, dDp = 0.f;
+    for (int round = 0; 4 * round < T16; ++round) {
+        const int J = 4 * round + ((round & 1) ? 3 - wave : wave);
+        if (J >= T16) continue;
+        const int jl = J * 16 + r;
+        const bool vj = jl < q;
+        const CsT csj = cs_s[jl];
+        f32x4 acc[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        state_term(acc, Bb + (int64_t)jl * G * N, vj, rp);
+        const float wj = exp_diff(csE, csj);
+        const T *xr = x + (row0 + (int64_t)jl * H) * P;
+        f32x4 xv[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            acc[pt] *= wj;
+            xv[pt] = vj ? load4(xr + pt * 16 + 4 * grp) : f32x4{0.f, 0.f, 0.f, 0.f};
+            vsum += dot4(acc[pt], xv[pt]);
+        }
+
+        const T *gcol = cbTc + (int64_t)jl * Q;  // cbT row j: M_ij / e^{cs_i - cs_j}, i contiguous
+        if constexpr (BF) {
+            for (int i0 = (J * 16) & ~31; i0 < q; i0 += 32) {
+                const int il = i0 + grp * 8;
+                bf16x8 bm;
+                if (il + 7 > jl && il < q) {
+                    const bf16x8 gv = as_bf16x8(*(const u32x4 *)(gcol + il));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int i = il + e;
+                        bm[e] = (bf16)((i > jl && i < q) ? exp_diff(cs_s[i], csj) * (float)gv[e]
+                                                         : 0.f);
+                    }
+                } else {
+                    bm = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+                }
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const bf16x8 ad = *(const bf16x8 *)(ops_s + (pt * 16 + r) * XLD + il);
+                    acc[pt] = mfma_bf16(ad, bm, acc[pt]);
+                }
+            }
+        } else {
+            for (int i0 = J * 16; i0 < q; i0 += 16) {
+                const int il = i0 + grp * 4;
+                const f32x4 g4 = *(const f32x4 *)(gcol + il);
+                float m[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = il + e;
+                    m[e] = (i > jl && i < q) ? exp_diff(cs_s[i], csj) * g4[e] : 0.f;
+                }
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = il + e;
+                        const float da =
+                            i < q ? to_f32(dy[(row0 + (int64_t)i * H) * P + pt * 16 + r]) : 0.f;
+                        acc[pt] = mfma_f32(da, m[e], acc[pt]);
+                    }
+                }
+            }
+        }
+        float xd = 0.f;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) xd += dot4(acc[pt], xv[pt]);
+        xd = sum_groups(xd);
+        if (grp == 0 && vj) xdx_s[jl] = xd;
+        if (vj) {
+            const T *dyr = dy + (row0 + (int64_t)jl * H) * P;
+            T *dxr = dx + (row0 + (int64_t)jl * H) * P;
+            const float diag = to_f32(cbc[(int64_t)jl * Q + jl]) + Dh;  // M_jj + D
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const int p0 = pt * 16 + 4 * grp;
+                const f32x4 d4 = load4(dyr + p0);
+                dDp += dot4(d4, xv[pt]);
+                store4(dxr + p0, acc[pt] + diag * d4);
+            }
+        }
+    }
+    {
+        const float v0 = wave_sum(vsum), v1 = wave_sum(rh), v2 = wave_sum(dDp);
+        if (lane == 0) {
+            red_s[wave][0] = v0;
+            red_s[wave][1] = v1;
+            red_s[wave][2] = v2;
+        }
+    }
+    __syncthreads();
+
+    // ---------------- decay gradients ----------------
+    if (wave == 0) {
+        float tv[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) tv[k] = red_s[0][k] + red_s[1][k] + red_s[2][k] + red_s[3][k];
+        // <R_c, H_{c+1}> = e^{cs_e} <R_c, H_c> + sum_j x_j . (e^{cs_e - cs_j} R_c B_j)
+        const float Tend = __expf((float)csE) * tv[1] + tv[0];
+        float d[4], suf[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int k = 4 * lane + e;
+            d[e] = k < q ? yy_s[k] - xdx_s[k] + (k == q - 1 ? Tend : 0.f) : 0.f;
+        }
+        suf[3] = d[3];
+        suf[2] = d[2] + suf[3];
+        suf[1] = d[1] + suf[2];
+        suf[0] = d[0] + suf[1];
+        float tot = suf[0];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float o = __shfl_down(tot, off, 64);
+            if (lane + off < 64) tot += o;
+        }
+        const float after = tot - suf[0];  // sum over the lanes above this one
+        const float Ah = A[h];
+        float dAp = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int k = 4 * lane + e;
+            if (k < q) {
+                const float dda = suf[e] + after;
+                const int64_t o = (b * L + s + k) * H + h;
+                ddt[o] = from_f32<T>(Ah * dda);
+                dAp += to_f32(dt[o]) * dda;
+            }
+        }
+        dAp = wave_sum(dAp);
+        if (lane == 0) {
+            float *pp = part + ((((int64_t)b * nc + c) * H + h) * 2);
+            pp[0] = dAp;
+            pp[1] = tv[2];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per (b, c, g, 64-row tile): sums over the heads of group g of
+//   dCB[i][j] = exp(cs_i - cs_j) (dy_i . x_j)                  (j <= i)
+//   dCs[i][n] = exp(cs_i) sum_p dy_i[p] H_c[p][n]
+//   dBs[j][n] = exp(cs_e - cs_j) sum_p x_j[p] R_c[p][n]
+// Each wave owns 16 rows and keeps its accumulators in registers across the
+// head loop; the row operands (dy_i, x_i) are 16-byte fragments straight
+// from global memory, the column operands (x_j, a state column) likewise.
+// dCB is written in both orientations (dcb[i][j], dcbT[j][i]); tiles above
+// the diagonal are not written.
+// ---------------------------------------------------------------------------
+template <typename T, int P, int N, typename CsT>
+__global__ __launch_bounds__(256) void k_group_bwd(
+    const T *__restrict__ x, const T *__restrict__ dy, const CsT *__restrict__ cs,
+    const float *__restrict__ Hs, const float *__restrict__ Rs, float *__restrict__ dcb,
+    float *__restrict__ dcbT, float *__restrict__ dCs, float *__restrict__ dBs, int64_t L, int H,
+    int G, int Q, int nc) {
+    constexpr int KPL = Frag<T>::KPL, KSTEP = Frag<T>::KSTEP;
+    constexpr int KS = (P + KSTEP - 1) / KSTEP, NT = N / 16;
+    const int ntr = (Q + 63) / 64;
+    const int64_t work = xcd_remap(blockIdx.x, gridDim.x);
+    const int tile = (int)(work % ntr);
+    const int64_t bcg = work / ntr;
+    const int g = (int)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int c = (int)(bc % nc);
+    const int64_t b = bc / nc;
+    const int64_t s = (int64_t)c * Q;
+    const int q = (int)min<int64_t>(Q, L - s);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, grp = lane >> 4;
+    const int i0 = tile * 64 + wave * 16;
+    if (i0 >= q) return;  // no barriers below
+    const int Ti = i0 / 16;
+    const int ia = i0 + r;  // this lane's row in the row-operand fragments
+    const bool va = ia < q;
+
+    f32x4 acb[16], adc[NT], adb[NT];
+#pragma unroll
+    for (int J = 0; J < 16; ++J) acb[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) adc[t] = adb[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int hpg = H / G;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int hh = 0; hh < hpg; ++hh) {
+        const int h = g * hpg + hh;
+        const CsT *csh = cs + (((int64_t)b * H + h) * nc + c) * Q;
+        const CsT csE = csh[q - 1];
+        CsT csr[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) csr[e] = csh[min(i0 + 4 * grp + e, Q - 1)];
+        const CsT csa = csh[min(ia, Q - 1)];
+        const float ea = __expf((float)csa), wa = exp_diff(csE, csa);
+        const int64_t rowA = (b * L + s + ia) * H + h;
+        u32x4 fdy[KS], fdye[KS], fxw[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int kk = ks * KSTEP + grp * KPL;
+            const bool ok = va && kk < P;
+            const u32x4 dv = ok ? *(const u32x4 *)(dy + rowA * P + kk) : z;
+            const u32x4 xv = ok ? *(const u32x4 *)(x + rowA * P + kk) : z;
+            fdy[ks] = dv;
+            fdye[ks] = frag_scale<T>(dv, ea);
+            fxw[ks] = frag_scale<T>(xv, wa);
+        }
+        // masked dy_i . x_j, j-tiles up to the diagonal
+#pragma unroll
+        for (int J = 0; J < 16; ++J) {
+            if (J <= Ti) {
+                const int jr = J * 16 + r;
+                const bool vj = jr < q;
+                const int64_t rowB = (b * L + s + jr) * H + h;
+                f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int kk = ks * KSTEP + grp * KPL;
+                    const u32x4 bx = (vj && kk < P) ? *(const u32x4 *)(x + rowB * P + kk) : z;
+                    t = mma16<T>(fdy[ks], bx, t);
+                }
+                const CsT csj = csh[min(jr, Q - 1)];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = i0 + 4 * grp + e;
+                    acb[J][e] += (jr <= i && i < q) ? exp_diff(csr[e], csj) * t[e] : 0.f;
+                }
+            }
+        }
+        // state terms: column operand = state column n, KPL consecutive p
+        const int64_t soff = (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+        const float *hp = Hs + soff, *rp = Rs + soff;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int n = t * 16 + r;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int kk = ks * KSTEP + grp * KPL;
+                const u32x4 bh = kk < P ? frag_from_f32_col<T>(hp + (int64_t)kk * N + n, N) : z;
+                const u32x4 br = kk < P ? frag_from_f32_col<T>(rp + (int64_t)kk * N + n, N) : z;
+                adc[t] = mma16<T>(fdye[ks], bh, adc[t]);
+                adb[t] = mma16<T>(fxw[ks], br, adb[t]);
+            }
+        }
+    }
+
+    const int64_t cboff = bcg * (int64_t)Q * Q;
+#pragma unroll
+    for (int J = 0; J < 16; ++J) {
+        if (J <= Ti) {
+            const int jr = J * 16 + r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dcb[cboff + (int64_t)(i0 + 4 * grp + e) * Q + jr] = acb[J][e];
+            *(f32x4 *)(dcbT + cboff + (int64_t)jr * Q + i0 + 4 * grp) = acb[J];
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int n = t * 16 + r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = i0 + 4 * grp + e;
+            if (i < q) {
+                const int64_t o = ((b * L + s + i) * G + g) * N + n;
+                dCs[o] = adc[t][e];
+                dBs[o] = adb[t][e];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per (b, c, g, 16-row tile, which): which = 0: dC[i] = dCs[i] + sum_{j<=i}
+// dCB[i][j] B_j; which = 1: dB[j] = dBs[j] + sum_{i>=j} dCB[i][j] C_i.
+// float32 MFMA (16x16x4): the dCB operand is 4 consecutive float32 values of
+// one row, the B / C operand 4 scalar loads of one column.  Wave w owns the
+// n-tiles w, w + 4, ...
+// ---------------------------------------------------------------------------
+template <typename T, int N>
+__global__ __launch_bounds__(256) void k_group_combine(
+    const T *__restrict__ B, const T *__restrict__ C, const float *__restrict__ dcb,
+    const float *__restrict__ dcbT, const float *__restrict__ dCs, const float *__restrict__ dBs,
+    T *__restrict__ dB, T *__restrict__ dC, int64_t L, int G, int Q, int nc) {
+    constexpr int NT = N / 16, NTW = (NT + 3) / 4;
+    const int T16 = Q / 16;
+    const int64_t work = xcd_remap(blockIdx.x, gridDim.x);
+    const int tile = (int)(work % T16);
+    const int which = (int)((work / T16) % 2);
+    const int64_t bcg = work / (2 * T16);
+    const int g = (int)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int c = (int)(bc % nc);
+    const int64_t b = bc / nc;
+    const int64_t s = (int64_t)c * Q;
+    const int q = (int)min<int64_t>(Q, L - s);
+    const int t0 = tile * 16;
+    if (t0 >= q) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, grp = lane >> 4;
+    const int64_t cboff = bcg * (int64_t)Q * Q;
+    const float *arow = (which == 0 ? dcb : dcbT) + cboff + (int64_t)(t0 + r) * Q;
+    const T *V = which == 0 ? B : C;  // the column operand's rows
+    const int k_lo = which == 0 ? 0 : t0;
+    const int k_hi = which == 0 ? t0 + 16 : ((q + 15) & ~15);
+
+    f32x4 acc[NTW];
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = k_lo; k0 < k_hi; k0 += 16) {
+        const int kk = k0 + 4 * grp;
+        const f32x4 a4 = *(const f32x4 *)(arow + kk);
+#pragma unroll
+        for (int u = 0; u < NTW; ++u) {
+            const int t = wave + 4 * u;
+            if (t < NT) {
+                const int n = t * 16 + r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int k = kk + e;
+                    const float v = k < q ? to_f32(V[((b * L + s + k) * G + g) * N + n]) : 0.f;
+                    acc[u] = mfma_f32(a4[e], v, acc[u]);
+                }
+            }
+        }
+    }
+    const float *base = which == 0 ? dCs : dBs;
+    T *out = which == 0 ? dC : dB;
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) {
+        const int t = wave + 4 * u;
+        if (t < NT) {
+            const int n = t * 16 + r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = t0 + 4 * grp + e;
+                if (i < q) {
+                    const int64_t o = ((b * L + s + i) * G + g) * N + n;
+                    out[o] = from_f32<T>(acc[u][e] + base[o]);
+                }
+            }
+        }
+    }
+}
+
+// dA[h] = sum over (b, c) of the chunk partials, likewise dD (nullable).
+__global__ __launch_bounds__(256) void k_head_reduce(const float *__restrict__ part, float *dA,
+                                                     float *dD, int64_t nbc, int H) {
+    const int h = blockIdx.x;
+    float a = 0.f, d = 0.f;
+    for (int64_t k = threadIdx.x; k < nbc; k += 256) {
+        a += part[(k * H + h) * 2];
+        d += part[(k * H + h) * 2 + 1];
+    }
+    __shared__ float red[2][4];
+    a = wave_sum(a);
+    d = wave_sum(d);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        red[0][wave] = a;
+        red[1][wave] = d;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        dA[h] = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+        if (dD) dD[h] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.
+// ---------------------------------------------------------------------------
+#define SSD_BWD_DISPATCH_N(N_, ...)                                               \
+    switch (N_) {                                                                 \
+    case 16: { constexpr int NN = 16; __VA_ARGS__; } break;                       \
+    case 32: { constexpr int NN = 32; __VA_ARGS__; } break;                       \
+    case 64: { constexpr int NN = 64; __VA_ARGS__; } break;                       \
+    case 128: { constexpr int NN = 128; __VA_ARGS__; } break;                     \
+    case 256: { constexpr int NN = 256; __VA_ARGS__; } break;                     \
+    default: return hipErrorInvalidValue;                                         \
+    }
+#define SSD_BWD_DISPATCH_PN(P_, N_, ...)                                          \
+    do {                                                                          \
+        switch (P_) {                                                             \
+        case 16: { constexpr int PP = 16; SSD_BWD_DISPATCH_N(N_, __VA_ARGS__); } break; \
+        case 32: { constexpr int PP = 32; SSD_BWD_DISPATCH_N(N_, __VA_ARGS__); } break; \
+        case 64: { constexpr int PP = 64; SSD_BWD_DISPATCH_N(N_, __VA_ARGS__); } break; \
+        case 128: { constexpr int PP = 128; SSD_BWD_DISPATCH_N(N_, __VA_ARGS__); } break; \
+        default: return hipErrorInvalidValue;                                     \
+        }                                                                         \
+    } while (0)
+
+hipError_t launch_state_passing_rev(const Dims &d, float *S, const float *cs, const float *dfinal,
+                                    float *dinit, hipStream_t st) {
+    if (d.b == 0) return hipSuccess;
+    const int PN = (int)(d.P * d.N);
+    dim3 grid((unsigned)((PN / 4 + 255) / 256), (unsigned)d.H, (unsigned)d.b);
+    k_state_passing_rev<<<grid, 256, 0, st>>>(S, cs, dfinal, dinit, d.L, (int)d.H, PN, (int)d.Q,
+                                              (int)d.nc);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_cumsum64(const Dims &d, const void *dt, const float *A, double *cs,
+                                 hipStream_t st) {
+    if (d.b == 0 || d.nc == 0) return hipSuccess;
+    dim3 grid((unsigned)d.nc, (unsigned)d.H, (unsigned)d.b);
+    if (d.dtype == 1)
+        k_chunk_cumsum64<bf16><<<grid, 64, 0, st>>>((const bf16 *)dt, A, cs, d.L, (int)d.H, (int)d.Q,
+                                                    (int)d.nc);
+    else
+        k_chunk_cumsum64<float><<<grid, 64, 0, st>>>((const float *)dt, A, cs, d.L, (int)d.H,
+                                                     (int)d.Q, (int)d.nc);
+    return hipGetLastError();
+}
+
+// bf16 inputs use the float32 prefix (cs), float32 inputs the float64 one (cs64).
+hipError_t launch_chunk_bwd(const Dims &d, const void *x, const void *dy, const void *dt,
+                            const float *A, const void *B, const void *C, const void *cb,
+                            const void *cbT, const float *cs, const double *cs64, const float *Hs,
+                            const float *Rs, const float *D, void *dx, void *ddt, float *part,
+                            hipStream_t st) {
+    if (d.b == 0 || d.nc == 0) return hipSuccess;
+    const unsigned grid = (unsigned)(d.b * d.nc * d.H);
+    SSD_BWD_DISPATCH_PN(d.P, d.N, {
+        if (d.dtype == 1)
+            k_chunk_bwd<bf16, PP, NN, float><<<grid, 256, 0, st>>>(
+                (const bf16 *)x, (const bf16 *)dy, (const bf16 *)dt, A, (const bf16 *)B,
+                (const bf16 *)C, (const bf16 *)cb, (const bf16 *)cbT, cs, Hs, Rs, D, (bf16 *)dx,
+                (bf16 *)ddt, part, d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc);
+        else
+            k_chunk_bwd<float, PP, NN, double><<<grid, 256, 0, st>>>(
+                (const float *)x, (const float *)dy, (const float *)dt, A, (const float *)B,
+                (const float *)C, (const float *)cb, (const float *)cbT, cs64, Hs, Rs, D,
+                (float *)dx, (float *)ddt, part, d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc);
+    });
+    return hipGetLastError();
+}
+
+hipError_t launch_group_bwd(const Dims &d, const void *x, const void *dy, const float *cs,
+                            const double *cs64, const float *Hs, const float *Rs, float *dcb,
+                            float *dcbT, float *dCs, float *dBs, hipStream_t st) {
+    if (d.b == 0 || d.nc == 0) return hipSuccess;
+    const unsigned grid = (unsigned)(d.b * d.nc * d.G * ((d.Q + 63) / 64));
+    SSD_BWD_DISPATCH_PN(d.P, d.N, {
+        if (d.dtype == 1)
+            k_group_bwd<bf16, PP, NN, float><<<grid, 256, 0, st>>>(
+                (const bf16 *)x, (const bf16 *)dy, cs, Hs, Rs, dcb, dcbT, dCs, dBs, d.L, (int)d.H,
+                (int)d.G, (int)d.Q, (int)d.nc);
+        else
+            k_group_bwd<float, PP, NN, double><<<grid, 256, 0, st>>>(
+                (const float *)x, (const float *)dy, cs64, Hs, Rs, dcb, dcbT, dCs, dBs, d.L,
+                (int)d.H, (int)d.G, (int)d.Q, (int)d.nc);
+    });
+    return hipGetLastError();
+}
+
+hipError_t launch_group_combine(const Dims &d, const void *B, const void *C, const float *dcb,
+                                const float *dcbT, const float *dCs, const float *dBs, void *dB,
+                                void *dC, hipStream_t st) {
+    if (d.b == 0 || d.nc == 0) return hipSuccess;
+    const unsigned grid = (unsigned)(d.b * d.nc * d.G * 2 * (d.Q / 16));
+    SSD_BWD_DISPATCH_N(d.N, {
+        if (d.dtype == 1)
+            k_group_combine<bf16, NN><<<grid, 256, 0, st>>>((const bf16 *)B, (const bf16 *)C, dcb,
+                                                           dcbT, dCs, dBs, (bf16 *)dB, (bf16 *)dC,
+                                                           d.L, (int)d.G, (int)d.Q, (int)d.nc);
+        else
+            k_group_combine<float, NN><<<grid, 256, 0, st>>>((const float *)B, (const float *)C,
+                                                            dcb, dcbT, dCs, dBs, (float *)dB,
+                                                            (float *)dC, d.L, (int)d.G, (int)d.Q,
+                                                            (int)d.nc);
+    });
+    return hipGetLastError();
+}
+
+hipError_t launch_head_reduce(const Dims &d, const float *part, float *dA, float *dD,
+                              hipStream_t st) {
+    k_head_reduce<<<(unsigned)d.H, 256, 0, st>>>(part, dA, dD, d.b * d.nc, (int)d.H);
+    return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -39,6 +39,69 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
 
+// 16-byte fragments for either element type.  A lane holds KPL consecutive
+// values of the contraction index (bf16: 8, one 16x16x32 MFMA; f32: 4, four
+// 16x16x4 MFMAs, the e-th taking element e), so a fragment step covers KSTEP
+// = 4 KPL values of k across the four lane groups.
+template <typename T> struct Frag {
+    static constexpr int KPL = 16 / (int)sizeof(T);
+    static constexpr int KSTEP = 4 * KPL;
+};
+
+template <typename T>
+__device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (sizeof(T) == 2) {
+        return mfma_bf16(as_bf16x8(a), as_bf16x8(b), c);
+    } else {
+        // Each element goes through a scalar first: clang's __builtin_bit_cast of an
+        // ext-vector element expression reads element 0 whatever the index.
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t ua = a[e], ub = b[e];
+            c = mfma_f32(__builtin_bit_cast(float, ua), __builtin_bit_cast(float, ub), c);
+        }
+        return c;
+    }
+}
+
+// Every element of a fragment times s (bf16: rounded back to bf16).
+template <typename T>
+__device__ __forceinline__ u32x4 frag_scale(u32x4 v, float s) {
+    if constexpr (sizeof(T) == 2) {
+        bf16x8 t = as_bf16x8(v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = (bf16)((float)t[e] * s);
+        return as_u32x4(t);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t u = v[e];
+            v[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, u) * s);
+        }
+        return v;
+    }
+}
+
+// A fragment from KPL float32 values base[0], base[ld], base[2 ld], ...
+// (a column of a row-major float32 matrix), converted to T.
+template <typename T>
+__device__ __forceinline__ u32x4 frag_from_f32_col(const float *base, int64_t ld) {
+    if constexpr (sizeof(T) == 2) {
+        bf16x8 t;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = (bf16)base[e * ld];
+        return as_u32x4(t);
+    } else {
+        u32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float f = base[e * ld];
+            v[e] = __builtin_bit_cast(uint32_t, f);
+        }
+        return v;
+    }
+}
+
 // Blocks are dealt to the 8 XCDs round-robin (block k runs on XCD k % 8), and
 // each XCD has its own L2.  Work items that share operands (all heads of one
 // chunk share C, B and C B^T) should land on the same XCD, so map block k to

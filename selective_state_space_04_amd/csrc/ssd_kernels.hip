@@ -66,12 +66,14 @@ __global__ __launch_bounds__(64) void k_chunk_cumsum(const T *__restrict__ dt,
 // C B^T per (b, c, g): one wave per 16 x 16 tile on or below the diagonal,
 // K = N in MFMA steps.  A operand = C rows (m = i), B operand = B rows
 // (n = j); both are read straight from global memory with the contraction
-// index contiguous.
+// index contiguous.  When cbT is given, the same tiles are also written
+// transposed (cbT[j][i] = C_i . B_j), which the gradient kernels read with
+// the step index i contiguous.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void k_chunk_cb(const T *__restrict__ B, const T *__restrict__ C,
-                                                  T *__restrict__ cb, int64_t L, int G, int N,
-                                                  int Q, int nc) {
+                                                  T *__restrict__ cb, T *__restrict__ cbT,
+                                                  int64_t L, int G, int N, int Q, int nc) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, grp = lane >> 4;
     const int T16 = Q / 16;
@@ -111,20 +113,32 @@ __global__ __launch_bounds__(256) void k_chunk_cb(const T *__restrict__ B, const
             for (int e = 0; e < 4; ++e) acc = mfma_f32(a[e], bb[e], acc);
         }
     }
-    T *out = cb + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
+    const int64_t off = (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
+    T *out = cb + off;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         out[(int64_t)(ti * 16 + 4 * grp + e) * Q + tj * 16 + r] = from_f32<T>(acc[e]);
+    if (cbT) {
+        T v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = from_f32<T>(acc[e]);
+        T *dst = cbT + off + (int64_t)(tj * 16 + r) * Q + ti * 16 + 4 * grp;
+        if constexpr (sizeof(T) == 2) *(u32x2 *)dst = *(const u32x2 *)v;
+        else *(f32x4 *)dst = *(const f32x4 *)v;
+    }
 }
 
 // ---------------------------------------------------------------------------
 // Chunk state S_c^T[n][p] = sum_j B_j[n] (w_j x_j[p]), one workgroup per
-// (b, c, h).  bf16: 64-step slabs of x (pre-scaled by w_j) and B are staged
+// (b, c, h).  w_j = exp(cs_{q-1} - cs_j) (decay to the chunk end) for the
+// forward state; with FROM_START, w_j = exp(cs_j) (decay from the chunk
+// start), which with (x, B) -> (dy, C) gives the gradient that a chunk's
+// outputs send back to the state entering it.  bf16: 64-step slabs of x (pre-scaled by w_j) and B are staged
 // in LDS transposed (step index contiguous) so each MFMA fragment is one
 // 16-byte LDS read.  f32: fragments come straight from global memory (one
 // element per lane per MFMA).  Wave w owns n-tiles w, w + 4, ...
 // ---------------------------------------------------------------------------
-template <typename T, int P, int N>
+template <typename T, int P, int N, bool FROM_START>
 __global__ __launch_bounds__(256) void k_chunk_state(const T *__restrict__ x,
                                                      const T *__restrict__ B,
                                                      const float *__restrict__ cs,
@@ -145,7 +159,8 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T *__restrict__ x,
     __shared__ float w_s[256];
     const float *csc = cs + (((int64_t)b * H + h) * nc + c) * Q;
     const float cs_last = csc[q - 1];
-    for (int j = threadIdx.x; j < Q; j += 256) w_s[j] = __expf(cs_last - csc[j]);
+    for (int j = threadIdx.x; j < Q; j += 256)
+        w_s[j] = FROM_START ? __expf(csc[j]) : __expf(cs_last - csc[j]);
     __syncthreads();
 
     f32x4 acc[NTW][PT];
@@ -551,34 +566,41 @@ hipError_t launch_chunk_cumsum(const Dims &d, const void *dt, const float *A, fl
     return hipGetLastError();
 }
 
-hipError_t launch_chunk_cb(const Dims &d, const void *B, const void *C, void *cb, hipStream_t st) {
+hipError_t launch_chunk_cb(const Dims &d, const void *B, const void *C, void *cb, void *cbT,
+                           hipStream_t st) {
     if (d.b == 0 || d.nc == 0) return hipSuccess;
     const int T16 = (int)(d.Q / 16);
     const int ntiles = T16 * (T16 + 1) / 2;
     dim3 grid((unsigned)(d.b * d.nc * d.G), (unsigned)((ntiles + 3) / 4));
     if (d.dtype == 1)
-        k_chunk_cb<bf16><<<grid, 256, 0, st>>>((const bf16 *)B, (const bf16 *)C, (bf16 *)cb, d.L,
-                                               (int)d.G, (int)d.N, (int)d.Q, (int)d.nc);
+        k_chunk_cb<bf16><<<grid, 256, 0, st>>>((const bf16 *)B, (const bf16 *)C, (bf16 *)cb,
+                                               (bf16 *)cbT, d.L, (int)d.G, (int)d.N, (int)d.Q,
+                                               (int)d.nc);
     else
         k_chunk_cb<float><<<grid, 256, 0, st>>>((const float *)B, (const float *)C, (float *)cb,
-                                                d.L, (int)d.G, (int)d.N, (int)d.Q, (int)d.nc);
+                                                (float *)cbT, d.L, (int)d.G, (int)d.N, (int)d.Q,
+                                                (int)d.nc);
     return hipGetLastError();
 }
 
 hipError_t launch_chunk_state(const Dims &d, const void *x, const void *B, const float *cs,
-                              float *S, hipStream_t st) {
+                              float *S, bool from_start, hipStream_t st) {
     if (d.b == 0 || d.nc == 0) return hipSuccess;
     const unsigned grid = (unsigned)(d.b * d.nc * d.H);
-    SSD_DISPATCH_PN(d.P, d.N, {
-        if (d.dtype == 1)
-            k_chunk_state<bf16, PP, NN><<<grid, 256, 0, st>>>((const bf16 *)x, (const bf16 *)B, cs,
-                                                             S, d.L, (int)d.H, (int)d.G, (int)d.Q,
-                                                             (int)d.nc);
-        else
-            k_chunk_state<float, PP, NN><<<grid, 256, 0, st>>>((const float *)x, (const float *)B,
-                                                              cs, S, d.L, (int)d.H, (int)d.G,
-                                                              (int)d.Q, (int)d.nc);
-    });
+#define SSD_LAUNCH_STATE(FS)                                                                      \
+    SSD_DISPATCH_PN(d.P, d.N, {                                                                   \
+        if (d.dtype == 1)                                                                         \
+            k_chunk_state<bf16, PP, NN, FS><<<grid, 256, 0, st>>>(                                \
+                (const bf16 *)x, (const bf16 *)B, cs, S, d.L, (int)d.H, (int)d.G, (int)d.Q,       \
+                (int)d.nc);                                                                       \
+        else                                                                                      \
+            k_chunk_state<float, PP, NN, FS><<<grid, 256, 0, st>>>(                               \
+                (const float *)x, (const float *)B, cs, S, d.L, (int)d.H, (int)d.G, (int)d.Q,     \
+                (int)d.nc);                                                                       \
+    })
+    if (from_start) SSD_LAUNCH_STATE(true);
+    else SSD_LAUNCH_STATE(false);
+#undef SSD_LAUNCH_STATE
     return hipGetLastError();
 }
 

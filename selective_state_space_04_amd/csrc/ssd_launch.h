@@ -14,9 +14,10 @@ struct Dims {
 
 hipError_t launch_chunk_cumsum(const Dims &d, const void *dt, const float *A, float *cs,
                                hipStream_t st);
-hipError_t launch_chunk_cb(const Dims &d, const void *B, const void *C, void *cb, hipStream_t st);
+hipError_t launch_chunk_cb(const Dims &d, const void *B, const void *C, void *cb, void *cbT,
+                           hipStream_t st);
 hipError_t launch_chunk_state(const Dims &d, const void *x, const void *B, const float *cs,
-                              float *S, hipStream_t st);
+                              float *S, bool from_start, hipStream_t st);
 hipError_t launch_state_passing(const Dims &d, float *S, const float *cs, const float *init,
                                 float *fin, hipStream_t st);
 hipError_t launch_chunk_scan(const Dims &d, const void *x, const void *C, const void *cb,
@@ -33,5 +34,24 @@ hipError_t launch_fused_main(const Dims &d, const void *x, const void *dt, const
                              const float *init, void *y, float *fin, float *ring, int *flags,
                              hipStream_t st);
 hipError_t launch_zero_state(const Dims &d, const float *init, float *fin, hipStream_t st);
+
+// Gradient kernels (ssd_backward.hip).
+hipError_t launch_state_passing_rev(const Dims &d, float *S, const float *cs, const float *dfinal,
+                                    float *dinit, hipStream_t st);
+hipError_t launch_chunk_cumsum64(const Dims &d, const void *dt, const float *A, double *cs,
+                                 hipStream_t st);
+hipError_t launch_chunk_bwd(const Dims &d, const void *x, const void *dy, const void *dt,
+                            const float *A, const void *B, const void *C, const void *cb,
+                            const void *cbT, const float *cs, const double *cs64, const float *Hs,
+                            const float *Rs, const float *D, void *dx, void *ddt, float *part,
+                            hipStream_t st);
+hipError_t launch_group_bwd(const Dims &d, const void *x, const void *dy, const float *cs,
+                            const double *cs64, const float *Hs, const float *Rs, float *dcb,
+                            float *dcbT, float *dCs, float *dBs, hipStream_t st);
+hipError_t launch_group_combine(const Dims &d, const void *B, const void *C, const float *dcb,
+                                const float *dcbT, const float *dCs, const float *dBs, void *dB,
+                                void *dC, hipStream_t st);
+hipError_t launch_head_reduce(const Dims &d, const float *part, float *dA, float *dD,
+                              hipStream_t st);
 
 }  // namespace ssd

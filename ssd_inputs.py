@@ -126,6 +126,17 @@ def make_forward_inputs(w: Workload, seed: int | None = None) -> dict:
     }
 
 
+def make_output_grads(w: Workload, seed: int | None = None, with_final: bool = True) -> dict:
+    """Seeded output gradients for a backward call: dy ~ N(0, 1) [b, L, H, P]
+    in the workload's dtype and dfinal ~ N(0, 1) [b, H, P, N] float32 (None
+    when with_final is False).  Seeded by seed (default w.seed + 500000)."""
+    g = _gen(w.seed + 500000 if seed is None else seed)
+    b, L, H, P, N = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate
+    dy = torch.randn((b, L, H, P), generator=g, dtype=torch.float32)
+    dfinal = torch.randn((b, H, P, N), generator=g, dtype=torch.float32) if with_final else None
+    return {"dy": dy.to(DTYPES[w.dtype]).contiguous(), "dfinal": dfinal}
+
+
 def make_decode_params(w: Workload) -> dict:
     """A, D and the initial state of a decode run (seeded by w.seed)."""
     g = _gen(w.seed)

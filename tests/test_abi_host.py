@@ -199,3 +199,81 @@ def test_entry_points_reject_before_launch():
                                          a["x"], None)] == "SSD_ERR_ALIAS"
     assert ssd.STATUS[LIB.ssd_decode_step(ctypes.byref(dims(dtype=5)), *([a["x"]] * 8), None, None)] == \
         "SSD_ERR_DTYPE"
+
+
+# ------------------------------------------------------------------ backward
+BWD_NAMES = ["x", "dt", "A", "B", "C", "D", "init", "dy", "dfinal", "dx", "ddt", "dA", "dB", "dC", "dD",
+             "dinit"]
+
+
+def bwd_args(d, **over):
+    b = Bufs()
+    args = {k: b.take() for k in BWD_NAMES}
+    args["ws"] = b.take()
+    args["ws_bytes"] = ssd.backward_workspace_bytes(d)
+    args.update(over)
+    return args
+
+
+def vbwd(d, a):
+    return LIB.ssd_validate_backward(ctypes.byref(d), *[a[k] for k in BWD_NAMES], a["ws"], a["ws_bytes"])
+
+
+def test_backward_valid_and_nullable():
+    d = dims()
+    assert vbwd(d, bwd_args(d)) == 0
+    assert vbwd(d, bwd_args(d, D=None, init=None, dfinal=None, dD=None, dinit=None)) == 0
+
+
+@pytest.mark.parametrize("name", ["x", "dt", "A", "B", "C", "dy", "dx", "ddt", "dA", "dB", "dC"])
+def test_backward_null_required(name):
+    d = dims()
+    assert ssd.STATUS[vbwd(d, bwd_args(d, **{name: None}))] == "SSD_ERR_NULL"
+
+
+@pytest.mark.parametrize("name", BWD_NAMES)
+def test_backward_misaligned(name):
+    d = dims()
+    a = bwd_args(d)
+    a[name] += 4
+    assert ssd.STATUS[vbwd(d, a)] == "SSD_ERR_ALIGN"
+
+
+def test_backward_workspace_and_alias():
+    d = dims()
+    a = bwd_args(d)
+    assert ssd.STATUS[vbwd(d, dict(a, ws_bytes=a["ws_bytes"] - 1))] == "SSD_ERR_WORKSPACE"
+    assert ssd.STATUS[vbwd(d, dict(a, ws=None))] == "SSD_ERR_WORKSPACE"
+    assert ssd.STATUS[vbwd(d, dict(a, dx=a["x"]))] == "SSD_ERR_ALIAS"        # output over an input
+    assert ssd.STATUS[vbwd(d, dict(a, dB=a["dC"] + 16))] == "SSD_ERR_ALIAS"  # two outputs overlap
+    assert ssd.STATUS[vbwd(d, dict(a, dinit=a["dfinal"]))] == "SSD_ERR_ALIAS"
+    assert ssd.STATUS[vbwd(d, dict(a, ws=a["dy"]))] == "SSD_ERR_ALIAS"
+    assert ssd.STATUS[vbwd(dims(headdim=48), a)] == "SSD_ERR_UNSUPPORTED"
+
+
+def test_backward_empty_allows_null_arrays():
+    d = dims(seqlen=0)
+    assert ssd.backward_workspace_bytes(d) == 0
+    a = bwd_args(d, x=None, dt=None, B=None, C=None, dy=None, dx=None, ddt=None, dB=None, dC=None, ws=None,
+                 ws_bytes=0)
+    assert vbwd(d, a) == 0
+
+
+def test_backward_workspace_bytes():
+    b, L, H, P, N, G, Q = 2, 100, 4, 64, 128, 2, 64
+    nc = 2
+    al = lambda v: (v + 255) & ~255
+    o = 0
+    for nbytes in [b * H * nc * Q * 4, b * nc * G * Q * Q * 2, b * nc * G * Q * Q * 2, b * nc * H * P * N * 4,
+                   b * nc * H * P * N * 4, b * nc * G * Q * Q * 4, b * nc * G * Q * Q * 4, b * L * G * N * 4,
+                   b * L * G * N * 4, b * nc * H * 2 * 4, 0]:
+        o = al(o + nbytes)
+    assert ssd.backward_workspace_bytes(dims()) == o
+    # float32 inputs add a float64 decay prefix
+    o32 = 0
+    for nbytes in [b * H * nc * Q * 4, b * nc * G * Q * Q * 4, b * nc * G * Q * Q * 4, b * nc * H * P * N * 4,
+                   b * nc * H * P * N * 4, b * nc * G * Q * Q * 4, b * nc * G * Q * Q * 4, b * L * G * N * 4,
+                   b * L * G * N * 4, b * nc * H * 2 * 4, b * H * nc * Q * 8]:
+        o32 = al(o32 + nbytes)
+    assert ssd.backward_workspace_bytes(dims(dtype=ssd.F32)) == o32
+    assert ssd.backward_workspace_bytes(dims(headdim=48)) == 0

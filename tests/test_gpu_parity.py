@@ -382,3 +382,205 @@ def test_single_pass_launches_compose(ssd):
                                     p(t["D"]), p(t["init"]), p(y2), p(f2), p(ws), ws.numel(), s) == 0
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+# ------------------------------------------------------------------ backward
+# Gradients of Loss = sum(dy * y) + sum(dfinal * final_state), against the
+# float64 reverse-mode oracle.  Slices: dx, ddt per (batch, head); dB, dC per
+# (batch, group); dinit per (batch, head).
+#
+# Sums whose terms cancel are measured against the size of their terms: each
+# term carries its own rounding error, and independent errors add in
+# quadrature, so the error of a computed sum scales with the L2 norm of its
+# terms, not with |sum| (probabilistic rounding-error model):
+#   * dD_h = sum of dy . x: max_h |gpu - oracle| / sqrt(sum term^2).
+#   * dA_h = sum_t dt_t ddA_t = sum_k W_k dLoss/dcs_k with W_k the sum of dt
+#     over the steps of k's chunk up to k, so each per-step term of the decay
+#     gradient enters dA weighted by W_k: its scale is sqrt(sum_t (dt_t
+#     ddA_t)^2 + sum_k (W_k term_k)^2), term_k as below.
+#   * ddA_t is formed inside each chunk as the suffix sum over k >= t of
+#     dy_k.y''_k - x_k.dx''_k (plus one end-of-chunk term), where y''_k =
+#     y_k - (D + C_k.B_k) x_k and dx''_k = dx_k - (D + C_k.B_k) dy_k; where a
+#     head forgets fast these terms nearly telescope and ddA_t is far smaller
+#     than they are.  mag_t = sqrt(sum_{k >= t in t's chunk} (dy_k.y''_k)^2 +
+#     (x_k.dx''_k)^2), from the oracle's own y and dx (no chunked
+#     intermediate); ddt's error in slice (b, h) is measured against
+#     max(|A_h| ||mag||, ||ddt||) along L.  For terms of random sign mag_t is
+#     about |ddA_t|, so this is the plain relative error except where the
+#     terms telescope.
+BWD_TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def oracle_backward(inp, g):
+    return oracle.backward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["init"],
+                           g["dy"], g["dfinal"])
+
+
+def run_backward(ssd, inp, g, chunk, **kw):
+    out = ssd.backward(dev(inp["x"]), dev(inp["dt"]), dev(inp["A"]), dev(inp["B"]), dev(inp["C"]),
+                       dev(g["dy"]), D=dev(inp["D"]), init_state=dev(inp["init"]),
+                       dfinal_state=dev(g["dfinal"]), chunk=chunk, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def sum_rel(a, r, mag):
+    """max over h of |a_h - r_h| / mag_h (mag_h = L2 norm of r_h's terms)."""
+    a, r = np.asarray(a, np.float64), np.asarray(r, np.float64)
+    return float(np.max(np.abs(a - r) / np.maximum(mag, 1e-30))) if len(r) else 0.0
+
+
+def decay_grad_scale(inp, g, ref, chunk):
+    """(mag, term) [b, L, H]: term_k = sqrt((dy_k.y''_k)^2 + (x_k.dx''_k)^2), the
+    size of the per-step terms the chunked decay gradient adds, and mag_t the
+    L2 norm of term over the steps k >= t of t's chunk (see above)."""
+    x, dy = si.to_f64(inp["x"]), si.to_f64(g["dy"])
+    B, C = si.to_f64(inp["B"]), si.to_f64(inp["C"])
+    b, L, H, P = x.shape
+    G = B.shape[2]
+    y, _ = oracle_forward(inp)
+    D = np.zeros(H) if inp["D"] is None else si.to_f64(inp["D"])
+    cbd = np.repeat(np.einsum("blgn,blgn->blg", C, B), H // G, axis=2)  # C_k . B_k per head
+    diag = D[None, None, :] + cbd
+    ypp = y - diag[..., None] * x
+    dxpp = ref["dx"] - diag[..., None] * dy
+    term2 = np.einsum("blhp,blhp->blh", dy, ypp) ** 2 + np.einsum("blhp,blhp->blh", x, dxpp) ** 2
+    mag2 = np.zeros_like(term2)
+    for c0 in range(0, L, chunk):
+        seg = term2[:, c0:c0 + chunk]
+        mag2[:, c0:c0 + chunk] = np.cumsum(seg[:, ::-1], axis=1)[:, ::-1]
+    return np.sqrt(mag2), np.sqrt(term2)
+
+
+def slice_rel_scaled(a, r, scale):
+    """worst over (b, h) of ||a - r|| / max(||scale||, ||r||) along L, for [b, L, H] arrays."""
+    num = np.linalg.norm(a - r, axis=1)
+    den = np.maximum(np.maximum(np.linalg.norm(scale, axis=1), np.linalg.norm(r, axis=1)), 1e-30)
+    return float(np.max(num / den)) if num.size else 0.0
+
+
+def bwd_errors(out, ref, inp, g, chunk):
+    dt, A = si.to_f64(inp["dt"]), si.to_f64(inp["A"])
+    mag, term = decay_grad_scale(inp, g, ref, chunk)
+    W = np.zeros_like(dt)                                              # chunk-local inclusive sums of dt
+    for c0 in range(0, dt.shape[1], chunk):
+        W[:, c0:c0 + chunk] = np.cumsum(dt[:, c0:c0 + chunk], axis=1)
+    mag_dA = np.sqrt(((dt * ref["ddt"] / A) ** 2).sum(axis=(0, 1)) + ((W * term) ** 2).sum(axis=(0, 1)))
+    mag_dD = np.sqrt(((si.to_f64(g["dy"]) * si.to_f64(inp["x"])).sum(axis=3) ** 2).sum(axis=(0, 1)))
+    e = {"dx": worst_rel(f64(out["dx"]), ref["dx"], "y"),
+         "ddt": slice_rel_scaled(f64(out["ddt"]), ref["ddt"], np.abs(A)[None, None, :] * mag),
+         "dB": worst_rel(f64(out["dB"]), ref["dB"], "y"),
+         "dC": worst_rel(f64(out["dC"]), ref["dC"], "y"),
+         "dA": sum_rel(f64(out["dA"]), ref["dA"], mag_dA)}
+    if "dD" in out:
+        e["dD"] = sum_rel(f64(out["dD"]), ref["dD"], mag_dD)
+    if "dinit" in out:
+        e["dinit"] = worst_rel(f64(out["dinit"]), ref["dinit"], "state")
+    return e
+
+
+def check_bwd(out, ref, dtype, inp, g):
+    e = bwd_errors(out, ref, inp, g, inp["workload"].chunk)
+    print("backward errors:", {k: f"{v:.2e}" for k, v in e.items()}, flush=True)
+    bad = {k: v for k, v in e.items() if not v < BWD_TOL[dtype]}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [16, 48, 64, 128, 256])
+def test_backward_small(ssd, dtype, chunk):
+    w = small(dtype, chunk=chunk)
+    inp = si.make_forward_inputs(w)
+    g = si.make_output_grads(w)
+    check_bwd(run_backward(ssd, inp, g, chunk), oracle_backward(inp, g), dtype, inp, g)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("P", [16, 32, 64, 128])
+@pytest.mark.parametrize("N", [16, 32, 64, 128, 256])
+def test_backward_shapes(ssd, dtype, P, N):
+    w = small(dtype, batch=1, seqlen=77, nheads=2, headdim=P, dstate=N, ngroups=1, chunk=32,
+              seed=P * 1000 + N)
+    inp = si.make_forward_inputs(w)
+    g = si.make_output_grads(w)
+    check_bwd(run_backward(ssd, inp, g, w.chunk), oracle_backward(inp, g), dtype, inp, g)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_optional_absent(ssd, dtype):
+    """D, init_state and dfinal_state absent; dD and dinit not requested."""
+    w = small(dtype, d_mode="zero", init_mode="zero")
+    inp = si.make_forward_inputs(w)
+    g = si.make_output_grads(w, with_final=False)
+    out = run_backward(ssd, inp, g, 64, want_dD=False, want_dinit=False)
+    assert "dD" not in out and "dinit" not in out
+    check_bwd(out, oracle_backward(inp, g), dtype, inp, g)
+
+
+@pytest.mark.parametrize("L", [1, 10, 16, 63, 64, 65, 200])
+def test_backward_short_and_ragged(ssd, L):
+    w = small("f32", seqlen=L, chunk=64)
+    inp = si.make_forward_inputs(w)
+    g = si.make_output_grads(w)
+    check_bwd(run_backward(ssd, inp, g, 64), oracle_backward(inp, g), "f32", inp, g)
+
+
+def test_backward_empty(ssd):
+    w = small("f32", seqlen=0)
+    inp = si.make_forward_inputs(w)
+    g = si.make_output_grads(w)
+    out = run_backward(ssd, inp, g, 64)
+    assert out["dx"].shape[1] == 0
+    assert torch.equal(out["dinit"].cpu(), g["dfinal"])
+    assert torch.count_nonzero(out["dA"]).item() == 0 and torch.count_nonzero(out["dD"]).item() == 0
+
+
+def test_backward_many_heads_per_group(ssd):
+    """16 heads share one group: dB and dC sum 16 head contributions."""
+    w = small("bf16", batch=2, seqlen=700, nheads=16, headdim=64, dstate=128, ngroups=1, chunk=256, seed=11)
+    inp = si.make_forward_inputs(w)
+    g = si.make_output_grads(w)
+    check_bwd(run_backward(ssd, inp, g, 256), oracle_backward(inp, g), "bf16", inp, g)
+
+
+def test_backward_long_carried_f32(ssd):
+    """Long-memory and fast-decay heads (split dt), nonzero init, 32 chunks."""
+    w = small("f32", batch=1, seqlen=8192, nheads=4, headdim=64, dstate=128, ngroups=1, chunk=256,
+              init_mode="normal", dt_mode="split", seed=13)
+    inp = si.make_forward_inputs(w)
+    g = si.make_output_grads(w)
+    check_bwd(run_backward(ssd, inp, g, 256), oracle_backward(inp, g), "f32", inp, g)
+
+
+def test_backward_full_size_2p7b_layer(ssd):
+    """The 2.7B-layer shape (b=4, L=4096, H=80, P=64, N=128, chunk 256, bf16)
+    at full size, in the configuration the benchmark times.  Batch rows are
+    independent, so every gradient of row 0 except the batch-summed dA and dD
+    is checked exactly against the oracle run on row 0 alone."""
+    w = si.WORKLOADS[2]
+    inp = si.make_forward_inputs(w)
+    g = si.make_output_grads(w)
+    out = run_backward(ssd, inp, g, w.chunk)
+    for k in ("dx", "ddt", "dB", "dC", "dinit"):
+        assert torch.isfinite(out[k].float()).all(), k
+    row = {k: (v[:1] if isinstance(v, torch.Tensor) and k not in ("A", "D") else v) for k, v in inp.items()}
+    g0 = {"dy": g["dy"][:1], "dfinal": g["dfinal"][:1]}
+    ref = oracle_backward(row, g0)
+    out0 = {k: out[k][:1] for k in ("dx", "ddt", "dB", "dC", "dinit")}
+    e = {"dx": worst_rel(f64(out0["dx"]), ref["dx"], "y"),
+         "ddt": worst_rel(f64(out0["ddt"])[..., None], ref["ddt"][..., None], "y"),
+         "dB": worst_rel(f64(out0["dB"]), ref["dB"], "y"),
+         "dC": worst_rel(f64(out0["dC"]), ref["dC"], "y"),
+         "dinit": worst_rel(f64(out0["dinit"]), ref["dinit"], "state")}
+    print("full-size backward errors (row 0):", {k: f"{v:.2e}" for k, v in e.items()}, flush=True)
+    assert max(e.values()) < BWD_TOL["bf16"], e
+
+
+def test_backward_long_carried_bf16(ssd):
+    """As the float32 case, with bfloat16 inputs (fast-decay heads make the
+    per-step decay gradients small against the terms they are built from)."""
+    w = small("bf16", batch=1, seqlen=4096, nheads=4, headdim=64, dstate=128, ngroups=1, chunk=256,
+              init_mode="normal", dt_mode="split", seed=17)
+    inp = si.make_forward_inputs(w)
+    g = si.make_output_grads(w)
+    check_bwd(run_backward(ssd, inp, g, 256), oracle_backward(inp, g), "bf16", inp, g)

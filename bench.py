@@ -9,8 +9,10 @@ timed step a 512 MiB buffer is overwritten so the 256 MB Infinity Cache does
 not hold the inputs; HIP events on the launch stream bracket the forward call
 alone.  Prints one JSON line.
 
-Other modes: ``--workload decode`` (512 single-token steps on a
-[256, 80, 64, 128] float32 state) and ``--workload copy`` (a plain
+Other modes: ``--workload backward`` (the gradient of the same layer at the
+same shape: ``ssd_backward`` with dy drawn N(0, 1), D present, no initial or
+final state, as in training), ``--workload decode`` (512 single-token steps
+on a [256, 80, 64, 128] float32 state) and ``--workload copy`` (a plain
 device-to-device copy used to calibrate hardware byte counters).
 """
 from __future__ import annotations
@@ -35,7 +37,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["forward", "decode", "copy"], default="forward")
+    ap.add_argument("--workload", choices=["forward", "backward", "decode", "copy"], default="forward")
     ap.add_argument("--path", choices=["fused", "staged"], default="fused")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
@@ -101,6 +103,183 @@ def kernel_flops(w) -> dict:
     tri = sum(min(Q, L - c * Q) * (min(Q, L - c * Q) + 1) // 2 for c in range((L + Q - 1) // Q))
     return {"chunk_cb": 2 * N * tri * b * G, "chunk_state": 2 * L * N * P * b * H,
             "chunk_scan": (2 * P * tri + 2 * L * N * P) * b * H}
+
+
+def backward_bytes(w) -> int:
+    """Compulsory bytes of one gradient call without initial or final state:
+    read x, dy, dt, B, C, A, D once, write dx, ddt, dB, dC, dA, dD once."""
+    e = 2 if w.dtype == "bf16" else 4
+    b, L, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    return 3 * b * L * H * P * e + 2 * b * L * H * e + 4 * b * L * G * N * e + 4 * H * 4
+
+
+def backward_flops(w) -> int:
+    """Matrix flops of the gradient as computed here (lower-triangular blocks):
+    per (b, h) the transposed intra-chunk product and the state term of dx,
+    the masked dy x^T of dCB, the state terms of dC and dB, the forward and
+    reverse chunk states, and the forward output again for the decay
+    gradients; per (b, g) C B^T and the two dCB products."""
+    b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    tri = sum(min(Q, L - c * Q) * (min(Q, L - c * Q) + 1) // 2 for c in range((L + Q - 1) // Q))
+    per_bh = 3 * 2 * P * tri + 6 * 2 * L * N * P
+    per_bg = 3 * 2 * N * tri
+    return b * H * per_bh + b * G * per_bg
+
+
+def backward_kernel_bytes(w) -> dict:
+    """Algorithmic bytes of each launch of the gradient (its own inputs and
+    outputs once; workspace intermediates count where a kernel reads or
+    writes them)."""
+    e = 2 if w.dtype == "bf16" else 4
+    b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    nc = (L + Q - 1) // Q
+    T16 = Q // 16
+    cs = b * H * nc * Q * 4
+    cb = b * nc * G * (T16 * (T16 + 1) // 2) * 256 * e
+    S = b * nc * H * P * N * 4
+    x = b * L * H * P * e
+    BC = b * L * G * N * e
+    dtb = b * L * H * e
+    dcb = b * nc * G * (T16 * (T16 + 1) // 2) * 256 * 4
+    gst = b * L * G * N * 4
+    part = b * nc * H * 8
+    return {
+        "chunk_cumsum": dtb + H * 4 + cs,
+        "chunk_cumsum64": dtb + H * 4 + 2 * cs if w.dtype == "f32" else 0,
+        "chunk_cb": 2 * BC + 2 * cb,
+        "chunk_state": x + BC + cs + S,
+        "state_passing": 2 * S + b * H * nc * 4,
+        "chunk_state_rev": x + BC + cs + S,
+        "state_passing_rev": 2 * S + b * H * nc * 4,
+        "chunk_bwd": 3 * x + 2 * dtb + 2 * BC + 2 * cb + cs + 2 * S + 2 * H * 4 + part,
+        "group_bwd": 2 * x + cs + 2 * S + 2 * dcb + 2 * gst,
+        "group_combine": 2 * BC + 2 * dcb + 2 * gst + 2 * BC,
+        "head_reduce": part + 2 * H * 4,
+    }
+
+
+def run_backward_bench(args):
+    import ctypes
+
+    import torch
+
+    import selective_state_space_04_amd as ssd
+    import ssd_inputs as si
+
+    w = si.WORKLOADS[2]
+    dev = torch.device("cuda:0")
+    inp = si.make_forward_inputs(w)
+    grads = si.make_output_grads(w, with_final=False)
+    g = lambda t: None if t is None else t.to(dev)
+    x, dt, A, B, C, D, init = (g(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "init"))
+    dy = g(grads["dy"])
+    dims = ssd.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk,
+                         ssd.BF16 if w.dtype == "bf16" else ssd.F32)
+    ws = torch.empty(max(ssd.backward_workspace_bytes(dims), 1), dtype=torch.uint8, device=dev)
+    out = {"dx": torch.empty_like(x), "ddt": torch.empty_like(dt), "dB": torch.empty_like(B),
+           "dC": torch.empty_like(C), "dA": torch.empty_like(A), "dD": torch.empty_like(D)}
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def step():
+        ssd.backward(x, dt, A, B, C, dy, D=D, init_state=init, chunk=w.chunk, out=out, workspace=ws,
+                     want_dinit=False)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        if flush is not None:
+            flush.fill_(k & 0xFF)
+        starts[k].record()
+        step()
+        ends[k].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(b_) for a, b_ in zip(starts, ends)]
+    ms_per_step = statistics.mean(ms)
+    tokens = w.batch * w.seqlen
+    t_hbm = backward_bytes(w) / (HBM_PEAK_GBS * 1e3)
+    t_mfma = backward_flops(w) / (BF16_PEAK_TFLOPS * 1e6)
+    t_roof_us = max(t_hbm, t_mfma)
+    result = {
+        "metric": "SSD bwd tokens/s at H=80,P=64,N=128,L=4096; % of MFMA/HBM roofline",
+        "value": tokens / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded; distributions of the workload)",
+        "config": {"workload": "2.7B-layer-shaped SSD backward", "batch": w.batch, "seqlen": w.seqlen,
+                   "nheads": w.nheads, "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
+                   "chunk": w.chunk, "inputs": "bf16", "accumulate": "fp32",
+                   "grads": "dx, ddt, dA, dB, dC, dD (no initial or final state)",
+                   "mall_flushed": flush is not None},
+        "backward_roofline": {"bound": "hbm" if t_hbm >= t_mfma else "mfma", "t_roof_us": t_roof_us,
+                              "t_hbm_us": t_hbm, "t_mfma_us": t_mfma,
+                              "frac": t_roof_us / (ms_per_step * 1e3), "alg_bytes": backward_bytes(w),
+                              "alg_flops": backward_flops(w)},
+        "ms_min": min(ms), "ms_median": statistics.median(ms), "wall_s": wall,
+    }
+    if not args.no_kernel_timing:
+        # per-launch durations: hipEvents recorded by the library between its launches
+        hip = ctypes.CDLL("libamdhip64.so")
+        dp = ctypes.byref(dims)
+        n = ssd.lib.ssd_backward_launch_count(dp)
+        names = [ssd.lib.ssd_backward_launch_name(dp, i).decode() for i in range(n)]
+        evs = (ctypes.c_void_p * (n + 1))()
+        for i in range(n + 1):
+            if hip.hipEventCreate(ctypes.byref(evs, i * ctypes.sizeof(ctypes.c_void_p))) != 0:
+                raise RuntimeError("hipEventCreate failed")
+        p = ssd._p
+        times = {nm: [] for nm in names}
+        reps = max(args.steps, 5)
+        for rep in range(reps + 2):
+            if flush is not None:
+                flush.fill_(rep & 0xFF)
+            st = ssd.lib.ssd_backward_timed(dp, p(x), p(dt), p(A), p(B), p(C), p(D), p(init), p(dy), None,
+                                            p(out["dx"]), p(out["ddt"]), p(out["dA"]), p(out["dB"]),
+                                            p(out["dC"]), p(out["dD"]), None, p(ws), ws.numel(), ssd._stream(),
+                                            evs, n + 1)
+            if st != 0:
+                raise RuntimeError(f"ssd_backward_timed: status {st}")
+            torch.cuda.synchronize()
+            if rep >= 2:
+                for i, nm in enumerate(names):
+                    f = ctypes.c_float()
+                    hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(evs[i]), ctypes.c_void_p(evs[i + 1]))
+                    times[nm].append(f.value * 1e3)
+        for i in range(n + 1):
+            hip.hipEventDestroy(ctypes.c_void_p(evs[i]))
+        avg = {nm: statistics.mean(v) for nm, v in times.items()}
+        dom = max(avg, key=avg.get)
+        kb = backward_kernel_bytes(w)[dom]
+        achieved = kb / (avg[dom] * 1e-6) / 1e9
+        result["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                              "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                              "traffic": measured_traffic("bwd_" + dom), "alg_bytes_per_launch": kb,
+                              "avg_launch_us": avg[dom]}
+        result["kernels_us"] = avg
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_backward(w, inp, grads)
+    return result
+
+
+def cpu_baseline_backward(w, inp, grads):
+    """The float64 adjoint oracle on a bounded sample: the first two batch rows
+    at full length and all heads (half the workload's (batch, head)
+    sequences; every sequence costs the same, so tokens/s is that of the
+    sample)."""
+    import oracle
+
+    nb = 2
+    f = oracle._f64
+    t0 = time.perf_counter()
+    oracle.backward(f(inp["x"][:nb]), f(inp["dt"][:nb]), f(inp["A"]), f(inp["B"][:nb]), f(inp["C"][:nb]),
+                    f(inp["D"]), None, f(grads["dy"][:nb]), None)
+    t = time.perf_counter() - t0
+    return {"value": nb * w.seqlen / t, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"batch rows 0-{nb - 1} of {w.batch} at full length, all {w.nheads} heads, float64 "
+            f"reverse-mode recurrence, {t:.2f} s"}
 
 
 def run_forward_bench(args):
@@ -346,6 +525,8 @@ def main():
         sys.exit(2)
     if args.workload == "forward":
         res = run_forward_bench(args)
+    elif args.workload == "backward":
+        res = run_backward_bench(args)
     elif args.workload == "decode":
         res = run_decode_bench(args)
     else:

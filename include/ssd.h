@@ -186,6 +186,26 @@ ssd_status ssd_backward(const ssd_dims *dims, const void *x, const void *dt, con
                         void *dB, void *dC, float *dD, float *dinit_state, void *workspace,
                         size_t workspace_bytes, void *stream);
 
+/* Timing hook for ssd_backward: the same call and result, and in addition
+ * hipEventRecord(events[0]) on `stream` before the first kernel launch and
+ * hipEventRecord(events[i + 1]) after launch i, so the caller can time each
+ * launch with hipEventElapsedTime.  events: nevents hipEvent_t handles
+ * created by the caller (not NULL, not owned); nevents must be
+ * ssd_backward_launch_count(dims) + 1 (else SSD_ERR_SHAPE).
+ * ssd_backward_launch_count: number of launch slots for these dims (0 for
+ * invalid dims); ssd_backward_launch_name(dims, i): the kernel name of slot i
+ * (static storage; NULL out of range).  A slot that launches nothing for
+ * these dims (the float64 decay prefix, which only float32 inputs use) has
+ * an empty interval. */
+int ssd_backward_launch_count(const ssd_dims *dims);
+const char *ssd_backward_launch_name(const ssd_dims *dims, int i);
+ssd_status ssd_backward_timed(const ssd_dims *dims, const void *x, const void *dt, const float *A,
+                              const void *B, const void *C, const float *D,
+                              const float *init_state, const void *dy, const float *dfinal_state,
+                              void *dx, void *ddt, float *dA, void *dB, void *dC, float *dD,
+                              float *dinit_state, void *workspace, size_t workspace_bytes,
+                              void *stream, void *const *events, int nevents);
+
 /* ------------------------------------------------------------------------
  * The steps of the chunked algorithm, one entry point each.  nc =
  * ceil(seqlen / chunk); chunk c covers steps [c*chunk, min((c+1)*chunk, L)).

@@ -61,6 +61,9 @@ _SIGS = {
     "ssd_backward_workspace_bytes": (ctypes.c_size_t, [_dp]),
     "ssd_backward": (ctypes.c_int, [_dp] + [_vp] * 17 + [ctypes.c_size_t, _vp]),
     "ssd_validate_backward": (ctypes.c_int, [_dp] + [_vp] * 17 + [ctypes.c_size_t]),
+    "ssd_backward_launch_count": (ctypes.c_int, [_dp]),
+    "ssd_backward_launch_name": (ctypes.c_char_p, [_dp, ctypes.c_int]),
+    "ssd_backward_timed": (ctypes.c_int, [_dp] + [_vp] * 17 + [ctypes.c_size_t, _vp, _vp, ctypes.c_int]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)

@@ -298,16 +298,51 @@ ssd_status run_staged(const ssd::Dims &d, const void *x, const void *dt, const f
     return SSD_OK;
 }
 
+// Names of the kernel launches the gradient makes, in order.
+const char *const kBwdNames[] = {"chunk_cumsum",      "chunk_cumsum64", "chunk_cb",
+                                 "chunk_state",       "state_passing",  "chunk_state_rev",
+                                 "state_passing_rev", "chunk_bwd",      "group_bwd",
+                                 "group_combine",     "head_reduce"};
+const char *const kBwdEmptyNames[] = {"copy_state", "head_reduce"};
+
+int bwd_launches(const ssd::Dims &d, const char *const **names) {
+    if (d.b == 0 || d.nc == 0) {
+        if (names) *names = kBwdEmptyNames;
+        return 2;
+    }
+    if (names) *names = kBwdNames;
+    return 11;  // for bfloat16 inputs the chunk_cumsum64 slot launches nothing
+}
+
+// Records caller-supplied events around the launches (no-op without events).
+struct Marks {
+    void *const *ev;
+    int n, k;
+    hipStream_t st;
+    hipError_t mark() {
+        if (!ev || k >= n) return hipSuccess;
+        return hipEventRecord((hipEvent_t)ev[k++], st);
+    }
+};
+
 // The gradient: forward states recomputed, state gradients passed backwards,
 // then the per-chunk and per-group gradient kernels.
 ssd_status run_backward(const ssd::Dims &d, const void *x, const void *dt, const float *A,
                         const void *B, const void *C, const float *D, const float *init,
                         const void *dy, const float *dfinal, void *dx, void *ddt, float *dA,
-                        void *dB, void *dC, float *dD, float *dinit, void *ws, hipStream_t st) {
+                        void *dB, void *dC, float *dD, float *dinit, void *ws, hipStream_t st,
+                        Marks mk) {
     hipError_t e;
+#define SSD_STEP(call)                                                                            \
+    do {                                                                                          \
+        if ((e = (call)) != hipSuccess) return hip_status(e);                                     \
+        if ((e = mk.mark()) != hipSuccess) return hip_status(e);                                  \
+    } while (0)
+    if ((e = mk.mark()) != hipSuccess) return hip_status(e);
     if (d.b == 0 || d.nc == 0) {
-        if ((e = ssd::launch_zero_state(d, dfinal, dinit, st)) != hipSuccess) return hip_status(e);
-        return hip_status(ssd::launch_head_reduce(d, nullptr, dA, dD, st));
+        SSD_STEP(ssd::launch_zero_state(d, dfinal, dinit, st));
+        SSD_STEP(ssd::launch_head_reduce(d, nullptr, dA, dD, st));
+        return SSD_OK;
     }
     const BwdLayout w = bwd_layout(d);
     char *base = (char *)ws;
@@ -317,25 +352,20 @@ ssd_status run_backward(const ssd::Dims &d, const void *x, const void *dt, const
     float *part = (float *)(base + w.part);
     double *cs64 = d.dtype == SSD_F32 ? (double *)(base + w.cs64) : nullptr;
     void *cb = base + w.cb, *cbT = base + w.cbT;
-    if ((e = ssd::launch_chunk_cumsum(d, dt, A, cs, st)) != hipSuccess) return hip_status(e);
-    if (cs64 && (e = ssd::launch_chunk_cumsum64(d, dt, A, cs64, st)) != hipSuccess)
-        return hip_status(e);
-    if ((e = ssd::launch_chunk_cb(d, B, C, cb, cbT, st)) != hipSuccess) return hip_status(e);
-    if ((e = ssd::launch_chunk_state(d, x, B, cs, Hs, false, st)) != hipSuccess) return hip_status(e);
-    if ((e = ssd::launch_state_passing(d, Hs, cs, init, nullptr, st)) != hipSuccess)
-        return hip_status(e);
-    if ((e = ssd::launch_chunk_state(d, dy, C, cs, Rs, true, st)) != hipSuccess) return hip_status(e);
-    if ((e = ssd::launch_state_passing_rev(d, Rs, cs, dfinal, dinit, st)) != hipSuccess)
-        return hip_status(e);
-    if ((e = ssd::launch_chunk_bwd(d, x, dy, dt, A, B, C, cb, cbT, cs, cs64, Hs, Rs, D, dx, ddt,
-                                   part, st)) != hipSuccess)
-        return hip_status(e);
-    if ((e = ssd::launch_group_bwd(d, x, dy, cs, cs64, Hs, Rs, dcb, dcbT, dCs, dBs, st)) !=
-        hipSuccess)
-        return hip_status(e);
-    if ((e = ssd::launch_group_combine(d, B, C, dcb, dcbT, dCs, dBs, dB, dC, st)) != hipSuccess)
-        return hip_status(e);
-    return hip_status(ssd::launch_head_reduce(d, part, dA, dD, st));
+    SSD_STEP(ssd::launch_chunk_cumsum(d, dt, A, cs, st));
+    SSD_STEP(cs64 ? ssd::launch_chunk_cumsum64(d, dt, A, cs64, st) : hipSuccess);
+    SSD_STEP(ssd::launch_chunk_cb(d, B, C, cb, cbT, st));
+    SSD_STEP(ssd::launch_chunk_state(d, x, B, cs, Hs, false, st));
+    SSD_STEP(ssd::launch_state_passing(d, Hs, cs, init, nullptr, st));
+    SSD_STEP(ssd::launch_chunk_state(d, dy, C, cs, Rs, true, st));
+    SSD_STEP(ssd::launch_state_passing_rev(d, Rs, cs, dfinal, dinit, st));
+    SSD_STEP(ssd::launch_chunk_bwd(d, x, dy, dt, A, B, C, cb, cbT, cs, cs64, Hs, Rs, D, dx, ddt,
+                                   part, st));
+    SSD_STEP(ssd::launch_group_bwd(d, x, dy, cs, cs64, Hs, Rs, dcb, dcbT, dCs, dBs, st));
+    SSD_STEP(ssd::launch_group_combine(d, B, C, dcb, dcbT, dCs, dBs, dB, dC, st));
+    SSD_STEP(ssd::launch_head_reduce(d, part, dA, dD, st));
+#undef SSD_STEP
+    return SSD_OK;
 }
 
 ssd_status run_fused_prep(const ssd::Dims &d, const void *B, const void *C, void *ws,
@@ -488,7 +518,42 @@ ssd_status ssd_backward(const ssd_dims *dims, const void *x, const void *dt, con
                                       &d);
     if (st != SSD_OK) return st;
     return run_backward(d, x, dt, A, B, C, D, init_state, dy, dfinal_state, dx, ddt, dA, dB, dC,
-                        dD, dinit_state, workspace, (hipStream_t)stream);
+                        dD, dinit_state, workspace, (hipStream_t)stream,
+                        Marks{nullptr, 0, 0, (hipStream_t)stream});
+}
+
+int ssd_backward_launch_count(const ssd_dims *dims) {
+    ssd::Dims d;
+    if (check_dims(dims, false, &d) != SSD_OK) return 0;
+    return bwd_launches(d, nullptr);
+}
+
+const char *ssd_backward_launch_name(const ssd_dims *dims, int i) {
+    ssd::Dims d;
+    if (check_dims(dims, false, &d) != SSD_OK) return nullptr;
+    const char *const *names = nullptr;
+    const int n = bwd_launches(d, &names);
+    return (i >= 0 && i < n) ? names[i] : nullptr;
+}
+
+ssd_status ssd_backward_timed(const ssd_dims *dims, const void *x, const void *dt, const float *A,
+                              const void *B, const void *C, const float *D,
+                              const float *init_state, const void *dy, const float *dfinal_state,
+                              void *dx, void *ddt, float *dA, void *dB, void *dC, float *dD,
+                              float *dinit_state, void *workspace, size_t workspace_bytes,
+                              void *stream, void *const *events, int nevents) {
+    ssd::Dims d;
+    ssd_status st = validate_backward(dims, x, dt, A, B, C, D, init_state, dy, dfinal_state, dx,
+                                      ddt, dA, dB, dC, dD, dinit_state, workspace, workspace_bytes,
+                                      &d);
+    if (st != SSD_OK) return st;
+    if (!events) return SSD_ERR_NULL;
+    if (nevents != bwd_launches(d, nullptr) + 1) return SSD_ERR_SHAPE;
+    for (int i = 0; i < nevents; ++i)
+        if (!events[i]) return SSD_ERR_NULL;
+    return run_backward(d, x, dt, A, B, C, D, init_state, dy, dfinal_state, dx, ddt, dA, dB, dC,
+                        dD, dinit_state, workspace, (hipStream_t)stream,
+                        Marks{events, nevents, 0, (hipStream_t)stream});
 }
 
 ssd_status ssd_decode_step(const ssd_dims *dims, float *state, const void *x, const void *dt,

@@ -31,10 +31,16 @@
 // first by the step kernels of ssd_kernels.hip and k_state_passing_rev):
 //   k_chunk_bwd     per (b, c, h): recomputes y'_i, computes dx and the
 //                   decay gradients of the chunk; per-chunk partial sums of
-//                   dA_h and dD_h.
+//                   dA_h and dD_h (k_chunk_bwd_pf: the bf16 version with each
+//                   tile's operands loaded one tile ahead).
 //   k_group_bwd     per (b, c, g, 64 rows): loops over the heads of the group
 //                   and sums exp(cs_i - cs_j)(dy_i.x_j) (dCB, both
-//                   orientations) and the state terms of dC and dB.
+//                   orientations) and the state terms of dC and dB (float32
+//                   inputs, and bf16 shapes with N = 256 or P N > 8192).
+//   k_group_dcb,    the same sums for the other bf16 shapes, split so each
+//   k_group_state   kernel's accumulators stay in registers at several waves
+//                   per SIMD: dCB per 64 x 64 block pair, the state terms per
+//                   64 rows with the state staged in LDS.
 //   k_group_combine per (b, c, g, 16 rows): dC = dC_state + dCB B,
 //                   dB = dB_state + dCB^T C, rounded to the input dtype.
 //   k_head_reduce   per h: sums the per-chunk partials of dA_h and dD_h.
@@ -512,6 +518,296 @@ __global__ __launch_bounds__(256) void k_chunk_bwd(
 }
 
 // ---------------------------------------------------------------------------
+// bfloat16 version of k_chunk_bwd with each tile's global operands gathered
+// into one register set and loaded one tile ahead: a wave issues every load
+// of its next tile (the C or B row, the C B^T row segments, the dy and x
+// rows it dots with) before it computes the current one, so the loads of a
+// tile wait once instead of one after another inside the loops.  Same
+// phases, results and outputs as k_chunk_bwd.
+// ---------------------------------------------------------------------------
+template <int P, int N>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_chunk_bwd_pf(
+    const bf16 *__restrict__ x, const bf16 *__restrict__ dy, const bf16 *__restrict__ dt,
+    const float *__restrict__ A, const bf16 *__restrict__ B, const bf16 *__restrict__ C,
+    const bf16 *__restrict__ cb, const bf16 *__restrict__ cbT, const float *__restrict__ cs,
+    const float *__restrict__ Hs, const float *__restrict__ Rs, const float *__restrict__ D,
+    bf16 *__restrict__ dx, bf16 *__restrict__ ddt, float *__restrict__ part, int64_t L, int H,
+    int G, int Q, int nc) {
+    constexpr int PT = P / 16, NCF = (N + 31) / 32, NSEG = 8;
+    const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = (int)(wid % H);
+    const int64_t bc = wid / H;
+    const int c = (int)(bc % nc);
+    const int64_t b = bc / nc;
+    const int g = h / (H / G);
+    const int64_t s = (int64_t)c * Q;
+    const int q = (int)min<int64_t>(Q, L - s);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, grp = lane >> 4;
+    const int Qp = (Q + 31) & ~31;
+
+    __shared__ float cs_s[256], yy_s[256], xdx_s[256], red_s[4][3];
+    const float *csc = cs + (((int64_t)b * H + h) * nc + c) * Q;
+    for (int j = threadIdx.x; j < 256; j += 256) {
+        cs_s[j] = csc[min(j, Q - 1)];
+        yy_s[j] = 0.f;
+        xdx_s[j] = 0.f;
+    }
+    const int64_t row0 = (b * L + s) * H + h;
+    const bf16 *Cb = C + ((b * L + s) * G + g) * N;
+    const bf16 *Bb = B + ((b * L + s) * G + g) * N;
+    const int64_t cboff = (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
+    const bf16 *cbc = cb + cboff, *cbTc = cbT + cboff;
+    const int64_t soff = (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+    const float *hp = Hs + soff, *rp = Rs + soff;
+    const float Dh = D ? D[h] : 0.f;
+
+    constexpr int XLD = 256 + 8, HLD = N + 8;
+    __shared__ bf16 ops_s[P * XLD];
+    __shared__ bf16 st_s[P * HLD];
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+    const u32x2 z2 = {0u, 0u};
+    const int T16 = (q + 15) / 16;
+    auto tile_of = [&](int round) { return 4 * round + ((round & 1) ? 3 - wave : wave); };
+    const int nrounds = (T16 + 3) / 4;
+
+    // operands of one tile: the lane's row of C (phase Y) or B (phase X), its C B^T
+    // segments, and 4 channels of the rows it dots with (dy; in phase X also x)
+    struct Ops {
+        u32x4 vr[NCF];
+        u32x4 gs[NSEG];
+        u32x2 d4[PT], x4[PT];
+    };
+    auto state_mma = [&](f32x4 *acc, const Ops &o) {
+#pragma unroll
+        for (int kc = 0; kc < NCF; ++kc) {
+            const int kk = kc * 32 + grp * 8;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                const u32x4 av = kk < N ? *(const u32x4 *)(st_s + (pt * 16 + r) * HLD + kk) : z4;
+                acc[pt] = mfma_bf16(as_bf16x8(av), as_bf16x8(o.vr[kc]), acc[pt]);
+            }
+        }
+    };
+
+    // ---------------- phase Y ----------------
+    auto load_y = [&](int I, Ops &o) {
+        const int il = I * 16 + r;
+        const bool vi = il < q;
+        const bf16 *crow = Cb + (int64_t)il * G * N;
+#pragma unroll
+        for (int kc = 0; kc < NCF; ++kc) {
+            const int kk = kc * 32 + grp * 8;
+            o.vr[kc] = (vi && kk < N) ? *(const u32x4 *)(crow + kk) : z4;
+        }
+        const bf16 *grow = cbc + (int64_t)il * Q;
+#pragma unroll
+        for (int sg = 0; sg < NSEG; ++sg) {
+            const int jl = sg * 32 + grp * 8;
+            o.gs[sg] = (sg * 32 <= I * 16 + 15 && jl < il) ? *(const u32x4 *)(grow + jl) : z4;
+        }
+        const bf16 *dyr = dy + (row0 + (int64_t)il * H) * P;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) o.d4[pt] = vi ? *(const u32x2 *)(dyr + pt * 16 + 4 * grp) : z2;
+    };
+    stage_transposed_bf16<false>(x + row0 * P, (int64_t)H * P, Qp, P, q, ops_s, XLD, nullptr);
+    stage_state_bf16<P, N>(hp, st_s, HLD);
+    Ops cur, nxt;
+    if (nrounds > 0 && tile_of(0) < T16) load_y(tile_of(0), cur);
+    __syncthreads();
+    for (int round = 0; round < nrounds; ++round) {
+        const int I = tile_of(round);
+        const bool have = I < T16;
+        const int In = tile_of(round + 1);
+        if (round + 1 < nrounds && In < T16) load_y(In, nxt);
+        if (have) {
+            const int il = I * 16 + r;
+            const bool vi = il < q;
+            const float csi = cs_s[il];
+            f32x4 acc[PT];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            state_mma(acc, cur);
+            const float ei = __expf(csi);
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) acc[pt] *= ei;
+#pragma unroll
+            for (int sg = 0; sg < NSEG; ++sg) {
+                if (sg * 32 <= I * 16 + 15) {
+                    const int jl = sg * 32 + grp * 8;
+                    const bf16x8 gv = as_bf16x8(cur.gs[sg]);
+                    bf16x8 bm;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = jl + e;
+                        bm[e] = (bf16)((j < il) ? __expf(csi - cs_s[j]) * (float)gv[e] : 0.f);
+                    }
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) {
+                        const bf16x8 ax = *(const bf16x8 *)(ops_s + (pt * 16 + r) * XLD + jl);
+                        acc[pt] = mfma_bf16(ax, bm, acc[pt]);
+                    }
+                }
+            }
+            float yy = 0.f;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) yy += dot4(acc[pt], load4((const bf16 *)&cur.d4[pt]));
+            yy = sum_groups(yy);
+            if (grp == 0 && vi) yy_s[il] = yy;
+        }
+        cur = nxt;
+    }
+    __syncthreads();
+
+    // ---------------- phase X ----------------
+    auto load_x = [&](int J, Ops &o) {
+        const int jl = J * 16 + r;
+        const bool vj = jl < q;
+        const bf16 *brow = Bb + (int64_t)jl * G * N;
+#pragma unroll
+        for (int kc = 0; kc < NCF; ++kc) {
+            const int kk = kc * 32 + grp * 8;
+            o.vr[kc] = (vj && kk < N) ? *(const u32x4 *)(brow + kk) : z4;
+        }
+        const bf16 *gcol = cbTc + (int64_t)jl * Q;
+        const int ilo = (J * 16) & ~31;
+#pragma unroll
+        for (int sg = 0; sg < NSEG; ++sg) {
+            const int i0 = sg * 32, il = i0 + grp * 8;
+            o.gs[sg] = (i0 >= ilo && i0 < q && il + 7 > jl && il < q) ? *(const u32x4 *)(gcol + il) : z4;
+        }
+        const bf16 *dyr = dy + (row0 + (int64_t)jl * H) * P;
+        const bf16 *xr = x + (row0 + (int64_t)jl * H) * P;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            o.d4[pt] = vj ? *(const u32x2 *)(dyr + pt * 16 + 4 * grp) : z2;
+            o.x4[pt] = vj ? *(const u32x2 *)(xr + pt * 16 + 4 * grp) : z2;
+        }
+    };
+    stage_transposed_bf16<false>(dy + row0 * P, (int64_t)H * P, Qp, P, q, ops_s, XLD, nullptr);
+    stage_state_bf16<P, N>(rp, st_s, HLD);
+    float rh = 0.f;  // <R_c, H_c>
+    for (int idx = threadIdx.x; idx < P * N / 4; idx += 256)
+        rh += dot4(*(const f32x4 *)(rp + 4 * idx), *(const f32x4 *)(hp + 4 * idx));
+    if (nrounds > 0 && tile_of(0) < T16) load_x(tile_of(0), cur);
+    __syncthreads();
+
+    const float csE = cs_s[q - 1];
+    float vsum = 0.f, dDp = 0.f;
+    for (int round = 0; round < nrounds; ++round) {
+        const int J = tile_of(round);
+        const bool have = J < T16;
+        const int Jn = tile_of(round + 1);
+        if (round + 1 < nrounds && Jn < T16) load_x(Jn, nxt);
+        if (have) {
+            const int jl = J * 16 + r;
+            const bool vj = jl < q;
+            const float csj = cs_s[jl];
+            f32x4 acc[PT];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            state_mma(acc, cur);
+            const float wj = __expf(csE - csj);
+            f32x4 xv[PT];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) {
+                acc[pt] *= wj;
+                xv[pt] = load4((const bf16 *)&cur.x4[pt]);
+                vsum += dot4(acc[pt], xv[pt]);
+            }
+            const int ilo = (J * 16) & ~31;
+#pragma unroll
+            for (int sg = 0; sg < NSEG; ++sg) {
+                const int i0 = sg * 32;
+                if (i0 >= ilo && i0 < q) {
+                    const int il = i0 + grp * 8;
+                    const bf16x8 gv = as_bf16x8(cur.gs[sg]);
+                    bf16x8 bm;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int i = il + e;
+                        bm[e] = (bf16)((i > jl && i < q) ? __expf(cs_s[i] - csj) * (float)gv[e] : 0.f);
+                    }
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) {
+                        const bf16x8 ad = *(const bf16x8 *)(ops_s + (pt * 16 + r) * XLD + il);
+                        acc[pt] = mfma_bf16(ad, bm, acc[pt]);
+                    }
+                }
+            }
+            float xd = 0.f;
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) xd += dot4(acc[pt], xv[pt]);
+            xd = sum_groups(xd);
+            if (grp == 0 && vj) xdx_s[jl] = xd;
+            if (vj) {
+                bf16 *dxr = dx + (row0 + (int64_t)jl * H) * P;
+                const float diag = (float)cbc[(int64_t)jl * Q + jl] + Dh;  // M_jj + D
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    const f32x4 d4 = load4((const bf16 *)&cur.d4[pt]);
+                    dDp += dot4(d4, xv[pt]);
+                    store4(dxr + pt * 16 + 4 * grp, acc[pt] + diag * d4);
+                }
+            }
+        }
+        cur = nxt;
+    }
+    {
+        const float v0 = wave_sum(vsum), v1 = wave_sum(rh), v2 = wave_sum(dDp);
+        if (lane == 0) {
+            red_s[wave][0] = v0;
+            red_s[wave][1] = v1;
+            red_s[wave][2] = v2;
+        }
+    }
+    __syncthreads();
+
+    // ---------------- decay gradients ----------------
+    if (wave == 0) {
+        float tv[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) tv[k] = red_s[0][k] + red_s[1][k] + red_s[2][k] + red_s[3][k];
+        const float Tend = __expf(csE) * tv[1] + tv[0];
+        float d[4], suf[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int k = 4 * lane + e;
+            d[e] = k < q ? yy_s[k] - xdx_s[k] + (k == q - 1 ? Tend : 0.f) : 0.f;
+        }
+        suf[3] = d[3];
+        suf[2] = d[2] + suf[3];
+        suf[1] = d[1] + suf[2];
+        suf[0] = d[0] + suf[1];
+        float tot = suf[0];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float o = __shfl_down(tot, off, 64);
+            if (lane + off < 64) tot += o;
+        }
+        const float after = tot - suf[0];
+        const float Ah = A[h];
+        float dAp = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int k = 4 * lane + e;
+            if (k < q) {
+                const float dda = suf[e] + after;
+                const int64_t o = (b * L + s + k) * H + h;
+                ddt[o] = (bf16)(Ah * dda);
+                dAp += (float)dt[o] * dda;
+            }
+        }
+        dAp = wave_sum(dAp);
+        if (lane == 0) {
+            float *pp = part + ((((int64_t)b * nc + c) * H + h) * 2);
+            pp[0] = dAp;
+            pp[1] = tv[2];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Per (b, c, g, 64-row tile): sums over the heads of group g of
 //   dCB[i][j] = exp(cs_i - cs_j) (dy_i . x_j)                  (j <= i)
 //   dCs[i][n] = exp(cs_i) sum_p dy_i[p] H_c[p][n]
@@ -637,6 +933,234 @@ __global__ __launch_bounds__(256) void k_group_bwd(
                 dCs[o] = adc[t][e];
                 dBs[o] = adb[t][e];
             }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bfloat16: dCB[i][j] = sum_h exp(cs_i - cs_j) (dy_i . x_j) alone, one
+// workgroup per (b, c, g, 64 x 64 block on or below the diagonal); wave
+// (wr, wc) owns the 32 x 32 piece at rows 32 wr, columns 32 wc of the block
+// (the piece wholly above the diagonal of a diagonal block is skipped).  The
+// head loop keeps only this piece's accumulators, with the next head's row
+// and column fragments and decay prefix values loaded while the current head
+// computes.  Writes dcb[i][j] and dcbT[j][i] for the 16 x 16 tiles on or
+// below the diagonal (the others are never read).
+// ---------------------------------------------------------------------------
+template <int P>
+__global__ __launch_bounds__(256) void k_group_dcb(const bf16 *__restrict__ x,
+                                                   const bf16 *__restrict__ dy,
+                                                   const float *__restrict__ cs,
+                                                   float *__restrict__ dcb,
+                                                   float *__restrict__ dcbT, int64_t L, int H,
+                                                   int G, int Q, int nc) {
+    constexpr int KS = P / 32 > 0 ? P / 32 : 1;
+    const int nbk = (Q + 63) / 64, npair = nbk * (nbk + 1) / 2;
+    const int64_t work = xcd_remap(blockIdx.x, gridDim.x);
+    const int pair = (int)(work % npair);
+    const int64_t bcg = work / npair;
+    int IB = (int)((sqrtf(8.f * pair + 1.f) - 1.f) * 0.5f);
+    while ((IB + 1) * (IB + 2) / 2 <= pair) ++IB;
+    while (IB * (IB + 1) / 2 > pair) --IB;
+    const int JB = pair - IB * (IB + 1) / 2;
+    const int g = (int)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int c = (int)(bc % nc);
+    const int64_t b = bc / nc;
+    const int64_t s = (int64_t)c * Q;
+    const int q = (int)min<int64_t>(Q, L - s);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, grp = lane >> 4;
+    const int wr = wave >> 1, wc = wave & 1;
+    const int i0 = IB * 64 + 32 * wr, j0 = JB * 64 + 32 * wc;
+    if (i0 >= q || j0 > i0 + 31) return;  // nothing of this piece is read; no barriers below
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int hpg = H / G;
+
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) acc[a][bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 pa[2][KS], pb[2][KS];
+    float pci[2][4], pcj[2];
+    auto load = [&](int h) {
+        const float *csh = cs + (((int64_t)b * H + h) * nc + c) * Q;
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const int ir = i0 + 16 * a + r, jr = j0 + 16 * a + r;
+            const int64_t ri = (b * L + s + ir) * H + h, rj = (b * L + s + jr) * H + h;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int kk = ks * 32 + grp * 8;
+                pa[a][ks] = (ir < q && kk < P) ? *(const u32x4 *)(dy + ri * P + kk) : z;
+                pb[a][ks] = (jr < q && kk < P) ? *(const u32x4 *)(x + rj * P + kk) : z;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pci[a][e] = csh[min(i0 + 16 * a + 4 * grp + e, Q - 1)];
+            pcj[a] = csh[min(jr, Q - 1)];
+        }
+    };
+    load(g * hpg);
+    for (int hh = 0; hh < hpg; ++hh) {
+        u32x4 fa[2][KS], fb[2][KS];
+        float ci[2][4], cj[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                fa[a][ks] = pa[a][ks];
+                fb[a][ks] = pb[a][ks];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ci[a][e] = pci[a][e];
+            cj[a] = pcj[a];
+        }
+        if (hh + 1 < hpg) load(g * hpg + hh + 1);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    t = mfma_bf16(as_bf16x8(fa[a][ks]), as_bf16x8(fb[bb][ks]), t);
+                const int j = j0 + 16 * bb + r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = i0 + 16 * a + 4 * grp + e;
+                    acc[a][bb][e] += (j <= i && i < q) ? __expf(ci[a][e] - cj[bb]) * t[e] : 0.f;
+                }
+            }
+        }
+    }
+    const int64_t cboff = bcg * (int64_t)Q * Q;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+            const int it = i0 + 16 * a, jt = j0 + 16 * bb;
+            if (jt > it || it >= Q) continue;  // tile above the diagonal or past the chunk
+            const int j = jt + r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dcb[cboff + (int64_t)(it + 4 * grp + e) * Q + j] = acc[a][bb][e];
+            *(f32x4 *)(dcbT + cboff + (int64_t)j * Q + it + 4 * grp) = acc[a][bb];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bfloat16: the state terms alone, one workgroup per (b, c, g, 64-row tile,
+// which): which = 0: dCs[i] = sum_h exp(cs_i) dy_i^T H_c; which = 1:
+// dBs[j] = sum_h exp(cs_e - cs_j) x_j^T R_c.  Each wave owns 16 rows (row
+// fragments straight from global memory); per head the state is staged once
+// into LDS as bf16 [N][P + 8] (transposed in registers) and prefetched one
+// head ahead.
+// ---------------------------------------------------------------------------
+template <int P, int N>
+__global__ __launch_bounds__(256) void k_group_state(
+    const bf16 *__restrict__ x, const bf16 *__restrict__ dy, const float *__restrict__ cs,
+    const float *__restrict__ Hs, const float *__restrict__ Rs, float *__restrict__ dCs,
+    float *__restrict__ dBs, int64_t L, int H, int G, int Q, int nc) {
+    constexpr int KS = P / 32 > 0 ? P / 32 : 1, NT = N / 16, SLD = P + 8;
+    constexpr int NBLK = (P / 4) * (N / 4);
+    constexpr int BPT = (NBLK + 255) / 256;
+    const int ntr = (Q + 63) / 64;
+    const int64_t work = xcd_remap(blockIdx.x, gridDim.x);
+    const int tile = (int)(work % ntr);
+    const int which = (int)((work / ntr) % 2);
+    const int64_t bcg = work / (2 * ntr);
+    const int g = (int)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int c = (int)(bc % nc);
+    const int64_t b = bc / nc;
+    const int64_t s = (int64_t)c * Q;
+    const int q = (int)min<int64_t>(Q, L - s);
+    if (tile * 64 >= q) return;  // the whole workgroup: no barrier is reached
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, grp = lane >> 4;
+    const int i0 = tile * 64 + wave * 16;
+    const bool active = i0 < q;
+    const int ia = i0 + r;
+    const bool va = ia < q;
+    const bf16 *rowsrc = which == 0 ? dy : x;
+    const float *St = which == 0 ? Hs : Rs;
+
+    __shared__ bf16 st_s[N * SLD];
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int hpg = H / G;
+    f32x4 pst[BPT][4];
+    u32x4 prow[KS];
+    float pw = 0.f;
+    auto load = [&](int h) {
+        const int64_t soff = (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int bi = tid + 256 * u;
+            if (bi < NBLK) {
+                const int nb = bi % (N / 4), pb = bi / (N / 4);
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    pst[u][k] = *(const f32x4 *)(St + soff + (int64_t)(4 * pb + k) * N + 4 * nb);
+            }
+        }
+        const float *csh = cs + (((int64_t)b * H + h) * nc + c) * Q;
+        const float ca = csh[min(ia, Q - 1)];
+        pw = which == 0 ? __expf(ca) : __expf(csh[q - 1] - ca);
+        const int64_t row = (b * L + s + ia) * H + h;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int kk = ks * 32 + grp * 8;
+            prow[ks] = (va && kk < P) ? *(const u32x4 *)(rowsrc + row * P + kk) : z;
+        }
+    };
+    load(g * hpg);
+    for (int hh = 0; hh < hpg; ++hh) {
+        __syncthreads();  // the previous head's LDS reads are done
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int bi = tid + 256 * u;
+            if (bi < NBLK) {
+                const int nb = bi % (N / 4), pb = bi / (N / 4);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    bf16 tv[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) tv[k] = (bf16)pst[u][k][m];
+                    *(u32x2 *)(st_s + (4 * nb + m) * SLD + 4 * pb) = *(const u32x2 *)tv;
+                }
+            }
+        }
+        u32x4 fr[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) fr[ks] = frag_scale<bf16>(prow[ks], pw);
+        __syncthreads();
+        if (hh + 1 < hpg) load(g * hpg + hh + 1);
+        if (!active) continue;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int kk = ks * 32 + grp * 8;
+                const u32x4 bv = kk < P ? *(const u32x4 *)(st_s + (t * 16 + r) * SLD + kk) : z;
+                acc[t] = mfma_bf16(as_bf16x8(fr[ks]), as_bf16x8(bv), acc[t]);
+            }
+        }
+    }
+    if (!active) return;
+    float *out = which == 0 ? dCs : dBs;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int n = t * 16 + r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = i0 + 4 * grp + e;
+            if (i < q) out[((b * L + s + i) * G + g) * N + n] = acc[t][e];
         }
     }
 }
@@ -793,7 +1317,12 @@ hipError_t launch_chunk_bwd(const Dims &d, const void *x, const void *dy, const 
     if (d.b == 0 || d.nc == 0) return hipSuccess;
     const unsigned grid = (unsigned)(d.b * d.nc * d.H);
     SSD_BWD_DISPATCH_PN(d.P, d.N, {
-        if (d.dtype == 1)
+        if (d.dtype == 1 && d.Q <= 256)
+            k_chunk_bwd_pf<PP, NN><<<grid, 256, 0, st>>>(
+                (const bf16 *)x, (const bf16 *)dy, (const bf16 *)dt, A, (const bf16 *)B,
+                (const bf16 *)C, (const bf16 *)cb, (const bf16 *)cbT, cs, Hs, Rs, D, (bf16 *)dx,
+                (bf16 *)ddt, part, d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc);
+        else if (d.dtype == 1)
             k_chunk_bwd<bf16, PP, NN, float><<<grid, 256, 0, st>>>(
                 (const bf16 *)x, (const bf16 *)dy, (const bf16 *)dt, A, (const bf16 *)B,
                 (const bf16 *)C, (const bf16 *)cb, (const bf16 *)cbT, cs, Hs, Rs, D, (bf16 *)dx,
@@ -813,7 +1342,21 @@ hipError_t launch_group_bwd(const Dims &d, const void *x, const void *dy, const 
     if (d.b == 0 || d.nc == 0) return hipSuccess;
     const unsigned grid = (unsigned)(d.b * d.nc * d.G * ((d.Q + 63) / 64));
     SSD_BWD_DISPATCH_PN(d.P, d.N, {
-        if (d.dtype == 1)
+        // bf16 with N <= 128 and P N <= 8192: dCB and the state terms in two
+        // kernels (their accumulators and prefetch fit without spills)
+        constexpr bool kSplit = NN <= 128 && PP * NN <= 8192;
+        if (kSplit && d.dtype == 1) {
+            if constexpr (kSplit) {
+                const int nbk = (int)((d.Q + 63) / 64);
+                const unsigned g1 = (unsigned)(d.b * d.nc * d.G * (nbk * (nbk + 1) / 2));
+                k_group_dcb<PP><<<g1, 256, 0, st>>>((const bf16 *)x, (const bf16 *)dy, cs, dcb,
+                                                   dcbT, d.L, (int)d.H, (int)d.G, (int)d.Q,
+                                                   (int)d.nc);
+                k_group_state<PP, NN><<<2 * grid, 256, 0, st>>>(
+                    (const bf16 *)x, (const bf16 *)dy, cs, Hs, Rs, dCs, dBs, d.L, (int)d.H,
+                    (int)d.G, (int)d.Q, (int)d.nc);
+            }
+        } else if (d.dtype == 1)
             k_group_bwd<bf16, PP, NN, float><<<grid, 256, 0, st>>>(
                 (const bf16 *)x, (const bf16 *)dy, cs, Hs, Rs, dcb, dcbT, dCs, dBs, d.L, (int)d.H,
                 (int)d.G, (int)d.Q, (int)d.nc);

@@ -12,6 +12,9 @@ Contents
   (``ssd_recurrence.c``), parallel over independent (batch, head) sequences.
 * ``backward``: reverse-mode differentiation of that recurrence, step by
   step in reverse order (``ssd_backward.c``), float64.
+* ``preprocess_dt`` / ``forward_ex`` / ``decode_step_ex``: the step size
+  through bias, softplus and clamp, and the Euler or zero-order-hold input
+  scale, ahead of the same recurrence (numpy float64).
 * ``chunked``: float64 numpy versions of each step of the chunked algorithm
   (decay prefix, C B^T, intra-chunk masked product, chunk state, state
   passing, output combine) used to check the GPU's intermediates.
@@ -143,6 +146,70 @@ def backward(x, dt, A, B, C, D, init, dy, dfinal=None):
     return {"dx": dx, "ddt": ddt, "dA": dA_bh.sum(axis=0),
             "dB": dB_h.reshape(b, L, G, hg, N).sum(axis=3), "dC": dC_h.reshape(b, L, G, hg, N).sum(axis=3),
             "dD": dD_bh.sum(axis=0), "dinit": dinit}
+
+
+SCALES = ("none", "euler", "zoh")
+
+
+def preprocess_dt(dt, A, dt_bias=None, softplus=False, dt_min=0.0, dt_max=0.0, scale="none"):
+    """The step size and input scale of one (step, head), float64.
+
+    dt_eff = softplus(dt + dt_bias) when ``softplus`` (Mamba review, section
+    3.1: the step size is a softplus of a linear map of the input, whose bias
+    is dt_bias), else dt + dt_bias; then clamped to [dt_min, dt_max] when
+    dt_max > dt_min.  The input scale s multiplies x in the state update:
+      "none":  s = 1 (the SSD pages add B x with no step factor);
+      "euler": s = dt_eff (Mamba review, section 3.3: B discretised as dt B);
+      "zoh":   s = integral_0^dt_eff exp(u A) du = expm1(dt_eff A) / A, dt_eff
+               when A = 0 (Mamba review, section 2.2; guide, equation (2)).
+    dt [..., H], A [H].  Returns (dt_eff, s), both shaped like dt.
+    """
+    if scale not in SCALES:
+        raise ValueError(f"scale must be one of {SCALES}")
+    d = _f64(dt)
+    A = _f64(A)
+    if dt_bias is not None:
+        d = d + _f64(dt_bias)
+    if softplus:
+        d = np.logaddexp(0.0, d)          # log(1 + e^d), without overflow
+    if dt_max > dt_min:
+        d = np.clip(d, dt_min, dt_max)
+    if scale == "none":
+        s = np.ones_like(d)
+    elif scale == "euler":
+        s = d.copy()
+    else:
+        Ab = np.broadcast_to(A, d.shape)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            s = np.where(Ab != 0.0, np.expm1(d * Ab) / Ab, d)
+    return d, s
+
+
+def forward_ex(x, dt, A, B, C, D=None, init=None, dt_bias=None, softplus=False, dt_min=0.0,
+               dt_max=0.0, scale="none", chunk: int = 0):
+    """forward() with the step size preprocessed and the input scaled as in
+    preprocess_dt: the recurrence runs on (s x, dt_eff), and the skip term
+    uses the raw input, y += D x (Mamba review, section 3.4: D is a separate
+    block parameter)."""
+    d, s_ = preprocess_dt(dt, A, dt_bias, softplus, dt_min, dt_max, scale)
+    x = _f64(x)
+    out = forward(s_[..., None] * x, d, A, B, C, None, init, chunk=chunk)
+    y = out[0]
+    if D is not None:
+        y = y + _f64(D)[None, None, :, None] * x
+    return (y,) + tuple(out[1:])
+
+
+def decode_step_ex(state, x, dt, A, B, C, D=None, dt_bias=None, softplus=False, dt_min=0.0,
+                   dt_max=0.0, scale="none"):
+    """decode_step() with preprocess_dt applied to the step's dt [b, H] and
+    the skip term on the raw input."""
+    d, s_ = preprocess_dt(dt, A, dt_bias, softplus, dt_min, dt_max, scale)
+    x = _f64(x)
+    y, state = decode_step(state, s_[..., None] * x, d, A, B, C, None)
+    if D is not None:
+        y = y + _f64(D)[None, :, None] * x
+    return y, state
 
 
 def decode_step(state, x, dt, A, B, C, D=None):

@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=["forward", "backward", "decode", "copy"], default="forward")
     ap.add_argument("--path", choices=["fused", "staged"], default="fused")
+    ap.add_argument("--options", choices=["none", "mamba2", "zoh"], default="none",
+                    help="forward step-size options: mamba2 = dt_bias + softplus + Euler input "
+                         "scale; zoh = zero-order-hold input scale (ssd_forward_ex)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
@@ -300,10 +303,20 @@ def run_forward_bench(args):
     fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
     staged = args.path == "staged"
     flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    okw = {}
+    if args.options == "mamba2":
+        # raw step = inverse softplus of the workload's dt minus the bias, so the
+        # preprocessed step keeps the workload's magnitudes
+        gen = torch.Generator().manual_seed(903)
+        bias = (torch.randn(w.nheads, generator=gen) * 0.5).float()
+        dt = (torch.log(torch.expm1(inp["dt"].float())) - bias).to(inp["dt"].dtype).to(dev)
+        okw = dict(dt_bias=bias.to(dev), dt_softplus=True, input_scale="euler")
+    elif args.options == "zoh":
+        okw = dict(input_scale="zoh")
 
     def step():
         ssd.forward(x, dt, A, B, C, D, init, chunk=w.chunk, staged=staged, y=y, final_state=fin,
-                    workspace=ws)
+                    workspace=ws, **okw)
 
     for _ in range(args.warmup):
         step()
@@ -333,13 +346,13 @@ def run_forward_bench(args):
         "config": {"workload": "2.7B-layer-shaped SSD forward", "batch": w.batch, "seqlen": w.seqlen,
                    "nheads": w.nheads, "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
                    "chunk": w.chunk, "inputs": "bf16", "accumulate": "fp32", "path": args.path,
-                   "mall_flushed": flush is not None},
+                   "dt_options": args.options, "mall_flushed": flush is not None},
         "forward_roofline": {"bound": "hbm", "t_roof_us": t_roof_us, "frac": t_roof_us / (ms_per_step * 1e3),
                              "alg_bytes": forward_bytes(w), "alg_flops": forward_flops(w)},
         "ms_min": min(ms), "ms_median": statistics.median(ms), "wall_s": wall,
     }
 
-    if not args.no_kernel_timing:
+    if not args.no_kernel_timing and args.options == "none":
         result["roofline"], result["kernels_us"] = kernel_roofline(ssd, w, x, dt, A, B, C, D, init, ws,
                                                                   y, fin, flush, args)
     if not args.no_cpu_baseline:

@@ -142,6 +142,48 @@ ssd_status ssd_forward_main(const ssd_dims *dims, const void *x, const void *dt,
                             void *stream);
 
 /*
+ * Step-size preprocessing and input scaling, the neighbours of the core in a
+ * Mamba layer, applied inside the kernels.  For every step and head:
+ *   dt_eff = softplus(dt + dt_bias)   if dt_softplus  (Mamba review page,
+ *            dt + dt_bias             otherwise        section 3.1: the step
+ *                                                      size is a softplus of a
+ *                                                      linear map, dt_bias its bias)
+ *   dt_eff = min(max(dt_eff, dt_min), dt_max)   when dt_max > dt_min
+ *   a_t    = exp(dt_eff A_h);   the state update adds s x B^T with
+ *   s = 1                          SSD_SCALE_NONE (the SSD pages' +B x)
+ *   s = dt_eff                     SSD_SCALE_EULER (Mamba review, section 3.3)
+ *   s = (exp(dt_eff A_h) - 1)/A_h  SSD_SCALE_ZOH (Mamba review, section 2.2;
+ *                                  guide page, equation (2); dt_eff if A_h = 0)
+ * The skip term stays D x on the raw x.  dt_bias: [nheads] float32 device
+ * array, nullable (zero bias), 16-byte aligned, must not overlap an output.
+ * An unknown input_scale returns SSD_ERR_UNSUPPORTED.  A NULL options
+ * pointer, or all fields zero, is the plain map of ssd_forward.
+ */
+typedef enum { SSD_SCALE_NONE = 0, SSD_SCALE_EULER = 1, SSD_SCALE_ZOH = 2 } ssd_input_scale;
+typedef struct {
+    const float *dt_bias;  /* [nheads] or NULL */
+    int32_t dt_softplus;   /* nonzero: softplus(dt + dt_bias) */
+    float dt_min, dt_max;  /* clamp when dt_max > dt_min */
+    int32_t input_scale;   /* ssd_input_scale */
+} ssd_dt_options;
+
+/* ssd_forward / ssd_forward_staged / ssd_decode_step with step-size options
+ * (same contracts otherwise; the same workspace size).  The single-pass
+ * arrangement takes the options in its own kernel variant. */
+ssd_status ssd_forward_ex(const ssd_dims *dims, const ssd_dt_options *opts, const void *x,
+                          const void *dt, const float *A, const void *B, const void *C,
+                          const float *D, const float *init_state, void *y, float *final_state,
+                          void *workspace, size_t workspace_bytes, void *stream);
+ssd_status ssd_forward_staged_ex(const ssd_dims *dims, const ssd_dt_options *opts, const void *x,
+                                 const void *dt, const float *A, const void *B, const void *C,
+                                 const float *D, const float *init_state, void *y,
+                                 float *final_state, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+ssd_status ssd_decode_step_ex(const ssd_dims *dims, const ssd_dt_options *opts, float *state,
+                              const void *x, const void *dt, const float *A, const void *B,
+                              const void *C, const float *D, void *y, void *stream);
+
+/*
  * One recurrent step for `batch` sequences (review page, section
  * "4つのトークンで計算してみる").  `state` [batch, H, P, N] float32 is read and
  * overwritten in place with a_t * state + x B^T; y [batch, H, P] receives
@@ -267,6 +309,11 @@ ssd_status ssd_validate_forward(const ssd_dims *dims, const void *x, const void 
 ssd_status ssd_validate_decode(const ssd_dims *dims, const float *state, const void *x,
                                const void *dt, const float *A, const void *B, const void *C,
                                const float *D, const void *y);
+ssd_status ssd_validate_forward_ex(const ssd_dims *dims, const ssd_dt_options *opts,
+                                   const void *x, const void *dt, const float *A, const void *B,
+                                   const void *C, const float *D, const float *init_state,
+                                   const void *y, const float *final_state, const void *workspace,
+                                   size_t workspace_bytes);
 ssd_status ssd_validate_backward(const ssd_dims *dims, const void *x, const void *dt,
                                  const float *A, const void *B, const void *C, const float *D,
                                  const float *init_state, const void *dy,

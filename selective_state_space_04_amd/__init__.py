@@ -34,6 +34,13 @@ class Dims(ctypes.Structure):
                 ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32)]
 
 
+class DtOptions(ctypes.Structure):
+    """ssd_dt_options: step-size bias/softplus/clamp and the input scale."""
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int32), ("dt_min", ctypes.c_float),
+                ("dt_max", ctypes.c_float), ("input_scale", ctypes.c_int32)]
+
+
+SCALES = {"none": 0, "euler": 1, "zoh": 2}
 F32, BF16 = 0, 1
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE", 4: "SSD_ERR_ALIGN",
@@ -61,6 +68,10 @@ _SIGS = {
     "ssd_backward_workspace_bytes": (ctypes.c_size_t, [_dp]),
     "ssd_backward": (ctypes.c_int, [_dp] + [_vp] * 17 + [ctypes.c_size_t, _vp]),
     "ssd_validate_backward": (ctypes.c_int, [_dp] + [_vp] * 17 + [ctypes.c_size_t]),
+    "ssd_forward_ex": (ctypes.c_int, [_dp, _vp] + [_vp] * 10 + [ctypes.c_size_t, _vp]),
+    "ssd_forward_staged_ex": (ctypes.c_int, [_dp, _vp] + [_vp] * 10 + [ctypes.c_size_t, _vp]),
+    "ssd_decode_step_ex": (ctypes.c_int, [_dp, _vp] + [_vp] * 9),
+    "ssd_validate_forward_ex": (ctypes.c_int, [_dp, _vp] + [_vp] * 10 + [ctypes.c_size_t]),
     "ssd_backward_launch_count": (ctypes.c_int, [_dp]),
     "ssd_backward_launch_name": (ctypes.c_char_p, [_dp, ctypes.c_int]),
     "ssd_backward_timed": (ctypes.c_int, [_dp] + [_vp] * 17 + [ctypes.c_size_t, _vp, _vp, ctypes.c_int]),
@@ -139,18 +150,36 @@ def _forward_dims(x, dt, A, B, C, D, init, chunk):
     return make_dims(b, L, H, P, N, G, chunk, _DT[x.dtype])
 
 
+def make_options(A, dt_bias=None, dt_softplus=False, dt_limit=None, input_scale="none"):
+    """DtOptions for the keyword arguments of forward / decode_step, or None
+    when they are all at their defaults (the plain map).  dt_limit: (lo, hi)
+    clamp of the step after softplus."""
+    if input_scale not in SCALES:
+        raise ValueError(f"input_scale must be one of {tuple(SCALES)}")
+    lo, hi = (0.0, 0.0) if dt_limit is None else (float(dt_limit[0]), float(dt_limit[1]))
+    if dt_bias is None and not dt_softplus and not hi > lo and input_scale == "none":
+        return None
+    if dt_bias is not None:
+        _need(dt_bias, "dt_bias", A.shape, torch.float32, A.device)
+    return DtOptions(_p(dt_bias), int(bool(dt_softplus)), lo, hi, SCALES[input_scale])
+
+
 def workspace_bytes(dims: Dims) -> int:
     return int(lib.ssd_forward_workspace_bytes(ctypes.byref(dims)))
 
 
 def forward(x, dt, A, B, C, D=None, init_state=None, chunk: int = 256, *, staged: bool = False,
-            y=None, final_state=None, workspace=None, want_final: bool = True):
+            y=None, final_state=None, workspace=None, want_final: bool = True, dt_bias=None,
+            dt_softplus: bool = False, dt_limit=None, input_scale: str = "none"):
     """Layer forward (chunked algorithm).  Returns (y, final_state).
 
     ``y`` / ``final_state`` / ``workspace`` may be preallocated (the
     workspace as a uint8 CUDA tensor of at least ``workspace_bytes``);
     ``final_state`` may be ``init_state`` itself for an in-place carry.
+    ``dt_bias`` / ``dt_softplus`` / ``dt_limit`` / ``input_scale`` select the
+    step-size preprocessing and input scaling of ssd_forward_ex.
     """
+    opts = make_options(A, dt_bias, dt_softplus, dt_limit, input_scale)
     dims = _forward_dims(x, dt, A, B, C, D, init_state, chunk)
     b, L, H, P = x.shape
     N = B.shape[3]
@@ -165,9 +194,14 @@ def forward(x, dt, A, B, C, D=None, init_state=None, chunk: int = 256, *, staged
     nbytes = workspace_bytes(dims)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
-    fn = lib.ssd_forward_staged if staged else lib.ssd_forward
-    _check(fn(ctypes.byref(dims), _p(x), _p(dt), _p(A), _p(B), _p(C), _p(D), _p(init_state), _p(y),
-              _p(final_state), _p(workspace), workspace.numel(), _stream()))
+    args = (_p(x), _p(dt), _p(A), _p(B), _p(C), _p(D), _p(init_state), _p(y), _p(final_state),
+            _p(workspace), workspace.numel(), _stream())
+    if opts is None:
+        fn = lib.ssd_forward_staged if staged else lib.ssd_forward
+        _check(fn(ctypes.byref(dims), *args))
+    else:
+        fn = lib.ssd_forward_staged_ex if staged else lib.ssd_forward_ex
+        _check(fn(ctypes.byref(dims), ctypes.byref(opts), *args))
     return y, final_state
 
 
@@ -211,10 +245,12 @@ def backward(x, dt, A, B, C, dy, D=None, init_state=None, dfinal_state=None, chu
     return out
 
 
-def decode_step(state, x, dt, A, B, C, D=None, y=None):
+def decode_step(state, x, dt, A, B, C, D=None, y=None, *, dt_bias=None, dt_softplus: bool = False,
+                dt_limit=None, input_scale: str = "none"):
     """One recurrent step; ``state`` [b, H, P, N] float32 is updated in place.
 
-    x [b, H, P], dt [b, H], B, C [b, G, N].  Returns y [b, H, P]."""
+    x [b, H, P], dt [b, H], B, C [b, G, N].  Returns y [b, H, P].  The
+    step-size keywords are those of forward (ssd_decode_step_ex)."""
     if x.dim() != 3 or B.dim() != 3:
         raise ValueError("x must be [b, H, P] and B, C [b, G, N]")
     if x.dtype not in _DT:
@@ -233,8 +269,12 @@ def decode_step(state, x, dt, A, B, C, D=None, y=None):
     if y is None:
         y = torch.empty_like(x)
     dims = make_dims(b, 1, H, P, N, G, 16, _DT[x.dtype])
-    _check(lib.ssd_decode_step(ctypes.byref(dims), _p(state), _p(x), _p(dt), _p(A), _p(B), _p(C),
-                               _p(D), _p(y), _stream()))
+    opts = make_options(A, dt_bias, dt_softplus, dt_limit, input_scale)
+    args = (_p(state), _p(x), _p(dt), _p(A), _p(B), _p(C), _p(D), _p(y), _stream())
+    if opts is None:
+        _check(lib.ssd_decode_step(ctypes.byref(dims), *args))
+    else:
+        _check(lib.ssd_decode_step_ex(ctypes.byref(dims), ctypes.byref(opts), *args))
     return y
 
 

@@ -91,9 +91,10 @@ int64_t esize(const ssd::Dims &d) { return d.dtype == SSD_BF16 ? 2 : 4; }
 
 int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
 
-// Workspace of the staged arrangement: cs | C B^T | chunk states.
+// Workspace of the staged arrangement: cs | C B^T | chunk states | input
+// scale of every step (used with Euler or zero-order-hold scaling).
 struct WsLayout {
-    int64_t cs = 0, cb = 0, S = 0, total = 0;
+    int64_t cs = 0, cb = 0, S = 0, sc = 0, total = 0;
 };
 
 WsLayout ws_layout(const ssd::Dims &d) {
@@ -104,7 +105,8 @@ WsLayout ws_layout(const ssd::Dims &d) {
     w.cs = 0;
     w.cb = align256(w.cs + cs_bytes);
     w.S = align256(w.cb + cb_bytes);
-    w.total = align256(w.S + s_bytes);
+    w.sc = align256(w.S + s_bytes);
+    w.total = align256(w.sc + cs_bytes);
     if (d.b == 0 || d.nc == 0) w.total = 0;
     return w;
 }
@@ -162,6 +164,26 @@ BwdLayout bwd_layout(const ssd::Dims &d) {
     w.total = align256(w.cs64 + (d.dtype == SSD_F32 ? d.b * d.H * d.nc * d.Q * 8 : 0));
     if (d.b == 0 || d.nc == 0) w.total = 0;
     return w;
+}
+
+// Step-size options: validated, and converted for the kernels.  Inactive
+// options (NULL, or all fields at their defaults) take the plain kernels.
+bool opts_active(const ssd_dt_options *o) {
+    return o && (o->dt_bias || o->dt_softplus || o->dt_max > o->dt_min || o->input_scale != SSD_SCALE_NONE);
+}
+
+ssd_status check_opts(const ssd_dt_options *o, const ssd::Dims &d) {
+    if (!o) return SSD_OK;
+    if (o->input_scale != SSD_SCALE_NONE && o->input_scale != SSD_SCALE_EULER &&
+        o->input_scale != SSD_SCALE_ZOH)
+        return SSD_ERR_UNSUPPORTED;
+    if (o->dt_bias && ((uintptr_t)o->dt_bias % 16) != 0) return SSD_ERR_ALIGN;
+    (void)d;
+    return SSD_OK;
+}
+
+ssd::DtOpts to_dev(const ssd_dt_options *o) {
+    return ssd::DtOpts{o->dt_bias, o->dt_min, o->dt_max, o->dt_softplus ? 1 : 0, (int)o->input_scale};
 }
 
 ssd_status hip_status(hipError_t e) {
@@ -278,10 +300,13 @@ ssd_status validate_ptrs(const void *const *req, int nreq, const void *const *op
     return SSD_OK;
 }
 
-// The five steps one after another, intermediates in the workspace.
+// The five steps one after another, intermediates in the workspace.  With
+// step-size options the prefix kernel preprocesses dt and (for Euler or
+// zero-order-hold scaling) writes each step's input factor, which the
+// chunk-state and scan kernels fold into their weights.
 ssd_status run_staged(const ssd::Dims &d, const void *x, const void *dt, const float *A,
                       const void *B, const void *C, const float *D, const float *init, void *y,
-                      float *fin, void *ws, hipStream_t st) {
+                      float *fin, void *ws, hipStream_t st, const ssd::DtOpts *o = nullptr) {
     if (d.b == 0) return SSD_OK;
     if (d.nc == 0) return hip_status(ssd::launch_zero_state(d, init, fin, st));
     const WsLayout w = ws_layout(d);
@@ -289,12 +314,15 @@ ssd_status run_staged(const ssd::Dims &d, const void *x, const void *dt, const f
     float *cs = (float *)(base + w.cs);
     void *cb = base + w.cb;
     float *S = (float *)(base + w.S);
+    float *sc = (o && o->scale != 0) ? (float *)(base + w.sc) : nullptr;
     hipError_t e;
-    if ((e = ssd::launch_chunk_cumsum(d, dt, A, cs, st)) != hipSuccess) return hip_status(e);
+    if (o) e = ssd::launch_chunk_cumsum_opts(d, dt, A, *o, cs, sc, st);
+    else e = ssd::launch_chunk_cumsum(d, dt, A, cs, st);
+    if (e != hipSuccess) return hip_status(e);
     if ((e = ssd::launch_chunk_cb(d, B, C, cb, nullptr, st)) != hipSuccess) return hip_status(e);
-    if ((e = ssd::launch_chunk_state(d, x, B, cs, S, false, st)) != hipSuccess) return hip_status(e);
+    if ((e = ssd::launch_chunk_state(d, x, B, cs, S, false, st, sc)) != hipSuccess) return hip_status(e);
     if ((e = ssd::launch_state_passing(d, S, cs, init, fin, st)) != hipSuccess) return hip_status(e);
-    if ((e = ssd::launch_chunk_scan(d, x, C, cb, cs, S, D, y, st)) != hipSuccess) return hip_status(e);
+    if ((e = ssd::launch_chunk_scan(d, x, C, cb, cs, S, D, y, st, sc)) != hipSuccess) return hip_status(e);
     return SSD_OK;
 }
 
@@ -378,12 +406,12 @@ ssd_status run_fused_prep(const ssd::Dims &d, const void *B, const void *C, void
 
 ssd_status run_fused_main(const ssd::Dims &d, const void *x, const void *dt, const float *A,
                           const void *C, const float *D, const float *init, void *y, float *fin,
-                          void *ws, hipStream_t st) {
+                          void *ws, hipStream_t st, const ssd::DtOpts *o = nullptr) {
     const FusedLayout f = fused_layout(d);
     char *base = (char *)ws;
     return hip_status(ssd::launch_fused_main(d, x, dt, A, base + f.Btf, base + f.Cf, base + f.Gf, D,
                                              init, y, fin, (float *)(base + f.ring),
-                                             (int *)(base + f.flags), st));
+                                             (int *)(base + f.flags), st, o));
 }
 
 }  // namespace
@@ -427,33 +455,90 @@ ssd_status ssd_validate_decode(const ssd_dims *dims, const float *state, const v
     return validate_decode(dims, state, x, dt, A, B, C, D, y, nullptr);
 }
 
+// Validation shared by the forward entry points with options: the forward's
+// checks, the options' own, and dt_bias kept clear of every output.
+static ssd_status validate_forward_ex(const ssd_dims *dims, const ssd_dt_options *opts, const void *x,
+                               const void *dt, const float *A, const void *B, const void *C,
+                               const float *D, const float *init, const void *y, const float *fin,
+                               const void *ws, size_t ws_bytes, ssd::Dims *out) {
+    ssd::Dims d;
+    ssd_status st = validate_forward(dims, x, dt, A, B, C, D, init, y, fin, ws, ws_bytes, &d);
+    if (st != SSD_OK) return st;
+    if ((st = check_opts(opts, d)) != SSD_OK) return st;
+    if (opts && opts->dt_bias) {
+        const Range rb = range_of(opts->dt_bias, d.H * 4);
+        const int64_t es = esize(d);
+        if (overlap(rb, range_of(y, d.b * d.L * d.H * d.P * es)) ||
+            overlap(rb, range_of(fin, d.b * d.H * d.P * d.N * 4)) ||
+            overlap(rb, range_of(ws, ws_total(d))))
+            return SSD_ERR_ALIAS;
+    }
+    if (out) *out = d;
+    return SSD_OK;
+}
+
+static ssd_status forward_any(const ssd_dims *dims, const ssd_dt_options *opts, bool staged_only,
+                       const void *x, const void *dt, const float *A, const void *B, const void *C,
+                       const float *D, const float *init_state, void *y, float *final_state,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    ssd::Dims d;
+    ssd_status st = validate_forward_ex(dims, opts, x, dt, A, B, C, D, init_state, y, final_state,
+                                        workspace, workspace_bytes, &d);
+    if (st != SSD_OK) return st;
+    ssd::DtOpts dev{};
+    const ssd::DtOpts *o = nullptr;
+    if (opts_active(opts)) {
+        dev = to_dev(opts);
+        o = &dev;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (!staged_only && d.b > 0 && d.nc > 0 && ssd::fused_supported(d)) {
+        if ((st = run_fused_prep(d, B, C, workspace, s)) != SSD_OK) return st;
+        return run_fused_main(d, x, dt, A, C, D, init_state, y, final_state, workspace, s, o);
+    }
+    return run_staged(d, x, dt, A, B, C, D, init_state, y, final_state, workspace, s, o);
+}
+
 ssd_status ssd_forward_staged(const ssd_dims *dims, const void *x, const void *dt,
                               const float *A, const void *B, const void *C, const float *D,
                               const float *init_state, void *y, float *final_state,
                               void *workspace, size_t workspace_bytes, void *stream) {
-    ssd::Dims d;
-    ssd_status st = validate_forward(dims, x, dt, A, B, C, D, init_state, y, final_state,
-                                     workspace, workspace_bytes, &d);
-    if (st != SSD_OK) return st;
-    return run_staged(d, x, dt, A, B, C, D, init_state, y, final_state, workspace,
-                      (hipStream_t)stream);
+    return forward_any(dims, nullptr, true, x, dt, A, B, C, D, init_state, y, final_state,
+                       workspace, workspace_bytes, stream);
 }
 
 ssd_status ssd_forward(const ssd_dims *dims, const void *x, const void *dt, const float *A,
                        const void *B, const void *C, const float *D, const float *init_state,
                        void *y, float *final_state, void *workspace, size_t workspace_bytes,
                        void *stream) {
-    ssd::Dims d;
-    ssd_status st = validate_forward(dims, x, dt, A, B, C, D, init_state, y, final_state,
-                                     workspace, workspace_bytes, &d);
-    if (st != SSD_OK) return st;
-    if (d.b > 0 && d.nc > 0 && ssd::fused_supported(d)) {
-        hipStream_t s = (hipStream_t)stream;
-        if ((st = run_fused_prep(d, B, C, workspace, s)) != SSD_OK) return st;
-        return run_fused_main(d, x, dt, A, C, D, init_state, y, final_state, workspace, s);
-    }
-    return run_staged(d, x, dt, A, B, C, D, init_state, y, final_state, workspace,
-                      (hipStream_t)stream);
+    return forward_any(dims, nullptr, false, x, dt, A, B, C, D, init_state, y, final_state,
+                       workspace, workspace_bytes, stream);
+}
+
+ssd_status ssd_forward_ex(const ssd_dims *dims, const ssd_dt_options *opts, const void *x,
+                          const void *dt, const float *A, const void *B, const void *C,
+                          const float *D, const float *init_state, void *y, float *final_state,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    return forward_any(dims, opts, false, x, dt, A, B, C, D, init_state, y, final_state,
+                       workspace, workspace_bytes, stream);
+}
+
+ssd_status ssd_forward_staged_ex(const ssd_dims *dims, const ssd_dt_options *opts, const void *x,
+                                 const void *dt, const float *A, const void *B, const void *C,
+                                 const float *D, const float *init_state, void *y,
+                                 float *final_state, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+    return forward_any(dims, opts, true, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                       workspace_bytes, stream);
+}
+
+ssd_status ssd_validate_forward_ex(const ssd_dims *dims, const ssd_dt_options *opts,
+                                   const void *x, const void *dt, const float *A, const void *B,
+                                   const void *C, const float *D, const float *init_state,
+                                   const void *y, const float *final_state, const void *workspace,
+                                   size_t workspace_bytes) {
+    return validate_forward_ex(dims, opts, x, dt, A, B, C, D, init_state, y, final_state,
+                               workspace, workspace_bytes, nullptr);
 }
 
 int ssd_forward_is_single_pass(const ssd_dims *dims) {
@@ -559,10 +644,29 @@ ssd_status ssd_backward_timed(const ssd_dims *dims, const void *x, const void *d
 ssd_status ssd_decode_step(const ssd_dims *dims, float *state, const void *x, const void *dt,
                            const float *A, const void *B, const void *C, const float *D, void *y,
                            void *stream) {
+    return ssd_decode_step_ex(dims, nullptr, state, x, dt, A, B, C, D, y, stream);
+}
+
+ssd_status ssd_decode_step_ex(const ssd_dims *dims, const ssd_dt_options *opts, float *state,
+                              const void *x, const void *dt, const float *A, const void *B,
+                              const void *C, const float *D, void *y, void *stream) {
     ssd::Dims d;
     ssd_status st = validate_decode(dims, state, x, dt, A, B, C, D, y, &d);
     if (st != SSD_OK) return st;
-    return hip_status(ssd::launch_decode(d, state, x, dt, A, B, C, D, y, (hipStream_t)stream));
+    if ((st = check_opts(opts, d)) != SSD_OK) return st;
+    if (opts && opts->dt_bias) {
+        const Range rb = range_of(opts->dt_bias, d.H * 4);
+        if (overlap(rb, range_of(state, d.b * d.H * d.P * d.N * 4)) ||
+            overlap(rb, range_of(y, d.b * d.H * d.P * esize(d))))
+            return SSD_ERR_ALIAS;
+    }
+    ssd::DtOpts dev{};
+    const ssd::DtOpts *o = nullptr;
+    if (opts_active(opts)) {
+        dev = to_dev(opts);
+        o = &dev;
+    }
+    return hip_status(ssd::launch_decode(d, state, x, dt, A, B, C, D, y, (hipStream_t)stream, o));
 }
 
 ssd_status ssd_chunk_cumsum(const ssd_dims *dims, const void *dt, const float *A, float *cs,

@@ -102,6 +102,31 @@ __device__ __forceinline__ u32x4 frag_from_f32_col(const float *base, int64_t ld
     }
 }
 
+// Step-size preprocessing and input scaling (Mamba review, section 3.1: the
+// step size is a softplus of a linear map of the input, whose bias is
+// dt_bias; section 2.2 and guide equation (2): the zero-order-hold input
+// factor is the integral of exp(u A) over the step; section 3.3: the Euler
+// factor is the step itself).
+struct DtOpts {
+    const float *bias;  // [H] or null
+    float lo, hi;       // clamp to [lo, hi] when hi > lo, after softplus
+    int softplus;       // nonzero: softplus(dt + bias)
+    int scale;          // 0: x as is, 1: dt x (Euler), 2: expm1(dt A) / A x (zero-order hold)
+};
+
+__device__ __forceinline__ float dt_effective(float raw, int h, const DtOpts &o) {
+    float v = raw + (o.bias ? o.bias[h] : 0.f);
+    if (o.softplus) v = v > 20.f ? v : log1pf(expf(v));
+    if (o.hi > o.lo) v = fminf(fmaxf(v, o.lo), o.hi);
+    return v;
+}
+
+__device__ __forceinline__ float input_scale(float d, float Ah, int scale) {
+    if (scale == 1) return d;
+    if (scale == 2) return Ah != 0.f ? expm1f(d * Ah) / Ah : d;
+    return 1.f;
+}
+
 // Blocks are dealt to the 8 XCDs round-robin (block k runs on XCD k % 8), and
 // each XCD has its own L2.  Work items that share operands (all heads of one
 // chunk share C, B and C B^T) should land on the same XCD, so map block k to

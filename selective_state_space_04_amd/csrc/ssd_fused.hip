@@ -286,16 +286,22 @@ __device__ __forceinline__ void tile_load(TileOps<NG> &t, const bf16 *Gfc, const
     for (int kn = 0; kn < 4; ++kn) t.cf[kn] = *(const u32x4 *)(Cfc + ((I * 4 + kn) * 64 + lane) * 8);
 }
 
-template <int P, int N>
+// OPTS: the step is preprocessed (bias, softplus, clamp) and x scaled by the
+// step's input factor s_j (Euler or zero-order hold), folded into the
+// chunk-state weights, the mask factors v_j and the diagonal mask; the skip
+// term keeps the raw x.  s_j takes 1 KB more LDS, so this variant runs two
+// workgroups per CU.
+template <int P, int N, bool OPTS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_ssd_fused(
     const bf16 *__restrict__ x, const bf16 *__restrict__ dt, const float *__restrict__ A,
     const bf16 *__restrict__ Btf, const bf16 *__restrict__ Cf, const bf16 *__restrict__ Gf,
     const float *__restrict__ D, const float *init, bf16 *__restrict__ y, float *fin,
-    float *ring, int *flags, int L, int H, int G, int Q, int nc, int nbh) {
+    float *ring, int *flags, int L, int H, int G, int Q, int nc, int nbh, DtOpts o) {
     constexpr int PT = P / 16, NT = N / 16, NTW = NT / 4, NKN = N / 32;
     static_assert(NT % 4 == 0 && N % 32 == 0, "N must be a multiple of 64");
     constexpr int XW = 256, HW = N;   // unpadded rows, chunk-swizzled (swz)
     __shared__ float cs_s[256];
+    __shared__ float s_s[OPTS ? 256 : 1];  // input factor of each step (OPTS)
     // w_j = exp(cs_last - cs_j) (chunk-state weights) until step 4 is done in
     // every wave, then v_j = exp(r_J(j) - cs_j) (intra-chunk mask factor).
     // One array keeps the workgroup within a third of the CU's LDS.
@@ -364,8 +370,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     }
 
     // 1. decay prefix
+    float sx_own = 1.f;  // this thread's step's input factor (OPTS)
     {
-        float v = (tid < q) ? (float)dt[(b * L + s + tid) * H + h] * A[h] : 0.f;
+        float v;
+        if constexpr (OPTS) {
+            const float de = (tid < q) ? dt_effective((float)dt[(b * L + s + tid) * H + h], h, o) : 0.f;
+            sx_own = (tid < q) ? input_scale(de, A[h], o.scale) : 0.f;
+            s_s[tid] = sx_own;
+            v = de * A[h];
+        } else {
+            v = (tid < q) ? (float)dt[(b * L + s + tid) * H + h] * A[h] : 0.f;
+        }
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float o = __shfl_up(v, off, 64);
@@ -377,7 +392,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         cs_s[tid] = v;  // past q: repeats the last valid value
         __syncthreads();
         if (tid < 8) ref_s[tid] = cs_s[min(32 * tid + 31, q - 1)];
-        wv_s[tid] = __expf(cs_s[q - 1] - v);
+        wv_s[tid] = __expf(cs_s[q - 1] - v) * sx_own;
     }
     const float cs_last = cs_s[q - 1];
 
@@ -470,7 +485,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 
     __syncthreads();  // step 4 is done in every wave: w may be replaced by v
     // v_j relative to the end of j's own 32-block (cs past q repeats)
-    wv_s[tid] = __expf(ref_s[tid >> 5] - cs_s[tid]);
+    wv_s[tid] = __expf(ref_s[tid >> 5] - cs_s[tid]) * sx_own;
 
     // 5. hand-off, second half: h_c = exp(cs_last) h_{c-1} + S_c to this
     // wave's ring slice (or final_state); h_{c-1} as bf16 to LDS.  The wave
@@ -554,7 +569,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int j = jl + e;
-            bm[e] = (bf16)((j <= il) ? __expf(csi - cs_s[j]) * (float)gd[e] : 0.f);
+            const float sj = OPTS ? s_s[j] : 1.f;
+            bm[e] = (bf16)((j <= il) ? __expf(csi - cs_s[j]) * (float)gd[e] * sj : 0.f);
         }
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
@@ -647,12 +663,18 @@ hipError_t launch_fused_prep(const Dims &d, const void *B, const void *C, void *
 hipError_t launch_fused_main(const Dims &d, const void *x, const void *dt, const float *A,
                              const void *Btf, const void *Cf, const void *Gf, const float *D,
                              const float *init, void *y, float *fin, float *ring, int *flags,
-                             hipStream_t st) {
+                             hipStream_t st, const DtOpts *o) {
     const unsigned grid = (unsigned)(d.b * d.nc * d.H);
-    k_ssd_fused<64, 128><<<grid, 256, 0, st>>>(
-        (const bf16 *)x, (const bf16 *)dt, A, (const bf16 *)Btf, (const bf16 *)Cf, (const bf16 *)Gf, D,
-        init, (bf16 *)y, fin, ring, flags, (int)d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc,
-        (int)(d.b * d.H));
+    if (o)
+        k_ssd_fused<64, 128, true><<<grid, 256, 0, st>>>(
+            (const bf16 *)x, (const bf16 *)dt, A, (const bf16 *)Btf, (const bf16 *)Cf, (const bf16 *)Gf,
+            D, init, (bf16 *)y, fin, ring, flags, (int)d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc,
+            (int)(d.b * d.H), *o);
+    else
+        k_ssd_fused<64, 128, false><<<grid, 256, 0, st>>>(
+            (const bf16 *)x, (const bf16 *)dt, A, (const bf16 *)Btf, (const bf16 *)Cf, (const bf16 *)Gf,
+            D, init, (bf16 *)y, fin, ring, flags, (int)d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc,
+            (int)(d.b * d.H), DtOpts{nullptr, 0.f, 0.f, 0, 0});
     return hipGetLastError();
 }
 

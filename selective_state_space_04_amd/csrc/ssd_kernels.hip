@@ -62,6 +62,55 @@ __global__ __launch_bounds__(64) void k_chunk_cumsum(const T *__restrict__ dt,
     }
 }
 
+// The same prefix over the preprocessed step dt_eff = dt_effective(dt) (bias,
+// softplus, clamp), and, when sc is given, the input scale of every step
+// (zero past a short chunk's end, where x is zero too).
+template <typename T>
+__global__ __launch_bounds__(64) void k_chunk_cumsum_opts(const T *__restrict__ dt,
+                                                          const float *__restrict__ A, DtOpts o,
+                                                          float *__restrict__ cs,
+                                                          float *__restrict__ sc, int64_t L,
+                                                          int H, int Q, int nc) {
+    const int c = blockIdx.x, h = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int64_t s = (int64_t)c * Q;
+    const int q = (int)min<int64_t>(Q, L - s);
+    const float Ah = A[h];
+    const int per = (Q + 63) / 64;
+    float v[4], sv[4];
+    float run = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = lane * per + e;
+        float d = 0.f, sx = 0.f;
+        if (e < per && i < q) {
+            const float de = dt_effective(to_f32(dt[((b * L) + s + i) * H + h]), h, o);
+            d = de * Ah;
+            sx = input_scale(de, Ah, o.scale);
+        }
+        run += d;
+        v[e] = run;
+        sv[e] = sx;
+    }
+    float tot = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float t = __shfl_up(tot, off, 64);
+        if (lane >= off) tot += t;
+    }
+    const float excl = tot - run;
+    const int64_t base = (((int64_t)b * H + h) * nc + c) * Q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int i = lane * per + e;
+        if (e < per && i < Q) {
+            cs[base + i] = v[e] + excl;
+            if (sc) sc[base + i] = sv[e];
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // C B^T per (b, c, g): one wave per 16 x 16 tile on or below the diagonal,
 // K = N in MFMA steps.  A operand = C rows (m = i), B operand = B rows
@@ -143,7 +192,8 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T *__restrict__ x,
                                                      const T *__restrict__ B,
                                                      const float *__restrict__ cs,
                                                      float *__restrict__ S, int64_t L, int H,
-                                                     int G, int Q, int nc) {
+                                                     int G, int Q, int nc,
+                                                     const float *__restrict__ sc) {
     constexpr int PT = P / 16, NT = N / 16, NTW = (NT + 3) / 4;
     const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
     const int h = (int)(wid % H);
@@ -159,8 +209,9 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T *__restrict__ x,
     __shared__ float w_s[256];
     const float *csc = cs + (((int64_t)b * H + h) * nc + c) * Q;
     const float cs_last = csc[q - 1];
+    const float *scc = sc ? sc + (((int64_t)b * H + h) * nc + c) * Q : nullptr;
     for (int j = threadIdx.x; j < Q; j += 256)
-        w_s[j] = FROM_START ? __expf(csc[j]) : __expf(cs_last - csc[j]);
+        w_s[j] = (FROM_START ? __expf(csc[j]) : __expf(cs_last - csc[j])) * (scc ? scc[j] : 1.f);
     __syncthreads();
 
     f32x4 acc[NTW][PT];
@@ -312,7 +363,8 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const T *__restrict__ x, con
                                                     const float *__restrict__ cs,
                                                     const float *__restrict__ hprev,
                                                     const float *__restrict__ D, T *__restrict__ y,
-                                                    int64_t L, int H, int G, int Q, int nc) {
+                                                    int64_t L, int H, int G, int Q, int nc,
+                                                    const float *__restrict__ sc) {
     constexpr int PT = P / 16;
     const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
     const int h = (int)(wid % H);
@@ -326,9 +378,13 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const T *__restrict__ x, con
     const int r = lane & 15, grp = lane >> 4;
     const int Qp = (Q + 31) & ~31;
 
-    __shared__ float cs_s[256];
+    __shared__ float cs_s[256], sc_s[256];
     const float *csc = cs + (((int64_t)b * H + h) * nc + c) * Q;
-    for (int j = threadIdx.x; j < Qp; j += 256) cs_s[j] = csc[min(j, Q - 1)];
+    const float *scc = sc ? sc + (((int64_t)b * H + h) * nc + c) * Q : nullptr;
+    for (int j = threadIdx.x; j < Qp; j += 256) {
+        cs_s[j] = csc[min(j, Q - 1)];
+        sc_s[j] = scc ? scc[min(j, Q - 1)] : 1.f;
+    }
 
     const T *cbc = cb + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
     const float *hp = hprev ? hprev + (((b * nc + c) * H + h) * (int64_t)P) * N : nullptr;
@@ -414,7 +470,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const T *__restrict__ x, con
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int j = jl + e;
-                        const float m = (j <= il) ? __expf(csi - cs_s[j]) * (float)gv[e] : 0.f;
+                        const float m = (j <= il) ? __expf(csi - cs_s[j]) * (float)gv[e] * sc_s[j] : 0.f;
                         bm[e] = (bf16)m;
                     }
                 } else {
@@ -434,7 +490,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const T *__restrict__ x, con
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int j = jl + e;
-                    m[e] = (j <= il) ? __expf(csi - cs_s[j]) * g4[e] : 0.f;
+                    m[e] = (j <= il) ? __expf(csi - cs_s[j]) * g4[e] * sc_s[j] : 0.f;
                 }
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt) {
@@ -481,14 +537,16 @@ __global__ __launch_bounds__(256) void k_decode(float *__restrict__ state, const
                                                 const float *__restrict__ A,
                                                 const T *__restrict__ B, const T *__restrict__ C,
                                                 const float *__restrict__ D, T *__restrict__ y,
-                                                int H, int G, int P) {
+                                                int H, int G, int P, DtOpts o, int use_opts) {
     constexpr int NL = N / 4, RPI = 256 / NL, U = 8;
     const int64_t bh = blockIdx.x;
     const int h = (int)(bh % H);
     const int64_t b = bh / H;
     const int g = h / (H / G);
     const int nl = threadIdx.x % NL, slot = threadIdx.x / NL;
-    const float a = __expf(to_f32(dt[bh]) * A[h]);
+    const float dte = use_opts ? dt_effective(to_f32(dt[bh]), h, o) : to_f32(dt[bh]);
+    const float a = __expf(dte * A[h]);
+    const float xsc = use_opts ? input_scale(dte, A[h], o.scale) : 1.f;  // x's factor in the update
     const float Dh = D ? D[h] : 0.f;
     float bv[4], cv[4];
 #pragma unroll
@@ -518,7 +576,7 @@ __global__ __launch_bounds__(256) void k_decode(float *__restrict__ state, const
                 f32x4 nh;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    nh[e] = a * hv[u][e] + xv[u] * bv[e];
+                    nh[e] = a * hv[u][e] + (xsc * xv[u]) * bv[e];
                     part += nh[e] * cv[e];
                 }
                 *(f32x4 *)(st + (int64_t)p * N + nl * 4) = nh;
@@ -566,6 +624,19 @@ hipError_t launch_chunk_cumsum(const Dims &d, const void *dt, const float *A, fl
     return hipGetLastError();
 }
 
+hipError_t launch_chunk_cumsum_opts(const Dims &d, const void *dt, const float *A,
+                                    const DtOpts &o, float *cs, float *sc, hipStream_t st) {
+    if (d.b == 0 || d.nc == 0) return hipSuccess;
+    dim3 grid((unsigned)d.nc, (unsigned)d.H, (unsigned)d.b);
+    if (d.dtype == 1)
+        k_chunk_cumsum_opts<bf16><<<grid, 64, 0, st>>>((const bf16 *)dt, A, o, cs, sc, d.L, (int)d.H,
+                                                       (int)d.Q, (int)d.nc);
+    else
+        k_chunk_cumsum_opts<float><<<grid, 64, 0, st>>>((const float *)dt, A, o, cs, sc, d.L,
+                                                        (int)d.H, (int)d.Q, (int)d.nc);
+    return hipGetLastError();
+}
+
 hipError_t launch_chunk_cb(const Dims &d, const void *B, const void *C, void *cb, void *cbT,
                            hipStream_t st) {
     if (d.b == 0 || d.nc == 0) return hipSuccess;
@@ -584,7 +655,7 @@ hipError_t launch_chunk_cb(const Dims &d, const void *B, const void *C, void *cb
 }
 
 hipError_t launch_chunk_state(const Dims &d, const void *x, const void *B, const float *cs,
-                              float *S, bool from_start, hipStream_t st) {
+                              float *S, bool from_start, hipStream_t st, const float *sc) {
     if (d.b == 0 || d.nc == 0) return hipSuccess;
     const unsigned grid = (unsigned)(d.b * d.nc * d.H);
 #define SSD_LAUNCH_STATE(FS)                                                                      \
@@ -592,11 +663,11 @@ hipError_t launch_chunk_state(const Dims &d, const void *x, const void *B, const
         if (d.dtype == 1)                                                                         \
             k_chunk_state<bf16, PP, NN, FS><<<grid, 256, 0, st>>>(                                \
                 (const bf16 *)x, (const bf16 *)B, cs, S, d.L, (int)d.H, (int)d.G, (int)d.Q,       \
-                (int)d.nc);                                                                       \
+                (int)d.nc, sc);                                                                   \
         else                                                                                      \
             k_chunk_state<float, PP, NN, FS><<<grid, 256, 0, st>>>(                               \
                 (const float *)x, (const float *)B, cs, S, d.L, (int)d.H, (int)d.G, (int)d.Q,     \
-                (int)d.nc);                                                                       \
+                (int)d.nc, sc);                                                                   \
     })
     if (from_start) SSD_LAUNCH_STATE(true);
     else SSD_LAUNCH_STATE(false);
@@ -629,36 +700,39 @@ hipError_t launch_zero_state(const Dims &d, const float *init, float *fin, hipSt
 
 hipError_t launch_chunk_scan(const Dims &d, const void *x, const void *C, const void *cb,
                              const float *cs, const float *hprev, const float *D, void *y,
-                             hipStream_t st) {
+                             hipStream_t st, const float *sc) {
     if (d.b == 0 || d.nc == 0) return hipSuccess;
     const unsigned grid = (unsigned)(d.b * d.nc * d.H);
     SSD_DISPATCH_PN(d.P, d.N, {
         if (d.dtype == 1)
             k_chunk_scan<bf16, PP, NN><<<grid, 256, 0, st>>>(
                 (const bf16 *)x, (const bf16 *)C, (const bf16 *)cb, cs, hprev, D, (bf16 *)y, d.L,
-                (int)d.H, (int)d.G, (int)d.Q, (int)d.nc);
+                (int)d.H, (int)d.G, (int)d.Q, (int)d.nc, sc);
         else
             k_chunk_scan<float, PP, NN><<<grid, 256, 0, st>>>(
                 (const float *)x, (const float *)C, (const float *)cb, cs, hprev, D, (float *)y,
-                d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc);
+                d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc, sc);
     });
     return hipGetLastError();
 }
 
 hipError_t launch_decode(const Dims &d, float *state, const void *x, const void *dt,
                          const float *A, const void *B, const void *C, const float *D, void *y,
-                         hipStream_t st) {
+                         hipStream_t st, const DtOpts *o) {
     if (d.b == 0) return hipSuccess;
+    const DtOpts oo = o ? *o : DtOpts{nullptr, 0.f, 0.f, 0, 0};
+    const int use = o ? 1 : 0;
     const unsigned grid = (unsigned)(d.b * d.H);
     SSD_DISPATCH_N(d.N, {
         if (d.dtype == 1)
             k_decode<bf16, NN><<<grid, 256, 0, st>>>(state, (const bf16 *)x, (const bf16 *)dt, A,
                                                     (const bf16 *)B, (const bf16 *)C, D, (bf16 *)y,
-                                                    (int)d.H, (int)d.G, (int)d.P);
+                                                    (int)d.H, (int)d.G, (int)d.P, oo, use);
         else
             k_decode<float, NN><<<grid, 256, 0, st>>>(state, (const float *)x, (const float *)dt, A,
                                                      (const float *)B, (const float *)C, D,
-                                                     (float *)y, (int)d.H, (int)d.G, (int)d.P);
+                                                     (float *)y, (int)d.H, (int)d.G, (int)d.P, oo,
+                                                     use);
     });
     return hipGetLastError();
 }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ssd_device.h"
+
 namespace ssd {
 
 struct Dims {
@@ -14,25 +16,30 @@ struct Dims {
 
 hipError_t launch_chunk_cumsum(const Dims &d, const void *dt, const float *A, float *cs,
                                hipStream_t st);
+// With step-size options: cs from the preprocessed dt and, when sc is given,
+// the input scale of every step (same layout as cs).
+hipError_t launch_chunk_cumsum_opts(const Dims &d, const void *dt, const float *A,
+                                    const DtOpts &o, float *cs, float *sc, hipStream_t st);
 hipError_t launch_chunk_cb(const Dims &d, const void *B, const void *C, void *cb, void *cbT,
                            hipStream_t st);
 hipError_t launch_chunk_state(const Dims &d, const void *x, const void *B, const float *cs,
-                              float *S, bool from_start, hipStream_t st);
+                              float *S, bool from_start, hipStream_t st,
+                              const float *sc = nullptr);
 hipError_t launch_state_passing(const Dims &d, float *S, const float *cs, const float *init,
                                 float *fin, hipStream_t st);
 hipError_t launch_chunk_scan(const Dims &d, const void *x, const void *C, const void *cb,
                              const float *cs, const float *hprev, const float *D, void *y,
-                             hipStream_t st);
+                             hipStream_t st, const float *sc = nullptr);
 hipError_t launch_decode(const Dims &d, float *state, const void *x, const void *dt,
                          const float *A, const void *B, const void *C, const float *D, void *y,
-                         hipStream_t st);
+                         hipStream_t st, const DtOpts *o = nullptr);
 bool fused_supported(const Dims &d);
 hipError_t launch_fused_prep(const Dims &d, const void *B, const void *C, void *Gf, void *Btf,
                              void *Cf, int *flags, hipStream_t st);
 hipError_t launch_fused_main(const Dims &d, const void *x, const void *dt, const float *A,
                              const void *Btf, const void *Cf, const void *Gf, const float *D,
                              const float *init, void *y, float *fin, float *ring, int *flags,
-                             hipStream_t st);
+                             hipStream_t st, const DtOpts *o = nullptr);
 hipError_t launch_zero_state(const Dims &d, const float *init, float *fin, hipStream_t st);
 
 // Gradient kernels (ssd_backward.hip).

@@ -72,13 +72,13 @@ def test_valid_forward_passes():
 
 def test_workspace_bytes():
     al = lambda v: (v + 255) // 256 * 256
-    # staged layout: cs | C B^T | chunk states
+    # staged layout: cs | C B^T | chunk states | per-step input scale (as cs)
     d = dims(batch=2, seqlen=100, nheads=4, headdim=32, dstate=128, ngroups=2, chunk=64)
     nc = 2
     cs = 2 * 4 * nc * 64 * 4
     cb = 2 * nc * 2 * 64 * 64 * 2
     S = 2 * nc * 4 * 32 * 128 * 4
-    staged = al(al(al(cs) + cb) + S)
+    staged = al(al(al(al(cs) + cb) + S) + cs)
     assert LIB.ssd_forward_is_single_pass(ctypes.byref(d)) == 0
     assert ssd.workspace_bytes(d) == staged
     # single-pass layout (bf16, P=64, N=128): C B^T fragments | B^T fragments |
@@ -87,7 +87,7 @@ def test_workspace_bytes():
     d = dims(batch=2, seqlen=100, nheads=4, headdim=64, dstate=128, ngroups=2, chunk=64)
     assert LIB.ssd_forward_is_single_pass(ctypes.byref(d)) == 1
     S = 2 * nc * 4 * 64 * 128 * 4
-    staged = al(al(al(cs) + cb) + S)
+    staged = al(al(al(al(cs) + cb) + S) + cs)
     nbcg, t16, nj = 2 * nc * 2, 64 // 16, 64 // 32
     gf = nbcg * t16 * nj * 1024
     btf = nbcg * 128 * nj * 64
@@ -277,3 +277,34 @@ def test_backward_workspace_bytes():
         o32 = al(o32 + nbytes)
     assert ssd.backward_workspace_bytes(dims(dtype=ssd.F32)) == o32
     assert ssd.backward_workspace_bytes(dims(headdim=48)) == 0
+
+
+# ------------------------------------------------------------------ step-size options
+def vfwd_ex(d, opts, a):
+    return LIB.ssd_validate_forward_ex(ctypes.byref(d), None if opts is None else ctypes.byref(opts), a["x"], a["dt"],
+                                       a["A"], a["B"], a["C"], a["D"], a["init"], a["y"], a["fin"], a["ws"],
+                                       a["ws_bytes"])
+
+
+def test_forward_ex_options_validation():
+    d = dims()
+    a = fwd_args(d)
+    bias = Bufs().take() + (1 << 45)
+    assert vfwd_ex(d, None, a) == 0
+    assert vfwd_ex(d, ssd.DtOptions(bias, 1, 0.0, 0.0, 2), a) == 0
+    assert ssd.STATUS[vfwd_ex(d, ssd.DtOptions(None, 0, 0.0, 0.0, 3), a)] == "SSD_ERR_UNSUPPORTED"
+    assert ssd.STATUS[vfwd_ex(d, ssd.DtOptions(bias + 4, 0, 0.0, 0.0, 0), a)] == "SSD_ERR_ALIGN"
+    assert ssd.STATUS[vfwd_ex(d, ssd.DtOptions(a["y"], 1, 0.0, 0.0, 0), a)] == "SSD_ERR_ALIAS"
+    assert ssd.STATUS[vfwd_ex(d, ssd.DtOptions(a["ws"] + 256, 1, 0.0, 0.0, 0), a)] == "SSD_ERR_ALIAS"
+    # the forward's own checks still apply
+    assert ssd.STATUS[vfwd_ex(d, ssd.DtOptions(bias, 1, 0.0, 0.0, 1), dict(a, x=None))] == "SSD_ERR_NULL"
+
+
+def test_make_options_defaults_are_the_plain_map():
+    import torch
+    A = torch.zeros(4)
+    assert ssd.make_options(A) is None
+    o = ssd.make_options(A, dt_softplus=True, dt_limit=(0.001, 0.5), input_scale="zoh")
+    assert (o.dt_softplus, o.input_scale) == (1, 2) and abs(o.dt_max - 0.5) < 1e-7
+    with pytest.raises(ValueError):
+        ssd.make_options(A, input_scale="bilinear")

@@ -584,3 +584,101 @@ def test_backward_long_carried_bf16(ssd):
     inp = si.make_forward_inputs(w)
     g = si.make_output_grads(w)
     check_bwd(run_backward(ssd, inp, g, 256), oracle_backward(inp, g), "bf16", inp, g)
+
+
+# ------------------------------------------------------------------ step-size options
+# ssd_forward_ex / ssd_decode_step_ex against oracle.forward_ex / decode_step_ex.
+# The raw step is the inverse softplus of the workload's dt minus a bias, so
+# softplus(raw + bias) has the workload's magnitudes.
+OPTION_SETS = {
+    "euler": dict(input_scale="euler"),
+    "zoh": dict(input_scale="zoh"),
+    "bias": dict(bias=True),
+    "mamba2": dict(bias=True, dt_softplus=True, input_scale="euler"),
+    "softplus_clamp_zoh": dict(bias=True, dt_softplus=True, dt_limit=(0.002, 0.05), input_scale="zoh"),
+}
+
+
+def option_inputs(inp, opt, seed=0):
+    """(gpu kwargs, oracle kwargs, dt tensor) for one option set."""
+    w = inp["workload"]
+    g = torch.Generator().manual_seed(900 + seed)
+    H = w.nheads
+    bias = (torch.randn(H, generator=g) * 0.5).float() if opt.get("bias") else None
+    dt = inp["dt"].float()
+    if opt.get("dt_softplus"):
+        raw = torch.log(torch.expm1(dt)) - (bias if bias is not None else 0.0)
+    else:
+        raw = dt
+        if bias is not None:
+            bias = bias.abs() * 1e-3          # without softplus, dt + bias stays positive
+    raw = raw.to(inp["dt"].dtype)
+    lim = opt.get("dt_limit")
+    gk = dict(dt_bias=dev(bias), dt_softplus=bool(opt.get("dt_softplus")), dt_limit=lim,
+              input_scale=opt.get("input_scale", "none"))
+    ok = dict(dt_bias=None if bias is None else bias.double().numpy(), softplus=bool(opt.get("dt_softplus")),
+              dt_min=lim[0] if lim else 0.0, dt_max=lim[1] if lim else 0.0, scale=opt.get("input_scale", "none"))
+    return gk, ok, raw
+
+
+@pytest.mark.parametrize("opt", sorted(OPTION_SETS))
+@pytest.mark.parametrize("route", ["fused-bf16", "staged-bf16", "staged-f32"])
+def test_forward_options(ssd, opt, route):
+    dtype = route.split("-")[1]
+    w = small(dtype, batch=2, seqlen=700, nheads=4, headdim=64, dstate=128, ngroups=2, chunk=256, seed=21)
+    inp = si.make_forward_inputs(w)
+    gk, ok, raw = option_inputs(inp, OPTION_SETS[opt])
+    y, fin = ssd.forward(dev(inp["x"]), dev(raw), dev(inp["A"]), dev(inp["B"]), dev(inp["C"]), dev(inp["D"]),
+                         dev(inp["init"]), chunk=w.chunk, staged=route.startswith("staged"), **gk)
+    torch.cuda.synchronize()
+    y_ref, f_ref = oracle.forward_ex(inp["x"], raw, inp["A"], inp["B"], inp["C"], inp["D"], inp["init"], **ok)
+    assert worst_rel(f64(y), y_ref, "y") < TOL[dtype]
+    assert worst_rel(f64(fin), f_ref, "state") < TOL[dtype]
+
+
+@pytest.mark.parametrize("opt", ["mamba2", "softplus_clamp_zoh"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_options_short_chunks(ssd, opt, dtype):
+    w = small(dtype, seqlen=301, chunk=48)
+    inp = si.make_forward_inputs(w)
+    gk, ok, raw = option_inputs(inp, OPTION_SETS[opt], seed=1)
+    y, fin = ssd.forward(dev(inp["x"]), dev(raw), dev(inp["A"]), dev(inp["B"]), dev(inp["C"]), dev(inp["D"]),
+                         dev(inp["init"]), chunk=w.chunk, **gk)
+    torch.cuda.synchronize()
+    y_ref, f_ref = oracle.forward_ex(inp["x"], raw, inp["A"], inp["B"], inp["C"], inp["D"], inp["init"], **ok)
+    assert worst_rel(f64(y), y_ref, "y") < TOL[dtype]
+    assert worst_rel(f64(fin), f_ref, "state") < TOL[dtype]
+
+
+@pytest.mark.parametrize("opt", ["mamba2", "softplus_clamp_zoh"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_options(ssd, opt, dtype):
+    w = small(dtype, batch=3, seqlen=6, nheads=8, headdim=64, dstate=128, ngroups=2, seed=23)
+    inp = si.make_forward_inputs(w)
+    gk, ok, raw = option_inputs(inp, OPTION_SETS[opt], seed=2)
+    state = dev(inp["init"]).clone()
+    st_ref = inp["init"].double().numpy().copy()
+    for t in range(w.seqlen):
+        y = ssd.decode_step(state, dev(inp["x"][:, t].contiguous()), dev(raw[:, t].contiguous()), dev(inp["A"]),
+                            dev(inp["B"][:, t].contiguous()), dev(inp["C"][:, t].contiguous()), dev(inp["D"]), **gk)
+        y_ref, st_ref = oracle.decode_step_ex(st_ref, inp["x"][:, t], raw[:, t], inp["A"], inp["B"][:, t],
+                                              inp["C"][:, t], inp["D"], **ok)
+        torch.cuda.synchronize()
+        a = f64(y)
+        assert np.linalg.norm(a - y_ref) / np.linalg.norm(y_ref) < TOL[dtype]
+    assert worst_rel(f64(state), st_ref, "state") < TOL[dtype]
+
+
+def test_forward_options_full_size_2p7b_layer(ssd):
+    """The 2.7B-layer shape at full size with the Mamba-2 preprocessing
+    (bias, softplus, Euler input scale) on the single-pass route."""
+    w = si.WORKLOADS[2]
+    inp = si.make_forward_inputs(w)
+    gk, ok, raw = option_inputs(inp, OPTION_SETS["mamba2"], seed=3)
+    y, fin = ssd.forward(dev(inp["x"]), dev(raw), dev(inp["A"]), dev(inp["B"]), dev(inp["C"]), dev(inp["D"]),
+                         None, chunk=w.chunk, **gk)
+    torch.cuda.synchronize()
+    y_ref, f_ref = oracle.forward_ex(inp["x"], raw, inp["A"], inp["B"], inp["C"], inp["D"], None, **ok)
+    e = (worst_rel(f64(y), y_ref, "y"), worst_rel(f64(fin), f_ref, "state"))
+    print("full-size forward with options:", e, flush=True)
+    assert max(e) < TOL["bf16"]

@@ -37,7 +37,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["forward", "backward", "decode", "copy"], default="forward")
+    ap.add_argument("--workload", choices=["forward", "backward", "decode", "gated_norm", "copy"],
+                    default="forward")
+    ap.add_argument("--ngroups", type=int, default=0,
+                    help="forward: B/C groups (0 = the workload's own, 1)")
     ap.add_argument("--path", choices=["fused", "staged"], default="fused")
     ap.add_argument("--options", choices=["none", "mamba2", "zoh"], default="none",
                     help="forward step-size options: mamba2 = dt_bias + softplus + Euler input "
@@ -292,6 +295,8 @@ def run_forward_bench(args):
     import ssd_inputs as si
 
     w = si.WORKLOADS[2]
+    if args.ngroups:
+        w = w.with_(ngroups=args.ngroups)
     dev = torch.device("cuda:0")
     inp = si.make_forward_inputs(w)
     g = lambda t: None if t is None else t.to(dev)
@@ -460,6 +465,59 @@ def cpu_baseline(w, inp):
             f"float64 sequential recurrence, {t:.2f} s"}
 
 
+def run_gated_norm_bench(args):
+    """The normalisation after the gate on the 2.7B-layer output
+    ([4, 4096, 80, 64] bf16): reads y and z, writes out, once each."""
+    import torch
+
+    import selective_state_space_04_amd as ssd
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator().manual_seed(1005)
+    b, L, H, P = 4, 4096, 80, 64
+    y = torch.randn((b, L, H, P), generator=gen).to(torch.bfloat16).to(dev)
+    z = torch.randn((b, L, H, P), generator=gen).to(torch.bfloat16).to(dev)
+    wt = torch.randn(H * P, generator=gen).to(dev)
+    out = torch.empty_like(y)
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        ssd.gated_rmsnorm(y, z, wt, out=out)
+    torch.cuda.synchronize()
+    ms = []
+    for k in range(args.steps):
+        if flush is not None:
+            flush.fill_(k & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ssd.gated_rmsnorm(y, z, wt, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    avg = statistics.mean(ms)
+    nbytes = 3 * b * L * H * P * 2 + H * P * 4
+    achieved = nbytes / (avg * 1e-3) / 1e9
+    res = {"metric": "gated RMSNorm tokens/s, [4,4096,80,64] bf16", "value": b * L / (avg * 1e-3),
+           "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": avg,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic", "config": {"workload": "gated RMSNorm after the SSD output", "batch": b,
+                                           "seqlen": L, "nheads": H, "headdim": P, "norm_groups": 1,
+                                           "mall_flushed": flush is not None},
+           "roofline": {"kernel": "gated_rmsnorm", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("gated_norm"),
+                        "alg_bytes_per_launch": nbytes, "avg_launch_us": avg * 1e3}}
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = 2048
+        yc = y.reshape(-1, H, P)[:rows].cpu()
+        zc = z.reshape(-1, H, P)[:rows].cpu()
+        t0 = time.perf_counter()
+        oracle.gated_rmsnorm(yc, zc, wt.cpu())
+        t = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": rows / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{rows} of {b * L} token rows, numpy float64, {t:.2f} s"}
+    return res
+
+
 def run_decode_bench(args):
     import torch
 
@@ -540,6 +598,8 @@ def main():
         res = run_forward_bench(args)
     elif args.workload == "backward":
         res = run_backward_bench(args)
+    elif args.workload == "gated_norm":
+        res = run_gated_norm_bench(args)
     elif args.workload == "decode":
         res = run_decode_bench(args)
     else:

@@ -194,6 +194,24 @@ ssd_status ssd_decode_step(const ssd_dims *dims, float *state, const void *x, co
                            void *y, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Normalisation after the gate (review page, section "Mamba-2 ブロック": one
+ * normalisation layer after the SSM output is multiplied by the gate, before
+ * the output projection; Mamba review page, section 3.4: the gate is SiLU of a
+ * second projection z).  The kind of normalisation is not stated; this is
+ * the root-mean-square one.  For every token (b, t), over its H * P channels
+ * c = h * P + p split into norm_groups equal contiguous groups:
+ *   g_c   = y_c * z_c / (1 + exp(-z_c))
+ *   out_c = g_c / sqrt(mean over c's group of g^2 + eps) * weight[c]
+ * y, z, out [batch, seqlen, nheads, headdim] in dtype (dims->dstate, ngroups
+ * and chunk are checked as for the forward but otherwise unused); weight
+ * [nheads * headdim] float32.  out may be y itself (in place) but must not
+ * otherwise overlap y, z or weight.  (H * P / norm_groups) must be a
+ * multiple of 8 and eps >= 0 (else SSD_ERR_SHAPE).
+ * ---------------------------------------------------------------------- */
+ssd_status ssd_gated_rmsnorm(const ssd_dims *dims, int64_t norm_groups, float eps, const void *y,
+                             const void *z, const float *weight, void *out, void *stream);
+
+/* ------------------------------------------------------------------------
  * Gradient of the layer (reverse-mode differentiation of the map that
  * ssd_forward evaluates; the pages define the forward map, in the review
  * page's sections "SSM を一つの行列として書く" and "2つのルートを半分ずつ", and the

@@ -12,6 +12,7 @@ Contents
   (``ssd_recurrence.c``), parallel over independent (batch, head) sequences.
 * ``backward``: reverse-mode differentiation of that recurrence, step by
   step in reverse order (``ssd_backward.c``), float64.
+* ``gated_rmsnorm``: the normalisation after the gate (numpy float64).
 * ``preprocess_dt`` / ``forward_ex`` / ``decode_step_ex``: the step size
   through bias, softplus and clamp, and the Euler or zero-order-hold input
   scale, ahead of the same recurrence (numpy float64).
@@ -210,6 +211,30 @@ def decode_step_ex(state, x, dt, A, B, C, D=None, dt_bias=None, softplus=False, 
     if D is not None:
         y = y + _f64(D)[None, :, None] * x
     return y, state
+
+
+def gated_rmsnorm(y, z, weight, norm_groups: int = 1, eps: float = 1e-5):
+    """The normalisation after the gate, float64.
+
+    The review page (section "Mamba-2 ブロック") adds one normalisation layer
+    after the SSM output is multiplied by the gate and before the output
+    projection; the Mamba review (section 3.4) gates with SiLU of a second
+    projection z.  Reading (the kind of normalisation is not stated): per
+    token, g = y * silu(z) over its H * P channels, split into norm_groups
+    equal contiguous groups, each scaled to unit root mean square,
+      out = g / sqrt(mean_group(g^2) + eps) * weight.
+    y, z [..., H, P]; weight [H * P].  Returns out, shaped like y.
+    """
+    y, z, w = _f64(y), _f64(z), _f64(weight)
+    shp = y.shape
+    D = shp[-2] * shp[-1]
+    if D % norm_groups:
+        raise ValueError("norm_groups must divide H * P")
+    g = y * (z / (1.0 + np.exp(-z)))                     # silu(z) = z sigmoid(z)
+    g = g.reshape(-1, norm_groups, D // norm_groups)
+    ms = np.mean(g * g, axis=-1, keepdims=True)
+    out = g / np.sqrt(ms + eps) * w.reshape(1, norm_groups, D // norm_groups)
+    return out.reshape(shp)
 
 
 def decode_step(state, x, dt, A, B, C, D=None):

@@ -72,6 +72,7 @@ _SIGS = {
     "ssd_forward_staged_ex": (ctypes.c_int, [_dp, _vp] + [_vp] * 10 + [ctypes.c_size_t, _vp]),
     "ssd_decode_step_ex": (ctypes.c_int, [_dp, _vp] + [_vp] * 9),
     "ssd_validate_forward_ex": (ctypes.c_int, [_dp, _vp] + [_vp] * 10 + [ctypes.c_size_t]),
+    "ssd_gated_rmsnorm": (ctypes.c_int, [_dp, ctypes.c_int64, ctypes.c_float] + [_vp] * 5),
     "ssd_backward_launch_count": (ctypes.c_int, [_dp]),
     "ssd_backward_launch_name": (ctypes.c_char_p, [_dp, ctypes.c_int]),
     "ssd_backward_timed": (ctypes.c_int, [_dp] + [_vp] * 17 + [ctypes.c_size_t, _vp, _vp, ctypes.c_int]),
@@ -242,6 +243,30 @@ def backward(x, dt, A, B, C, dy, D=None, init_state=None, dfinal_state=None, chu
                             _p(init_state), _p(dy), _p(dfinal_state), _p(out["dx"]), _p(out["ddt"]),
                             _p(out["dA"]), _p(out["dB"]), _p(out["dC"]), _p(out.get("dD")),
                             _p(out.get("dinit")), _p(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def gated_rmsnorm(y, z, weight, norm_groups: int = 1, eps: float = 1e-5, out=None):
+    """out = RMSNorm(y * silu(z)) * weight per token over its H * P channels
+    (norm_groups equal groups).  y, z [b, L, H, P] (or [b, H, P] for one
+    token), weight [H * P] float32.  out may be y (in place)."""
+    if y.dim() == 3:
+        y4, z4 = y.unsqueeze(1), z.unsqueeze(1)
+    else:
+        y4, z4 = y, z
+    if y4.dim() != 4 or y.dtype not in _DT:
+        raise ValueError("y must be [b, L, H, P] or [b, H, P] float32 / bfloat16")
+    b, L, H, P = y4.shape
+    _need(z, "z", y.shape, y.dtype, y.device)
+    _need(weight, "weight", (H * P,), torch.float32, y.device)
+    _need(y, "y", y.shape, y.dtype, y.device)
+    if out is None:
+        out = torch.empty_like(y)
+    else:
+        _need(out, "out", y.shape, y.dtype, y.device)
+    dims = make_dims(b, L, H, P, 16, 1, 16, _DT[y.dtype])
+    _check(lib.ssd_gated_rmsnorm(ctypes.byref(dims), int(norm_groups), float(eps), _p(y), _p(z), _p(weight),
+                                 _p(out), _stream()))
     return out
 
 

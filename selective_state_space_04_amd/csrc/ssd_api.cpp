@@ -575,6 +575,26 @@ ssd_status ssd_forward_main(const ssd_dims *dims, const void *x, const void *dt,
                           (hipStream_t)stream);
 }
 
+ssd_status ssd_gated_rmsnorm(const ssd_dims *dims, int64_t norm_groups, float eps, const void *y,
+                             const void *z, const float *weight, void *out, void *stream) {
+    ssd::Dims d;
+    ssd_status st = check_dims(dims, false, &d);
+    if (st != SSD_OK) return st;
+    const int64_t D = d.H * d.P;
+    if (norm_groups < 1 || D % norm_groups != 0 || (D / norm_groups) % 8 != 0) return SSD_ERR_SHAPE;
+    if (!(eps >= 0.f)) return SSD_ERR_SHAPE;
+    if (d.b * d.L == 0) return SSD_OK;
+    if (d.b * d.L > INT32_MAX) return SSD_ERR_UNSUPPORTED;
+    const void *req[] = {y, z, weight, out};
+    if ((st = validate_ptrs(req, 4, nullptr, 0)) != SSD_OK) return st;
+    const int64_t bytes = d.b * d.L * D * esize(d);
+    const Range ro = range_of(out, bytes), ry = range_of(y, bytes), rz = range_of(z, bytes),
+                rw = range_of(weight, D * 4);
+    if (overlap(ro, rz) || overlap(ro, rw) || (overlap(ro, ry) && out != y)) return SSD_ERR_ALIAS;
+    return hip_status(
+        ssd::launch_gated_rmsnorm(d, norm_groups, eps, y, z, weight, out, (hipStream_t)stream));
+}
+
 size_t ssd_backward_workspace_bytes(const ssd_dims *dims) {
     ssd::Dims d;
     if (check_dims(dims, false, &d) != SSD_OK) return 0;

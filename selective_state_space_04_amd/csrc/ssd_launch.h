@@ -42,6 +42,10 @@ hipError_t launch_fused_main(const Dims &d, const void *x, const void *dt, const
                              hipStream_t st, const DtOpts *o = nullptr);
 hipError_t launch_zero_state(const Dims &d, const float *init, float *fin, hipStream_t st);
 
+// Normalisation after the gate (ssd_epilogue.hip).
+hipError_t launch_gated_rmsnorm(const Dims &d, int64_t ngroups, float eps, const void *y,
+                                const void *z, const float *w, void *out, hipStream_t st);
+
 // Gradient kernels (ssd_backward.hip).
 hipError_t launch_state_passing_rev(const Dims &d, float *S, const float *cs, const float *dfinal,
                                     float *dinit, hipStream_t st);

@@ -308,3 +308,18 @@ def test_make_options_defaults_are_the_plain_map():
     assert (o.dt_softplus, o.input_scale) == (1, 2) and abs(o.dt_max - 0.5) < 1e-7
     with pytest.raises(ValueError):
         ssd.make_options(A, input_scale="bilinear")
+
+
+def test_gated_rmsnorm_validation():
+    d = dims()                                     # H * P = 256
+    b = Bufs()
+    y, z, w, out = b.take(), b.take(), b.take(), b.take()
+    f = lambda dd, g, e, *p: ssd.STATUS[LIB.ssd_gated_rmsnorm(ctypes.byref(dd), g, e, *p, None)]
+    assert f(d, 3, 1e-5, y, z, w, out) == "SSD_ERR_SHAPE"          # 3 does not divide 256
+    assert f(d, 64, 1e-5, y, z, w, out) == "SSD_ERR_SHAPE"         # groups of 4 channels
+    assert f(d, 1, -1.0, y, z, w, out) == "SSD_ERR_SHAPE"
+    assert f(d, 1, 1e-5, y, z, None, out) == "SSD_ERR_NULL"
+    assert f(d, 1, 1e-5, y, z, w, z) == "SSD_ERR_ALIAS"
+    assert f(d, 1, 1e-5, y, z, w, y + 16) == "SSD_ERR_ALIAS"
+    assert f(d, 1, 1e-5, y + 8, z, w, out) == "SSD_ERR_ALIGN"
+    assert f(dims(seqlen=0), 1, 1e-5, None, None, None, None) == "SSD_OK"

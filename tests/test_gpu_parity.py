@@ -682,3 +682,53 @@ def test_forward_options_full_size_2p7b_layer(ssd):
     e = (worst_rel(f64(y), y_ref, "y"), worst_rel(f64(fin), f_ref, "state"))
     print("full-size forward with options:", e, flush=True)
     assert max(e) < TOL["bf16"]
+
+
+# ------------------------------------------------------------------ gated normalisation
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("groups", [1, 2, 8])
+def test_gated_rmsnorm(ssd, dtype, groups):
+    w = small(dtype, batch=3, seqlen=37, nheads=8, headdim=64, seed=31)
+    g = torch.Generator().manual_seed(31)
+    dt_ = si.DTYPES[dtype]
+    y = torch.randn((3, 37, 8, 64), generator=g).to(dt_)
+    z = torch.randn((3, 37, 8, 64), generator=g).to(dt_)
+    wt = torch.randn(8 * 64, generator=g)
+    out = ssd.gated_rmsnorm(dev(y), dev(z), dev(wt), norm_groups=groups, eps=1e-5)
+    torch.cuda.synchronize()
+    ref = oracle.gated_rmsnorm(y, z, wt, norm_groups=groups, eps=1e-5)
+    assert worst_rel(f64(out), ref, "y") < TOL[dtype]
+    # in place, and one token per call (decode)
+    yy = dev(y).clone()
+    ssd.gated_rmsnorm(yy, dev(z), dev(wt), norm_groups=groups, eps=1e-5, out=yy)
+    o1 = ssd.gated_rmsnorm(dev(y[:, 5].contiguous()), dev(z[:, 5].contiguous()), dev(wt), norm_groups=groups)
+    torch.cuda.synchronize()
+    assert torch.equal(yy.cpu(), out.cpu())
+    assert worst_rel(f64(o1)[:, None], ref[:, 5:6], "y") < TOL[dtype]
+
+
+def test_gated_rmsnorm_2p7b_layer_rows(ssd):
+    """The 2.7B-layer output shape ([4, 4096, 80, 64] bf16, H * P = 5120)."""
+    g = torch.Generator().manual_seed(32)
+    y = torch.randn((4, 4096, 80, 64), generator=g).to(torch.bfloat16)
+    z = torch.randn((4, 4096, 80, 64), generator=g).to(torch.bfloat16)
+    wt = torch.randn(5120, generator=g)
+    out = ssd.gated_rmsnorm(dev(y), dev(z), dev(wt))
+    torch.cuda.synchronize()
+    rows = [0, 1, 4095, 8191, 16383]
+    yr, zr = y.reshape(-1, 80, 64)[rows], z.reshape(-1, 80, 64)[rows]
+    ref = oracle.gated_rmsnorm(yr, zr, wt)
+    got = f64(out.reshape(-1, 80, 64)[rows])
+    assert worst_rel(got[:, None], ref[:, None], "y") < TOL["bf16"]
+
+
+def test_forward_full_size_2p7b_layer_8_groups(ssd):
+    """The 2.7B-layer shape with 8 B/C groups (10 heads per group) at full
+    size, single-pass route, against the full oracle."""
+    w = si.WORKLOADS[2].with_(ngroups=8)
+    inp = si.make_forward_inputs(w)
+    y, fin = run_forward(ssd, inp, w.chunk)
+    y_ref, f_ref = oracle_forward(inp)
+    e = (worst_rel(f64(y), y_ref, "y"), worst_rel(f64(fin), f_ref, "state"))
+    print("full-size forward, 8 groups:", e, flush=True)
+    assert max(e) < TOL["bf16"]

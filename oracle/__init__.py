@@ -13,6 +13,8 @@ Contents
 * ``backward``: reverse-mode differentiation of that recurrence, step by
   step in reverse order (``ssd_backward.c``), float64.
 * ``gated_rmsnorm``: the normalisation after the gate (numpy float64).
+* ``selective_scan``: the Mamba-1 scan with a diagonal A per channel, its
+  skip term and gate (``selective_scan.c``, float64).
 * ``preprocess_dt`` / ``forward_ex`` / ``decode_step_ex``: the step size
   through bias, softplus and clamp, and the Euler or zero-order-hold input
   scale, ahead of the same recurrence (numpy float64).
@@ -36,6 +38,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_recurrence.c")
 _SRC_BWD = os.path.join(_HERE, "ssd_backward.c")
+_SRC_SCAN = os.path.join(_HERE, "selective_scan.c")
 _LIB_PATH = os.path.join(_HERE, "_build", "libssd_oracle.so")
 _lib = None
 
@@ -46,7 +49,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-                               _SRC, _SRC_BWD, "-o", tmp, "-lm"])
+                               _SRC, _SRC_BWD, _SRC_SCAN, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -62,6 +65,8 @@ def _load():
         lib.ssd_oracle_forward.restype = ctypes.c_int
         lib.ssd_oracle_backward.argtypes = [i64] * 6 + [dp] * 16
         lib.ssd_oracle_backward.restype = ctypes.c_int
+        lib.ssd_oracle_selective_scan.argtypes = [i64] * 5 + [dp] * 8 + [i64] + [dp] * 3
+        lib.ssd_oracle_selective_scan.restype = ctypes.c_int
         lib.ssd_oracle_decode_step.argtypes = [i64] * 5 + [dp] * 8
         lib.ssd_oracle_decode_step.restype = ctypes.c_int
         lib.ssd_oracle_num_threads.restype = ctypes.c_int
@@ -211,6 +216,29 @@ def decode_step_ex(state, x, dt, A, B, C, D=None, dt_bias=None, softplus=False, 
     if D is not None:
         y = y + _f64(D)[None, :, None] * x
     return y, state
+
+
+def selective_scan(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+                   init=None):
+    """The selective (Mamba-1) scan in float64 (``selective_scan.c``).
+
+    x, delta, z [b, L, Dch]; A [Dch, N]; B, C [b, L, G, N] (or [b, L, N] for
+    one group); D, delta_bias [Dch]; init [b, Dch, N].  Returns (y, final).
+    """
+    x, delta, A, B, C, D, z, delta_bias, init = (_f64(v) for v in (x, delta, A, B, C, D, z, delta_bias, init))
+    if B.ndim == 3:
+        B, C = B[:, :, None, :], C[:, :, None, :]
+    b, L, Dch = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert A.shape == (Dch, N) and delta.shape == x.shape and C.shape == B.shape
+    y = np.empty((b, L, Dch))
+    final = np.empty((b, Dch, N))
+    rc = _load().ssd_oracle_selective_scan(b, L, Dch, N, G, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                           _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)),
+                                           _ptr(init), _ptr(y), _ptr(final))
+    if rc != 0:
+        raise ValueError("oracle selective_scan: bad shape")
+    return y, final
 
 
 def gated_rmsnorm(y, z, weight, norm_groups: int = 1, eps: float = 1e-5):

@@ -12,8 +12,11 @@ alone.  Prints one JSON line.
 Other modes: ``--workload backward`` (the gradient of the same layer at the
 same shape: ``ssd_backward`` with dy drawn N(0, 1), D present, no initial or
 final state, as in training), ``--workload decode`` (512 single-token steps
-on a [256, 80, 64, 128] float32 state) and ``--workload copy`` (a plain
-device-to-device copy used to calibrate hardware byte counters).
+on a [256, 80, 64, 128] float32 state), ``--workload gated_norm`` (the
+normalisation after the gate on the forward's output), ``--workload scan``
+(the selective Mamba-1 scan on the 2.8B-layer shape: batch 4, L 4096, 5120
+channels, N 16) and ``--workload copy`` (a plain device-to-device copy used
+to calibrate hardware byte counters).
 """
 from __future__ import annotations
 
@@ -37,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["forward", "backward", "decode", "gated_norm", "copy"],
+    ap.add_argument("--workload", choices=["forward", "backward", "decode", "gated_norm", "scan", "copy"],
                     default="forward")
     ap.add_argument("--ngroups", type=int, default=0,
                     help="forward: B/C groups (0 = the workload's own, 1)")
@@ -45,6 +48,8 @@ def parse():
     ap.add_argument("--options", choices=["none", "mamba2", "zoh"], default="none",
                     help="forward step-size options: mamba2 = dt_bias + softplus + Euler input "
                          "scale; zoh = zero-order-hold input scale (ssd_forward_ex)")
+    ap.add_argument("--scan-algo", choices=["auto", "segments", "rows"], default="auto",
+                    help="scan: the arrangement (ssd_scan_dims.algo)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
@@ -517,6 +522,150 @@ def run_gated_norm_bench(args):
                                "sample": f"{rows} of {b * L} token rows, numpy float64, {t:.2f} s"}
     return res
 
+# Vector-ALU issue rate of the chip: 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz,
+# one full-rate fp32 operation per lane per clock (packed fp32 is not used),
+# the exponential (v_exp_f32) at half that rate (measured on gfx950: 19.0 T
+# exp/s against 38.1 T fma/s on the whole chip).
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+EXP_RATE = 0.5
+SCAN_FLOPS_PER_UPDATE = 7      # dt*A, exp, (dt x)*B, fma into h, fma C.h into y (fma = 2)
+SCAN_SLOTS_PER_UPDATE = 4 + 1 / EXP_RATE  # issue slots of those five operations
+SCAN_PEAK_TFLOPS = SCAN_FLOPS_PER_UPDATE * VALU_LANE_OPS / SCAN_SLOTS_PER_UPDATE / 1e12
+
+
+def scan_inputs(b, L, Dch, N, seed=4077):
+    """Seeded inputs of the Mamba-1 layer shape: x, z ~ N(0, 1); B, C ~
+    N(0, 1)/sqrt(N) (one group); A = -U(1, 16) per (channel, state); the
+    step log-uniform in [1e-3, 1e-1], given raw (inverse softplus minus the
+    bias, bias ~ N(0, 0.25)); D ~ N(0, 1)."""
+    import math
+
+    import torch
+
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((b, L, Dch), generator=g)
+    Bm = torch.randn((b, L, 1, N), generator=g) / math.sqrt(N)
+    Cm = torch.randn((b, L, 1, N), generator=g) / math.sqrt(N)
+    A = -(torch.rand((Dch, N), generator=g) * 15 + 1)
+    step = torch.exp(torch.rand((b, L, Dch), generator=g) * (math.log(1e-1) - math.log(1e-3)) + math.log(1e-3))
+    bias = torch.randn(Dch, generator=g) * 0.5
+    delta = torch.log(torch.expm1(step)) - bias
+    D = torch.randn(Dch, generator=g)
+    z = torch.randn((b, L, Dch), generator=g)
+    bf = torch.bfloat16
+    return dict(x=x.to(bf), delta=delta.to(bf), A=A, B=Bm.to(bf), C=Cm.to(bf), D=D, z=z.to(bf), delta_bias=bias)
+
+
+def run_scan_bench(args):
+    """The selective scan on the Mamba-2.8B layer shape (batch 4, L 4096,
+    5120 channels, N 16, bf16 inputs, softplus step with bias, D and the
+    SiLU gate, no initial state, final state written)."""
+    import ctypes
+
+    import torch
+
+    import selective_state_space_04_amd as ssd
+
+    b, L, Dch, N = 4, 4096, 5120, 16
+    dev = torch.device("cuda:0")
+    host = scan_inputs(b, L, Dch, N)
+    c = {k: v.to(dev) for k, v in host.items()}
+    y = torch.empty_like(c["x"])
+    fin = torch.empty((b, Dch, N), dtype=torch.float32, device=dev)
+    dims = ssd.ScanDims(b, L, Dch, N, 1, ssd.BF16, ssd.SCAN_ALGOS[args.scan_algo])
+    dp = ctypes.byref(dims)
+    ws = torch.empty(max(int(ssd.lib.ssd_selective_scan_workspace_bytes(dp)), 1), dtype=torch.uint8, device=dev)
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    p = ssd._p
+    args_abi = lambda: (dp, p(c["x"]), p(c["delta"]), p(c["A"]), p(c["B"]), p(c["C"]), p(c["D"]), p(c["z"]),
+                        p(c["delta_bias"]), 1, None, p(y), p(fin), p(ws), ws.numel(), ssd._stream())
+
+    def step():
+        st = ssd.lib.ssd_selective_scan(*args_abi())
+        if st != 0:
+            raise RuntimeError(f"ssd_selective_scan: status {st}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        if flush is not None:
+            flush.fill_(k & 0xFF)
+        starts[k].record()
+        step()
+        ends[k].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(e) for a, e in zip(starts, ends)]
+    ms_per_step = statistics.mean(ms)
+    updates = b * L * Dch * N
+    alg_bytes = 4 * b * L * Dch * 2 + 2 * b * L * N * 2 + Dch * N * 4 + 2 * Dch * 4 + b * Dch * N * 4
+    t_alu = updates * SCAN_SLOTS_PER_UPDATE / VALU_LANE_OPS * 1e6
+    t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e3)
+    res = {
+        "metric": "selective scan tokens/s at D=5120,N=16,L=4096; % of ALU roofline", "value": b * L /
+        (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded; distributions of the layer)",
+        "config": {"workload": "Mamba-2.8B-layer-shaped selective scan", "batch": b, "seqlen": L,
+                   "channels": Dch, "dstate": N, "ngroups": 1, "inputs": "bf16", "accumulate": "fp32",
+                   "step": "softplus(delta + bias)", "D": True, "gate": True, "mall_flushed": flush is not None},
+        "scan_roofline": {"bound": "alu" if t_alu >= t_hbm else "hbm", "t_alu_us": t_alu, "t_hbm_us": t_hbm,
+                          "frac": max(t_alu, t_hbm) / (ms_per_step * 1e3), "updates": updates,
+                          "alg_bytes": alg_bytes},
+        "ms_min": min(ms), "ms_median": statistics.median(ms), "wall_s": wall,
+    }
+    if not args.no_kernel_timing:
+        hip = ctypes.CDLL("libamdhip64.so")
+        algo = ssd.lib.ssd_selective_scan_algo(dp)
+        names = ["scan_seg_state", "scan_pass", "scan_seg_out"] if algo == 1 else ["scan_bc_transpose", "scan_rows"]
+        res["config"]["algo"] = "segments" if algo == 1 else "rows"
+        nev = len(names) + 1
+        evs = (ctypes.c_void_p * nev)()
+        for i in range(nev):
+            if hip.hipEventCreate(ctypes.byref(evs, i * ctypes.sizeof(ctypes.c_void_p))) != 0:
+                raise RuntimeError("hipEventCreate failed")
+        times = {nm: [] for nm in names}
+        for rep in range(max(args.steps, 5) + 2):
+            if flush is not None:
+                flush.fill_(rep & 0xFF)
+            st = ssd.lib.ssd_selective_scan_timed(*args_abi(), evs, nev)
+            if st != 0:
+                raise RuntimeError(f"ssd_selective_scan_timed: status {st}")
+            torch.cuda.synchronize()
+            if rep >= 2:
+                for i, nm in enumerate(names):
+                    f = ctypes.c_float()
+                    hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(evs[i]), ctypes.c_void_p(evs[i + 1]))
+                    times[nm].append(f.value * 1e3)
+        for i in range(nev):
+            hip.hipEventDestroy(ctypes.c_void_p(evs[i]))
+        avg = {nm: statistics.mean(v) for nm, v in times.items()}
+        # the dominant kernel runs every update once (rows: the whole scan;
+        # segments: the output pass, which rescans from the entering states)
+        dom = names[-1]
+        us = avg[dom]
+        achieved = updates * SCAN_FLOPS_PER_UPDATE / (us * 1e-6) / 1e12
+        res["roofline"] = {"kernel": dom, "bound": "alu", "achieved": achieved,
+                           "peak": SCAN_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / SCAN_PEAK_TFLOPS,
+                           "traffic": measured_traffic(dom),
+                           "alg_flops_per_launch": updates * SCAN_FLOPS_PER_UPDATE, "avg_launch_us": us}
+        res["kernels_us"] = avg
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        oracle.selective_scan(host["x"], host["delta"], host["A"], host["B"], host["C"], host["D"], host["z"],
+                              host["delta_bias"], True)
+        t = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": b * L / t, "unit": "tokens/s", "cores": oracle.num_threads(),
+                               "kind": "oracle", "sample": f"the full workload ({b}x{L} tokens, {Dch} channels), "
+                               f"float64 sequential recurrence, {t:.2f} s"}
+    return res
+
+
 
 def run_decode_bench(args):
     import torch
@@ -602,6 +751,8 @@ def main():
         res = run_gated_norm_bench(args)
     elif args.workload == "decode":
         res = run_decode_bench(args)
+    elif args.workload == "scan":
+        res = run_scan_bench(args)
     else:
         res = run_copy(args)
     print(json.dumps(res))

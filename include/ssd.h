@@ -194,6 +194,70 @@ ssd_status ssd_decode_step(const ssd_dims *dims, float *state, const void *x, co
                            void *y, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Selective scan (the Mamba-1 scan; Mamba review page, section 3.3): per
+ * batch row b and channel d, with a diagonal state matrix A[d, :] of N
+ * entries and group g = d / (channels / ngroups),
+ *   dt  = delta[b,t,d] + delta_bias[d];  dt = softplus(dt) if delta_softplus
+ *         (section 3.1: the step size is a softplus of a linear map)
+ *   h_t[n] = exp(dt A[d,n]) h_{t-1}[n] + dt x[b,t,d] B[b,t,g,n]
+ *   y[b,t,d] = (sum_n C[b,t,g,n] h_t[n] + D[d] x[b,t,d]) * silu(z[b,t,d])
+ *         (section 3.4: skip term D and the gate branch; no gate when z is
+ *         NULL)
+ * with h_{-1} = init_state (zeros when NULL); final_state receives h_{L-1}.
+ * Layouts: x, delta, z, y [batch, seqlen, channels] in dtype; A [channels,
+ * dstate] float32; B, C [batch, seqlen, ngroups, dstate] in dtype; D,
+ * delta_bias [channels] float32; states [batch, channels, dstate] float32.
+ * Nullable: D, z, delta_bias, init_state, final_state.  dstate in {4, 8, 16,
+ * 32, 64}; channels a multiple of ngroups, and (channels / ngroups) a
+ * multiple of 64 when ngroups > 1 (else SSD_ERR_UNSUPPORTED).  y must not
+ * overlap an input or final_state; final_state may be init_state itself.
+ * Workspace of ssd_selective_scan_workspace_bytes(dims) bytes, 256-byte
+ * aligned (segment end states and step sums).  Same stream and error rules
+ * as the layer entry points.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int64_t batch, seqlen, channels, dstate, ngroups;
+    int32_t dtype;  /* ssd_dtype of x, delta, z, B, C, y */
+    int32_t algo;   /* 0: default (segments); 1: segments (any dstate):
+                       segment end states, state passing, rescan with
+                       output; 2: rows (dstate 16, (seqlen + 16) * channels
+                       below 2^31, else SSD_ERR_UNSUPPORTED): one pass with
+                       a lane per (channel, state).  Both give the same
+                       results up to rounding; the workspace size depends
+                       on the choice. */
+} ssd_scan_dims;
+size_t ssd_selective_scan_workspace_bytes(const ssd_scan_dims *dims);
+/* The arrangement a call with these dims runs: 1 (segments: three launches,
+ * segment states, state passing, output) or 2 (rows: two launches, the
+ * B/C transpose and the scan); minus the ssd_status when dims are invalid. */
+int32_t ssd_selective_scan_algo(const ssd_scan_dims *dims);
+ssd_status ssd_selective_scan(const ssd_scan_dims *dims, const void *x, const void *delta,
+                              const float *A, const void *B, const void *C, const float *D,
+                              const void *z, const float *delta_bias, int32_t delta_softplus,
+                              const float *init_state, void *y, float *final_state,
+                              void *workspace, size_t workspace_bytes, void *stream);
+/* The same scan with timing marks: events[0] is recorded on the stream
+ * before the first launch and events[k] after launch k (segments: the
+ * segment-state, state-passing and output launches; rows: the B/C transpose
+ * and the scan), as hipEvent_t handles created by the caller, who reads them
+ * with hipEventElapsedTime.  Only the first n_events
+ * are recorded; where a launch is skipped (empty batch or sequence) its
+ * marks are recorded at once.  SSD_ERR_NULL when n_events > 0 and events is
+ * NULL, or n_events < 0. */
+ssd_status ssd_selective_scan_timed(const ssd_scan_dims *dims, const void *x, const void *delta,
+                                    const float *A, const void *B, const void *C, const float *D,
+                                    const void *z, const float *delta_bias, int32_t delta_softplus,
+                                    const float *init_state, void *y, float *final_state,
+                                    void *workspace, size_t workspace_bytes, void *stream,
+                                    void *const *events, int32_t n_events);
+ssd_status ssd_validate_selective_scan(const ssd_scan_dims *dims, const void *x, const void *delta,
+                                       const float *A, const void *B, const void *C,
+                                       const float *D, const void *z, const float *delta_bias,
+                                       const float *init_state, const void *y,
+                                       const float *final_state, const void *workspace,
+                                       size_t workspace_bytes);
+
+/* ------------------------------------------------------------------------
  * Normalisation after the gate (review page, section "Mamba-2 ブロック": one
  * normalisation layer after the SSM output is multiplied by the gate, before
  * the output projection; Mamba review page, section 3.4: the gate is SiLU of a

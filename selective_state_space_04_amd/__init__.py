@@ -73,6 +73,12 @@ _SIGS = {
     "ssd_decode_step_ex": (ctypes.c_int, [_dp, _vp] + [_vp] * 9),
     "ssd_validate_forward_ex": (ctypes.c_int, [_dp, _vp] + [_vp] * 10 + [ctypes.c_size_t]),
     "ssd_gated_rmsnorm": (ctypes.c_int, [_dp, ctypes.c_int64, ctypes.c_float] + [_vp] * 5),
+    "ssd_selective_scan_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
+    "ssd_selective_scan_algo": (ctypes.c_int32, [ctypes.c_void_p]),
+    "ssd_selective_scan": (ctypes.c_int, [_vp] * 9 + [ctypes.c_int32] + [_vp] * 4 + [ctypes.c_size_t, _vp]),
+    "ssd_validate_selective_scan": (ctypes.c_int, [_vp] * 13 + [ctypes.c_size_t]),
+    "ssd_selective_scan_timed": (ctypes.c_int, [_vp] * 9 + [ctypes.c_int32] + [_vp] * 4
+                                 + [ctypes.c_size_t, _vp, _vp, ctypes.c_int32]),
     "ssd_backward_launch_count": (ctypes.c_int, [_dp]),
     "ssd_backward_launch_name": (ctypes.c_char_p, [_dp, ctypes.c_int]),
     "ssd_backward_timed": (ctypes.c_int, [_dp] + [_vp] * 17 + [ctypes.c_size_t, _vp, _vp, ctypes.c_int]),
@@ -244,6 +250,55 @@ def backward(x, dt, A, B, C, dy, D=None, init_state=None, dfinal_state=None, chu
                             _p(out["dA"]), _p(out["dB"]), _p(out["dC"]), _p(out.get("dD")),
                             _p(out.get("dinit")), _p(workspace), workspace.numel(), _stream()))
     return out
+
+
+SCAN_ALGOS = {"auto": 0, "segments": 1, "rows": 2}
+
+
+class ScanDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("channels", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("algo", ctypes.c_int32)]
+
+
+def selective_scan(x, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: bool = False,
+                   init_state=None, *, y=None, final_state=None, want_final: bool = True, workspace=None,
+                   algo: str = "auto"):
+    """The selective (Mamba-1) scan, ssd_selective_scan.  x, delta, z
+    [b, L, Dch]; A [Dch, N] float32; B, C [b, L, G, N] (or [b, L, N]); D,
+    delta_bias [Dch] float32; init_state [b, Dch, N] float32.  algo: "auto",
+    "segments" or "rows" (N = 16 only).  Returns (y, final_state)."""
+    if x.dim() != 3 or x.dtype not in _DT:
+        raise ValueError("x must be [b, L, channels] float32 / bfloat16")
+    if B.dim() == 3:
+        B, C = B.unsqueeze(2), C.unsqueeze(2)
+    b, L, Dch = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    _need(x, "x", (b, L, Dch), x.dtype, dev)
+    _need(delta, "delta", (b, L, Dch), x.dtype, dev)
+    _need(A, "A", (Dch, N), torch.float32, dev)
+    _need(B, "B", (b, L, G, N), x.dtype, dev)
+    _need(C, "C", (b, L, G, N), x.dtype, dev)
+    for t, nm in ((D, "D"), (delta_bias, "delta_bias")):
+        if t is not None:
+            _need(t, nm, (Dch,), torch.float32, dev)
+    if z is not None:
+        _need(z, "z", (b, L, Dch), x.dtype, dev)
+    if init_state is not None:
+        _need(init_state, "init_state", (b, Dch, N), torch.float32, dev)
+    dims = ScanDims(b, L, Dch, N, G, _DT[x.dtype], SCAN_ALGOS[algo])
+    if y is None:
+        y = torch.empty_like(x)
+    if final_state is None and want_final:
+        final_state = torch.empty((b, Dch, N), dtype=torch.float32, device=dev)
+    nbytes = int(lib.ssd_selective_scan_workspace_bytes(ctypes.byref(dims)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib.ssd_selective_scan(ctypes.byref(dims), _p(x), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z),
+                                  _p(delta_bias), int(bool(delta_softplus)), _p(init_state), _p(y),
+                                  _p(final_state), _p(workspace), workspace.numel(), _stream()))
+    return y, final_state
 
 
 def gated_rmsnorm(y, z, weight, norm_groups: int = 1, eps: float = 1e-5, out=None):

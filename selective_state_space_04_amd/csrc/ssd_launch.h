@@ -42,6 +42,21 @@ hipError_t launch_fused_main(const Dims &d, const void *x, const void *dt, const
                              hipStream_t st, const DtOpts *o = nullptr);
 hipError_t launch_zero_state(const Dims &d, const float *init, float *fin, hipStream_t st);
 
+// Selective (Mamba-1) scan (ssd_scan.hip).  algo 1 = segments (seg steps per
+// segment, nseg segments per sequence; S = segment states, sdl = step sums);
+// algo 2 = rows (N = 16; S = B and C transposed to float32 [b, G, N, Lp], Lp
+// = L rounded up to 16, B first).
+struct ScanDims {
+    int64_t b, L, Dch, N, G, seg, nseg, Lp;
+    int dtype;  // 0 = f32, 1 = bf16
+    int algo;
+};
+hipError_t launch_selective_scan(const ScanDims &d, const void *x, const void *delta,
+                                 const float *A, const void *B, const void *C, const float *D,
+                                 const void *z, const float *dbias, int softplus,
+                                 const float *init, void *y, float *fin, float *S, float *sdl,
+                                 hipStream_t st, void *const *marks = nullptr, int nmarks = 0);
+
 // Normalisation after the gate (ssd_epilogue.hip).
 hipError_t launch_gated_rmsnorm(const Dims &d, int64_t ngroups, float eps, const void *y,
                                 const void *z, const float *w, void *out, hipStream_t st);

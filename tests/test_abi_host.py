@@ -323,3 +323,44 @@ def test_gated_rmsnorm_validation():
     assert f(d, 1, 1e-5, y, z, w, y + 16) == "SSD_ERR_ALIAS"
     assert f(d, 1, 1e-5, y + 8, z, w, out) == "SSD_ERR_ALIGN"
     assert f(dims(seqlen=0), 1, 1e-5, None, None, None, None) == "SSD_OK"
+
+
+def test_selective_scan_validation():
+    sd = lambda **kw: ssd.ScanDims(**{**dict(batch=2, seqlen=300, channels=128, dstate=16, ngroups=1,
+                                            dtype=ssd.BF16), **kw})
+    b = Bufs()
+    p = {k: b.take() for k in ("x", "dl", "A", "B", "C", "D", "z", "bias", "init", "y", "fin", "ws")}
+    d = sd()
+    wsb = LIB.ssd_selective_scan_workspace_bytes(ctypes.byref(d))
+    assert wsb > 0
+    v = lambda dd, **o: ssd.STATUS[LIB.ssd_validate_selective_scan(
+        ctypes.byref(dd), *[o.get(k, p[k]) for k in ("x", "dl", "A", "B", "C", "D", "z", "bias", "init", "y", "fin",
+                                                     "ws")], o.get("wsb", wsb))]
+    assert v(d) == "SSD_OK"
+    assert v(d, D=None, z=None, bias=None, init=None, fin=None) == "SSD_OK"
+    assert v(sd(dstate=12)) == "SSD_ERR_UNSUPPORTED"
+    assert v(sd(ngroups=2, channels=96)) == "SSD_ERR_UNSUPPORTED"      # 48 channels per group
+    assert v(sd(ngroups=3)) == "SSD_ERR_SHAPE"
+    assert v(sd(dtype=7)) == "SSD_ERR_DTYPE"
+    assert v(d, x=None) == "SSD_ERR_NULL"
+    assert v(d, y=p["x"]) == "SSD_ERR_ALIAS"
+    assert v(d, fin=p["init"]) == "SSD_OK"                              # in-place carry
+    assert v(d, fin=p["init"] + 64) == "SSD_ERR_ALIAS"
+    assert v(d, wsb=wsb - 1) == "SSD_ERR_WORKSPACE"
+    assert v(d, z=p["z"] + 2) == "SSD_ERR_ALIGN"
+    assert LIB.ssd_selective_scan_workspace_bytes(ctypes.byref(sd(seqlen=0))) == 0
+    # arrangements: rows needs N = 16; the workspace follows the choice
+    assert v(sd(algo=2)) in ("SSD_OK", "SSD_ERR_WORKSPACE")
+    assert v(sd(algo=2, dstate=8)) == "SSD_ERR_UNSUPPORTED"
+    assert v(sd(algo=3)) == "SSD_ERR_UNSUPPORTED"
+    rows = LIB.ssd_selective_scan_workspace_bytes(ctypes.byref(sd(algo=2)))
+    assert rows == 2 * 2 * 1 * 16 * 304 * 4                      # B and C as float32 [b, G, N, 304]
+    assert LIB.ssd_selective_scan_workspace_bytes(ctypes.byref(sd(algo=1))) == wsb
+    assert LIB.ssd_selective_scan_algo(ctypes.byref(sd(batch=4, seqlen=4096, channels=5120))) == 1
+    assert LIB.ssd_selective_scan_algo(ctypes.byref(sd(algo=2))) == 2
+    assert LIB.ssd_selective_scan_algo(ctypes.byref(sd(algo=2, dstate=8))) < 0
+    # segments: as many as fit 8192 waves, at least 32 steps each
+    big = sd(batch=4, seqlen=4096, channels=5120, algo=1)            # 4 x 80 blocks -> 25 segments of 164
+    al = lambda v: (v + 255) // 256 * 256
+    states, sums = 4 * 25 * 5120 * 16 * 4, 4 * 25 * 5120 * 4     # segment end states, step sums
+    assert LIB.ssd_selective_scan_workspace_bytes(ctypes.byref(big)) == al(al(states) + sums)

@@ -732,3 +732,124 @@ def test_forward_full_size_2p7b_layer_8_groups(ssd):
     e = (worst_rel(f64(y), y_ref, "y"), worst_rel(f64(fin), f_ref, "state"))
     print("full-size forward, 8 groups:", e, flush=True)
     assert max(e) < TOL["bf16"]
+
+
+# ------------------------------------------------------------------ selective (Mamba-1) scan
+def scan_inputs(dtype, b, L, Dch, N, G=1, seed=0, softplus=True, with_D=True, with_z=True, with_init=False):
+    """Seeded scan inputs: x, z ~ N(0, 1); B, C ~ N(0, 1)/sqrt(N); A = -U(1, 16);
+    the step as in the layer workloads (log-uniform in [1e-3, 1e-1]), given raw
+    (the inverse softplus minus a bias) when softplus is on."""
+    g = torch.Generator().manual_seed(4000 + seed)
+    dt_ = si.DTYPES[dtype]
+    x = torch.randn((b, L, Dch), generator=g)
+    B = torch.randn((b, L, G, N), generator=g) / math.sqrt(N)
+    C = torch.randn((b, L, G, N), generator=g) / math.sqrt(N)
+    A = -(torch.rand((Dch, N), generator=g) * 15 + 1)
+    step = torch.exp(torch.rand((b, L, Dch), generator=g) * (math.log(1e-1) - math.log(1e-3)) + math.log(1e-3))
+    bias = (torch.randn(Dch, generator=g) * 0.5) if softplus else None
+    delta = (torch.log(torch.expm1(step)) - bias) if softplus else step
+    D = torch.randn(Dch, generator=g) if with_D else None
+    z = torch.randn((b, L, Dch), generator=g).to(dt_) if with_z else None
+    init = torch.randn((b, Dch, N), generator=g) if with_init else None
+    return dict(x=x.to(dt_), delta=delta.to(dt_), A=A, B=B.to(dt_), C=C.to(dt_), D=D, z=z, delta_bias=bias,
+                delta_softplus=softplus, init_state=init)
+
+
+def run_scan(ssd, c, algo="auto"):
+    y, fin = ssd.selective_scan(**{k: (dev(v) if isinstance(v, torch.Tensor) else v) for k, v in c.items()},
+                                algo=algo)
+    torch.cuda.synchronize()
+    ref_y, ref_f = oracle.selective_scan(c["x"], c["delta"], c["A"], c["B"], c["C"], c["D"], c["z"],
+                                         c["delta_bias"], c["delta_softplus"], c["init_state"])
+    return f64(y), f64(fin), ref_y, ref_f
+
+
+def scan_err(a, r):
+    """Worst relative L2 error over the (b, channel) sequences of a [b, L,
+    Dch] array; for sequences under 64 steps, the relative L2 error of the
+    whole array (a single step can cancel the state term against the skip
+    term, with condition numbers in the hundreds, so one element's relative
+    error measures that element's conditioning rather than the scan)."""
+    if r.shape[1] < 64:
+        return float(np.linalg.norm(np.asarray(a, np.float64) - r) / max(np.linalg.norm(r), 1e-30))
+    return worst_rel(a[..., None], r[..., None], "y")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N,algo", [(4, "segments"), (8, "segments"), (16, "segments"), (16, "rows"),
+                                    (32, "segments"), (64, "segments")])
+def test_selective_scan(ssd, dtype, N, algo):
+    c = scan_inputs(dtype, 2, 700, 192, N, seed=N, with_init=True)
+    y, fin, ry, rf = run_scan(ssd, c, algo)
+    assert scan_err(y, ry) < TOL[dtype]
+    assert worst_rel(fin[..., None], rf[..., None], "state") < TOL[dtype]
+
+
+@pytest.mark.parametrize("algo", ["segments", "rows"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_selective_scan_plain_and_groups(ssd, dtype, algo):
+    """No step preprocessing, skip term or gate (the page's loop), two B/C groups."""
+    c = scan_inputs(dtype, 2, 333, 256, 16, G=2, seed=5, softplus=False, with_D=False, with_z=False)
+    y, fin, ry, rf = run_scan(ssd, c, algo)
+    assert scan_err(y, ry) < TOL[dtype]
+    assert worst_rel(fin[..., None], rf[..., None], "state") < TOL[dtype]
+
+
+@pytest.mark.parametrize("algo", ["segments", "rows"])
+@pytest.mark.parametrize("L,Dch", [(1, 64), (31, 100), (1025, 64), (0, 64), (17, 7)])
+def test_selective_scan_ragged(ssd, L, Dch, algo):
+    c = scan_inputs("f32", 1, L, Dch, 16, seed=L, with_init=True)
+    y, fin, ry, rf = run_scan(ssd, c, algo)
+    if L:
+        assert scan_err(y, ry) < 1e-5
+    assert worst_rel(fin[..., None], rf[..., None], "state") < 1e-5
+
+
+def test_selective_scan_step_extremes(ssd):
+    """Raw steps over [-40, 40] through softplus (both tails of the
+    log1p form), float32."""
+    c = scan_inputs("f32", 1, 256, 64, 16, seed=3)
+    g = torch.Generator().manual_seed(11)
+    c["delta"] = torch.rand(c["delta"].shape, generator=g) * 80 - 40
+    c["A"] = c["A"] * 0.01                     # keep the state alive at large steps
+    for algo in ("segments", "rows"):
+        y, fin, ry, rf = run_scan(ssd, c, algo)
+        assert scan_err(y, ry) < 1e-5, algo
+        assert worst_rel(fin[..., None], rf[..., None], "state") < 1e-5, algo
+
+
+def test_selective_scan_algos_agree(ssd):
+    """Both arrangements on the same inputs widened to float32 agree to
+    float32 rounding; the default on the bf16 inputs agrees with rows to the
+    output's bf16 rounding."""
+    c = scan_inputs("bf16", 2, 500, 4096, 16, seed=21, with_init=True)
+    cf = dict(c, x=c["x"].float(), delta=c["delta"].float(), B=c["B"].float(), C=c["C"].float(),
+              z=c["z"].float())
+    ya, fa, _, _ = run_scan(ssd, cf, "segments")
+    yb, fb, _, _ = run_scan(ssd, cf, "rows")
+    yc, fc, _, _ = run_scan(ssd, c, "auto")
+    assert scan_err(yb, ya) < 1e-5 and worst_rel(fb[..., None], fa[..., None], "state") < 1e-5
+    assert scan_err(yc, yb) < 1e-2
+
+
+def test_selective_scan_split_call(ssd):
+    c = scan_inputs("f32", 2, 600, 128, 16, seed=9, with_init=True)
+    y, fin, _, _ = run_scan(ssd, c)
+    sl = lambda k, a, b_: c[k][:, a:b_].contiguous()
+    c1 = dict(c, x=sl("x", 0, 250), delta=sl("delta", 0, 250), B=sl("B", 0, 250), C=sl("C", 0, 250), z=sl("z", 0, 250))
+    y1, f1, _, _ = run_scan(ssd, c1)
+    c2 = dict(c, x=sl("x", 250, 600), delta=sl("delta", 250, 600), B=sl("B", 250, 600), C=sl("C", 250, 600),
+              z=sl("z", 250, 600), init_state=torch.tensor(f1, dtype=torch.float32))
+    y2, f2, _, _ = run_scan(ssd, c2)
+    assert np.allclose(np.concatenate([y1, y2], 1), y, rtol=2e-5, atol=1e-6)
+    assert np.allclose(f2, fin, rtol=2e-5, atol=1e-6)
+
+
+def test_selective_scan_full_size_mamba_2p8b_layer(ssd):
+    """The Mamba-2.8B-layer shape (batch 4, L 4096, 5120 channels, N 16, bf16,
+    softplus step with bias, D, gate) at full size against the full oracle."""
+    c = scan_inputs("bf16", 4, 4096, 5120, 16, seed=77)
+    y, fin, ry, rf = run_scan(ssd, c)
+    e = (scan_err(y, ry), worst_rel(fin[..., None], rf[..., None], "state"))
+    print("full-size scan errors:", e, flush=True)
+    assert max(e) < TOL["bf16"]

@@ -853,3 +853,75 @@ def test_selective_scan_full_size_mamba_2p8b_layer(ssd):
     e = (scan_err(y, ry), worst_rel(fin[..., None], rf[..., None], "state"))
     print("full-size scan errors:", e, flush=True)
     assert max(e) < TOL["bf16"]
+
+
+# ------------------------------------------------------------------ graph capture
+def test_graph_capture_replays(ssd):
+    """Every entry point, captured once in a HIP graph (torch.cuda.graph) and
+    replayed three times with eager work and synchronisation between the
+    replays, reproduces its eager result bit for bit: the library launches
+    only kernels on the caller's stream (no memset, no allocation) and the
+    single-pass forward clears its own hand-off flags with a kernel."""
+    dev_ = torch.device(DEV)
+    w = si.Workload("graph", 2, 600, 8, 64, 128, 1, 256, "bf16", "normal", "normal", seed=77)
+    inp = {k: dev(v) for k, v in si.make_forward_inputs(w).items() if isinstance(v, torch.Tensor)}
+    x, dt, A, B, C, D, init = (inp[k] for k in ("x", "dt", "A", "B", "C", "D", "init"))
+    dy = dev(si.make_output_grads(w, seed=78, with_final=False)["dy"])
+    dims = ssd.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk, ssd.BF16)
+    ws_f = torch.empty(max(ssd.workspace_bytes(dims), 1), dtype=torch.uint8, device=dev_)
+    ws_s = torch.empty_like(ws_f)
+    ws_b = torch.empty(max(ssd.backward_workspace_bytes(dims), 1), dtype=torch.uint8, device=dev_)
+    y_f, f_f = torch.empty_like(x), torch.empty_like(init)
+    y_s, f_s = torch.empty_like(x), torch.empty_like(init)
+    gb = {"dx": torch.empty_like(x), "ddt": torch.empty_like(dt), "dB": torch.empty_like(B),
+          "dC": torch.empty_like(C), "dA": torch.empty_like(A), "dD": torch.empty_like(D)}
+    # decode: one step continuing from init
+    state = init.clone()
+    state0 = init.clone()
+    xd, dtd, Bd, Cd = x[:, 0].contiguous(), dt[:, 0].contiguous(), B[:, 0].contiguous(), C[:, 0].contiguous()
+    y_d = torch.empty_like(xd)
+    # scan and the normalisation after the gate
+    sc = {k: (dev(v) if isinstance(v, torch.Tensor) else v)
+          for k, v in scan_inputs("bf16", 2, 300, 256, 16, seed=79, with_init=True).items()}
+    y_sc, f_sc = torch.empty_like(sc["x"]), torch.empty_like(sc["init_state"])
+    ws_sc = torch.empty(1 << 24, dtype=torch.uint8, device=dev_)
+    zg = torch.randn(x.shape, generator=torch.Generator().manual_seed(80)).to(torch.bfloat16).to(dev_)
+    wg = torch.randn(w.nheads * w.headdim, generator=torch.Generator().manual_seed(81)).to(dev_)
+    y_g = torch.empty_like(x)
+    outs = [y_f, f_f, y_s, f_s, *gb.values(), y_d, state, y_sc, f_sc, y_g]
+
+    def run_all():
+        ssd.forward(x, dt, A, B, C, D, init, chunk=w.chunk, y=y_f, final_state=f_f, workspace=ws_f)
+        ssd.forward(x, dt, A, B, C, D, init, chunk=w.chunk, staged=True, y=y_s, final_state=f_s, workspace=ws_s)
+        ssd.backward(x, dt, A, B, C, dy, D=D, chunk=w.chunk, out=gb, workspace=ws_b, want_dinit=False)
+        ssd.decode_step(state, xd, dtd, A, Bd, Cd, D, y=y_d)
+        ssd.selective_scan(**sc, y=y_sc, final_state=f_sc, workspace=ws_sc)
+        ssd.gated_rmsnorm(y_f, zg, wg, out=y_g)
+
+    run_all()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        state.copy_(state0)
+        run_all()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    state.copy_(state0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        run_all()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs:
+            t.fill_(7)
+        state.copy_(state0)
+        noise = torch.randn(512, 512, device=dev_) @ torch.randn(512, 512, device=dev_)  # eager work between
+        torch.cuda.synchronize()
+        assert torch.isfinite(noise).all()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(a, e), (rep, i)

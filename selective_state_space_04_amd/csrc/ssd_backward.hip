@@ -1166,73 +1166,108 @@ __global__ __launch_bounds__(256) void k_group_state(
 }
 
 // ---------------------------------------------------------------------------
-// Per (b, c, g, 16-row tile, which): which = 0: dC[i] = dCs[i] + sum_{j<=i}
-// dCB[i][j] B_j; which = 1: dB[j] = dBs[j] + sum_{i>=j} dCB[i][j] C_i.
-// float32 MFMA (16x16x4): the dCB operand is 4 consecutive float32 values of
-// one row, the B / C operand 4 scalar loads of one column.  Wave w owns the
-// n-tiles w, w + 4, ...
+// Per (b, c, g, which, 64-row block): which = 0: dC[i] = dCs[i] +
+// sum_{j<=i} dCB[i][j] B_j; which = 1: dB[j] = dBs[j] + sum_{i>=j} dCB[i][j]
+// C_i.  float32 MFMA (16x16x4).  The column operand (B or C rows) is staged
+// 32 steps at a time in LDS as float32 (16-byte loads, shared by the four
+// waves); wave w owns rows 16 w .. 16 w + 15 of the block and all N columns,
+// and reads its dCB row segments (4 consecutive float32 per lane) straight
+// from global memory.  dCB tiles above the diagonal are never written, so
+// each wave stops (which 0) or starts (which 1) at its own diagonal tile.
 // ---------------------------------------------------------------------------
 template <typename T, int N>
 __global__ __launch_bounds__(256) void k_group_combine(
     const T *__restrict__ B, const T *__restrict__ C, const float *__restrict__ dcb,
     const float *__restrict__ dcbT, const float *__restrict__ dCs, const float *__restrict__ dBs,
     T *__restrict__ dB, T *__restrict__ dC, int64_t L, int G, int Q, int nc) {
-    constexpr int NT = N / 16, NTW = (NT + 3) / 4;
-    const int T16 = Q / 16;
+    constexpr int NT = N / 16, SK = 32, VLD = N + 4;
+    const int NB64 = (Q + 63) / 64;
     const int64_t work = xcd_remap(blockIdx.x, gridDim.x);
-    const int tile = (int)(work % T16);
-    const int which = (int)((work / T16) % 2);
-    const int64_t bcg = work / (2 * T16);
+    const int blk = (int)(work % NB64);
+    const int which = (int)((work / NB64) % 2);
+    const int64_t bcg = work / (2 * NB64);
     const int g = (int)(bcg % G);
     const int64_t bc = bcg / G;
     const int c = (int)(bc % nc);
     const int64_t b = bc / nc;
     const int64_t s = (int64_t)c * Q;
     const int q = (int)min<int64_t>(Q, L - s);
-    const int t0 = tile * 16;
-    if (t0 >= q) return;
+    if (blk * 64 >= q) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, grp = lane >> 4;
+    const int t0 = blk * 64 + wave * 16;          // this wave's first row
+    const bool wv = t0 < q;
     const int64_t cboff = bcg * (int64_t)Q * Q;
     const float *arow = (which == 0 ? dcb : dcbT) + cboff + (int64_t)(t0 + r) * Q;
-    const T *V = which == 0 ? B : C;  // the column operand's rows
-    const int k_lo = which == 0 ? 0 : t0;
-    const int k_hi = which == 0 ? t0 + 16 : ((q + 15) & ~15);
+    const T *V = (which == 0 ? B : C) + ((b * L + s) * G + g) * N;
+    const int q16 = (q + 15) & ~15;
+    // this wave's k range, and the workgroup's (the union over its waves)
+    const int k_lo = which == 0 ? 0 : t0, k_hi = which == 0 ? t0 + 16 : q16;
+    const int g_lo = which == 0 ? 0 : blk * 64;
+    const int g_hi = which == 0 ? min(blk * 64 + 64, q16) : q16;
+    __shared__ float vs[SK * VLD];
 
-    f32x4 acc[NTW];
+    f32x4 acc[NT];
 #pragma unroll
-    for (int u = 0; u < NTW; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = k_lo; k0 < k_hi; k0 += 16) {
-        const int kk = k0 + 4 * grp;
-        const f32x4 a4 = *(const f32x4 *)(arow + kk);
+    for (int u = 0; u < NT; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = g_lo; k0 < g_hi; k0 += SK) {
+        // stage rows k0 .. k0 + 31 of V as float32 (zero past q)
+        for (int idx = threadIdx.x; idx < SK * N / 8; idx += 256) {
+            const int kr = idx / (N / 8), c8 = (idx % (N / 8)) * 8;
+            const int k = k0 + kr;
+            float f[8];
+            if (k < q) {
+                if constexpr (sizeof(T) == 2) {
+                    const bf16x8 t = as_bf16x8(*(const u32x4 *)(V + (int64_t)k * G * N + c8));
 #pragma unroll
-        for (int u = 0; u < NTW; ++u) {
-            const int t = wave + 4 * u;
-            if (t < NT) {
-                const int n = t * 16 + r;
+                    for (int e = 0; e < 8; ++e) f[e] = (float)t[e];
+                } else {
+                    const f32x4 lo = *(const f32x4 *)(V + (int64_t)k * G * N + c8);
+                    const f32x4 hi = *(const f32x4 *)(V + (int64_t)k * G * N + c8 + 4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int k = kk + e;
-                    const float v = k < q ? to_f32(V[((b * L + s + k) * G + g) * N + n]) : 0.f;
-                    acc[u] = mfma_f32(a4[e], v, acc[u]);
+                    for (int e = 0; e < 4; ++e) {
+                        f[e] = lo[e];
+                        f[e + 4] = hi[e];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] = 0.f;
+            }
+            *(f32x4 *)(vs + kr * VLD + c8) = f32x4{f[0], f[1], f[2], f[3]};
+            *(f32x4 *)(vs + kr * VLD + c8 + 4) = f32x4{f[4], f[5], f[6], f[7]};
+        }
+        __syncthreads();
+        if (wv) {
+#pragma unroll
+            for (int kq = 0; kq < SK; kq += 16) {
+                const int kb = k0 + kq;
+                if (kb >= k_lo && kb < k_hi) {
+                    const int kk = kb + 4 * grp;
+                    const f32x4 a4 = *(const f32x4 *)(arow + kk);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float *vrow = vs + (kq + 4 * grp + e) * VLD + r;
+#pragma unroll
+                        for (int u = 0; u < NT; ++u) acc[u] = mfma_f32(a4[e], vrow[16 * u], acc[u]);
+                    }
                 }
             }
         }
+        __syncthreads();
     }
+    if (!wv) return;
     const float *base = which == 0 ? dCs : dBs;
     T *out = which == 0 ? dC : dB;
 #pragma unroll
-    for (int u = 0; u < NTW; ++u) {
-        const int t = wave + 4 * u;
-        if (t < NT) {
-            const int n = t * 16 + r;
+    for (int u = 0; u < NT; ++u) {
+        const int n = u * 16 + r;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = t0 + 4 * grp + e;
-                if (i < q) {
-                    const int64_t o = ((b * L + s + i) * G + g) * N + n;
-                    out[o] = from_f32<T>(acc[u][e] + base[o]);
-                }
+        for (int e = 0; e < 4; ++e) {
+            const int i = t0 + 4 * grp + e;
+            if (i < q) {
+                const int64_t o = ((b * L + s + i) * G + g) * N + n;
+                out[o] = from_f32<T>(acc[u][e] + base[o]);
             }
         }
     }
@@ -1372,7 +1407,7 @@ hipError_t launch_group_combine(const Dims &d, const void *B, const void *C, con
                                 const float *dcbT, const float *dCs, const float *dBs, void *dB,
                                 void *dC, hipStream_t st) {
     if (d.b == 0 || d.nc == 0) return hipSuccess;
-    const unsigned grid = (unsigned)(d.b * d.nc * d.G * 2 * (d.Q / 16));
+    const unsigned grid = (unsigned)(d.b * d.nc * d.G * 2 * ((d.Q + 63) / 64));
     SSD_BWD_DISPATCH_N(d.N, {
         if (d.dtype == 1)
             k_group_combine<bf16, NN><<<grid, 256, 0, st>>>((const bf16 *)B, (const bf16 *)C, dcb,

@@ -138,6 +138,19 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t total) {
     return (bid % 8) * per + bid / 8;
 }
 
+// s_waitcnt immediate that waits for lgkmcnt 0 (LDS and scalar memory) and
+// leaves the vector-memory and export counters at their maxima.
+constexpr int kWaitScalar = 0xC07F;
+
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// operations (and scalar loads) and meets the other waves, without the
+// release fence of __syncthreads, which would also wait for every global
+// load in flight and defeat a prefetch of later operands.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(kWaitScalar);
+    __builtin_amdgcn_s_barrier();
+}
+
 // Copy a [rows x cols] bf16 tile from global memory (row stride `ld`
 // elements) into LDS transposed: dst[c * dstride + r] = src[r * ld + c],
 // optionally times scale[r] (rounded back to bf16).  Rows >= nvalid read as

@@ -187,6 +187,69 @@ __global__ __launch_bounds__(256) void k_chunk_cb(const T *__restrict__ B, const
 // 16-byte LDS read.  f32: fragments come straight from global memory (one
 // element per lane per MFMA).  Wave w owns n-tiles w, w + 4, ...
 // ---------------------------------------------------------------------------
+// One thread's share of a [64 x COLS] bf16 slab in registers: blocks of 4
+// rows x 8 columns, block tid + 256 i, as four 16-byte row pieces; rows at
+// or past nvalid read as zero.
+template <int COLS>
+struct SlabRegs {
+    static constexpr int NBLK = 16 * (COLS / 8);
+    static constexpr int PER = (NBLK + 255) / 256;
+    u32x4 v[PER][4];
+};
+
+template <int COLS>
+__device__ __forceinline__ void slab_load(SlabRegs<COLS> &st, const bf16 *__restrict__ src, int64_t ld,
+                                          int nvalid) {
+    constexpr int NBC = COLS / 8;
+#pragma unroll
+    for (int i = 0; i < SlabRegs<COLS>::PER; ++i) {
+        const int blk = threadIdx.x + 256 * i;
+        if (blk < SlabRegs<COLS>::NBLK) {
+            const int r0 = (blk / NBC) * 4, c0 = (blk % NBC) * 8;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                st.v[i][k] = r0 + k < nvalid ? *(const u32x4 *)(src + (int64_t)(r0 + k) * ld + c0)
+                                             : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+}
+
+// Write the slab transposed: dst[c * dstride + r] = slab[r][c] (times
+// scale[r] when SCALE, rounded back to bf16), as in stage_transposed_bf16.
+template <bool SCALE, int COLS>
+__device__ __forceinline__ void slab_write_transposed(const SlabRegs<COLS> &st, bf16 *dst, int dstride,
+                                                      const float *scale) {
+    constexpr int NBC = COLS / 8;
+#pragma unroll
+    for (int i = 0; i < SlabRegs<COLS>::PER; ++i) {
+        const int blk = threadIdx.x + 256 * i;
+        if (blk < SlabRegs<COLS>::NBLK) {
+            const int r0 = (blk / NBC) * 4, c0 = (blk % NBC) * 8;
+            u32x4 v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[k] = st.v[i][k];
+                if constexpr (SCALE) {
+                    bf16x8 t = as_bf16x8(v[k]);
+                    const float w = scale[r0 + k];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) t[e] = (bf16)((float)t[e] * w);
+                    v[k] = as_u32x4(t);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const uint32_t lo01 = __builtin_amdgcn_perm(v[1][m], v[0][m], 0x05040100u);
+                const uint32_t lo23 = __builtin_amdgcn_perm(v[3][m], v[2][m], 0x05040100u);
+                const uint32_t hi01 = __builtin_amdgcn_perm(v[1][m], v[0][m], 0x07060302u);
+                const uint32_t hi23 = __builtin_amdgcn_perm(v[3][m], v[2][m], 0x07060302u);
+                *(u32x2 *)(dst + (c0 + 2 * m) * dstride + r0) = u32x2{lo01, lo23};
+                *(u32x2 *)(dst + (c0 + 2 * m + 1) * dstride + r0) = u32x2{hi01, hi23};
+            }
+        }
+    }
+}
+
 template <typename T, int P, int N, bool FROM_START>
 __global__ __launch_bounds__(256) void k_chunk_state(const T *__restrict__ x,
                                                      const T *__restrict__ B,
@@ -226,13 +289,21 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T *__restrict__ x,
         constexpr int SL = 64, LD = SL + 8;
         __shared__ bf16 xs[P * LD];
         __shared__ bf16 bs[N * LD];
+        // slab jb + SL is loaded into registers while slab jb is multiplied;
+        // the barriers only order LDS, so the loads stay in flight
+        SlabRegs<P> rx;
+        SlabRegs<N> rb;
+        slab_load(rx, xb, (int64_t)H * P, min(SL, q));
+        slab_load(rb, Bb, (int64_t)G * N, min(SL, q));
         for (int jb = 0; jb < q; jb += SL) {
-            const int nvalid = min(SL, q - jb);
-            stage_transposed_bf16<true>(xb + (int64_t)jb * H * P, (int64_t)H * P, SL, P, nvalid, xs,
-                                        LD, w_s + jb);
-            stage_transposed_bf16<false>(Bb + (int64_t)jb * G * N, (int64_t)G * N, SL, N, nvalid, bs,
-                                         LD, nullptr);
-            __syncthreads();
+            slab_write_transposed<true>(rx, xs, LD, w_s + jb);
+            slab_write_transposed<false>(rb, bs, LD, nullptr);
+            lds_barrier();
+            if (jb + SL < q) {
+                const int nv = min(SL, q - jb - SL);
+                slab_load(rx, xb + (int64_t)(jb + SL) * H * P, (int64_t)H * P, nv);
+                slab_load(rb, Bb + (int64_t)(jb + SL) * G * N, (int64_t)G * N, nv);
+            }
 #pragma unroll
             for (int kk = 0; kk < SL; kk += 32) {
                 bf16x8 bx[PT];
@@ -249,7 +320,7 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T *__restrict__ x,
                     }
                 }
             }
-            __syncthreads();
+            lds_barrier();
         }
     } else {
         for (int j0 = 0; j0 < q; j0 += 16) {

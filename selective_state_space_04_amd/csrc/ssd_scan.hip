@@ -34,9 +34,6 @@
 namespace ssd {
 
 constexpr float kLog2e = 1.4426950408889634f;
-// s_waitcnt immediate that waits for lgkmcnt 0 (LDS and scalar memory) and
-// leaves the vector-memory and export counters at their maxima.
-constexpr int kWaitScalar = 0xC07F;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // N consecutive values of a wave-uniform row (every lane reads the same
@@ -312,16 +309,6 @@ __device__ __forceinline__ void rows_steps(float dl, float u, float a2, const f3
 __device__ __forceinline__ int64_t xcd_local(int64_t wg, int64_t total) {
     const int64_t per = total / 8, rem = total % 8, x = wg % 8, k = wg / 8;
     return x < rem ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
-}
-
-// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
-// operations (lgkmcnt 0, vector-memory and export counters left at their
-// maxima) and meets the other waves, without the release fence of
-// __syncthreads, which would also wait for every global load in flight and
-// defeat the prefetch of later blocks.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(kWaitScalar);
-    __builtin_amdgcn_s_barrier();
 }
 
 constexpr int kRowQS = 20;   // LDS stride between a row's 16 lanes (words)

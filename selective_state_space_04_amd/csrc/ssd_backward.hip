@@ -1051,6 +1051,204 @@ __global__ __launch_bounds__(256) void k_group_dcb(const bf16 *__restrict__ x,
 }
 
 // ---------------------------------------------------------------------------
+// bfloat16 dCB for P in {32, 64}, one workgroup per (b, c, g, 64-row block
+// IB): the block pairs (IB, JB), JB <= IB, are split over the waves (two
+// waves per pair for P = 64, each with half its rows) and the head loop runs
+// once for all of them, so dy rows of block IB and x rows of blocks 0..IB
+// are loaded once per head for up to four pairs (instead of once per
+// pair).  Per head the waves copy those rows and the chunk's decay
+// prefix straight into a slot of a three-slot LDS ring with direct
+// global-to-LDS loads (no registers in flight), two heads ahead; each wave
+// waits only for its own copies of the head it is about to use (a counted
+// vmcnt: every wave issues the same number of copies per head, all lanes
+// active) and one barrier per head publishes the slot and frees the oldest.
+// Rows are 16-byte chunks stored at chunk ^ (row & (chunks per row - 1)),
+// so the MFMA fragment reads of 16 rows hit distinct banks; rows past the
+// chunk end are copies of its last row (their products are never stored).
+// ---------------------------------------------------------------------------
+namespace {
+
+__device__ __forceinline__ void copy16_to_lds(const void *src, void *dst_wave_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)dst_wave_base, 16, 0, 0);
+}
+
+// s_waitcnt with vmcnt = N (lgkmcnt and expcnt at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+constexpr int kDcbSlots = 3;
+template <int P>
+struct DcbRing {
+    static constexpr int ROWB = P * 2;               // bytes per row
+    static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
+    static constexpr int BLK = 64 * ROWB;            // bytes per 64-row block
+    static constexpr int IPB = BLK / 1024;           // wave copies per block
+    static constexpr int SLOT = 5 * BLK + 1024;      // dy block + up to 4 x blocks + cs
+};
+
+// NW waves: wave w computes rows 16 a, a in [NA * (w % (NW / 4)), + NA), of
+// the pair (IB, JB = w / (NW / 4)), NA = 16 / NW.
+template <int P>
+constexpr int dcb_waves() { return P == 64 ? 8 : 4; }
+
+template <int P, int IB>
+__device__ __forceinline__ void group_dcb_rb_body(unsigned char (*ring)[DcbRing<P>::SLOT],
+                                                  const bf16 *__restrict__ x, const bf16 *__restrict__ dy,
+                                                  const float *__restrict__ cs, float *__restrict__ dcb,
+                                                  float *__restrict__ dcbT, int64_t L, int H, int G, int Q,
+                                                  int nc, int64_t bcg) {
+    using R = DcbRing<P>;
+    constexpr int NW = dcb_waves<P>(), WPP = NW / 4, NA = 4 / WPP;
+    constexpr int NBLK = IB + 2;                      // dy block IB, x blocks 0..IB
+    constexpr int NBI = NBLK * R::IPB;                // block copies per head
+    static_assert(NBI % NW == 0, "block copies split evenly over the waves");
+    constexpr int NIW = NBI / NW + 1;                 // copies per wave per head (+ its share of cs)
+    constexpr int CSL = 64 / NW;                      // lanes per cs share (16 bytes each)
+    constexpr int KS = P / 32;
+    const int g = (int)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int c = (int)(bc % nc);
+    const int64_t b = bc / nc;
+    const int64_t s = (int64_t)c * Q;
+    const int q = (int)min<int64_t>(Q, L - s);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, grp = lane >> 4;
+    const int hpg = H / G, h0 = g * hpg;
+    const int JB = wave / WPP, a0 = NA * (wave % WPP);
+    const bool active = JB <= IB;                     // computes rows a0.. of pair (IB, JB)
+
+    auto issue = [&](int hh, int slot) {
+        const int h = h0 + hh;
+        unsigned char *base = ring[slot];
+#pragma unroll
+        for (int k0 = 0; k0 < NBI; k0 += NW) {
+            const int k = k0 + wave;
+            const int blk = k / R::IPB, sub = k % R::IPB;
+            constexpr int RPI = 1024 / R::ROWB;       // rows per copy
+            const int row = sub * RPI + lane / R::CPR;
+            const int chunk = (lane % R::CPR) ^ (row & (R::CPR - 1));
+            const int grow = min((blk == 0 ? IB : blk - 1) * 64 + row, q - 1);
+            const bf16 *src = (blk == 0 ? dy : x) + ((b * L + s + grow) * H + h) * P + chunk * 8;
+            copy16_to_lds(src, base + blk * R::BLK + sub * 1024);
+        }
+        // decay prefix: wave w copies floats 4 CSL w .. + 4 CSL - 1 with lanes 0..CSL-1
+        // (16 bytes each); the copy always has active lanes, so it counts once per
+        // wave like the block copies
+        if (lane < CSL) {
+            const int f = min(4 * (CSL * wave + lane), Q - 4);
+            copy16_to_lds(cs + (((int64_t)b * H + h) * nc + c) * Q + f,
+                          base + 5 * R::BLK + wave * (16 * CSL));
+        }
+    };
+
+    f32x4 acc[NA][4];
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) acc[a][bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    issue(0, 0);
+    if (hpg > 1) issue(1, 1);
+    constexpr float kL2e = 1.4426950408889634f;
+    for (int hh = 0; hh < hpg; ++hh) {
+        const int slot = hh % kDcbSlots;
+        // this wave's copies of head hh are done once at most the next head's are in flight
+        if (hh + 1 < hpg) wait_vmcnt<NIW>(); else wait_vmcnt<0>();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep LDS accesses on their side of the barrier
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (hh + 2 < hpg) issue(hh + 2, (hh + 2) % kDcbSlots);
+        if (!active) continue;
+        const unsigned char *base = ring[slot];
+        const bf16 *dys = (const bf16 *)base;
+        const bf16 *xsb = (const bf16 *)(base + (1 + JB) * R::BLK);
+        const float *css = (const float *)(base + 5 * R::BLK);
+        float cj[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) cj[bb] = css[64 * JB + 16 * bb + r] * kL2e;
+        bf16x8 fb[4][KS];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+            for (int kc = 0; kc < KS; ++kc) {
+                const int row = 16 * bb + r, ch = (4 * kc + grp) ^ (row & (R::CPR - 1));
+                fb[bb][kc] = *(const bf16x8 *)(xsb + row * P + ch * 8);
+            }
+#pragma unroll
+        for (int ai = 0; ai < NA; ++ai) {
+            const int a = a0 + ai;
+            bf16x8 fa[KS];
+#pragma unroll
+            for (int kc = 0; kc < KS; ++kc) {
+                const int row = 16 * a + r, ch = (4 * kc + grp) ^ (row & (R::CPR - 1));
+                fa[kc] = *(const bf16x8 *)(dys + row * P + ch * 8);
+            }
+            float ci[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ci[e] = css[64 * IB + 16 * a + 4 * grp + e] * kL2e;
+            // all four products first, then the masks (independent work covers the MFMA latency)
+            f32x4 t[4];
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                t[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kc = 0; kc < KS; ++kc) t[bb] = mfma_bf16(fa[kc], fb[bb][kc], t[bb]);
+            }
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const int j = 64 * JB + 16 * bb + r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 64 * IB + 16 * a + 4 * grp + e;
+                    const bool keep = (IB > JB || j <= i) && i < q;
+                    acc[ai][bb][e] += keep ? __builtin_amdgcn_exp2f(ci[e] - cj[bb]) * t[bb][e] : 0.f;
+                }
+            }
+        }
+    }
+    if (!active) return;
+    const int64_t cboff = bcg * (int64_t)Q * Q;
+#pragma unroll
+    for (int ai = 0; ai < NA; ++ai) {
+        const int a = a0 + ai;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const int it = 64 * IB + 16 * a, jt = 64 * JB + 16 * bb;
+            if (jt > it || it >= Q) continue;  // tile above the diagonal or past the chunk
+            const int j = jt + r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dcb[cboff + (int64_t)(it + 4 * grp + e) * Q + j] = acc[ai][bb][e];
+            *(f32x4 *)(dcbT + cboff + (int64_t)j * Q + it + 4 * grp) = acc[ai][bb];
+        }
+    }
+}
+
+}  // namespace
+
+template <int P>
+__global__ __launch_bounds__(64 * dcb_waves<P>()) void k_group_dcb_rb(const bf16 *__restrict__ x, const bf16 *__restrict__ dy,
+                                                      const float *__restrict__ cs, float *__restrict__ dcb,
+                                                      float *__restrict__ dcbT, int64_t L, int H, int G, int Q,
+                                                      int nc) {
+    __shared__ __attribute__((aligned(16))) unsigned char ring[kDcbSlots][DcbRing<P>::SLOT];
+    const int nbk = (Q + 63) / 64;
+    // the nbk row blocks of one (b, c, g) are neighbours, so they share an XCD's L2
+    const int64_t work = xcd_remap(blockIdx.x, gridDim.x);
+    const int IB = (int)(work % nbk);
+    const int64_t bcg = work / nbk;
+    switch (IB) {
+    case 0: group_dcb_rb_body<P, 0>(ring, x, dy, cs, dcb, dcbT, L, H, G, Q, nc, bcg); break;
+    case 1: group_dcb_rb_body<P, 1>(ring, x, dy, cs, dcb, dcbT, L, H, G, Q, nc, bcg); break;
+    case 2: group_dcb_rb_body<P, 2>(ring, x, dy, cs, dcb, dcbT, L, H, G, Q, nc, bcg); break;
+    default: group_dcb_rb_body<P, 3>(ring, x, dy, cs, dcb, dcbT, L, H, G, Q, nc, bcg); break;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // bfloat16: the state terms alone, one workgroup per (b, c, g, 64-row tile,
 // which): which = 0: dCs[i] = sum_h exp(cs_i) dy_i^T H_c; which = 1:
 // dBs[j] = sum_h exp(cs_e - cs_j) x_j^T R_c.  Each wave owns 16 rows (row
@@ -1383,10 +1581,17 @@ hipError_t launch_group_bwd(const Dims &d, const void *x, const void *dy, const 
         if (kSplit && d.dtype == 1) {
             if constexpr (kSplit) {
                 const int nbk = (int)((d.Q + 63) / 64);
-                const unsigned g1 = (unsigned)(d.b * d.nc * d.G * (nbk * (nbk + 1) / 2));
-                k_group_dcb<PP><<<g1, 256, 0, st>>>((const bf16 *)x, (const bf16 *)dy, cs, dcb,
-                                                   dcbT, d.L, (int)d.H, (int)d.G, (int)d.Q,
-                                                   (int)d.nc);
+                if constexpr (PP == 32 || PP == 64) {
+                    const unsigned g1 = (unsigned)(d.b * d.nc * d.G * nbk);
+                    k_group_dcb_rb<PP><<<g1, 64 * dcb_waves<PP>(), 0, st>>>((const bf16 *)x, (const bf16 *)dy, cs, dcb,
+                                                          dcbT, d.L, (int)d.H, (int)d.G, (int)d.Q,
+                                                          (int)d.nc);
+                } else {
+                    const unsigned g1 = (unsigned)(d.b * d.nc * d.G * (nbk * (nbk + 1) / 2));
+                    k_group_dcb<PP><<<g1, 256, 0, st>>>((const bf16 *)x, (const bf16 *)dy, cs, dcb,
+                                                       dcbT, d.L, (int)d.H, (int)d.G, (int)d.Q,
+                                                       (int)d.nc);
+                }
                 k_group_state<PP, NN><<<2 * grid, 256, 0, st>>>(
                     (const bf16 *)x, (const bf16 *)dy, cs, Hs, Rs, dCs, dBs, d.L, (int)d.H,
                     (int)d.G, (int)d.Q, (int)d.nc);

@@ -148,7 +148,9 @@ constexpr int kWaitScalar = 0xC07F;
 // load in flight and defeat a prefetch of later operands.
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(kWaitScalar);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // compiler-only: memory accesses stay on their side
     __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Copy a [rows x cols] bf16 tile from global memory (row stride `ld`

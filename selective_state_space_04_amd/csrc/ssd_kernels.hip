@@ -14,6 +14,8 @@
 // for the block split into a quadratic part inside blocks and states across
 // them.)  The within-chunk weights exp(cs_{q-1} - cs_j) on the chunk state are
 // what makes the split exact.
+#include <algorithm>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -363,6 +365,174 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T *__restrict__ x,
             for (int pt = 0; pt < PT; ++pt)
                 *(f32x4 *)(So + (int64_t)(pt * 16 + r) * N + nt * 16 + 4 * grp) = acc[t][pt];
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk states for bfloat16 with P in {32, 64}, N in {64, 128} and Q a
+// multiple of 32 (both backward passes and the staged forward use it): one
+// workgroup per (b, c, g, part of the group's heads) keeps the chunk's B rows
+// in LDS for all its heads and streams x head by head through a two-slot LDS
+// ring.  Both arrive by direct global-to-LDS copies (row-major, 16-byte
+// chunks stored at chunk ^ (row & (chunks per row - 1))); the MFMA operands,
+// which contract over the steps, are read with transposing LDS reads
+// (ds_read_b64_tr_b16: in each 16-lane group, lane l points at the 4 columns
+// 4 (l % 4) + 4-wide piece of row l / 4 and receives column l % 16 of the 4
+// rows), two per fragment.  The step weights w_j (exp(cs_e - cs_j), or
+// exp(cs_j) from the chunk start, times the optional input factor) scale the
+// B^T fragments.  Per head: wait for this wave's copies of x (the S stores of
+// the previous head may stay in flight), one barrier, copy x of the next
+// head, multiply, store S, compute the next head's weights.
+// ---------------------------------------------------------------------------
+namespace {
+
+__device__ __forceinline__ void copy16_to_lds_k(const void *src, void *dst_wave_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)dst_wave_base, 16, 0, 0);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Column c0 + (lane % 16) of rows r0 .. r0 + 3 of a row-major bf16 tile with
+// rows of ROWB bytes, 16-byte chunks swizzled by (row & (ROWB / 16 - 1)).
+template <int ROWB>
+__device__ __forceinline__ i16x4 read_tr4(const unsigned char *tile, int r0, int c0, int lane) {
+    constexpr int CPR = ROWB / 16;
+    const int j = lane & 15;
+    const int row = r0 + (j >> 2);
+    const int col = c0 + 4 * (j & 3);                    // element column of this lane's piece
+    const int chunk = (col >> 3) ^ (row & (CPR - 1));
+    const unsigned char *a = tile + row * ROWB + chunk * 16 + ((col >> 2) & 1) * 8;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)a);
+}
+
+// MFMA fragment (8 steps k0 + 8 grp .. + 7 of column c0 + r) from a row-major tile
+template <int ROWB>
+__device__ __forceinline__ bf16x8 frag_tr(const unsigned char *tile, int k0, int c0, int lane) {
+    const int grp = lane >> 4;
+    const i16x4 lo = read_tr4<ROWB>(tile, k0 + 8 * grp, c0, lane);
+    const i16x4 hi = read_tr4<ROWB>(tile, k0 + 8 * grp + 4, c0, lane);
+    bf16x8 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const short a = lo[e], b = hi[e];
+        f[e] = __builtin_bit_cast(bf16, a);
+        f[e + 4] = __builtin_bit_cast(bf16, b);
+    }
+    return f;
+}
+
+// Copy rows 0 .. nrows - 1 (row index clamped to nvalid - 1) of a bf16 tile with
+// rows of ROWB bytes at global row stride ld (elements) into LDS, swizzled;
+// copies k = wave, wave + NW, ... of 1 KiB each (NW waves).
+template <int ROWB, int NW>
+__device__ __forceinline__ void copy_tile_to_lds(const bf16 *__restrict__ src, int64_t ld, int nrows,
+                                                 int nvalid, unsigned char *dst, int wave, int lane) {
+    constexpr int CPR = ROWB / 16, RPC = 1024 / ROWB;
+    const int ncopies = nrows * ROWB / 1024;
+    for (int k = wave; k < ncopies; k += NW) {
+        const int row = k * RPC + lane / CPR;
+        const int chunk = (lane % CPR) ^ (row & (CPR - 1));
+        const bf16 *g = src + (int64_t)min(row, nvalid - 1) * ld + chunk * 8;
+        copy16_to_lds_k(g, dst + k * 1024);
+    }
+}
+
+}  // namespace
+
+template <int P, int N, bool FROM_START>
+__global__ __launch_bounds__(64 * (N / 16)) void k_chunk_state_mh(const bf16 *__restrict__ x,
+                                                        const bf16 *__restrict__ B,
+                                                        const float *__restrict__ cs,
+                                                        float *__restrict__ S, int64_t L, int H,
+                                                        int G, int Q, int nc,
+                                                        const float *__restrict__ sc, int nparts) {
+    constexpr int XROWB = P * 2, BROWB = N * 2;
+    constexpr int PT = P / 16, NT = N / 16, NW = NT;  // one wave per 16-column tile of N
+    static_assert(NT % 4 == 0 && (P == 32 || P == 64), "shape");
+    __shared__ __attribute__((aligned(16))) unsigned char bsm[256 * BROWB];
+    __shared__ __attribute__((aligned(16))) unsigned char xsm[2][256 * XROWB];
+    __shared__ float wsm[2][256];
+    const int64_t wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int part = (int)(wg % nparts);
+    const int64_t bcg = wg / nparts;
+    const int g = (int)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int c = (int)(bc % nc);
+    const int64_t b = bc / nc;
+    const int64_t s = (int64_t)c * Q;
+    const int q = (int)min<int64_t>(Q, L - s);
+    const int hpg = H / G, hpp = (hpg + nparts - 1) / nparts;
+    const int h_lo = g * hpg + part * hpp, h_hi = min(h_lo + hpp, (g + 1) * hpg);
+    const int nh = h_hi - h_lo;
+    if (nh <= 0) return;  // uniform over the workgroup; no barrier reached
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, grp = lane >> 4;
+
+    // B rows of the chunk, once
+    copy_tile_to_lds<BROWB, NW>(B + ((b * L + s) * G + g) * N, (int64_t)G * N, Q, q, bsm, wave, lane);
+    auto copy_x = [&](int h, int slot) {
+        copy_tile_to_lds<XROWB, NW>(x + ((b * L + s) * H + h) * P, (int64_t)H * P, Q, q, xsm[slot], wave, lane);
+    };
+    // thread tid < 256 holds step j = tid of a head: its weight (zero past q)
+    auto weight = [&](float csj, float cse, float scj) {
+        return tid < q ? (FROM_START ? __expf(csj) : __expf(cse - csj)) * scj : 0.f;
+    };
+    const bool wthread = tid < 256;
+    float n_csj = 0.f, n_cse = 0.f, n_scj = 1.f;
+    auto load_cs = [&](int h) {
+        const int64_t o = (((int64_t)b * H + h) * nc + c) * Q;
+        n_csj = tid < Q ? cs[o + min(tid, q - 1)] : 0.f;
+        n_cse = cs[o + q - 1];
+        n_scj = (sc && tid < q) ? sc[o + tid] : 1.f;
+    };
+    copy_x(h_lo, 0);
+    if (wthread) {
+        load_cs(h_lo);
+        wsm[0][tid] = weight(n_csj, n_cse, n_scj);
+    }
+    constexpr int NST = PT;  // S stores per wave per head
+
+    for (int hh = 0; hh < nh; ++hh) {
+        const int slot = hh & 1;
+        // this wave's copies for head hh (and B) are done once at most the
+        // previous head's S stores are still in flight; lgkmcnt(0) completes
+        // its weight writes before the barrier publishes them
+        if (hh == 0) __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+        else __builtin_amdgcn_s_waitcnt((NST & 15) | ((NST >> 4) << 14) | 0x70);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const bool more = hh + 1 < nh;
+        if (more) {
+            copy_x(h_lo + hh + 1, slot ^ 1);
+            if (wthread) load_cs(h_lo + hh + 1);
+        }
+        f32x4 acc[PT];
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const float *w = wsm[slot];
+        for (int k0 = 0; k0 < Q; k0 += 32) {
+            bf16x8 bx[PT];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) bx[pt] = frag_tr<XROWB>(xsm[slot], k0, pt * 16, lane);
+            const f32x4 w0 = *(const f32x4 *)(w + k0 + 8 * grp);
+            const f32x4 w1 = *(const f32x4 *)(w + k0 + 8 * grp + 4);
+            bf16x8 ab = frag_tr<BROWB>(bsm, k0, wave * 16, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ab[e] = (bf16)((float)ab[e] * w0[e]);
+                ab[e + 4] = (bf16)((float)ab[e + 4] * w1[e]);
+            }
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) acc[pt] = mfma_bf16(ab, bx[pt], acc[pt]);
+        }
+        // acc[pt][e] = S^T[n = 16 wave + 4 grp + e][p = 16 pt + r]
+        float *So = S + (((b * nc + c) * H + h_lo + hh) * (int64_t)P) * N;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+            *(f32x4 *)(So + (int64_t)(pt * 16 + r) * N + wave * 16 + 4 * grp) = acc[pt];
+        if (more && wthread) wsm[slot ^ 1][tid] = weight(n_csj, n_cse, n_scj);
     }
 }
 
@@ -728,6 +898,28 @@ hipError_t launch_chunk_cb(const Dims &d, const void *B, const void *C, void *cb
 hipError_t launch_chunk_state(const Dims &d, const void *x, const void *B, const float *cs,
                               float *S, bool from_start, hipStream_t st, const float *sc) {
     if (d.b == 0 || d.nc == 0) return hipSuccess;
+    if (d.dtype == 1 && (d.P == 32 || d.P == 64) && (d.N == 64 || d.N == 128) && d.Q % 32 == 0) {
+        // heads split into parts so that the workgroups fill every CU once
+        // (as many per CU as their LDS allows)
+        const int64_t nbcg = d.b * d.nc * d.G, hpg = d.H / d.G;
+        const int64_t lds = 256 * (2 * d.N + 4 * d.P) + 2048, per_cu = std::max<int64_t>(1, 163840 / lds);
+        const int64_t target = 256 * per_cu;
+        const int nparts = (int)std::max<int64_t>(1, std::min<int64_t>(hpg, (target + nbcg - 1) / nbcg));
+        const unsigned g2 = (unsigned)(nbcg * nparts);
+#define SSD_LAUNCH_STATE_MH(PV, NV)                                                               \
+        if (from_start)                                                                           \
+            k_chunk_state_mh<PV, NV, true><<<g2, 64 * (NV / 16), 0, st>>>((const bf16 *)x, (const bf16 *)B, cs, S, \
+                d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc, sc, nparts);                        \
+        else                                                                                      \
+            k_chunk_state_mh<PV, NV, false><<<g2, 64 * (NV / 16), 0, st>>>((const bf16 *)x, (const bf16 *)B, cs, S, \
+                d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc, sc, nparts);
+        if (d.P == 32 && d.N == 64) { SSD_LAUNCH_STATE_MH(32, 64) }
+        else if (d.P == 32) { SSD_LAUNCH_STATE_MH(32, 128) }
+        else if (d.N == 64) { SSD_LAUNCH_STATE_MH(64, 64) }
+        else { SSD_LAUNCH_STATE_MH(64, 128) }
+#undef SSD_LAUNCH_STATE_MH
+        return hipGetLastError();
+    }
     const unsigned grid = (unsigned)(d.b * d.nc * d.H);
 #define SSD_LAUNCH_STATE(FS)                                                                      \
     SSD_DISPATCH_PN(d.P, d.N, {                                                                   \

@@ -1068,11 +1068,6 @@ __global__ __launch_bounds__(256) void k_group_dcb(const bf16 *__restrict__ x,
 // ---------------------------------------------------------------------------
 namespace {
 
-__device__ __forceinline__ void copy16_to_lds(const void *src, void *dst_wave_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                     (__attribute__((address_space(3))) void *)dst_wave_base, 16, 0, 0);
-}
-
 // s_waitcnt with vmcnt = N (lgkmcnt and expcnt at their maxima)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

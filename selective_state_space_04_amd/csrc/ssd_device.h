@@ -153,6 +153,114 @@ __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Direct global-to-LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's bytes land at dst_wave_base + 16 l (dst_wave_base is uniform).
+// The copy counts in vmcnt like a load and bypasses the registers.
+__device__ __forceinline__ void copy16_to_lds(const void *src, void *dst_wave_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)dst_wave_base, 16, 0, 0);
+}
+
+
+// Row-major bf16 tiles filled by direct copies and read with transposing
+// reads use a pair swizzle: the 32-byte pair p of row r (16-byte chunks 2 p,
+// 2 p + 1) is stored at pair p ^ (tr_swz(r) & (pairs per row - 1)).  A
+// transposing read touches rows r0 + 8 grp + m (m < 4, grp < 4) at one pair;
+// tr_swz mixes the row bits that vary there (0, 1, 3, 4) so those 16 rows
+// fall on every 32-byte bank slot of a 256-byte window at most twice.
+__device__ __forceinline__ int tr_swz(int row) {
+    return (((row >> 3) & 3) ^ (((row >> 1) & 1) << 1)) | ((row & 1) << 2);
+}
+
+template <int ROWB>
+__device__ __forceinline__ int tr_chunk_slot(int row, int chunk) {
+    constexpr int NP = ROWB / 32;  // 32-byte pairs per row
+    if constexpr (NP <= 1) return chunk;
+    else return (((chunk >> 1) ^ (tr_swz(row) & (NP - 1))) << 1) | (chunk & 1);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: in each 16-lane group, lane j points at the 4-element
+// piece (row r0 + j / 4, columns c0 + 4 (j % 4) ..) and receives column
+// c0 + j of rows r0 .. r0 + 3.
+template <int ROWB>
+__device__ __forceinline__ i16x4 read_tr4(const unsigned char *tile, int r0, int c0, int lane) {
+    const int j = lane & 15;
+    const int row = r0 + (j >> 2);
+    const int col = c0 + 4 * (j & 3);                    // first element of this lane's piece
+    const int slot = tr_chunk_slot<ROWB>(row, col >> 3);
+    const unsigned char *a = tile + row * ROWB + slot * 16 + ((col >> 2) & 1) * 8;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)a);
+}
+
+// MFMA fragment (8 steps k0 + 8 grp .. + 7 of column c0 + r) from a row-major tile
+template <int ROWB>
+__device__ __forceinline__ bf16x8 frag_tr(const unsigned char *tile, int k0, int c0, int lane) {
+    const int grp = lane >> 4;
+    const i16x4 lo = read_tr4<ROWB>(tile, k0 + 8 * grp, c0, lane);
+    const i16x4 hi = read_tr4<ROWB>(tile, k0 + 8 * grp + 4, c0, lane);
+    bf16x8 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const short a = lo[e], b = hi[e];
+        f[e] = __builtin_bit_cast(bf16, a);
+        f[e + 4] = __builtin_bit_cast(bf16, b);
+    }
+    return f;
+}
+
+// The same fragment through a per-lane byte offset computed once: for k0 a
+// multiple of 32 the lane's rows k0 + 8 grp + 4 h + j / 4 have the same
+// swizzle for every k0 and h, so only (k0 + 4 h) * ROWB changes (an
+// immediate offset of the LDS read).  c0 is a multiple of 16.
+template <int ROWB>
+__device__ __forceinline__ int tr_lane_offset(int c0, int lane) {
+    const int j = lane & 15, grp = lane >> 4;
+    const int row = 8 * grp + (j >> 2);
+    const int col = c0 + 4 * (j & 3);
+    return row * ROWB + tr_chunk_slot<ROWB>(row, col >> 3) * 16 + ((col >> 2) & 1) * 8;
+}
+
+template <int ROWB>
+__device__ __forceinline__ bf16x8 frag_tr_off(const unsigned char *tile, int k0, int off) {
+    const unsigned char *a = tile + off + k0 * ROWB;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)a);
+    const i16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(a + 4 * ROWB));
+    bf16x8 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const short a0 = lo[e], b0 = hi[e];
+        f[e] = __builtin_bit_cast(bf16, a0);
+        f[e + 4] = __builtin_bit_cast(bf16, b0);
+    }
+    return f;
+}
+
+// Four consecutive elements (col % 4 == 0) of row `row` of such a tile.
+template <int ROWB>
+__device__ __forceinline__ u32x2 lds_row4(const unsigned char *tile, int row, int col) {
+    const int slot = tr_chunk_slot<ROWB>(row, col >> 3);
+    return *(const u32x2 *)(tile + row * ROWB + slot * 16 + ((col >> 2) & 1) * 8);
+}
+
+// Copy rows 0 .. nrows - 1 (row index clamped to nvalid - 1) of a bf16 tile with
+// rows of ROWB bytes at global row stride ld (elements) into LDS with the pair
+// swizzle; copies k = wave, wave + NW, ... of 1 KiB each (NW waves).
+template <int ROWB, int NW>
+__device__ __forceinline__ void copy_tile_to_lds(const bf16 *__restrict__ src, int64_t ld, int nrows,
+                                                 int nvalid, unsigned char *dst, int wave, int lane) {
+    constexpr int CPR = ROWB / 16, RPC = 1024 / ROWB;
+    const int ncopies = nrows * ROWB / 1024;
+    for (int k = wave; k < ncopies; k += NW) {
+        const int row = k * RPC + lane / CPR;
+        const int chunk = tr_chunk_slot<ROWB>(row, lane % CPR);  // the swizzle is an involution
+        const bf16 *g = src + (int64_t)min(row, nvalid - 1) * ld + chunk * 8;
+        copy16_to_lds(g, dst + k * 1024);
+    }
+}
+
 // Copy a [rows x cols] bf16 tile from global memory (row stride `ld`
 // elements) into LDS transposed: dst[c * dstride + r] = src[r * ld + c],
 // optionally times scale[r] (rounded back to bf16).  Rows >= nvalid read as

@@ -384,62 +384,6 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T *__restrict__ x,
 // the previous head may stay in flight), one barrier, copy x of the next
 // head, multiply, store S, compute the next head's weights.
 // ---------------------------------------------------------------------------
-namespace {
-
-__device__ __forceinline__ void copy16_to_lds_k(const void *src, void *dst_wave_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                     (__attribute__((address_space(3))) void *)dst_wave_base, 16, 0, 0);
-}
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-// Column c0 + (lane % 16) of rows r0 .. r0 + 3 of a row-major bf16 tile with
-// rows of ROWB bytes, 16-byte chunks swizzled by (row & (ROWB / 16 - 1)).
-template <int ROWB>
-__device__ __forceinline__ i16x4 read_tr4(const unsigned char *tile, int r0, int c0, int lane) {
-    constexpr int CPR = ROWB / 16;
-    const int j = lane & 15;
-    const int row = r0 + (j >> 2);
-    const int col = c0 + 4 * (j & 3);                    // element column of this lane's piece
-    const int chunk = (col >> 3) ^ (row & (CPR - 1));
-    const unsigned char *a = tile + row * ROWB + chunk * 16 + ((col >> 2) & 1) * 8;
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)a);
-}
-
-// MFMA fragment (8 steps k0 + 8 grp .. + 7 of column c0 + r) from a row-major tile
-template <int ROWB>
-__device__ __forceinline__ bf16x8 frag_tr(const unsigned char *tile, int k0, int c0, int lane) {
-    const int grp = lane >> 4;
-    const i16x4 lo = read_tr4<ROWB>(tile, k0 + 8 * grp, c0, lane);
-    const i16x4 hi = read_tr4<ROWB>(tile, k0 + 8 * grp + 4, c0, lane);
-    bf16x8 f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const short a = lo[e], b = hi[e];
-        f[e] = __builtin_bit_cast(bf16, a);
-        f[e + 4] = __builtin_bit_cast(bf16, b);
-    }
-    return f;
-}
-
-// Copy rows 0 .. nrows - 1 (row index clamped to nvalid - 1) of a bf16 tile with
-// rows of ROWB bytes at global row stride ld (elements) into LDS, swizzled;
-// copies k = wave, wave + NW, ... of 1 KiB each (NW waves).
-template <int ROWB, int NW>
-__device__ __forceinline__ void copy_tile_to_lds(const bf16 *__restrict__ src, int64_t ld, int nrows,
-                                                 int nvalid, unsigned char *dst, int wave, int lane) {
-    constexpr int CPR = ROWB / 16, RPC = 1024 / ROWB;
-    const int ncopies = nrows * ROWB / 1024;
-    for (int k = wave; k < ncopies; k += NW) {
-        const int row = k * RPC + lane / CPR;
-        const int chunk = (lane % CPR) ^ (row & (CPR - 1));
-        const bf16 *g = src + (int64_t)min(row, nvalid - 1) * ld + chunk * 8;
-        copy16_to_lds_k(g, dst + k * 1024);
-    }
-}
-
-}  // namespace
-
 template <int P, int N, bool FROM_START>
 __global__ __launch_bounds__(64 * (N / 16)) void k_chunk_state_mh(const bf16 *__restrict__ x,
                                                         const bf16 *__restrict__ B,

@@ -138,15 +138,19 @@ int64_t ws_total(const ssd::Dims &d) {
 
 // Workspace of the gradient: cs | C B^T | (C B^T)^T | forward states H_c |
 // state gradients R_c | dCB | dCB^T | state terms of dC and dB | per-chunk
-// partials of dA and dD | float64 prefix (float32 inputs only).
+// partials of dA and dD | float64 prefix (float32 inputs only) | C and B
+// rows and the diagonal of C B^T in fragment order (when the chunk backward
+// reads fragments; C B^T and its transpose are then fragment blocks too).
 struct BwdLayout {
     int64_t cs = 0, cb = 0, cbT = 0, Hs = 0, Rs = 0, dcb = 0, dcbT = 0, dCs = 0, dBs = 0,
-            part = 0, cs64 = 0, total = 0;
+            part = 0, cs64 = 0, Cf = 0, Bf = 0, dg = 0, total = 0;
 };
 
 BwdLayout bwd_layout(const ssd::Dims &d) {
     BwdLayout w;
-    const int64_t cb_bytes = d.b * d.nc * d.G * d.Q * d.Q * esize(d);
+    const bool fr = ssd::chunk_bwd_frags(d);
+    const ssd::BwdFragBytes fb = fr ? ssd::bwd_frag_bytes(d) : ssd::BwdFragBytes{0, 0, 0};
+    const int64_t cb_bytes = fr ? fb.blocks : d.b * d.nc * d.G * d.Q * d.Q * esize(d);
     const int64_t s_bytes = d.b * d.nc * d.H * d.P * d.N * 4;
     const int64_t dcb_bytes = d.b * d.nc * d.G * d.Q * d.Q * 4;
     const int64_t g_bytes = d.b * d.L * d.G * d.N * 4;
@@ -161,7 +165,10 @@ BwdLayout bwd_layout(const ssd::Dims &d) {
     w.dBs = align256(w.dCs + g_bytes);
     w.part = align256(w.dBs + g_bytes);
     w.cs64 = align256(w.part + d.b * d.nc * d.H * 2 * 4);
-    w.total = align256(w.cs64 + (d.dtype == SSD_F32 ? d.b * d.H * d.nc * d.Q * 8 : 0));
+    w.Cf = align256(w.cs64 + (d.dtype == SSD_F32 ? d.b * d.H * d.nc * d.Q * 8 : 0));
+    w.Bf = align256(w.Cf + fb.rows);
+    w.dg = align256(w.Bf + fb.rows);
+    w.total = align256(w.dg + fb.diag);
     if (d.b == 0 || d.nc == 0) w.total = 0;
     return w;
 }
@@ -464,13 +471,16 @@ ssd_status run_backward(const ssd::Dims &d, const void *x, const void *dt, const
     void *cb = base + w.cb, *cbT = base + w.cbT;
     SSD_STEP(ssd::launch_chunk_cumsum(d, dt, A, cs, st));
     SSD_STEP(cs64 ? ssd::launch_chunk_cumsum64(d, dt, A, cs64, st) : hipSuccess);
-    SSD_STEP(ssd::launch_chunk_cb(d, B, C, cb, cbT, st));
+    void *Cf = base + w.Cf, *Bf = base + w.Bf;
+    float *dg = (float *)(base + w.dg);
+    SSD_STEP(ssd::chunk_bwd_frags(d) ? ssd::launch_bwd_frags(d, B, C, cb, cbT, Cf, Bf, dg, st)
+                                     : ssd::launch_chunk_cb(d, B, C, cb, cbT, st));
     SSD_STEP(ssd::launch_chunk_state(d, x, B, cs, Hs, false, st));
     SSD_STEP(ssd::launch_state_passing(d, Hs, cs, init, nullptr, st));
     SSD_STEP(ssd::launch_chunk_state(d, dy, C, cs, Rs, true, st));
     SSD_STEP(ssd::launch_state_passing_rev(d, Rs, cs, dfinal, dinit, st));
-    SSD_STEP(ssd::launch_chunk_bwd(d, x, dy, dt, A, B, C, cb, cbT, cs, cs64, Hs, Rs, D, dx, ddt,
-                                   part, st));
+    SSD_STEP(ssd::launch_chunk_bwd(d, x, dy, dt, A, B, C, cb, cbT, Cf, Bf, dg, cs, cs64, Hs, Rs, D,
+                                   dx, ddt, part, st));
     SSD_STEP(ssd::launch_group_bwd(d, x, dy, cs, cs64, Hs, Rs, dcb, dcbT, dCs, dBs, st));
     SSD_STEP(ssd::launch_group_combine(d, B, C, dcb, dcbT, dCs, dBs, dB, dC, st));
     SSD_STEP(ssd::launch_head_reduce(d, part, dA, dD, st));

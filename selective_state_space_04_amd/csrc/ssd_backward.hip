@@ -44,6 +44,8 @@
 //   k_group_combine per (b, c, g, 16 rows): dC = dC_state + dCB B,
 //                   dB = dB_state + dCB^T C, rounded to the input dtype.
 //   k_head_reduce   per h: sums the per-chunk partials of dA_h and dD_h.
+#include <type_traits>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -518,21 +520,160 @@ __global__ __launch_bounds__(256) void k_chunk_bwd(
 }
 
 // ---------------------------------------------------------------------------
-// bfloat16 version of k_chunk_bwd with each tile's global operands gathered
-// into one register set and loaded one tile ahead: a wave issues every load
-// of its next tile (the C or B row, the C B^T row segments, the dy and x
-// rows it dots with) before it computes the current one, so the loads of a
-// tile wait once instead of one after another inside the loops.  Same
-// phases, results and outputs as k_chunk_bwd.
+// The chunk's C and B rows and the blocks of M = C B^T that k_chunk_bwd_pf
+// reads, written in the order its waves load them: every wave load is then
+// one contiguous 1 KiB block (64 lanes x 16 bytes) instead of sixteen pieces
+// of different rows.  Per (b, c, g), with T16 = Q / 16 row tiles, a lane
+// l = 16 grp + r and NCF = ceil(N / 32):
+//   Cf, Bf [T16][NCF][64][8]  C (B) row 16 I + r, columns 32 kc + 8 grp ...
+//   Gy     [T16][8][64][8]    M row 16 I + r, columns 32 sg + 8 grp ...
+//                             (blocks sg <= I / 2: the rows' causal part)
+//   Gx     [T16][8][64][8]    M column 16 J + r, rows 32 sg + 8 grp ...
+//                             (blocks sg >= J / 2)
+//   dg     [Q]                M_jj (float32)
+// Steps at or past the chunk's length read as zero.  One workgroup per
+// (b, c, g, tile I): the row pieces of tile I, the Gy blocks of row tile I
+// and the Gx blocks of column tile J = I, one 16 x 16 MFMA tile per wave.
 // ---------------------------------------------------------------------------
+template <int N>
+__global__ __launch_bounds__(256) void k_bwd_frags(const bf16 *__restrict__ B,
+                                                   const bf16 *__restrict__ C, bf16 *__restrict__ Gy,
+                                                   bf16 *__restrict__ Gx, bf16 *__restrict__ Cf,
+                                                   bf16 *__restrict__ Bf, float *__restrict__ dg,
+                                                   int64_t L, int G, int Q, int nc) {
+    constexpr int NCF = (N + 31) / 32;
+    const int T16 = Q / 16, I = blockIdx.y;
+    const int64_t bcg = blockIdx.x;
+    const int g = (int)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int c = (int)(bc % nc);
+    const int64_t b = bc / nc;
+    const int64_t s = (int64_t)c * Q;
+    const int q = (int)min<int64_t>(Q, L - s);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, grp = lane >> 4;
+    const bf16 *Cc = C + ((b * L + s) * G + g) * N, *Bc = B + ((b * L + s) * G + g) * N;
+    const int64_t ld = (int64_t)G * N;
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+    auto row_piece = [&](const bf16 *base, int i, int k) {
+        return (i < q && k < N) ? *(const u32x4 *)(base + i * ld + k) : z4;
+    };
+    const int64_t tile0 = bcg * T16;  // first tile of this (b, c, g)
+
+    // row pieces of tile I
+    for (int kc = wave; kc < NCF; kc += 4) {
+        const int i = 16 * I + r, k = 32 * kc + 8 * grp;
+        const int64_t o = (((tile0 + I) * NCF + kc) * 64 + lane) * 8;
+        *(u32x4 *)(Cf + o) = row_piece(Cc, i, k);
+        *(u32x4 *)(Bf + o) = row_piece(Bc, i, k);
+    }
+    // 16 x 16 tile of M: rows 16 ti .., columns 16 tj ..; TRANS: lane (r, grp)
+    // ends with M[16 ti + 4 grp + e][16 tj + r], else M[16 ti + r][16 tj + 4 grp + e]
+    auto mtile = [&](int ti, int tj, bool trans) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int ia = trans ? 16 * ti + r : 16 * tj + r;  // A rows: C (trans) or B
+        const int ib = trans ? 16 * tj + r : 16 * ti + r;  // B rows: B (trans) or C
+        const bf16 *Abase = trans ? Cc : Bc, *Bbase = trans ? Bc : Cc;
+#pragma unroll
+        for (int kc = 0; kc < NCF; ++kc) {
+            const int k = 32 * kc + 8 * grp;
+            acc = mfma_bf16(as_bf16x8(row_piece(Abase, ia, k)), as_bf16x8(row_piece(Bbase, ib, k)), acc);
+        }
+        return acc;
+    };
+    auto put4 = [&](bf16 *dst, f32x4 v) {
+        bf16 o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+        *(u32x2 *)dst = *(const u32x2 *)o;
+    };
+    // a 16-step tile t inside 32-block t / 2 goes to lane group 2 (t % 2) + grp / 2,
+    // elements 4 (grp % 2) ..
+    auto frag_off = [&](int tile, int t) {
+        return ((((tile0 + tile) * 8 + t / 2) * 64) + (2 * (t & 1) + grp / 2) * 16 + r) * 8 + 4 * (grp & 1);
+    };
+    // Gy: row tile I, column tiles 0 .. 2 (I / 2) + 1 (the last 32-block is the diagonal one)
+    const int ny = min(2 * (I / 2) + 2, T16);
+    for (int t = wave; t < ny; t += 4) put4(Gy + frag_off(I, t), mtile(I, t, false));
+    // Gx: column tile J = I, row tiles 2 (I / 2) .. T16 - 1
+    for (int t = 2 * (I / 2) + wave; t < T16; t += 4) {
+        const f32x4 m = mtile(t, I, true);
+        put4(Gx + frag_off(I, t), m);
+        if (t == I) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * grp + e == r) dg[bcg * Q + 16 * I + r] = m[e];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 [P][N] state -> bf16 [P][ld] in LDS by NT threads with every load
+// issued before the first conversion.  With DOT, also this thread's part of
+// sum(src * other) over the same elements (other has src's layout).
+// ---------------------------------------------------------------------------
+template <int P, int N, int NT, bool DOT>
+__device__ __forceinline__ float stage_state_all(const float *__restrict__ src,
+                                                 const float *__restrict__ other, bf16 *dst,
+                                                 int ld) {
+    constexpr int NI = P * N / 8, IT = (NI + NT - 1) / NT;
+    f32x4 a[IT][2], o[IT][2];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int idx = min((int)threadIdx.x + it * NT, NI - 1);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            a[it][k] = *(const f32x4 *)(src + 8 * idx + 4 * k);
+            if constexpr (DOT) o[it][k] = *(const f32x4 *)(other + 8 * idx + 4 * k);
+        }
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int idx = (int)threadIdx.x + it * NT;
+        if (NI % NT == 0 || idx < NI) {
+            const int p = idx / (N / 8), n0 = (idx - p * (N / 8)) * 8;
+            bf16x8 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = (bf16)a[it][0][e];
+                v[e + 4] = (bf16)a[it][1][e];
+            }
+            *(bf16x8 *)(dst + p * ld + n0) = v;
+            if constexpr (DOT) acc += dot4(a[it][0], o[it][0]) + dot4(a[it][1], o[it][1]);
+        }
+    }
+    return acc;
+}
+
+// ---------------------------------------------------------------------------
+// bfloat16 version of k_chunk_bwd, one workgroup per (b, c, h), that keeps
+// the global loads of the next row tile in flight while the current one
+// computes.  A wave's tile operands (its row of C or B, the blocks of M =
+// C B^T of that row or column, 4 channels of the dy and x rows it dots with,
+// the diagonal M_jj) are one register set; two sets alternate, so set k + 1
+// loads while set k computes.  C, B and the M blocks come in the fragment
+// order k_bwd_frags writes, one contiguous 1 KiB block per wave load.  Every
+// global access goes through a buffer resource and a lane with nothing to
+// load is given an offset past the resource's end, so no load or store sits
+// behind a branch and the compiler's counted waits stay exact (a load behind
+// a branch makes it wait for every load in flight).  The four rounds of row
+// tiles are unrolled, and round R loads only the M blocks its tiles can use
+// (2 R + 2 causal blocks of a row; 8 - 2 R of a column).  Same phases,
+// results and outputs as k_chunk_bwd.  The launcher requires Q <= 256 and
+// Q * H * P * 2 < 2^31 (every offset fits the 32-bit range).
+// ---------------------------------------------------------------------------
+template <int R>
+using RoundC = std::integral_constant<int, R>;
+
 template <int P, int N>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_chunk_bwd_pf(
     const bf16 *__restrict__ x, const bf16 *__restrict__ dy, const bf16 *__restrict__ dt,
-    const float *__restrict__ A, const bf16 *__restrict__ B, const bf16 *__restrict__ C,
-    const bf16 *__restrict__ cb, const bf16 *__restrict__ cbT, const float *__restrict__ cs,
-    const float *__restrict__ Hs, const float *__restrict__ Rs, const float *__restrict__ D,
-    bf16 *__restrict__ dx, bf16 *__restrict__ ddt, float *__restrict__ part, int64_t L, int H,
-    int G, int Q, int nc) {
+    const float *__restrict__ A, const bf16 *__restrict__ Bf, const bf16 *__restrict__ Cf,
+    const bf16 *__restrict__ Gy, const bf16 *__restrict__ Gx, const float *__restrict__ dg,
+    const float *__restrict__ cs, const float *__restrict__ Hs, const float *__restrict__ Rs,
+    const float *__restrict__ D, bf16 *__restrict__ dx, bf16 *__restrict__ ddt,
+    float *__restrict__ part, int64_t L, int H, int G, int Q, int nc) {
     constexpr int PT = P / 16, NCF = (N + 31) / 32, NSEG = 8;
     const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
     const int h = (int)(wid % H);
@@ -544,7 +685,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int q = (int)min<int64_t>(Q, L - s);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, grp = lane >> 4;
-    const int Qp = (Q + 31) & ~31;
 
     __shared__ float cs_s[256], yy_s[256], xdx_s[256], red_s[4][3];
     const float *csc = cs + (((int64_t)b * H + h) * nc + c) * Q;
@@ -554,29 +694,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         xdx_s[j] = 0.f;
     }
     const int64_t row0 = (b * L + s) * H + h;
-    const bf16 *Cb = C + ((b * L + s) * G + g) * N;
-    const bf16 *Bb = B + ((b * L + s) * G + g) * N;
-    const int64_t cboff = (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
-    const bf16 *cbc = cb + cboff, *cbTc = cbT + cboff;
+    const int T16Q = Q / 16;
+    const int64_t tile0 = (((int64_t)b * nc + c) * G + g) * T16Q;  // first fragment tile
     const int64_t soff = (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
     const float *hp = Hs + soff, *rp = Rs + soff;
     const float Dh = D ? D[h] : 0.f;
+    // byte stride between consecutive steps of one head's rows
+    const uint32_t rowb = (uint32_t)H * P * 2;
+    const auto rsCf = buf_rsrc(Cf + tile0 * NCF * 512, (uint32_t)T16Q * NCF * 1024);
+    const auto rsBf = buf_rsrc(Bf + tile0 * NCF * 512, (uint32_t)T16Q * NCF * 1024);
+    const auto rsGy = buf_rsrc(Gy + tile0 * NSEG * 512, (uint32_t)T16Q * NSEG * 1024);
+    const auto rsGx = buf_rsrc(Gx + tile0 * NSEG * 512, (uint32_t)T16Q * NSEG * 1024);
+    const auto rsDg = buf_rsrc(dg + tile0 * 16, (uint32_t)Q * 4);
+    const auto rsDY = buf_rsrc(dy + row0 * P, (uint32_t)q * rowb);
+    const auto rsX = buf_rsrc(x + row0 * P, (uint32_t)q * rowb);
+    const auto rsDX = buf_rsrc(dx + row0 * P, (uint32_t)q * rowb);
 
     constexpr int XLD = 256 + 8, HLD = N + 8;
     __shared__ bf16 ops_s[P * XLD];
     __shared__ bf16 st_s[P * HLD];
     const u32x4 z4 = {0u, 0u, 0u, 0u};
-    const u32x2 z2 = {0u, 0u};
     const int T16 = (q + 15) / 16;
     auto tile_of = [&](int round) { return 4 * round + ((round & 1) ? 3 - wave : wave); };
-    const int nrounds = (T16 + 3) / 4;
 
-    // operands of one tile: the lane's row of C (phase Y) or B (phase X), its C B^T
-    // segments, and 4 channels of the rows it dots with (dy; in phase X also x)
     struct Ops {
         u32x4 vr[NCF];
         u32x4 gs[NSEG];
         u32x2 d4[PT], x4[PT];
+        float dg;
     };
     auto state_mma = [&](f32x4 *acc, const Ops &o) {
 #pragma unroll
@@ -589,53 +734,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
     };
+    auto frag = [&](int tile, int blk) { return (uint32_t)((tile * NSEG + blk) * 64 + lane) * 16u; };
 
     // ---------------- phase Y ----------------
-    auto load_y = [&](int I, Ops &o) {
+    // round R: row tiles up to 4 R + 3, so causal blocks 0 .. 2 R + 1
+    auto load_y = [&](auto RC, Ops &o) {
+        constexpr int R = decltype(RC)::value, NSY = 2 * R + 2;
+        const int I = tile_of(R);
         const int il = I * 16 + r;
-        const bool vi = il < q;
-        const bf16 *crow = Cb + (int64_t)il * G * N;
+        const bool vi = I < T16 && il < q;
+        const uint32_t drow = (uint32_t)il * rowb;
 #pragma unroll
         for (int kc = 0; kc < NCF; ++kc) {
             const int kk = kc * 32 + grp * 8;
-            o.vr[kc] = (vi && kk < N) ? *(const u32x4 *)(crow + kk) : z4;
+            o.vr[kc] = buf_ld16(rsCf, (vi && kk < N) ? (uint32_t)((I * NCF + kc) * 64 + lane) * 16u : kBufOff);
         }
-        const bf16 *grow = cbc + (int64_t)il * Q;
 #pragma unroll
-        for (int sg = 0; sg < NSEG; ++sg) {
+        for (int sg = 0; sg < NSY; ++sg) {
             const int jl = sg * 32 + grp * 8;
-            o.gs[sg] = (sg * 32 <= I * 16 + 15 && jl < il) ? *(const u32x4 *)(grow + jl) : z4;
+            o.gs[sg] = buf_ld16(rsGy, (vi && sg * 32 <= I * 16 + 15 && jl < il) ? frag(I, sg) : kBufOff);
         }
-        const bf16 *dyr = dy + (row0 + (int64_t)il * H) * P;
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) o.d4[pt] = vi ? *(const u32x2 *)(dyr + pt * 16 + 4 * grp) : z2;
+        for (int pt = 0; pt < PT; ++pt)
+            o.d4[pt] = buf_ld8(rsDY, vi ? drow + 2u * (pt * 16 + 4 * grp) : kBufOff);
     };
-    stage_transposed_bf16<false>(x + row0 * P, (int64_t)H * P, Qp, P, q, ops_s, XLD, nullptr);
-    stage_state_bf16<P, N>(hp, st_s, HLD);
-    Ops cur, nxt;
-    if (nrounds > 0 && tile_of(0) < T16) load_y(tile_of(0), cur);
-    __syncthreads();
-    for (int round = 0; round < nrounds; ++round) {
-        const int I = tile_of(round);
-        const bool have = I < T16;
-        const int In = tile_of(round + 1);
-        if (round + 1 < nrounds && In < T16) load_y(In, nxt);
-        if (have) {
-            const int il = I * 16 + r;
-            const bool vi = il < q;
-            const float csi = cs_s[il];
-            f32x4 acc[PT];
+    auto comp_y = [&](auto RC, const Ops &o) {
+        constexpr int R = decltype(RC)::value, NSY = 2 * R + 2;
+        const int I = tile_of(R);
+        const int il = I * 16 + r;
+        f32x4 acc[PT];
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            state_mma(acc, cur);
+        for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (I < T16) {
+            const float csi = cs_s[min(il, 255)];
+            state_mma(acc, o);
             const float ei = __expf(csi);
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) acc[pt] *= ei;
 #pragma unroll
-            for (int sg = 0; sg < NSEG; ++sg) {
+            for (int sg = 0; sg < NSY; ++sg) {
                 if (sg * 32 <= I * 16 + 15) {
                     const int jl = sg * 32 + grp * 8;
-                    const bf16x8 gv = as_bf16x8(cur.gs[sg]);
+                    const bf16x8 gv = as_bf16x8(o.gs[sg]);
                     bf16x8 bm;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
@@ -649,79 +789,84 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     }
                 }
             }
-            float yy = 0.f;
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) yy += dot4(acc[pt], load4((const bf16 *)&cur.d4[pt]));
-            yy = sum_groups(yy);
-            if (grp == 0 && vi) yy_s[il] = yy;
         }
-        cur = nxt;
-    }
+        float yy = 0.f;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) yy += dot4(acc[pt], load4((const bf16 *)&o.d4[pt]));
+        yy = sum_groups(yy);
+        if (grp == 0 && il < q) yy_s[il] = yy;
+    };
+    stage_transposed_rs<256, P, 256>(rsX, rowb, q, ops_s, XLD);
+    stage_state_all<P, N, 256, false>(hp, nullptr, st_s, HLD);
+    Ops o0, o1;
+    load_y(RoundC<0>{}, o0);
+    __syncthreads();
+    load_y(RoundC<1>{}, o1);
+    comp_y(RoundC<0>{}, o0);
+    load_y(RoundC<2>{}, o0);
+    comp_y(RoundC<1>{}, o1);
+    load_y(RoundC<3>{}, o1);
+    comp_y(RoundC<2>{}, o0);
+    comp_y(RoundC<3>{}, o1);
     __syncthreads();
 
     // ---------------- phase X ----------------
-    auto load_x = [&](int J, Ops &o) {
+    // round R: column tiles from 4 R, so row blocks 2 R .. 7
+    auto load_x = [&](auto RC, Ops &o) {
+        constexpr int R = decltype(RC)::value, SX0 = 2 * R;
+        const int J = tile_of(R);
         const int jl = J * 16 + r;
-        const bool vj = jl < q;
-        const bf16 *brow = Bb + (int64_t)jl * G * N;
+        const bool vj = J < T16 && jl < q;
+        const uint32_t drow = (uint32_t)jl * rowb;
 #pragma unroll
         for (int kc = 0; kc < NCF; ++kc) {
             const int kk = kc * 32 + grp * 8;
-            o.vr[kc] = (vj && kk < N) ? *(const u32x4 *)(brow + kk) : z4;
+            o.vr[kc] = buf_ld16(rsBf, (vj && kk < N) ? (uint32_t)((J * NCF + kc) * 64 + lane) * 16u : kBufOff);
         }
-        const bf16 *gcol = cbTc + (int64_t)jl * Q;
         const int ilo = (J * 16) & ~31;
 #pragma unroll
-        for (int sg = 0; sg < NSEG; ++sg) {
+        for (int sg = SX0; sg < NSEG; ++sg) {
             const int i0 = sg * 32, il = i0 + grp * 8;
-            o.gs[sg] = (i0 >= ilo && i0 < q && il + 7 > jl && il < q) ? *(const u32x4 *)(gcol + il) : z4;
+            const bool need = vj && i0 >= ilo && i0 < q && il + 7 > jl && il < q;
+            o.gs[sg] = buf_ld16(rsGx, need ? frag(J, sg) : kBufOff);
         }
-        const bf16 *dyr = dy + (row0 + (int64_t)jl * H) * P;
-        const bf16 *xr = x + (row0 + (int64_t)jl * H) * P;
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
-            o.d4[pt] = vj ? *(const u32x2 *)(dyr + pt * 16 + 4 * grp) : z2;
-            o.x4[pt] = vj ? *(const u32x2 *)(xr + pt * 16 + 4 * grp) : z2;
+            const uint32_t off = vj ? drow + 2u * (pt * 16 + 4 * grp) : kBufOff;
+            o.d4[pt] = buf_ld8(rsDY, off);
+            o.x4[pt] = buf_ld8(rsX, off);
         }
+        o.dg = buf_ldf(rsDg, vj ? 4u * jl : kBufOff);  // M_jj
     };
-    stage_transposed_bf16<false>(dy + row0 * P, (int64_t)H * P, Qp, P, q, ops_s, XLD, nullptr);
-    stage_state_bf16<P, N>(rp, st_s, HLD);
-    float rh = 0.f;  // <R_c, H_c>
-    for (int idx = threadIdx.x; idx < P * N / 4; idx += 256)
-        rh += dot4(*(const f32x4 *)(rp + 4 * idx), *(const f32x4 *)(hp + 4 * idx));
-    if (nrounds > 0 && tile_of(0) < T16) load_x(tile_of(0), cur);
-    __syncthreads();
-
     const float csE = cs_s[q - 1];
     float vsum = 0.f, dDp = 0.f;
-    for (int round = 0; round < nrounds; ++round) {
-        const int J = tile_of(round);
-        const bool have = J < T16;
-        const int Jn = tile_of(round + 1);
-        if (round + 1 < nrounds && Jn < T16) load_x(Jn, nxt);
-        if (have) {
-            const int jl = J * 16 + r;
-            const bool vj = jl < q;
-            const float csj = cs_s[jl];
-            f32x4 acc[PT];
+    auto comp_x = [&](auto RC, const Ops &o) {
+        constexpr int R = decltype(RC)::value, SX0 = 2 * R;
+        const int J = tile_of(R);
+        const int jl = J * 16 + r;
+        const bool vj = jl < q;
+        f32x4 acc[PT], xv[PT];
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            state_mma(acc, cur);
+        for (int pt = 0; pt < PT; ++pt) {
+            acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            xv[pt] = load4((const bf16 *)&o.x4[pt]);
+        }
+        if (J < T16) {
+            const float csj = cs_s[min(jl, 255)];
+            state_mma(acc, o);
             const float wj = __expf(csE - csj);
-            f32x4 xv[PT];
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
                 acc[pt] *= wj;
-                xv[pt] = load4((const bf16 *)&cur.x4[pt]);
                 vsum += dot4(acc[pt], xv[pt]);
             }
             const int ilo = (J * 16) & ~31;
 #pragma unroll
-            for (int sg = 0; sg < NSEG; ++sg) {
+            for (int sg = SX0; sg < NSEG; ++sg) {
                 const int i0 = sg * 32;
                 if (i0 >= ilo && i0 < q) {
                     const int il = i0 + grp * 8;
-                    const bf16x8 gv = as_bf16x8(cur.gs[sg]);
+                    const bf16x8 gv = as_bf16x8(o.gs[sg]);
                     bf16x8 bm;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
@@ -735,29 +880,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     }
                 }
             }
-            float xd = 0.f;
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) xd += dot4(acc[pt], xv[pt]);
-            xd = sum_groups(xd);
-            if (grp == 0 && vj) xdx_s[jl] = xd;
-            if (vj) {
-                bf16 *dxr = dx + (row0 + (int64_t)jl * H) * P;
-                const float diag = (float)cbc[(int64_t)jl * Q + jl] + Dh;  // M_jj + D
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-                    const f32x4 d4 = load4((const bf16 *)&cur.d4[pt]);
-                    dDp += dot4(d4, xv[pt]);
-                    store4(dxr + pt * 16 + 4 * grp, acc[pt] + diag * d4);
-                }
-            }
         }
-        cur = nxt;
-    }
+        float xd = 0.f;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) xd += dot4(acc[pt], xv[pt]);
+        xd = sum_groups(xd);
+        if (grp == 0 && vj) xdx_s[jl] = xd;
+        const float diag = o.dg + Dh;  // M_jj + D
+        const uint32_t drow = (uint32_t)jl * rowb;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const f32x4 d4 = load4((const bf16 *)&o.d4[pt]);
+            dDp += dot4(d4, xv[pt]);
+            const f32x4 v = acc[pt] + diag * d4;
+            bf16 ob[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ob[e] = (bf16)v[e];
+            buf_st8(*(const u32x2 *)ob, rsDX, vj ? drow + 2u * (pt * 16 + 4 * grp) : kBufOff);
+        }
+    };
+    stage_transposed_rs<256, P, 256>(rsDY, rowb, q, ops_s, XLD);
     {
-        const float v0 = wave_sum(vsum), v1 = wave_sum(rh), v2 = wave_sum(dDp);
+        // <R_c, H_c>, reduced here so that the products are not kept to the end
+        const float rh = wave_sum(stage_state_all<P, N, 256, true>(rp, hp, st_s, HLD));
+        if (lane == 0) red_s[wave][1] = rh;
+    }
+    load_x(RoundC<0>{}, o0);
+    __syncthreads();
+    load_x(RoundC<1>{}, o1);
+    comp_x(RoundC<0>{}, o0);
+    load_x(RoundC<2>{}, o0);
+    comp_x(RoundC<1>{}, o1);
+    load_x(RoundC<3>{}, o1);
+    comp_x(RoundC<2>{}, o0);
+    comp_x(RoundC<3>{}, o1);
+    {
+        const float v0 = wave_sum(vsum), v2 = wave_sum(dDp);
         if (lane == 0) {
             red_s[wave][0] = v0;
-            red_s[wave][1] = v1;
             red_s[wave][2] = v2;
         }
     }
@@ -1537,19 +1697,40 @@ hipError_t launch_chunk_cumsum64(const Dims &d, const void *dt, const float *A, 
 }
 
 // bf16 inputs use the float32 prefix (cs), float32 inputs the float64 one (cs64).
+bool chunk_bwd_frags(const Dims &d) {
+    return d.dtype == 1 && d.Q <= 256 && d.Q % 16 == 0 && d.Q * d.H * d.P * 2 < (int64_t(1) << 31);
+}
+
+BwdFragBytes bwd_frag_bytes(const Dims &d) {
+    const int64_t nbcg = d.b * d.nc * d.G, t16 = d.Q / 16, ncf = (d.N + 31) / 32;
+    return BwdFragBytes{nbcg * t16 * ncf * 1024, nbcg * t16 * 8 * 1024, nbcg * d.Q * 4};
+}
+
+hipError_t launch_bwd_frags(const Dims &d, const void *B, const void *C, void *Gy, void *Gx,
+                            void *Cf, void *Bf, float *dg, hipStream_t st) {
+    if (d.b == 0 || d.nc == 0) return hipSuccess;
+    dim3 grid((unsigned)(d.b * d.nc * d.G), (unsigned)(d.Q / 16));
+    SSD_BWD_DISPATCH_N(d.N, {
+        k_bwd_frags<NN><<<grid, 256, 0, st>>>((const bf16 *)B, (const bf16 *)C, (bf16 *)Gy,
+                                              (bf16 *)Gx, (bf16 *)Cf, (bf16 *)Bf, dg, d.L, (int)d.G,
+                                              (int)d.Q, (int)d.nc);
+    });
+    return hipGetLastError();
+}
+
 hipError_t launch_chunk_bwd(const Dims &d, const void *x, const void *dy, const void *dt,
                             const float *A, const void *B, const void *C, const void *cb,
-                            const void *cbT, const float *cs, const double *cs64, const float *Hs,
-                            const float *Rs, const float *D, void *dx, void *ddt, float *part,
-                            hipStream_t st) {
+                            const void *cbT, const void *Cf, const void *Bf, const float *dg,
+                            const float *cs, const double *cs64, const float *Hs, const float *Rs,
+                            const float *D, void *dx, void *ddt, float *part, hipStream_t st) {
     if (d.b == 0 || d.nc == 0) return hipSuccess;
     const unsigned grid = (unsigned)(d.b * d.nc * d.H);
     SSD_BWD_DISPATCH_PN(d.P, d.N, {
-        if (d.dtype == 1 && d.Q <= 256)
+        if (chunk_bwd_frags(d))
             k_chunk_bwd_pf<PP, NN><<<grid, 256, 0, st>>>(
-                (const bf16 *)x, (const bf16 *)dy, (const bf16 *)dt, A, (const bf16 *)B,
-                (const bf16 *)C, (const bf16 *)cb, (const bf16 *)cbT, cs, Hs, Rs, D, (bf16 *)dx,
-                (bf16 *)ddt, part, d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc);
+                (const bf16 *)x, (const bf16 *)dy, (const bf16 *)dt, A, (const bf16 *)Bf,
+                (const bf16 *)Cf, (const bf16 *)cb, (const bf16 *)cbT, dg, cs, Hs, Rs, D,
+                (bf16 *)dx, (bf16 *)ddt, part, d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc);
         else if (d.dtype == 1)
             k_chunk_bwd<bf16, PP, NN, float><<<grid, 256, 0, st>>>(
                 (const bf16 *)x, (const bf16 *)dy, (const bf16 *)dt, A, (const bf16 *)B,

@@ -261,6 +261,49 @@ __device__ __forceinline__ void copy_tile_to_lds(const bf16 *__restrict__ src, i
     }
 }
 
+// Buffer resource over [base, base + bytes), bytes < 2^31.  A load at an
+// offset at or past `bytes` returns zero and a store there is dropped, so a
+// lane is switched off by giving it the offset kBufOff: no branch, and the
+// instruction counts in vmcnt like every other, which keeps the compiler's
+// counted waits exact across a loop.
+constexpr uint32_t kBufOff = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_ld8(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, 0);
+}
+__device__ __forceinline__ float buf_ldf(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint16_t buf_ld2(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(rs, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_st8(u32x2 v, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, rs, (int)off, 0, 0);
+}
+
+// Four rows r0..r0+3 of 8 bf16 columns c0..c0+7 (v[k] = row r0 + k) stored
+// transposed, dst[c * dstride + r]: a register transpose with byte permutes
+// and eight 8-byte LDS stores.
+__device__ __forceinline__ void write_transposed_4x8(const u32x4 (&v)[4], bf16 *dst, int dstride,
+                                                     int r0, int c0) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        // dword m of each row holds columns c0 + 2m (low half) and c0 + 2m + 1 (high half)
+        const uint32_t lo01 = __builtin_amdgcn_perm(v[1][m], v[0][m], 0x05040100u);
+        const uint32_t lo23 = __builtin_amdgcn_perm(v[3][m], v[2][m], 0x05040100u);
+        const uint32_t hi01 = __builtin_amdgcn_perm(v[1][m], v[0][m], 0x07060302u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(v[3][m], v[2][m], 0x07060302u);
+        *(u32x2 *)(dst + (c0 + 2 * m) * dstride + r0) = u32x2{lo01, lo23};
+        *(u32x2 *)(dst + (c0 + 2 * m + 1) * dstride + r0) = u32x2{hi01, hi23};
+    }
+}
+
 // Copy a [rows x cols] bf16 tile from global memory (row stride `ld`
 // elements) into LDS transposed: dst[c * dstride + r] = src[r * ld + c],
 // optionally times scale[r] (rounded back to bf16).  Rows >= nvalid read as
@@ -293,16 +336,35 @@ __device__ __forceinline__ void stage_transposed_bf16(const bf16 *__restrict__ s
                 v[k] = u32x4{0u, 0u, 0u, 0u};
             }
         }
+        write_transposed_4x8(v, dst, dstride, r0, c0);
+    }
+}
+
+// The same transposed copy for NROWS rows and COLS columns known at compile
+// time, by NT threads, reading through a buffer resource: row r starts at
+// byte r * ldb from the resource base, and rows at or past nvalid read as
+// zero.  Every load is issued before the first LDS store and none sits
+// behind a branch.
+template <int NROWS, int COLS, int NT>
+__device__ __forceinline__ void stage_transposed_rs(__amdgpu_buffer_rsrc_t rs, uint32_t ldb,
+                                                    int nvalid, bf16 *dst, int dstride) {
+    constexpr int NBC = COLS / 8, NB = (NROWS / 4) * NBC, IT = (NB + NT - 1) / NT;
+    u32x4 v[IT][4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            // dword m of each row holds columns c0 + 2m (low half) and c0 + 2m + 1 (high half)
-            const uint32_t lo01 = __builtin_amdgcn_perm(v[1][m], v[0][m], 0x05040100u);
-            const uint32_t lo23 = __builtin_amdgcn_perm(v[3][m], v[2][m], 0x05040100u);
-            const uint32_t hi01 = __builtin_amdgcn_perm(v[1][m], v[0][m], 0x07060302u);
-            const uint32_t hi23 = __builtin_amdgcn_perm(v[3][m], v[2][m], 0x07060302u);
-            *(u32x2 *)(dst + (c0 + 2 * m) * dstride + r0) = u32x2{lo01, lo23};
-            *(u32x2 *)(dst + (c0 + 2 * m + 1) * dstride + r0) = u32x2{hi01, hi23};
+    for (int it = 0; it < IT; ++it) {
+        const int blk = (int)threadIdx.x + it * NT;
+        const int br = blk / NBC, bc = blk - br * NBC;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = 4 * br + k;
+            v[it][k] = buf_ld16(rs, (blk < NB && r < nvalid) ? (uint32_t)r * ldb + 16u * bc : kBufOff);
         }
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int blk = (int)threadIdx.x + it * NT;
+        const int br = blk / NBC, bc = blk - br * NBC;
+        if (NB % NT == 0 || blk < NB) write_transposed_4x8(v[it], dst, dstride, 4 * br, 8 * bc);
     }
 }
 

@@ -66,11 +66,24 @@ hipError_t launch_state_passing_rev(const Dims &d, float *S, const float *cs, co
                                     float *dinit, hipStream_t st);
 hipError_t launch_chunk_cumsum64(const Dims &d, const void *dt, const float *A, double *cs,
                                  hipStream_t st);
+// bfloat16 chunk backward with its operands in fragment order: when true,
+// launch_chunk_bwd reads C, B and C B^T from the arrays launch_bwd_frags
+// writes (Gy and Gx in place of cb and cbT, whose workspace slots they take;
+// sizes in bwd_frag_bytes) and ignores B, C, cb's row-major form.
+bool chunk_bwd_frags(const Dims &d);
+struct BwdFragBytes {
+    int64_t rows;    // Cf, Bf each
+    int64_t blocks;  // Gy, Gx each
+    int64_t diag;    // dg
+};
+BwdFragBytes bwd_frag_bytes(const Dims &d);
+hipError_t launch_bwd_frags(const Dims &d, const void *B, const void *C, void *Gy, void *Gx,
+                            void *Cf, void *Bf, float *dg, hipStream_t st);
 hipError_t launch_chunk_bwd(const Dims &d, const void *x, const void *dy, const void *dt,
                             const float *A, const void *B, const void *C, const void *cb,
-                            const void *cbT, const float *cs, const double *cs64, const float *Hs,
-                            const float *Rs, const float *D, void *dx, void *ddt, float *part,
-                            hipStream_t st);
+                            const void *cbT, const void *Cf, const void *Bf, const float *dg,
+                            const float *cs, const double *cs64, const float *Hs, const float *Rs,
+                            const float *D, void *dx, void *ddt, float *part, hipStream_t st);
 hipError_t launch_group_bwd(const Dims &d, const void *x, const void *dy, const float *cs,
                             const double *cs64, const float *Hs, const float *Rs, float *dcb,
                             float *dcbT, float *dCs, float *dBs, hipStream_t st);

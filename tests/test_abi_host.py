@@ -263,10 +263,15 @@ def test_backward_workspace_bytes():
     b, L, H, P, N, G, Q = 2, 100, 4, 64, 128, 2, 64
     nc = 2
     al = lambda v: (v + 255) & ~255
+    # bfloat16: C B^T and its transpose as fragment blocks (per (b, c, g): Q / 16 row tiles x 8
+    # blocks of 1 KiB), then the C and B rows in fragment order (Q / 16 x ceil(N / 32) blocks of
+    # 1 KiB each) and the float32 diagonal of C B^T
+    nbcg, t16, ncf = b * nc * G, Q // 16, (N + 31) // 32
     o = 0
-    for nbytes in [b * H * nc * Q * 4, b * nc * G * Q * Q * 2, b * nc * G * Q * Q * 2, b * nc * H * P * N * 4,
+    for nbytes in [b * H * nc * Q * 4, nbcg * t16 * 8 * 1024, nbcg * t16 * 8 * 1024, b * nc * H * P * N * 4,
                    b * nc * H * P * N * 4, b * nc * G * Q * Q * 4, b * nc * G * Q * Q * 4, b * L * G * N * 4,
-                   b * L * G * N * 4, b * nc * H * 2 * 4, 0]:
+                   b * L * G * N * 4, b * nc * H * 2 * 4, 0, nbcg * t16 * ncf * 1024, nbcg * t16 * ncf * 1024,
+                   nbcg * Q * 4]:
         o = al(o + nbytes)
     assert ssd.backward_workspace_bytes(dims()) == o
     # float32 inputs add a float64 decay prefix

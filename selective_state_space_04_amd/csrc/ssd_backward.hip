@@ -608,14 +608,14 @@ __global__ __launch_bounds__(256) void k_bwd_frags(const bf16 *__restrict__ B,
 }
 
 // ---------------------------------------------------------------------------
-// fp32 [P][N] state -> bf16 [P][ld] in LDS by NT threads with every load
-// issued before the first conversion.  With DOT, also this thread's part of
+// fp32 [P][N] state -> bf16 [P][ld] in LDS (row p at rowof(p)) by NT
+// threads with every load issued before the first conversion.  With DOT, also this thread's part of
 // sum(src * other) over the same elements (other has src's layout).
 // ---------------------------------------------------------------------------
-template <int P, int N, int NT, bool DOT>
+template <int P, int N, int NT, bool DOT, typename RowOf = RowIdentity>
 __device__ __forceinline__ float stage_state_all(const float *__restrict__ src,
                                                  const float *__restrict__ other, bf16 *dst,
-                                                 int ld) {
+                                                 int ld, RowOf rowof = RowOf{}) {
     constexpr int NI = P * N / 8, IT = (NI + NT - 1) / NT;
     f32x4 a[IT][2], o[IT][2];
 #pragma unroll
@@ -639,7 +639,7 @@ __device__ __forceinline__ float stage_state_all(const float *__restrict__ src,
                 v[e] = (bf16)a[it][0][e];
                 v[e + 4] = (bf16)a[it][1][e];
             }
-            *(bf16x8 *)(dst + p * ld + n0) = v;
+            *(bf16x8 *)(dst + rowof(p) * ld + n0) = v;
             if constexpr (DOT) acc += dot4(a[it][0], o[it][0]) + dot4(a[it][1], o[it][1]);
         }
     }
@@ -735,6 +735,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     };
     auto frag = [&](int tile, int blk) { return (uint32_t)((tile * NSEG + blk) * 64 + lane) * 16u; };
+    // Channel order in LDS: row 16 pt + 4 grp + e holds channel (P / 4) grp + 4 pt + e, so the
+    // accumulators a lane ends with (tile pt, rows 4 grp + e) are the channels (P / 4) grp ..
+    // (P / 4) grp + P / 4 - 1: one contiguous piece of a dy, x or dx row.
+    auto prow = [](int p) { return 16 * ((p % (P / 4)) / 4) + 4 * (p / (P / 4)) + (p & 3); };
+    // this lane's piece of a row at byte offset drow (zero when !valid), as 4-channel pieces
+    auto row_load = [&](__amdgpu_buffer_rsrc_t rs, uint32_t drow, bool valid, u32x2(&out)[PT]) {
+        const uint32_t o = drow + 2u * (P / 4) * grp;
+        if constexpr (PT == 1) {
+            out[0] = buf_ld8(rs, valid ? o : kBufOff);
+        } else {
+#pragma unroll
+            for (int k2 = 0; k2 < PT / 2; ++k2) {
+                const u32x4 t = buf_ld16(rs, valid ? o + 16u * k2 : kBufOff);
+                out[2 * k2] = u32x2{t[0], t[1]};
+                out[2 * k2 + 1] = u32x2{t[2], t[3]};
+            }
+        }
+    };
 
     // ---------------- phase Y ----------------
     // round R: row tiles up to 4 R + 3, so causal blocks 0 .. 2 R + 1
@@ -754,9 +772,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int jl = sg * 32 + grp * 8;
             o.gs[sg] = buf_ld16(rsGy, (vi && sg * 32 <= I * 16 + 15 && jl < il) ? frag(I, sg) : kBufOff);
         }
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt)
-            o.d4[pt] = buf_ld8(rsDY, vi ? drow + 2u * (pt * 16 + 4 * grp) : kBufOff);
+        row_load(rsDY, drow, vi, o.d4);
     };
     auto comp_y = [&](auto RC, const Ops &o) {
         constexpr int R = decltype(RC)::value, NSY = 2 * R + 2;
@@ -796,8 +812,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         yy = sum_groups(yy);
         if (grp == 0 && il < q) yy_s[il] = yy;
     };
-    stage_transposed_rs<256, P, 256>(rsX, rowb, q, ops_s, XLD);
-    stage_state_all<P, N, 256, false>(hp, nullptr, st_s, HLD);
+    stage_transposed_rs<256, P, 256>(rsX, rowb, q, ops_s, XLD, prow);
+    stage_state_all<P, N, 256, false>(hp, nullptr, st_s, HLD, prow);
     Ops o0, o1;
     load_y(RoundC<0>{}, o0);
     __syncthreads();
@@ -830,12 +846,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const bool need = vj && i0 >= ilo && i0 < q && il + 7 > jl && il < q;
             o.gs[sg] = buf_ld16(rsGx, need ? frag(J, sg) : kBufOff);
         }
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            const uint32_t off = vj ? drow + 2u * (pt * 16 + 4 * grp) : kBufOff;
-            o.d4[pt] = buf_ld8(rsDY, off);
-            o.x4[pt] = buf_ld8(rsX, off);
-        }
+        row_load(rsDY, drow, vj, o.d4);
+        row_load(rsX, drow, vj, o.x4);
         o.dg = buf_ldf(rsDg, vj ? 4u * jl : kBufOff);  // M_jj
     };
     const float csE = cs_s[q - 1];
@@ -887,7 +899,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         xd = sum_groups(xd);
         if (grp == 0 && vj) xdx_s[jl] = xd;
         const float diag = o.dg + Dh;  // M_jj + D
-        const uint32_t drow = (uint32_t)jl * rowb;
+        const uint32_t drow = (uint32_t)jl * rowb + 2u * (P / 4) * grp;
+        u32x2 packed[PT];
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
             const f32x4 d4 = load4((const bf16 *)&o.d4[pt]);
@@ -896,13 +909,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             bf16 ob[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) ob[e] = (bf16)v[e];
-            buf_st8(*(const u32x2 *)ob, rsDX, vj ? drow + 2u * (pt * 16 + 4 * grp) : kBufOff);
+            packed[pt] = *(const u32x2 *)ob;
+        }
+        if constexpr (PT == 1) {
+            buf_st8(packed[0], rsDX, vj ? drow : kBufOff);
+        } else {
+#pragma unroll
+            for (int k2 = 0; k2 < PT / 2; ++k2)
+                buf_st16(u32x4{packed[2 * k2][0], packed[2 * k2][1], packed[2 * k2 + 1][0],
+                               packed[2 * k2 + 1][1]},
+                         rsDX, vj ? drow + 16u * k2 : kBufOff);
         }
     };
-    stage_transposed_rs<256, P, 256>(rsDY, rowb, q, ops_s, XLD);
+    stage_transposed_rs<256, P, 256>(rsDY, rowb, q, ops_s, XLD, prow);
     {
         // <R_c, H_c>, reduced here so that the products are not kept to the end
-        const float rh = wave_sum(stage_state_all<P, N, 256, true>(rp, hp, st_s, HLD));
+        const float rh = wave_sum(stage_state_all<P, N, 256, true>(rp, hp, st_s, HLD, prow));
         if (lane == 0) red_s[wave][1] = rh;
     }
     load_x(RoundC<0>{}, o0);

@@ -286,12 +286,20 @@ __device__ __forceinline__ uint16_t buf_ld2(__amdgpu_buffer_rsrc_t rs, uint32_t 
 __device__ __forceinline__ void buf_st8(u32x2 v, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b64(v, rs, (int)off, 0, 0);
 }
+__device__ __forceinline__ void buf_st16(u32x4 v, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, 0);
+}
 
 // Four rows r0..r0+3 of 8 bf16 columns c0..c0+7 (v[k] = row r0 + k) stored
 // transposed, dst[c * dstride + r]: a register transpose with byte permutes
 // and eight 8-byte LDS stores.
+// Column c goes to LDS row rowof(c) (the identity unless a caller permutes).
+struct RowIdentity {
+    __device__ int operator()(int c) const { return c; }
+};
+template <typename RowOf = RowIdentity>
 __device__ __forceinline__ void write_transposed_4x8(const u32x4 (&v)[4], bf16 *dst, int dstride,
-                                                     int r0, int c0) {
+                                                     int r0, int c0, RowOf rowof = RowOf{}) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         // dword m of each row holds columns c0 + 2m (low half) and c0 + 2m + 1 (high half)
@@ -299,8 +307,8 @@ __device__ __forceinline__ void write_transposed_4x8(const u32x4 (&v)[4], bf16 *
         const uint32_t lo23 = __builtin_amdgcn_perm(v[3][m], v[2][m], 0x05040100u);
         const uint32_t hi01 = __builtin_amdgcn_perm(v[1][m], v[0][m], 0x07060302u);
         const uint32_t hi23 = __builtin_amdgcn_perm(v[3][m], v[2][m], 0x07060302u);
-        *(u32x2 *)(dst + (c0 + 2 * m) * dstride + r0) = u32x2{lo01, lo23};
-        *(u32x2 *)(dst + (c0 + 2 * m + 1) * dstride + r0) = u32x2{hi01, hi23};
+        *(u32x2 *)(dst + rowof(c0 + 2 * m) * dstride + r0) = u32x2{lo01, lo23};
+        *(u32x2 *)(dst + rowof(c0 + 2 * m + 1) * dstride + r0) = u32x2{hi01, hi23};
     }
 }
 
@@ -345,9 +353,10 @@ __device__ __forceinline__ void stage_transposed_bf16(const bf16 *__restrict__ s
 // byte r * ldb from the resource base, and rows at or past nvalid read as
 // zero.  Every load is issued before the first LDS store and none sits
 // behind a branch.
-template <int NROWS, int COLS, int NT>
+template <int NROWS, int COLS, int NT, typename RowOf = RowIdentity>
 __device__ __forceinline__ void stage_transposed_rs(__amdgpu_buffer_rsrc_t rs, uint32_t ldb,
-                                                    int nvalid, bf16 *dst, int dstride) {
+                                                    int nvalid, bf16 *dst, int dstride,
+                                                    RowOf rowof = RowOf{}) {
     constexpr int NBC = COLS / 8, NB = (NROWS / 4) * NBC, IT = (NB + NT - 1) / NT;
     u32x4 v[IT][4];
 #pragma unroll
@@ -364,7 +373,7 @@ __device__ __forceinline__ void stage_transposed_rs(__amdgpu_buffer_rsrc_t rs, u
     for (int it = 0; it < IT; ++it) {
         const int blk = (int)threadIdx.x + it * NT;
         const int br = blk / NBC, bc = blk - br * NBC;
-        if (NB % NT == 0 || blk < NB) write_transposed_4x8(v[it], dst, dstride, 4 * br, 8 * bc);
+        if (NB % NT == 0 || blk < NB) write_transposed_4x8(v[it], dst, dstride, 4 * br, 8 * bc, rowof);
     }
 }
 

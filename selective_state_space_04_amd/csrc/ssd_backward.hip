@@ -609,42 +609,46 @@ __global__ __launch_bounds__(256) void k_bwd_frags(const bf16 *__restrict__ B,
 
 // ---------------------------------------------------------------------------
 // fp32 [P][N] state -> bf16 [P][ld] in LDS (row p at rowof(p)) by NT
-// threads with every load issued before the first conversion.  With DOT, also this thread's part of
+// threads, in two steps like TrStage: load() issues every load, write()
+// converts and stores.  With DOT, write() also returns this thread's part of
 // sum(src * other) over the same elements (other has src's layout).
 // ---------------------------------------------------------------------------
-template <int P, int N, int NT, bool DOT, typename RowOf = RowIdentity>
-__device__ __forceinline__ float stage_state_all(const float *__restrict__ src,
-                                                 const float *__restrict__ other, bf16 *dst,
-                                                 int ld, RowOf rowof = RowOf{}) {
-    constexpr int NI = P * N / 8, IT = (NI + NT - 1) / NT;
-    f32x4 a[IT][2], o[IT][2];
+template <int P, int N, int NT, bool DOT>
+struct StateStage {
+    static constexpr int NI = P * N / 8, IT = (NI + NT - 1) / NT;
+    f32x4 a[IT][2], o[DOT ? IT : 1][2];
+    __device__ __forceinline__ void load(const float *__restrict__ src, const float *__restrict__ other) {
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int idx = min((int)threadIdx.x + it * NT, NI - 1);
+        for (int it = 0; it < IT; ++it) {
+            const int idx = min((int)threadIdx.x + it * NT, NI - 1);
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            a[it][k] = *(const f32x4 *)(src + 8 * idx + 4 * k);
-            if constexpr (DOT) o[it][k] = *(const f32x4 *)(other + 8 * idx + 4 * k);
-        }
-    }
-    float acc = 0.f;
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int idx = (int)threadIdx.x + it * NT;
-        if (NI % NT == 0 || idx < NI) {
-            const int p = idx / (N / 8), n0 = (idx - p * (N / 8)) * 8;
-            bf16x8 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[e] = (bf16)a[it][0][e];
-                v[e + 4] = (bf16)a[it][1][e];
+            for (int k = 0; k < 2; ++k) {
+                a[it][k] = *(const f32x4 *)(src + 8 * idx + 4 * k);
+                if constexpr (DOT) o[it][k] = *(const f32x4 *)(other + 8 * idx + 4 * k);
             }
-            *(bf16x8 *)(dst + rowof(p) * ld + n0) = v;
-            if constexpr (DOT) acc += dot4(a[it][0], o[it][0]) + dot4(a[it][1], o[it][1]);
         }
     }
-    return acc;
-}
+    template <typename RowOf = RowIdentity>
+    __device__ __forceinline__ float write(bf16 *dst, int ld, RowOf rowof = RowOf{}) const {
+        float acc = 0.f;
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = (int)threadIdx.x + it * NT;
+            if (NI % NT == 0 || idx < NI) {
+                const int p = idx / (N / 8), n0 = (idx - p * (N / 8)) * 8;
+                bf16x8 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = (bf16)a[it][0][e];
+                    v[e + 4] = (bf16)a[it][1][e];
+                }
+                *(bf16x8 *)(dst + rowof(p) * ld + n0) = v;
+                if constexpr (DOT) acc += dot4(a[it][0], o[it][0]) + dot4(a[it][1], o[it][1]);
+            }
+        }
+        return acc;
+    }
+};
 
 // ---------------------------------------------------------------------------
 // bfloat16 version of k_chunk_bwd, one workgroup per (b, c, h), that keeps
@@ -683,16 +687,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int g = h / (H / G);
     const int64_t s = (int64_t)c * Q;
     const int q = (int)min<int64_t>(Q, L - s);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int r = lane & 15, grp = lane >> 4;
 
     __shared__ float cs_s[256], yy_s[256], xdx_s[256], red_s[4][3];
     const float *csc = cs + (((int64_t)b * H + h) * nc + c) * Q;
-    for (int j = threadIdx.x; j < 256; j += 256) {
-        cs_s[j] = csc[min(j, Q - 1)];
-        yy_s[j] = 0.f;
-        xdx_s[j] = 0.f;
-    }
+    const float cs_own = csc[min((int)threadIdx.x, Q - 1)];  // written to LDS below
     const int64_t row0 = (b * L + s) * H + h;
     const int T16Q = Q / 16;
     const int64_t tile0 = (((int64_t)b * nc + c) * G + g) * T16Q;  // first fragment tile
@@ -734,7 +734,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
     };
-    auto frag = [&](int tile, int blk) { return (uint32_t)((tile * NSEG + blk) * 64 + lane) * 16u; };
+    // A fragment block is 1 KiB: the lane's 16 bytes at lane * 16 (per-lane offset) plus the
+    // block's start (wave-uniform, a scalar offset).  Blocks of a round that a tile cannot use
+    // (at most one per tile) load too, unused, so the count of loads stays fixed.
+    auto blk = [&](int tile, int b_, int per) { return (uint32_t)(tile * per + b_) * 1024u; };
     // Channel order in LDS: row 16 pt + 4 grp + e holds channel (P / 4) grp + 4 pt + e, so the
     // accumulators a lane ends with (tile pt, rows 4 grp + e) are the channels (P / 4) grp ..
     // (P / 4) grp + P / 4 - 1: one contiguous piece of a dy, x or dx row.
@@ -762,16 +765,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int il = I * 16 + r;
         const bool vi = I < T16 && il < q;
         const uint32_t drow = (uint32_t)il * rowb;
+        const uint32_t vo = I < T16 ? lane * 16u : kBufOff;
 #pragma unroll
-        for (int kc = 0; kc < NCF; ++kc) {
-            const int kk = kc * 32 + grp * 8;
-            o.vr[kc] = buf_ld16(rsCf, (vi && kk < N) ? (uint32_t)((I * NCF + kc) * 64 + lane) * 16u : kBufOff);
-        }
+        for (int kc = 0; kc < NCF; ++kc) o.vr[kc] = buf_ld16s(rsCf, vo, blk(I, kc, NCF));
 #pragma unroll
-        for (int sg = 0; sg < NSY; ++sg) {
-            const int jl = sg * 32 + grp * 8;
-            o.gs[sg] = buf_ld16(rsGy, (vi && sg * 32 <= I * 16 + 15 && jl < il) ? frag(I, sg) : kBufOff);
-        }
+        for (int sg = 0; sg < NSY; ++sg) o.gs[sg] = buf_ld16s(rsGy, vo, blk(I, sg, NSEG));
         row_load(rsDY, drow, vi, o.d4);
     };
     auto comp_y = [&](auto RC, const Ops &o) {
@@ -812,10 +810,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         yy = sum_groups(yy);
         if (grp == 0 && il < q) yy_s[il] = yy;
     };
-    stage_transposed_rs<256, P, 256>(rsX, rowb, q, ops_s, XLD, prow);
-    stage_state_all<P, N, 256, false>(hp, nullptr, st_s, HLD, prow);
+    // x^T and H_c staged, with the first tile's loads issued before the LDS stores
     Ops o0, o1;
-    load_y(RoundC<0>{}, o0);
+    {
+        TrStage<256, P, 256> xst;
+        StateStage<P, N, 256, false> hst;
+        xst.load(rsX, rowb, q);
+        hst.load(hp, nullptr);
+        load_y(RoundC<0>{}, o0);
+        cs_s[threadIdx.x] = cs_own;
+        yy_s[threadIdx.x] = 0.f;
+        xdx_s[threadIdx.x] = 0.f;
+        xst.write(ops_s, XLD, prow);
+        hst.write(st_s, HLD, prow);
+    }
     __syncthreads();
     load_y(RoundC<1>{}, o1);
     comp_y(RoundC<0>{}, o0);
@@ -823,8 +831,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     comp_y(RoundC<1>{}, o1);
     load_y(RoundC<3>{}, o1);
     comp_y(RoundC<2>{}, o0);
+    // the loads of phase X's staging (dy^T, R_c, H_c) fly during the last tile
+    TrStage<256, P, 256> dyst;
+    StateStage<P, N, 256, true> rst;
+    dyst.load(rsDY, rowb, q);
+    rst.load(rp, hp);
     comp_y(RoundC<3>{}, o1);
-    __syncthreads();
+    lds_barrier();  // every wave is done with x^T and H_c in LDS
 
     // ---------------- phase X ----------------
     // round R: column tiles from 4 R, so row blocks 2 R .. 7
@@ -834,18 +847,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int jl = J * 16 + r;
         const bool vj = J < T16 && jl < q;
         const uint32_t drow = (uint32_t)jl * rowb;
+        const uint32_t vo = J < T16 ? lane * 16u : kBufOff;
 #pragma unroll
-        for (int kc = 0; kc < NCF; ++kc) {
-            const int kk = kc * 32 + grp * 8;
-            o.vr[kc] = buf_ld16(rsBf, (vj && kk < N) ? (uint32_t)((J * NCF + kc) * 64 + lane) * 16u : kBufOff);
-        }
-        const int ilo = (J * 16) & ~31;
+        for (int kc = 0; kc < NCF; ++kc) o.vr[kc] = buf_ld16s(rsBf, vo, blk(J, kc, NCF));
 #pragma unroll
-        for (int sg = SX0; sg < NSEG; ++sg) {
-            const int i0 = sg * 32, il = i0 + grp * 8;
-            const bool need = vj && i0 >= ilo && i0 < q && il + 7 > jl && il < q;
-            o.gs[sg] = buf_ld16(rsGx, need ? frag(J, sg) : kBufOff);
-        }
+        for (int sg = SX0; sg < NSEG; ++sg) o.gs[sg] = buf_ld16s(rsGx, vo, blk(J, sg, NSEG));
         row_load(rsDY, drow, vj, o.d4);
         row_load(rsX, drow, vj, o.x4);
         o.dg = buf_ldf(rsDg, vj ? 4u * jl : kBufOff);  // M_jj
@@ -921,14 +927,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                          rsDX, vj ? drow + 16u * k2 : kBufOff);
         }
     };
-    stage_transposed_rs<256, P, 256>(rsDY, rowb, q, ops_s, XLD, prow);
+    load_x(RoundC<0>{}, o0);
+    dyst.write(ops_s, XLD, prow);
     {
         // <R_c, H_c>, reduced here so that the products are not kept to the end
-        const float rh = wave_sum(stage_state_all<P, N, 256, true>(rp, hp, st_s, HLD, prow));
+        const float rh = wave_sum(rst.write(st_s, HLD, prow));
         if (lane == 0) red_s[wave][1] = rh;
     }
-    load_x(RoundC<0>{}, o0);
     __syncthreads();
+    // the step sizes of the chunk for the decay gradients (wave 0, lane l: steps 4 l ..)
+    const auto rsDT = buf_rsrc(dt + (b * L + s) * H + h, (uint32_t)q * H * 2);
+    const auto rsDDT = buf_rsrc(ddt + (b * L + s) * H + h, (uint32_t)q * H * 2);
+    uint16_t dtv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int k = 4 * lane + e;
+        dtv[e] = buf_ld2(rsDT, (wave == 0 && k < q) ? (uint32_t)(k * H * 2) : kBufOff);
+    }
     load_x(RoundC<1>{}, o1);
     comp_x(RoundC<0>{}, o0);
     load_x(RoundC<2>{}, o0);
@@ -973,12 +988,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int k = 4 * lane + e;
-            if (k < q) {
-                const float dda = suf[e] + after;
-                const int64_t o = (b * L + s + k) * H + h;
-                ddt[o] = (bf16)(Ah * dda);
-                dAp += (float)dt[o] * dda;
-            }
+            const float dda = suf[e] + after;
+            buf_st2(__builtin_bit_cast(uint16_t, (bf16)(Ah * dda)), rsDDT,
+                    k < q ? (uint32_t)(k * H * 2) : kBufOff);
+            dAp += k < q ? (float)__builtin_bit_cast(bf16, dtv[e]) * dda : 0.f;
         }
         dAp = wave_sum(dAp);
         if (lane == 0) {

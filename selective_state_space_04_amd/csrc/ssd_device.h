@@ -274,6 +274,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uin
 __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
 }
+// The same with a wave-uniform part of the offset in soff (a scalar register):
+// a lane switched off by voff = kBufOff stays past the end whether or not the
+// hardware counts soff in its range check (soff stays below 2^31).
+__device__ __forceinline__ u32x4 buf_ld16s(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, (int)soff, 0);
+}
 __device__ __forceinline__ u32x2 buf_ld8(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, 0);
 }
@@ -282,6 +288,9 @@ __device__ __forceinline__ float buf_ldf(__amdgpu_buffer_rsrc_t rs, uint32_t off
 }
 __device__ __forceinline__ uint16_t buf_ld2(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b16(rs, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_st2(uint16_t v, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, rs, (int)off, 0, 0);
 }
 __device__ __forceinline__ void buf_st8(u32x2 v, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b64(v, rs, (int)off, 0, 0);
@@ -351,30 +360,34 @@ __device__ __forceinline__ void stage_transposed_bf16(const bf16 *__restrict__ s
 // The same transposed copy for NROWS rows and COLS columns known at compile
 // time, by NT threads, reading through a buffer resource: row r starts at
 // byte r * ldb from the resource base, and rows at or past nvalid read as
-// zero.  Every load is issued before the first LDS store and none sits
-// behind a branch.
-template <int NROWS, int COLS, int NT, typename RowOf = RowIdentity>
-__device__ __forceinline__ void stage_transposed_rs(__amdgpu_buffer_rsrc_t rs, uint32_t ldb,
-                                                    int nvalid, bf16 *dst, int dstride,
-                                                    RowOf rowof = RowOf{}) {
-    constexpr int NBC = COLS / 8, NB = (NROWS / 4) * NBC, IT = (NB + NT - 1) / NT;
+// zero.  In two steps, so that a caller can issue other loads between them:
+// load() issues every load (none behind a branch), write() stores to LDS
+// once they have landed.
+template <int NROWS, int COLS, int NT>
+struct TrStage {
+    static constexpr int NBC = COLS / 8, NB = (NROWS / 4) * NBC, IT = (NB + NT - 1) / NT;
     u32x4 v[IT][4];
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t ldb, int nvalid) {
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int blk = (int)threadIdx.x + it * NT;
-        const int br = blk / NBC, bc = blk - br * NBC;
+        for (int it = 0; it < IT; ++it) {
+            const int blk = (int)threadIdx.x + it * NT;
+            const int br = blk / NBC, bc = blk - br * NBC;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int r = 4 * br + k;
-            v[it][k] = buf_ld16(rs, (blk < NB && r < nvalid) ? (uint32_t)r * ldb + 16u * bc : kBufOff);
+            for (int k = 0; k < 4; ++k) {
+                const int r = 4 * br + k;
+                v[it][k] = buf_ld16(rs, (blk < NB && r < nvalid) ? (uint32_t)r * ldb + 16u * bc : kBufOff);
+            }
         }
     }
+    template <typename RowOf = RowIdentity>
+    __device__ __forceinline__ void write(bf16 *dst, int dstride, RowOf rowof = RowOf{}) const {
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int blk = (int)threadIdx.x + it * NT;
-        const int br = blk / NBC, bc = blk - br * NBC;
-        if (NB % NT == 0 || blk < NB) write_transposed_4x8(v[it], dst, dstride, 4 * br, 8 * bc, rowof);
+        for (int it = 0; it < IT; ++it) {
+            const int blk = (int)threadIdx.x + it * NT;
+            const int br = blk / NBC, bc = blk - br * NBC;
+            if (NB % NT == 0 || blk < NB) write_transposed_4x8(v[it], dst, dstride, 4 * br, 8 * bc, rowof);
+        }
     }
-}
+};
 
 }  // namespace ssd

@@ -1439,22 +1439,29 @@ __global__ __launch_bounds__(64 * dcb_waves<P>()) void k_group_dcb_rb(const bf16
 }
 
 // ---------------------------------------------------------------------------
-// bfloat16: the state terms alone, one workgroup per (b, c, g, 64-row tile,
-// which): which = 0: dCs[i] = sum_h exp(cs_i) dy_i^T H_c; which = 1:
-// dBs[j] = sum_h exp(cs_e - cs_j) x_j^T R_c.  Each wave owns 16 rows (row
-// fragments straight from global memory); per head the state is staged once
-// into LDS as bf16 [N][P + 8] (transposed in registers) and prefetched one
-// head ahead.
+// bfloat16: the state terms alone, one workgroup of NW waves per (b, c, g,
+// which, block of 16 NW rows): which = 0: dCs[i] = sum_h exp(cs_i) dy_i^T
+// H_c; which = 1: dBs[j] = sum_h exp(cs_e - cs_j) x_j^T R_c.  Each wave owns
+// 16 rows and keeps their accumulators across the head loop.  Per head the
+// state is converted to bf16 once into LDS, row-major with the pair swizzle,
+// and read as MFMA fragments with transposing reads (two LDS buffers, one
+// barrier per head).  Every global load of a head (state, row fragments,
+// decay prefix) is issued two heads ahead and none sits behind a branch (the
+// head index is clamped), so the compiler's counted waits keep them in
+// flight.
 // ---------------------------------------------------------------------------
-template <int P, int N>
-__global__ __launch_bounds__(256) void k_group_state(
+template <int P, int N, int NW>
+__global__ __launch_bounds__(64 * NW) void k_group_state(
     const bf16 *__restrict__ x, const bf16 *__restrict__ dy, const float *__restrict__ cs,
     const float *__restrict__ Hs, const float *__restrict__ Rs, float *__restrict__ dCs,
     float *__restrict__ dBs, int64_t L, int H, int G, int Q, int nc) {
-    constexpr int KS = P / 32 > 0 ? P / 32 : 1, NT = N / 16, SLD = P + 8;
-    constexpr int NBLK = (P / 4) * (N / 4);
-    constexpr int BPT = (NBLK + 255) / 256;
-    const int ntr = (Q + 63) / 64;
+    constexpr int NTH = 64 * NW, ROWS = 16 * NW;
+    constexpr int KS = P / 32 > 0 ? P / 32 : 1, NT = N / 16;
+    constexpr int PR = P < 32 ? 32 : P;       // state rows in LDS (a fragment spans 32)
+    constexpr int ROWB = N * 2;               // bytes of one bf16 state row
+    constexpr int NCH = P * N / 8;            // 16-byte chunks of one bf16 state
+    constexpr int CPT = (NCH + NTH - 1) / NTH;
+    const int ntr = (Q + ROWS - 1) / ROWS;
     const int64_t work = xcd_remap(blockIdx.x, gridDim.x);
     const int tile = (int)(work % ntr);
     const int which = (int)((work / ntr) % 2);
@@ -1465,82 +1472,99 @@ __global__ __launch_bounds__(256) void k_group_state(
     const int64_t b = bc / nc;
     const int64_t s = (int64_t)c * Q;
     const int q = (int)min<int64_t>(Q, L - s);
-    if (tile * 64 >= q) return;  // the whole workgroup: no barrier is reached
+    if (tile * ROWS >= q) return;  // the whole workgroup: no barrier is reached
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int r = lane & 15, grp = lane >> 4;
-    const int i0 = tile * 64 + wave * 16;
-    const bool active = i0 < q;
-    const int ia = i0 + r;
-    const bool va = ia < q;
+    const int i0 = tile * ROWS + wave * 16;
+    const int ia = i0 + r, iac = min(ia, q - 1);
     const bf16 *rowsrc = which == 0 ? dy : x;
     const float *St = which == 0 ? Hs : Rs;
 
-    __shared__ bf16 st_s[N * SLD];
+    __shared__ __align__(16) unsigned char st_s[2][PR * ROWB];
+    if constexpr (PR > P) {
+        // rows P .. PR - 1 meet zero row fragments, but must not hold NaN patterns
+        for (int k = tid; k < 2 * (PR - P) * ROWB / 16; k += NTH) {
+            const int bfr = k / ((PR - P) * ROWB / 16), o = k % ((PR - P) * ROWB / 16);
+            *(u32x4 *)(st_s[bfr] + P * ROWB + 16 * o) = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
     f32x4 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const int hpg = H / G;
-    f32x4 pst[BPT][4];
-    u32x4 prow[KS];
-    float pw = 0.f;
-    auto load = [&](int h) {
-        const int64_t soff = (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+    const int hpg = H / G, hbase = g * hpg;
+
+    struct HeadRegs {
+        f32x4 st[CPT][2];
+        u32x4 row[KS];
+        float ca, ce;
+    };
+    auto load = [&](int hh, HeadRegs &R) {
+        const int h = hbase + min(hh, hpg - 1);
+        const float *src = St + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
 #pragma unroll
-        for (int u = 0; u < BPT; ++u) {
-            const int bi = tid + 256 * u;
-            if (bi < NBLK) {
-                const int nb = bi % (N / 4), pb = bi / (N / 4);
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    pst[u][k] = *(const f32x4 *)(St + soff + (int64_t)(4 * pb + k) * N + 4 * nb);
-            }
+        for (int u = 0; u < CPT; ++u) {
+            const int idx = min(tid + NTH * u, NCH - 1);
+            R.st[u][0] = *(const f32x4 *)(src + 8 * idx);
+            R.st[u][1] = *(const f32x4 *)(src + 8 * idx + 4);
         }
         const float *csh = cs + (((int64_t)b * H + h) * nc + c) * Q;
-        const float ca = csh[min(ia, Q - 1)];
-        pw = which == 0 ? __expf(ca) : __expf(csh[q - 1] - ca);
-        const int64_t row = (b * L + s + ia) * H + h;
+        R.ca = csh[min(ia, Q - 1)];
+        R.ce = csh[q - 1];
+        const bf16 *rp = rowsrc + ((b * L + s + iac) * H + h) * (int64_t)P;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int kk = ks * 32 + grp * 8;
-            prow[ks] = (va && kk < P) ? *(const u32x4 *)(rowsrc + row * P + kk) : z;
-        }
+        for (int ks = 0; ks < KS; ++ks) R.row[ks] = *(const u32x4 *)(rp + min(ks * 32 + grp * 8, P - 8));
     };
-    load(g * hpg);
-    for (int hh = 0; hh < hpg; ++hh) {
-        __syncthreads();  // the previous head's LDS reads are done
+    // live = false (the odd head past the group's end): the same steps, adding zero
+    auto head = [&](const HeadRegs &R, int buf, bool live) {
+        unsigned char *sb = st_s[buf];
 #pragma unroll
-        for (int u = 0; u < BPT; ++u) {
-            const int bi = tid + 256 * u;
-            if (bi < NBLK) {
-                const int nb = bi % (N / 4), pb = bi / (N / 4);
+        for (int u = 0; u < CPT; ++u) {
+            const int idx = tid + NTH * u;
+            if (NCH % NTH == 0 || idx < NCH) {
+                const int p = idx / (N / 8), ch = idx % (N / 8);
+                bf16x8 v;
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    bf16 tv[4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) tv[k] = (bf16)pst[u][k][m];
-                    *(u32x2 *)(st_s + (4 * nb + m) * SLD + 4 * pb) = *(const u32x2 *)tv;
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = (bf16)R.st[u][0][e];
+                    v[e + 4] = (bf16)R.st[u][1][e];
                 }
+                *(bf16x8 *)(sb + p * ROWB + tr_chunk_slot<ROWB>(p, ch) * 16) = v;
             }
         }
+        // (a weight of zero, not a branch: the compiler would move the row loads into one)
+        const float pw = (which == 0 ? __expf(R.ca) : __expf(R.ce - R.ca)) * (live ? 1.f : 0.f);
         u32x4 fr[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) fr[ks] = frag_scale<bf16>(prow[ks], pw);
-        __syncthreads();
-        if (hh + 1 < hpg) load(g * hpg + hh + 1);
-        if (!active) continue;
+        for (int ks = 0; ks < KS; ++ks)
+            fr[ks] = ks * 32 + grp * 8 < P ? frag_scale<bf16>(R.row[ks], pw) : u32x4{0u, 0u, 0u, 0u};
+        lds_barrier();  // this head's state is in LDS for every wave
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int kk = ks * 32 + grp * 8;
-                const u32x4 bv = kk < P ? *(const u32x4 *)(st_s + (t * 16 + r) * SLD + kk) : z;
-                acc[t] = mfma_bf16(as_bf16x8(fr[ks]), as_bf16x8(bv), acc[t]);
-            }
+            for (int ks = 0; ks < KS; ++ks)
+                acc[t] = mfma_bf16(as_bf16x8(fr[ks]), frag_tr<ROWB>(sb, ks * 32, t * 16, lane), acc[t]);
         }
+    };
+    // Buffer hh & 1 is rewritten at head hh + 2, after the barrier of head hh + 1,
+    // which every wave reaches only once its reads of head hh are done.  No head
+    // sits behind a branch (the compiler would move its loads there).
+    // sched_barrier: the scheduler keeps each group of loads where it is written.
+    HeadRegs R0, R1;
+    load(0, R0);
+    load(1, R1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int hh = 0; hh < hpg; hh += 2) {
+        head(R0, 0, true);
+        __builtin_amdgcn_sched_barrier(0);
+        load(hh + 2, R0);
+        __builtin_amdgcn_sched_barrier(0);
+        head(R1, 1, hh + 1 < hpg);
+        __builtin_amdgcn_sched_barrier(0);
+        load(hh + 3, R1);
+        __builtin_amdgcn_sched_barrier(0);
     }
-    if (!active) return;
+    if (i0 >= q) return;
     float *out = which == 0 ? dCs : dBs;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -1803,9 +1827,16 @@ hipError_t launch_group_bwd(const Dims &d, const void *x, const void *dy, const 
                                                        dcbT, d.L, (int)d.H, (int)d.G, (int)d.Q,
                                                        (int)d.nc);
                 }
-                k_group_state<PP, NN><<<2 * grid, 256, 0, st>>>(
-                    (const bf16 *)x, (const bf16 *)dy, cs, Hs, Rs, dCs, dBs, d.L, (int)d.H,
-                    (int)d.G, (int)d.Q, (int)d.nc);
+                if (d.Q > 64) {
+                    const unsigned g2 = (unsigned)(2 * d.b * d.nc * d.G * ((d.Q + 127) / 128));
+                    k_group_state<PP, NN, 8><<<g2, 512, 0, st>>>(
+                        (const bf16 *)x, (const bf16 *)dy, cs, Hs, Rs, dCs, dBs, d.L, (int)d.H,
+                        (int)d.G, (int)d.Q, (int)d.nc);
+                } else {
+                    k_group_state<PP, NN, 4><<<2 * grid, 256, 0, st>>>(
+                        (const bf16 *)x, (const bf16 *)dy, cs, Hs, Rs, dCs, dBs, d.L, (int)d.H,
+                        (int)d.G, (int)d.Q, (int)d.nc);
+                }
             }
         } else if (d.dtype == 1)
             k_group_bwd<bf16, PP, NN, float><<<grid, 256, 0, st>>>(

@@ -84,24 +84,20 @@ __device__ __forceinline__ int swz(int row, int col) {
 template <int P>
 __device__ __forceinline__ void stage_x_load(XStage<P> &st, const bf16 *__restrict__ src, int ld,
                                              int nvalid) {
+    // x is read once: a non-temporal load (cache policy bit 1) keeps it from
+    // displacing the per-chunk operands every head of the chunk re-reads.
+    // Rows past nvalid read as zero: their lanes are given an offset past the
+    // resource's end, so no load sits behind a branch.
+    const auto rs = buf_rsrc(src, (uint32_t)nvalid * (uint32_t)ld * 2u);
 #pragma unroll
     for (int i = 0; i < XStage<P>::XB; ++i) {
         int br, bc;
         xstage_block<P>(threadIdx.x + 256 * i, br, bc);
-        // x is read once: a non-temporal load keeps it from displacing the
-        // per-chunk operands every head of the chunk re-reads.  Rows past
-        // nvalid are zero (a full 256-row chunk needs no test).
-        if (nvalid >= 256) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                st.v[i][k] = __builtin_nontemporal_load((const u32x4 *)(src + (br * 4 + k) * ld + bc * 8));
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int rr = br * 4 + k;
-                st.v[i][k] = rr < nvalid ? __builtin_nontemporal_load((const u32x4 *)(src + rr * ld + bc * 8))
-                                         : u32x4{0u, 0u, 0u, 0u};
-            }
+        for (int k = 0; k < 4; ++k) {
+            const int rr = br * 4 + k;
+            st.v[i][k] = __builtin_amdgcn_raw_buffer_load_b128(
+                rs, (int)(rr < nvalid ? ((uint32_t)rr * ld + bc * 8) * 2u : kBufOff), 0, 2);
         }
     }
 }
@@ -263,8 +259,10 @@ __global__ __launch_bounds__(256) void k_fused_prep(const bf16 *__restrict__ B,
 // ---------------------------------------------------------------------------
 // Operands of one 16-row output tile I: its off-diagonal C B^T fragments
 // (32-blocks J < I / 2; NG is the most a tile in this slot can have), the
-// diagonal one and the four C fragments.  With `all` every off-diagonal slot
-// is loaded (in bounds, possibly unused), so the number of loads is fixed.
+// diagonal one and the four C fragments.  Every slot is loaded (through
+// buffer resources over this chunk's blocks: a slot past them reads zero,
+// and slots J >= I / 2 go unused), so the number of loads is fixed and none
+// sits behind a branch.
 template <int NG>
 struct TileOps {
     static constexpr int kNG = NG;
@@ -274,16 +272,15 @@ struct TileOps {
 };
 
 template <int NG>
-__device__ __forceinline__ void tile_load(TileOps<NG> &t, const bf16 *Gfc, const bf16 *Cfc, int I, int NJ,
-                                          int lane, bool all) {
-    const bf16 *gt = Gfc + I * NJ * 512 + lane * 8;
+__device__ __forceinline__ void tile_load(TileOps<NG> &t, __amdgpu_buffer_rsrc_t rsG,
+                                          __amdgpu_buffer_rsrc_t rsC, int I, int NJ, int lane) {
+    const uint32_t gt = (uint32_t)(I * NJ * 512 + lane * 8) * 2u;
     const int Jd = I >> 1;
 #pragma unroll
-    for (int J = 0; J < NG; ++J)
-        if (all || J < Jd) t.g[J] = *(const u32x4 *)(gt + J * 512);
-    t.gd = *(const u32x4 *)(gt + Jd * 512);
+    for (int J = 0; J < NG; ++J) t.g[J] = buf_ld16(rsG, gt + J * 1024u);
+    t.gd = buf_ld16(rsG, gt + (uint32_t)Jd * 1024u);
 #pragma unroll
-    for (int kn = 0; kn < 4; ++kn) t.cf[kn] = *(const u32x4 *)(Cfc + ((I * 4 + kn) * 64 + lane) * 8);
+    for (int kn = 0; kn < 4; ++kn) t.cf[kn] = buf_ld16(rsC, (uint32_t)(((I * 4 + kn) * 64 + lane) * 8) * 2u);
 }
 
 // OPTS: the step is preprocessed (bias, softplus, clamp) and x scaled by the
@@ -348,49 +345,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const bf16 *Cfc = Cf + bcg * (T16Q * NKN * 512);
     constexpr int PN = P * N;
 
-    // x, B^T and dt in one round
+    // dt, x and B^T in one round, dt first (the decay prefix waits for it
+    // alone).  Every load goes through a buffer resource, a lane with nothing
+    // to load pointing past its end, so none sits behind a branch and the
+    // compiler's counted waits leave the later loads in flight.
     const int row0 = (b * L + s) * H + h;
+    const auto rsY = buf_rsrc(y + row0 * P, (uint32_t)q * H * P * 2u);
+    const auto rsDt = buf_rsrc(dt + (b * L + s) * H + h, (uint32_t)q * H * 2u);
+    const uint16_t dt_raw = buf_ld2(rsDt, tid < q ? (uint32_t)tid * H * 2u : kBufOff);
     XStage<P> xst;
     stage_x_load<P>(xst, x + row0 * P, H * P, q);
-    // B^T fragments (rows past q are stored as zero; blocks past NJ are not read)
+    // B^T fragments (rows past q are stored as zero; blocks past NJ read as zero, unused)
+    const auto rsBt = buf_rsrc(Btc, (uint32_t)(N * NJ * 32) * 2u);
     bf16x8 bfr[8][NTW];
-    if (NJ == 8) {
 #pragma unroll
-        for (int J = 0; J < 8; ++J)
+    for (int J = 0; J < 8; ++J)
 #pragma unroll
-            for (int tt = 0; tt < NTW; ++tt)
-                bfr[J][tt] = as_bf16x8(*(const u32x4 *)(Btc + (((wave + 4 * tt) * 8 + J) * 64 + lane) * 8));
-    } else {
-#pragma unroll
-        for (int J = 0; J < 8; ++J)
-#pragma unroll
-            for (int tt = 0; tt < NTW; ++tt)
-                bfr[J][tt] = as_bf16x8(J < NJ ? *(const u32x4 *)(Btc + (((wave + 4 * tt) * NJ + J) * 64 + lane) * 8)
-                                              : z4);
-    }
+        for (int tt = 0; tt < NTW; ++tt)
+            bfr[J][tt] = as_bf16x8(buf_ld16(
+                rsBt, J < NJ ? (uint32_t)((((wave + 4 * tt) * NJ + J) * 64 + lane) * 8) * 2u : kBufOff));
 
     // 1. decay prefix
     float sx_own = 1.f;  // this thread's step's input factor (OPTS)
     {
         float v;
         if constexpr (OPTS) {
-            const float de = (tid < q) ? dt_effective((float)dt[(b * L + s + tid) * H + h], h, o) : 0.f;
+            const float de = (tid < q) ? dt_effective((float)__builtin_bit_cast(bf16, dt_raw), h, o) : 0.f;
             sx_own = (tid < q) ? input_scale(de, A[h], o.scale) : 0.f;
             s_s[tid] = sx_own;
             v = de * A[h];
         } else {
-            v = (tid < q) ? (float)dt[(b * L + s + tid) * H + h] * A[h] : 0.f;
+            v = (tid < q) ? (float)__builtin_bit_cast(bf16, dt_raw) * A[h] : 0.f;
         }
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float o = __shfl_up(v, off, 64);
             if (lane >= off) v += o;
         }
+        // (LDS-only barriers: the x and B^T loads stay in flight)
         if (lane == 63) wsum_s[wave] = v;
-        __syncthreads();
+        lds_barrier();
         for (int w = 0; w < wave; ++w) v += wsum_s[w];
         cs_s[tid] = v;  // past q: repeats the last valid value
-        __syncthreads();
+        lds_barrier();
         if (tid < 8) ref_s[tid] = cs_s[min(32 * tid + 31, q - 1)];
         wv_s[tid] = __expf(cs_s[q - 1] - v) * sx_own;
     }
@@ -398,7 +395,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 
     // 2. stage x^T (rows past q were loaded as zero)
     stage_x_write_swz<P>(xst, xs);
-    __syncthreads();
+    lds_barrier();
 
     // 3. hand-off, first half: wait until wave `wave` of chunk c - 1 of this
     // (b, h) has published its slice of h_{c-1}, then load the slice (it
@@ -476,14 +473,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     // With every tile of a full chunk valid, each load count is fixed, so the
     // wait before raising the flag can leave the later tiles' loads in flight.
     const int tI[4] = {wave, 7 - wave, 8 + wave, 15 - wave};
-    const bool full = T16 == 16 && T16Q == 16;
+    const auto rsG = buf_rsrc(Gfc, (uint32_t)(T16Q * NJ * 512) * 2u);
+    const auto rsC = buf_rsrc(Cfc, (uint32_t)(T16Q * NKN * 512) * 2u);
     TileOps<1> t0;
     TileOps<3> t1;
     TileOps<5> t2;
     TileOps<7> t3;
-    if (tI[0] < T16) tile_load(t0, Gfc, Cfc, tI[0], NJ, lane, full);
+    tile_load(t0, rsG, rsC, tI[0], NJ, lane);
 
-    __syncthreads();  // step 4 is done in every wave: w may be replaced by v
+    lds_barrier();  // step 4 is done in every wave: w may be replaced by v
     // v_j relative to the end of j's own 32-block (cs past q repeats)
     wv_s[tid] = __expf(ref_s[tid >> 5] - cs_s[tid]) * sx_own;
 
@@ -515,12 +513,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             *(u32x2 *)(hs + swz<HW>(p, n0)) = *(const u32x2 *)hb;
         }
     }
-    __syncthreads();  // hs and v complete in every wave
+    lds_barrier();  // hs and v complete in every wave
 
     // 6. output tiles
     const float Dh = D ? D[h] : 0.f;
-    if (tI[1] < T16) tile_load(t1, Gfc, Cfc, tI[1], NJ, lane, full);
-    if (tI[2] < T16) tile_load(t2, Gfc, Cfc, tI[2], NJ, lane, full);
+    tile_load(t1, rsG, rsC, tI[1], NJ, lane);
+    tile_load(t2, rsG, rsC, tI[2], NJ, lane);
 
     // acc[pt][e] = y[i = 16 I + r][p = 16 pt + 4 grp + e] (D[m = p][n = i] of the MFMAs):
     // the state term exp(cs_i) C_i h_{c-1} first (scaled once), then the intra product
@@ -610,35 +608,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         // order by source row: out[s] = t[s ^ g]
         const u32x2 a0 = g1 ? t1v : t0v, a1 = g1 ? t0v : t1v, a2 = g1 ? t3v : t2v, a3 = g1 ? t2v : t3v;
         const u32x2 o0 = g2 ? a2 : a0, o1 = g2 ? a3 : a1, o2 = g2 ? a0 : a2, o3 = g2 ? a1 : a3;
-        if (il < q) {
-            bf16 *yr = y + (row0 + il * H) * P + 16 * grp;
-            *(u32x4 *)yr = u32x4{o0[0], o0[1], o1[0], o1[1]};
-            *(u32x4 *)(yr + 8) = u32x4{o2[0], o2[1], o3[0], o3[1]};
-        }
+        // rows past q: offsets past the resource's end (no branch around the stores)
+        const uint32_t yo = il < q ? (uint32_t)(il * H * P + 16 * grp) * 2u : kBufOff;
+        buf_st16(u32x4{o0[0], o0[1], o1[0], o1[1]}, rsY, yo);
+        buf_st16(u32x4{o2[0], o2[1], o3[0], o3[1]}, rsY, yo + 16u);
     };
 
+    // Every tile is computed and stored without a branch (a tile past q, in a
+    // short last chunk, computes on zero operands and its stores are dropped),
+    // so the compiler's counted waits keep tile 3's loads in flight.
     f32x4 acc[PT];
-    if (tI[0] < T16) compute_tile(t0, tI[0], acc);
+    compute_tile(t0, tI[0], acc);
     if (!last) {
         // this wave's ring slice is complete: raise its flag (the loads of
         // tiles 1 and 2, issued above, are waited for here too)
         __builtin_amdgcn_s_waitcnt(0);
         if (lane == 0) __hip_atomic_store(myflag, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (tI[0] < T16) store_tile(tI[0], acc);
-    if (tI[3] < T16) tile_load(t3, Gfc, Cfc, tI[3], NJ, lane, full);
-    if (tI[1] < T16) {
-        compute_tile(t1, tI[1], acc);
-        store_tile(tI[1], acc);
-    }
-    if (tI[2] < T16) {
-        compute_tile(t2, tI[2], acc);
-        store_tile(tI[2], acc);
-    }
-    if (tI[3] < T16) {
-        compute_tile(t3, tI[3], acc);
-        store_tile(tI[3], acc);
-    }
+    store_tile(tI[0], acc);
+    tile_load(t3, rsG, rsC, tI[3], NJ, lane);
+    compute_tile(t1, tI[1], acc);
+    store_tile(tI[1], acc);
+    compute_tile(t2, tI[2], acc);
+    store_tile(tI[2], acc);
+    compute_tile(t3, tI[3], acc);
+    store_tile(tI[3], acc);
 }
 
 bool fused_supported(const Dims &d) {

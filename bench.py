@@ -154,15 +154,26 @@ def backward_kernel_bytes(w) -> dict:
     dcb = b * nc * G * (T16 * (T16 + 1) // 2) * 256 * 4
     gst = b * L * G * N * 4
     part = b * nc * H * 8
+    frags = w.dtype == "bf16" and Q <= 256
+    if frags:
+        # bfloat16: the prep writes C B^T as the 16 x 16 tiles the chunk backward reads
+        # (row tiles 0 .. 2 (I / 2) + 1 of row tile I, and the transposed column blocks),
+        # C and B in fragment order and the float32 diagonal; the chunk backward reads them
+        ntile = sum(min(2 * (I // 2) + 2, T16) for I in range(T16))
+        cb = b * nc * G * ntile * 256 * e
+        rows = 2 * BC
+        diag = b * nc * G * Q * 4
+    else:
+        rows, diag = 0, 0
     return {
         "chunk_cumsum": dtb + H * 4 + cs,
         "chunk_cumsum64": dtb + H * 4 + 2 * cs if w.dtype == "f32" else 0,
-        "chunk_cb": 2 * BC + 2 * cb,
+        "chunk_cb": 2 * BC + 2 * cb + rows + diag,
         "chunk_state": x + BC + cs + S,
         "state_passing": 2 * S + b * H * nc * 4,
         "chunk_state_rev": x + BC + cs + S,
         "state_passing_rev": 2 * S + b * H * nc * 4,
-        "chunk_bwd": 3 * x + 2 * dtb + 2 * BC + 2 * cb + cs + 2 * S + 2 * H * 4 + part,
+        "chunk_bwd": 3 * x + 2 * dtb + 2 * BC + 2 * cb + diag + cs + 2 * S + 2 * H * 4 + part,
         "group_bwd": 2 * x + cs + 2 * S + 2 * dcb + 2 * gst,
         "group_combine": 2 * BC + 2 * dcb + 2 * gst + 2 * BC,
         "head_reduce": part + 2 * H * 4,

@@ -364,6 +364,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         for (int tt = 0; tt < NTW; ++tt)
             bfr[J][tt] = as_bf16x8(buf_ld16(
                 rsBt, J < NJ ? (uint32_t)((((wave + 4 * tt) * NJ + J) * 64 + lane) * 8) * 2u : kBufOff));
+    // keep the whole round here: the scheduler would otherwise sink B^T loads
+    // towards their use, behind the ring loads that must land during step 4
+    __builtin_amdgcn_sched_barrier(0);
 
     // 1. decay prefix
     float sx_own = 1.f;  // this thread's step's input factor (OPTS)
@@ -411,6 +414,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     int *myflag = flags + bh * 4 + wave;
     const bool have_h = c > 0 || init != nullptr;
     f32x4 hv[NTW][PT];
+    // The first round (B^T above all) has landed by now; waiting for it here
+    // leaves only this hand-off's loads in flight on either branch, so the
+    // chunk-state MFMAs below need no wait (after the join the compiler
+    // would otherwise wait for most of the ring loads).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     if (c > 0) {
         int n = 0;
         while (__hip_atomic_load(myflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < c && n < kSpinLimit) {
@@ -492,6 +500,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const float lam_c = __expf(cs_last);
     const bool last = c == nc - 1;
     float *hout = last ? (fin ? fin + bh * PN : nullptr) : ring + (c & 1) * nbh * PN + bh * PN;
+    // Tile 0's loads (issued before the barrier above, long landed) are waited
+    // for here, before the ring stores: with loads and stores both in flight
+    // the compiler's wait for them would also wait for most of the stores.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 #pragma unroll
     for (int tt = 0; tt < NTW; ++tt) {
 #pragma unroll

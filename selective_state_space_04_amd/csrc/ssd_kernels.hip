@@ -368,21 +368,80 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T *__restrict__ x,
     }
 }
 
+// s_waitcnt vmcnt(n) lgkmcnt(0) for a run-time n (the instruction takes an
+// immediate); n past 47 waits for everything.
+__device__ __forceinline__ void wait_vmcnt_lgkm0(int n) {
+    switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(112); break;
+    case 1: __builtin_amdgcn_s_waitcnt(113); break;
+    case 2: __builtin_amdgcn_s_waitcnt(114); break;
+    case 3: __builtin_amdgcn_s_waitcnt(115); break;
+    case 4: __builtin_amdgcn_s_waitcnt(116); break;
+    case 5: __builtin_amdgcn_s_waitcnt(117); break;
+    case 6: __builtin_amdgcn_s_waitcnt(118); break;
+    case 7: __builtin_amdgcn_s_waitcnt(119); break;
+    case 8: __builtin_amdgcn_s_waitcnt(120); break;
+    case 9: __builtin_amdgcn_s_waitcnt(121); break;
+    case 10: __builtin_amdgcn_s_waitcnt(122); break;
+    case 11: __builtin_amdgcn_s_waitcnt(123); break;
+    case 12: __builtin_amdgcn_s_waitcnt(124); break;
+    case 13: __builtin_amdgcn_s_waitcnt(125); break;
+    case 14: __builtin_amdgcn_s_waitcnt(126); break;
+    case 15: __builtin_amdgcn_s_waitcnt(127); break;
+    case 16: __builtin_amdgcn_s_waitcnt(16496); break;
+    case 17: __builtin_amdgcn_s_waitcnt(16497); break;
+    case 18: __builtin_amdgcn_s_waitcnt(16498); break;
+    case 19: __builtin_amdgcn_s_waitcnt(16499); break;
+    case 20: __builtin_amdgcn_s_waitcnt(16500); break;
+    case 21: __builtin_amdgcn_s_waitcnt(16501); break;
+    case 22: __builtin_amdgcn_s_waitcnt(16502); break;
+    case 23: __builtin_amdgcn_s_waitcnt(16503); break;
+    case 24: __builtin_amdgcn_s_waitcnt(16504); break;
+    case 25: __builtin_amdgcn_s_waitcnt(16505); break;
+    case 26: __builtin_amdgcn_s_waitcnt(16506); break;
+    case 27: __builtin_amdgcn_s_waitcnt(16507); break;
+    case 28: __builtin_amdgcn_s_waitcnt(16508); break;
+    case 29: __builtin_amdgcn_s_waitcnt(16509); break;
+    case 30: __builtin_amdgcn_s_waitcnt(16510); break;
+    case 31: __builtin_amdgcn_s_waitcnt(16511); break;
+    case 32: __builtin_amdgcn_s_waitcnt(32880); break;
+    case 33: __builtin_amdgcn_s_waitcnt(32881); break;
+    case 34: __builtin_amdgcn_s_waitcnt(32882); break;
+    case 35: __builtin_amdgcn_s_waitcnt(32883); break;
+    case 36: __builtin_amdgcn_s_waitcnt(32884); break;
+    case 37: __builtin_amdgcn_s_waitcnt(32885); break;
+    case 38: __builtin_amdgcn_s_waitcnt(32886); break;
+    case 39: __builtin_amdgcn_s_waitcnt(32887); break;
+    case 40: __builtin_amdgcn_s_waitcnt(32888); break;
+    case 41: __builtin_amdgcn_s_waitcnt(32889); break;
+    case 42: __builtin_amdgcn_s_waitcnt(32890); break;
+    case 43: __builtin_amdgcn_s_waitcnt(32891); break;
+    case 44: __builtin_amdgcn_s_waitcnt(32892); break;
+    case 45: __builtin_amdgcn_s_waitcnt(32893); break;
+    case 46: __builtin_amdgcn_s_waitcnt(32894); break;
+    case 47: __builtin_amdgcn_s_waitcnt(32895); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0070); break;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Chunk states for bfloat16 with P in {32, 64}, N in {64, 128} and Q a
 // multiple of 32 (both backward passes and the staged forward use it): one
-// workgroup per (b, c, g, part of the group's heads) keeps the chunk's B rows
-// in LDS for all its heads and streams x head by head through a two-slot LDS
-// ring.  Both arrive by direct global-to-LDS copies (row-major, 16-byte
-// chunks stored at chunk ^ (row & (chunks per row - 1))); the MFMA operands,
+// workgroup per (b, c, g, part of the group's heads), one wave per 16-column
+// tile of N.  The chunk's B rows are read once into registers (as MFMA
+// fragments, through LDS) and x streams in head by head: each head's rows
+// are loaded into registers two heads ahead and stored to one of two LDS
+// buffers (row-major, pair-swizzled) one head ahead.  The MFMA operands,
 // which contract over the steps, are read with transposing LDS reads
-// (ds_read_b64_tr_b16: in each 16-lane group, lane l points at the 4 columns
-// 4 (l % 4) + 4-wide piece of row l / 4 and receives column l % 16 of the 4
-// rows), two per fragment.  The step weights w_j (exp(cs_e - cs_j), or
-// exp(cs_j) from the chunk start, times the optional input factor) scale the
-// B^T fragments.  Per head: wait for this wave's copies of x (the S stores of
-// the previous head may stay in flight), one barrier, copy x of the next
-// head, multiply, store S, compute the next head's weights.
+// (ds_read_b64_tr_b16), two per fragment.  The step weights w_j
+// (exp(cs_e - cs_j), or exp(cs_j) from the chunk start, times the optional
+// input factor) scale the B^T fragments.  Per head: one barrier, the loads of
+// head + 2 and the next prefix, multiply, store S, the next head's weights
+// and rows to LDS.  No load sits behind a branch (heads past the part's end
+// repeat its last head; copy indices are clamped), so the compiler's
+// counted waits leave the later heads' loads in flight.  (Direct global-to-
+// LDS copies would save the registers, but after one the compiler makes
+// every LDS read wait for all copies in flight.)
 // ---------------------------------------------------------------------------
 template <int P, int N, bool FROM_START>
 __global__ __launch_bounds__(64 * (N / 16)) void k_chunk_state_mh(const bf16 *__restrict__ x,
@@ -393,9 +452,12 @@ __global__ __launch_bounds__(64 * (N / 16)) void k_chunk_state_mh(const bf16 *__
                                                         const float *__restrict__ sc, int nparts) {
     constexpr int XROWB = P * 2, BROWB = N * 2;
     constexpr int PT = P / 16, NT = N / 16, NW = NT;  // one wave per 16-column tile of N
+    constexpr int XSLOT = 256 * XROWB;
+    constexpr int XCPR = XROWB / 16, XRPC = 1024 / XROWB;   // x: 16-byte chunks per row, rows per KiB
+    constexpr int CPW = (256 * XROWB / 1024 + NW - 1) / NW; // KiB pieces of a head per wave
     static_assert(NT % 4 == 0 && (P == 32 || P == 64), "shape");
-    __shared__ __attribute__((aligned(16))) unsigned char bsm[256 * BROWB];
-    __shared__ __attribute__((aligned(16))) unsigned char xsm[2][256 * XROWB];
+    constexpr int LDSB = 2 * XSLOT > 256 * BROWB ? 2 * XSLOT : 256 * BROWB;  // B is staged here first
+    __shared__ __attribute__((aligned(16))) unsigned char xsm[LDSB];
     __shared__ float wsm[2][256];
     const int64_t wg = xcd_remap(blockIdx.x, gridDim.x);
     const int part = (int)(wg % nparts);
@@ -410,73 +472,118 @@ __global__ __launch_bounds__(64 * (N / 16)) void k_chunk_state_mh(const bf16 *__
     const int h_lo = g * hpg + part * hpp, h_hi = min(h_lo + hpp, (g + 1) * hpg);
     const int nh = h_hi - h_lo;
     if (nh <= 0) return;  // uniform over the workgroup; no barrier reached
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int r = lane & 15, grp = lane >> 4;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int grp = lane >> 4;
+    const int nk = Q / 32;
 
-    // B rows of the chunk, once
-    copy_tile_to_lds<BROWB, NW>(B + ((b * L + s) * G + g) * N, (int64_t)G * N, Q, q, bsm, wave, lane);
-    auto copy_x = [&](int h, int slot) {
-        copy_tile_to_lds<XROWB, NW>(x + ((b * L + s) * H + h) * P, (int64_t)H * P, Q, q, xsm[slot], wave, lane);
-    };
-    // thread tid < 256 holds step j = tid of a head: its weight (zero past q)
-    auto weight = [&](float csj, float cse, float scj) {
-        return tid < q ? (FROM_START ? __expf(csj) : __expf(cse - csj)) * scj : 0.f;
-    };
-    const bool wthread = tid < 256;
-    float n_csj = 0.f, n_cse = 0.f, n_scj = 1.f;
-    auto load_cs = [&](int h) {
-        const int64_t o = (((int64_t)b * H + h) * nc + c) * Q;
-        n_csj = tid < Q ? cs[o + min(tid, q - 1)] : 0.f;
-        n_cse = cs[o + q - 1];
-        n_scj = (sc && tid < q) ? sc[o + tid] : 1.f;
-    };
-    copy_x(h_lo, 0);
-    if (wthread) {
-        load_cs(h_lo);
-        wsm[0][tid] = weight(n_csj, n_cse, n_scj);
-    }
-    constexpr int NST = PT;  // S stores per wave per head
+    // B rows of the chunk through LDS, into registers as this wave's fragments
+    // (rows k0 + 8 grp .. of column tile `wave`)
+    copy_tile_to_lds<BROWB, NW>(B + ((b * L + s) * G + g) * N, (int64_t)G * N, Q, q, xsm, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __syncthreads();
+    bf16x8 bfr[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        bfr[k] = k < nk ? frag_tr<BROWB>(xsm, 32 * k, wave * 16, lane) : bf16x8{};
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the reads are done before the buffers are reused
+    __syncthreads();
 
-    for (int hh = 0; hh < nh; ++hh) {
-        const int slot = hh & 1;
-        // this wave's copies for head hh (and B) are done once at most the
-        // previous head's S stores are still in flight; lgkmcnt(0) completes
-        // its weight writes before the barrier publishes them
-        if (hh == 0) __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-        else __builtin_amdgcn_s_waitcnt((NST & 15) | ((NST >> 4) << 14) | 0x70);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_barrier();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        const bool more = hh + 1 < nh;
-        if (more) {
-            copy_x(h_lo + hh + 1, slot ^ 1);
-            if (wthread) load_cs(h_lo + hh + 1);
+    // x of one head: this wave's KiB pieces k = wave, wave + NW, ... (lane's
+    // 16 bytes: row k XRPC + lane / XCPR, source chunk swizzled like
+    // copy_tile_to_lds), clamped so every wave issues CPW loads
+    const int ncopy = Q * XROWB / 1024;
+    struct XRegs {
+        u32x4 v[CPW];
+    };
+    auto load_x = [&](int hh, XRegs &R) {
+        const bf16 *src = x + ((b * L + s) * H + h_lo + min(hh, nh - 1)) * P;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int k = min(wave + NW * i, ncopy - 1);
+            const int row = k * XRPC + lane / XCPR;
+            const int chunk = tr_chunk_slot<XROWB>(row, lane % XCPR);
+            R.v[i] = *(const u32x4 *)(src + (int64_t)min(row, q - 1) * H * P + chunk * 8);
         }
+    };
+    auto write_x = [&](const XRegs &R, int buf) {
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int k = wave + NW * i;
+            if (k < ncopy) *(u32x4 *)(xsm + buf * XSLOT + k * 1024 + lane * 16) = R.v[i];
+        }
+    };
+    // thread tid < 256 holds step j = tid of a head: its weight (zero past q);
+    // every thread loads (the rest a clamped duplicate), so the counts are uniform
+    float n_csj = 0.f, n_cse = 0.f, n_scj = 1.f;
+    // this batch row's input factors [H][nc][Q] (empty without them)
+    const auto rs_sc = buf_rsrc(sc ? sc + (int64_t)b * H * nc * Q : nullptr, sc ? (uint32_t)(H * nc * Q * 4) : 0u);
+    auto load_cs = [&](int hh) {
+        const int h = h_lo + min(hh, nh - 1);
+        const int64_t o = (((int64_t)b * H + h) * nc + c) * Q;
+        const int j = min(tid & 255, q - 1);
+        n_csj = cs[o + j];
+        n_cse = cs[o + q - 1];
+        // (no input factor: the resource is empty and the load reads zero)
+        n_scj = buf_ldf(rs_sc, (uint32_t)((o - (int64_t)b * H * nc * Q) + j) * 4u) + (sc ? 0.f : 1.f);
+    };
+    auto weight = [&]() {
+        return tid < q ? (FROM_START ? __expf(n_csj) : __expf(n_cse - n_csj)) * n_scj : 0.f;
+    };
+
+    XRegs X0, X1;
+    load_cs(0);
+    load_x(0, X0);
+    load_x(1, X1);
+    if (tid < 256) wsm[0][tid] = weight();
+    write_x(X0, 0);
+    load_x(2, X0);
+    load_cs(1);
+    // Head hh: its rows and weights sit in LDS buffer hh & 1; the rows of
+    // head hh + 1 are in registers (X1 for even hh), those of hh + 2 loading.
+    auto head = [&](int hh, XRegs &Xnext, XRegs &Xfree) {
+        lds_barrier();  // buffer hh & 1 complete; every wave is done with buffer (hh + 1) & 1
+        const int bi = hh & 1;
         f32x4 acc[PT];
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const float *w = wsm[slot];
-        for (int k0 = 0; k0 < Q; k0 += 32) {
-            bf16x8 bx[PT];
+        const float *w = wsm[bi];
+        const unsigned char *xt = xsm + bi * XSLOT;
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) bx[pt] = frag_tr<XROWB>(xsm[slot], k0, pt * 16, lane);
-            const f32x4 w0 = *(const f32x4 *)(w + k0 + 8 * grp);
-            const f32x4 w1 = *(const f32x4 *)(w + k0 + 8 * grp + 4);
-            bf16x8 ab = frag_tr<BROWB>(bsm, k0, wave * 16, lane);
+        for (int k = 0; k < 8; ++k) {
+            if (k < nk) {
+                bf16x8 bx[PT];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                ab[e] = (bf16)((float)ab[e] * w0[e]);
-                ab[e + 4] = (bf16)((float)ab[e + 4] * w1[e]);
+                for (int pt = 0; pt < PT; ++pt) bx[pt] = frag_tr<XROWB>(xt, 32 * k, pt * 16, lane);
+                const f32x4 w0 = *(const f32x4 *)(w + 32 * k + 8 * grp);
+                const f32x4 w1 = *(const f32x4 *)(w + 32 * k + 8 * grp + 4);
+                bf16x8 ab = bfr[k];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ab[e] = (bf16)((float)ab[e] * w0[e]);
+                    ab[e + 4] = (bf16)((float)ab[e + 4] * w1[e]);
+                }
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) acc[pt] = mfma_bf16(ab, bx[pt], acc[pt]);
             }
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) acc[pt] = mfma_bf16(ab, bx[pt], acc[pt]);
         }
         // acc[pt][e] = S^T[n = 16 wave + 4 grp + e][p = 16 pt + r]
-        float *So = S + (((b * nc + c) * H + h_lo + hh) * (int64_t)P) * N;
+        float *So = S + (((b * nc + c) * H + h_lo + min(hh, nh - 1)) * (int64_t)P) * N;
+        const int r = lane & 15;
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt)
             *(f32x4 *)(So + (int64_t)(pt * 16 + r) * N + wave * 16 + 4 * grp) = acc[pt];
-        if (more && wthread) wsm[slot ^ 1][tid] = weight(n_csj, n_cse, n_scj);
+        // head hh + 1 into the other buffer, then the loads of head hh + 3
+        if (tid < 256) wsm[bi ^ 1][tid] = weight();
+        write_x(Xnext, bi ^ 1);
+        load_x(hh + 3, Xnext);
+        load_cs(hh + 2);
+        (void)Xfree;
+    };
+    // (no branch around a head: an odd count repeats the last head, whose
+    // second result equals the first)
+    for (int hh = 0; hh < nh; hh += 2) {
+        head(hh, X1, X0);
+        head(hh + 1, X0, X1);
     }
 }
 
@@ -846,11 +953,12 @@ hipError_t launch_chunk_state(const Dims &d, const void *x, const void *B, const
         // heads split into parts so that the workgroups fill every CU once
         // (as many per CU as their LDS allows)
         const int64_t nbcg = d.b * d.nc * d.G, hpg = d.H / d.G;
-        const int64_t lds = 256 * (2 * d.N + 4 * d.P) + 2048, per_cu = std::max<int64_t>(1, 163840 / lds);
-        const int64_t target = 256 * per_cu;
-        const int nparts = (int)std::max<int64_t>(1, std::min<int64_t>(hpg, (target + nbcg - 1) / nbcg));
-        const unsigned g2 = (unsigned)(nbcg * nparts);
+        // workgroups per CU that registers and LDS allow (8-wave workgroups for N = 128
+        // need about 176 VGPRs: one per CU; 4-wave ones for N = 64: two)
+        const int64_t target = 256 * (d.N == 128 ? 1 : 2);
 #define SSD_LAUNCH_STATE_MH(PV, NV)                                                               \
+        const int nparts = (int)std::max<int64_t>(1, std::min<int64_t>(hpg, (target + nbcg - 1) / nbcg)); \
+        const unsigned g2 = (unsigned)(nbcg * nparts);                                            \
         if (from_start)                                                                           \
             k_chunk_state_mh<PV, NV, true><<<g2, 64 * (NV / 16), 0, st>>>((const bf16 *)x, (const bf16 *)B, cs, S, \
                 d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc, sc, nparts);                        \

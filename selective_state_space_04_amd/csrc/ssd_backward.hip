@@ -1610,63 +1610,98 @@ __global__ __launch_bounds__(256) void k_group_combine(
     const int t0 = blk * 64 + wave * 16;          // this wave's first row
     const bool wv = t0 < q;
     const int64_t cboff = bcg * (int64_t)Q * Q;
-    const float *arow = (which == 0 ? dcb : dcbT) + cboff + (int64_t)(t0 + r) * Q;
+    // (row clamped: a wave past q still loads, unused, from inside this block)
+    const float *arow = (which == 0 ? dcb : dcbT) + cboff + (int64_t)min(t0 + r, Q - 1) * Q;
     const T *V = (which == 0 ? B : C) + ((b * L + s) * G + g) * N;
     const int q16 = (q + 15) & ~15;
     // this wave's k range, and the workgroup's (the union over its waves)
     const int k_lo = which == 0 ? 0 : t0, k_hi = which == 0 ? t0 + 16 : q16;
     const int g_lo = which == 0 ? 0 : blk * 64;
     const int g_hi = which == 0 ? min(blk * 64 + 64, q16) : q16;
-    __shared__ float vs[SK * VLD];
+    // V rows k0 .. k0 + 31 as float32 in one of two LDS buffers; the next
+    // slab's rows (and this wave's C B^T pieces) load into registers while the
+    // current one multiplies.  Loads are unconditional (row indices clamped,
+    // values past q zeroed after the load), so the compiler's counted waits
+    // keep them in flight.
+    __shared__ float vs[2][SK * VLD];
+    constexpr int VPT = (SK * N / 8 + 255) / 256;  // 8-value pieces per thread per slab
+    struct VRegs {
+        u32x4 v[VPT][sizeof(T) == 2 ? 1 : 2];
+    };
+    auto load_v = [&](int k0, VRegs &R) {
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int idx = min((int)threadIdx.x + 256 * u, SK * N / 8 - 1);
+            const int kr = idx / (N / 8), c8 = (idx % (N / 8)) * 8;
+            const T *src = V + (int64_t)min(k0 + kr, q - 1) * G * N + c8;
+            R.v[u][0] = *(const u32x4 *)src;
+            if constexpr (sizeof(T) == 4) R.v[u][1] = *(const u32x4 *)(src + 4);
+        }
+    };
+    auto write_v = [&](int k0, const VRegs &R, float *dst) {
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int idx = (int)threadIdx.x + 256 * u;
+            if ((SK * N / 8) % 256 == 0 || idx < SK * N / 8) {
+                const int kr = idx / (N / 8), c8 = (idx % (N / 8)) * 8;
+                const bool ok = k0 + kr < q;
+                float f[8];
+                if constexpr (sizeof(T) == 2) {
+                    const bf16x8 t = as_bf16x8(R.v[u][0]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) f[e] = ok ? (float)t[e] : 0.f;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        f[e] = ok ? __builtin_bit_cast(float, (uint32_t)R.v[u][0][e]) : 0.f;
+                        f[e + 4] = ok ? __builtin_bit_cast(float, (uint32_t)R.v[u][1][e]) : 0.f;
+                    }
+                }
+                *(f32x4 *)(dst + kr * VLD + c8) = f32x4{f[0], f[1], f[2], f[3]};
+                *(f32x4 *)(dst + kr * VLD + c8 + 4) = f32x4{f[4], f[5], f[6], f[7]};
+            }
+        }
+    };
+    // this wave's C B^T pieces of a slab (rows t0 + r, columns kb + 4 grp ..), clamped in range
+    auto load_a = [&](int k0, f32x4 (&a)[SK / 16]) {
+#pragma unroll
+        for (int kq = 0; kq < SK; kq += 16) {
+            const int kk = min(k0 + kq + 4 * grp, Q - 4);
+            a[kq / 16] = *(const f32x4 *)(arow + kk);
+        }
+    };
 
     f32x4 acc[NT];
 #pragma unroll
     for (int u = 0; u < NT; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = g_lo; k0 < g_hi; k0 += SK) {
-        // stage rows k0 .. k0 + 31 of V as float32 (zero past q)
-        for (int idx = threadIdx.x; idx < SK * N / 8; idx += 256) {
-            const int kr = idx / (N / 8), c8 = (idx % (N / 8)) * 8;
-            const int k = k0 + kr;
-            float f[8];
-            if (k < q) {
-                if constexpr (sizeof(T) == 2) {
-                    const bf16x8 t = as_bf16x8(*(const u32x4 *)(V + (int64_t)k * G * N + c8));
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) f[e] = (float)t[e];
-                } else {
-                    const f32x4 lo = *(const f32x4 *)(V + (int64_t)k * G * N + c8);
-                    const f32x4 hi = *(const f32x4 *)(V + (int64_t)k * G * N + c8 + 4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        f[e] = lo[e];
-                        f[e + 4] = hi[e];
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) f[e] = 0.f;
-            }
-            *(f32x4 *)(vs + kr * VLD + c8) = f32x4{f[0], f[1], f[2], f[3]};
-            *(f32x4 *)(vs + kr * VLD + c8 + 4) = f32x4{f[4], f[5], f[6], f[7]};
-        }
-        __syncthreads();
+    VRegs R0, R1;
+    f32x4 a0[SK / 16], a1[SK / 16];
+    auto slab = [&](int k0, VRegs &Rc, f32x4 (&ac)[SK / 16], VRegs &Rn, f32x4 (&an)[SK / 16], int buf) {
+        write_v(k0, Rc, vs[buf]);
+        lds_barrier();  // slab k0 complete; every wave is done with the other buffer
+        load_v(k0 + SK, Rn);
+        load_a(k0 + SK, an);
         if (wv) {
 #pragma unroll
             for (int kq = 0; kq < SK; kq += 16) {
                 const int kb = k0 + kq;
                 if (kb >= k_lo && kb < k_hi) {
-                    const int kk = kb + 4 * grp;
-                    const f32x4 a4 = *(const f32x4 *)(arow + kk);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float *vrow = vs + (kq + 4 * grp + e) * VLD + r;
+                        const float *vrow = vs[buf] + (kq + 4 * grp + e) * VLD + r;
 #pragma unroll
-                        for (int u = 0; u < NT; ++u) acc[u] = mfma_f32(a4[e], vrow[16 * u], acc[u]);
+                        for (int u = 0; u < NT; ++u) acc[u] = mfma_f32(ac[kq / 16][e], vrow[16 * u], acc[u]);
                     }
                 }
             }
         }
-        __syncthreads();
+    };
+    load_v(g_lo, R0);
+    load_a(g_lo, a0);
+    // (slabs past g_hi load clamped rows, unused; no slab sits behind a branch)
+    for (int k0 = g_lo; k0 < g_hi; k0 += 2 * SK) {
+        slab(k0, R0, a0, R1, a1, 0);
+        slab(k0 + SK, R1, a1, R0, a0, 1);
     }
     if (!wv) return;
     const float *base = which == 0 ? dCs : dBs;

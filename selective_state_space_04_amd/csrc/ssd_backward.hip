@@ -29,6 +29,9 @@
 //
 // Kernels (the forward states H_c and the state gradients R_c are produced
 // first by the step kernels of ssd_kernels.hip and k_state_passing_rev):
+//   k_bwd_frags     per (b, c, g, 16-row tile), bf16: C B^T, C and B in the
+//                   fragment order k_chunk_bwd_pf loads (else k_chunk_cb of
+//                   ssd_kernels.hip writes C B^T and its transpose row-major).
 //   k_chunk_bwd     per (b, c, h): recomputes y'_i, computes dx and the
 //                   decay gradients of the chunk; per-chunk partial sums of
 //                   dA_h and dD_h (k_chunk_bwd_pf: the bf16 version with each
@@ -37,11 +40,12 @@
 //                   and sums exp(cs_i - cs_j)(dy_i.x_j) (dCB, both
 //                   orientations) and the state terms of dC and dB (float32
 //                   inputs, and bf16 shapes with N = 256 or P N > 8192).
-//   k_group_dcb,    the same sums for the other bf16 shapes, split so each
-//   k_group_state   kernel's accumulators stay in registers at several waves
-//                   per SIMD: dCB per 64 x 64 block pair, the state terms per
-//                   64 rows with the state staged in LDS.
-//   k_group_combine per (b, c, g, 16 rows): dC = dC_state + dCB B,
+//   k_group_dcb_rb, the same sums for the other bf16 shapes, split so each
+//   k_group_dcb,    kernel's accumulators stay in registers at several waves
+//   k_group_state   per SIMD: dCB per 64-row block (k_group_dcb_rb, P 32 or
+//                   64) or per 64 x 64 block pair (k_group_dcb), the state
+//                   terms per 128 rows with each head's state in LDS.
+//   k_group_combine per (b, c, g, 64 rows): dC = dC_state + dCB B,
 //                   dB = dB_state + dCB^T C, rounded to the input dtype.
 //   k_head_reduce   per h: sums the per-chunk partials of dA_h and dD_h.
 #include <type_traits>

@@ -856,7 +856,8 @@ __global__ __launch_bounds__(256) void k_decode(float *__restrict__ state, const
         for (int u = 0; u < U; ++u) {
             const int p = p0 + u * RPI + slot;
             if (p < P) {
-                hv[u] = *(const f32x4 *)(st + (int64_t)p * N + nl * 4);
+                // the state streams through once per step: non-temporal
+                hv[u] = __builtin_nontemporal_load((const f32x4 *)(st + (int64_t)p * N + nl * 4));
                 xv[u] = to_f32(xp[p]);
             }
         }
@@ -871,7 +872,7 @@ __global__ __launch_bounds__(256) void k_decode(float *__restrict__ state, const
                     nh[e] = a * hv[u][e] + (xsc * xv[u]) * bv[e];
                     part += nh[e] * cv[e];
                 }
-                *(f32x4 *)(st + (int64_t)p * N + nl * 4) = nh;
+                __builtin_nontemporal_store(nh, (f32x4 *)(st + (int64_t)p * N + nl * 4));
             }
 #pragma unroll
             for (int off = NL / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);

@@ -11,31 +11,45 @@
 namespace ssd {
 
 template <typename T> struct Vec8;
+// NT: non-temporal accesses, for data that streams through once
 template <> struct Vec8<bf16> {
+    template <bool NT = false>
     static __device__ __forceinline__ void load(const bf16 *p, float *v) {
-        const bf16x8 t = *(const bf16x8 *)p;
+        const u32x4 w = NT ? __builtin_nontemporal_load((const u32x4 *)p) : *(const u32x4 *)p;
+        const bf16x8 t = as_bf16x8(w);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (float)t[e];
     }
+    template <bool NT = false>
     static __device__ __forceinline__ void store(bf16 *p, const float *v) {
         bf16x8 t;
 #pragma unroll
         for (int e = 0; e < 8; ++e) t[e] = (bf16)v[e];
-        *(bf16x8 *)p = t;
+        if (NT) __builtin_nontemporal_store(as_u32x4(t), (u32x4 *)p);
+        else *(bf16x8 *)p = t;
     }
 };
 template <> struct Vec8<float> {
+    template <bool NT = false>
     static __device__ __forceinline__ void load(const float *p, float *v) {
-        const f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
+        const f32x4 a = NT ? __builtin_nontemporal_load((const f32x4 *)p) : *(const f32x4 *)p;
+        const f32x4 b = NT ? __builtin_nontemporal_load((const f32x4 *)(p + 4)) : *(const f32x4 *)(p + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             v[e] = a[e];
             v[e + 4] = b[e];
         }
     }
+    template <bool NT = false>
     static __device__ __forceinline__ void store(float *p, const float *v) {
-        *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
-        *(f32x4 *)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        const f32x4 a = f32x4{v[0], v[1], v[2], v[3]}, b = f32x4{v[4], v[5], v[6], v[7]};
+        if (NT) {
+            __builtin_nontemporal_store(a, (f32x4 *)p);
+            __builtin_nontemporal_store(b, (f32x4 *)(p + 4));
+        } else {
+            *(f32x4 *)p = a;
+            *(f32x4 *)(p + 4) = b;
+        }
     }
 };
 
@@ -113,8 +127,8 @@ __global__ __launch_bounds__(128) void k_gated_rmsnorm_reg(const T *y, const T *
         const int pc = tid + 128 * u;
         if (pc < npieces) {
             float yv[8], zv[8];
-            Vec8<T>::load(yr + 8 * pc, yv);
-            Vec8<T>::load(zr + 8 * pc, zv);
+            Vec8<T>::template load<true>(yr + 8 * pc, yv);
+            Vec8<T>::template load<true>(zr + 8 * pc, zv);
             float acc = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -153,7 +167,7 @@ __global__ __launch_bounds__(128) void k_gated_rmsnorm_reg(const T *y, const T *
             float o[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[e] = g[u][e] * sc * (e < 4 ? w0[e] : w1[e - 4]);
-            Vec8<T>::store(orow + 8 * pc, o);
+            Vec8<T>::template store<true>(orow + 8 * pc, o);
         }
     }
 }

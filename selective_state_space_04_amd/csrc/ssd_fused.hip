@@ -39,16 +39,16 @@ namespace {
 
 constexpr int kSpinLimit = 1 << 21;
 
-// 8-byte load / store as a 64-bit agent-scope relaxed atomic: coherent
-// across the XCDs' separate L2 caches with no cache write-back/invalidate.
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ f32x2 ld_agent_f32x2(const float *p) {
-    const uint64_t a = __hip_atomic_load((const uint64_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return f32x2{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32))};
+// 16-byte ring load / store carrying the SC1 cache-policy bit (operand 16),
+// which is what the compiler emits for an agent-scope relaxed atomic load or
+// store on gfx950: coherent across the XCDs' separate L2 caches with no
+// cache write-back/invalidate, at twice the width of a 64-bit atomic.
+constexpr int kAgentCoherent = 16;
+__device__ __forceinline__ f32x4 ld_agent_f32x4(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, kAgentCoherent));
 }
-__device__ __forceinline__ void st_agent_f32x2(float *p, f32x2 v) {
-    const uint64_t a = ((uint64_t)__float_as_uint(v[1]) << 32) | __float_as_uint(v[0]);
-    __hip_atomic_store((uint64_t *)p, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void st_agent_f32x4(f32x4 v, __amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, (int)off, 0, kAgentCoherent);
 }
 
 // x staging, split so the loads can be issued long before the LDS writes.
@@ -403,14 +403,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     // 3. hand-off, first half: wait until wave `wave` of chunk c - 1 of this
     // (b, h) has published its slice of h_{c-1}, then load the slice (it
     // arrives while the chunk state is computed).  The ring is read and
-    // written with agent-scope atomic accesses (coherent across XCDs without
-    // cache maintenance), in a lane-major layout so each wave moves one
-    // contiguous 512-byte block per access; init / final_state use the
-    // [P][N] layout.  hv[tt][pt][e] = h_{c-1}[p = 16 pt + r][n = 16 (wave + 4 tt) + 4 grp + e]
-    // ring_off(tt, pt, half) = ring_base(tt) + (pt * 2 + half) * 128: the
-    // per-(pt, half) part folds into the access's immediate offset
-    auto ring_base = [&](int tt) -> int { return ((wave * NTW + tt) * PT * 2 * 64 + lane) * 2; };
-    auto ring_off = [&](int tt, int pt, int half) -> int { return ring_base(tt) + (pt * 2 + half) * 128; };
+    // written with agent-coherent accesses (see ld_agent_f32x4), in a
+    // lane-major layout so each wave moves one contiguous 1 KiB block per
+    // access; init / final_state use the [P][N] layout.
+    // hv[tt][pt][e] = h_{c-1}[p = 16 pt + r][n = 16 (wave + 4 tt) + 4 grp + e]
+    // sits at float ring_base(tt) + 256 pt of the (b, h) slice; the per-pt
+    // part folds into the access's immediate offset
+    auto ring_base = [&](int tt) -> int { return ((wave * NTW + tt) * PT * 64 + lane) * 4; };
     int *myflag = flags + bh * 4 + wave;
     const bool have_h = c > 0 || init != nullptr;
     f32x4 hv[NTW][PT];
@@ -426,17 +425,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             ++n;
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        const float *hp = ring + ((c - 1) & 1) * nbh * PN + bh * PN;
+        const auto rsH = buf_rsrc(ring + ((c - 1) & 1) * nbh * PN + bh * PN, (uint32_t)PN * 4u);
 #pragma unroll
-        for (int tt = 0; tt < NTW; ++tt) {
-            const float *hb = hp + ring_base(tt);
+        for (int tt = 0; tt < NTW; ++tt)
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) {
-                const f32x2 lo = ld_agent_f32x2(hb + (pt * 2) * 128);
-                const f32x2 hi = ld_agent_f32x2(hb + (pt * 2 + 1) * 128);
-                hv[tt][pt] = f32x4{lo[0], lo[1], hi[0], hi[1]};
-            }
-        }
+            for (int pt = 0; pt < PT; ++pt)
+                hv[tt][pt] = ld_agent_f32x4(rsH, (uint32_t)(ring_base(tt) + pt * 256) * 4u);
     } else {
 #pragma unroll
         for (int tt = 0; tt < NTW; ++tt)
@@ -500,6 +494,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const float lam_c = __expf(cs_last);
     const bool last = c == nc - 1;
     float *hout = last ? (fin ? fin + bh * PN : nullptr) : ring + (c & 1) * nbh * PN + bh * PN;
+    const auto rsO = buf_rsrc(hout, (uint32_t)PN * 4u);
     // Tile 0's loads (issued before the barrier above, long landed) are waited
     // for here, before the ring stores: with loads and stores both in flight
     // the compiler's wait for them would also wait for most of the stores.
@@ -514,9 +509,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 if (last) {
                     *(f32x4 *)(hout + p * N + n0) = hn;
                 } else {
-                    float *hb = hout + ring_base(tt);
-                    st_agent_f32x2(hb + (pt * 2) * 128, f32x2{hn[0], hn[1]});
-                    st_agent_f32x2(hb + (pt * 2 + 1) * 128, f32x2{hn[2], hn[3]});
+                    st_agent_f32x4(hn, rsO, (uint32_t)(ring_base(tt) + pt * 256) * 4u);
                 }
             }
             bf16 hb[4];

@@ -819,6 +819,265 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const T *__restrict__ x, con
 }
 
 // ---------------------------------------------------------------------------
+// float32 chunk state and output, with the chunk's rows staged in LDS as they
+// lie in memory ([j][col], row stride COLS + 4 floats).  The fp32 MFMA takes
+// one value per lane: lanes r = 0..15 of a k-group read 16 consecutive
+// columns of one row, and the four k-groups read rows 4 apart, which the
+// padding of 4 floats puts on the two halves of the 32 banks.  Lane group
+// grp of the e-th MFMA of a 16-step block j0 contracts step j0 + 4 grp + e.
+// Every global load is unconditional: rows past q are clamped to row q - 1
+// and their values replaced by zero, so no branch splits the compiler's
+// counted waits.
+// ---------------------------------------------------------------------------
+
+// Chunk state S^T[n][p] = sum_j B[j][n] w_j x[j][p] in 64-step slabs: the
+// next slab's rows load into registers while the current one is multiplied.
+template <int P, int N, bool FROM_START>
+__global__ __launch_bounds__(256) void k_chunk_state_f32(const float *__restrict__ x,
+                                                         const float *__restrict__ B,
+                                                         const float *__restrict__ cs,
+                                                         float *__restrict__ S, int64_t L, int H,
+                                                         int G, int Q, int nc,
+                                                         const float *__restrict__ sc) {
+    constexpr int PT = P / 16, NT = N / 16, NTW = (NT + 3) / 4;
+    constexpr int SL = 64, XLD = P + 4, BLD = N + 4;
+    constexpr int XPC = P / 4, BPC = N / 4;            // 16-byte pieces per row
+    constexpr int XPT = SL * XPC / 256, BPT = SL * BPC / 256;  // pieces per thread
+    const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = (int)(wid % H);
+    const int64_t bc = wid / H;
+    const int c = (int)(bc % nc);
+    const int64_t b = bc / nc;
+    const int g = h / (H / G);
+    const int64_t s = (int64_t)c * Q;
+    const int q = (int)min<int64_t>(Q, L - s);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, grp = lane >> 4;
+
+    __shared__ float w_s[256];
+    __shared__ float xs[SL * XLD];
+    __shared__ float bs[SL * BLD];
+    const float *csc = cs + (((int64_t)b * H + h) * nc + c) * Q;
+    const float cs_last = csc[q - 1];
+    const float *scc = sc ? sc + (((int64_t)b * H + h) * nc + c) * Q : nullptr;
+    for (int j = tid; j < Q; j += 256)
+        w_s[j] = (FROM_START ? __expf(csc[j]) : __expf(cs_last - csc[j])) * (scc ? scc[j] : 1.f);
+
+    const float *xb = x + ((b * L + s) * H + h) * P;
+    const float *Bb = B + ((b * L + s) * G + g) * N;
+    const int64_t xld = (int64_t)H * P, bld = (int64_t)G * N;
+    f32x4 xr[XPT], br[BPT];
+    auto load = [&](int jb) {
+#pragma unroll
+        for (int k = 0; k < XPT; ++k) {
+            const int idx = tid + 256 * k, j = jb + idx / XPC;
+            xr[k] = *(const f32x4 *)(xb + min(j, q - 1) * xld + 4 * (idx % XPC));
+        }
+#pragma unroll
+        for (int k = 0; k < BPT; ++k) {
+            const int idx = tid + 256 * k, j = jb + idx / BPC;
+            br[k] = *(const f32x4 *)(Bb + min(j, q - 1) * bld + 4 * (idx % BPC));
+        }
+    };
+    // x rows scaled by w_j; rows past q as zero
+    auto write = [&](int jb) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < XPT; ++k) {
+            const int idx = tid + 256 * k, jr = idx / XPC;
+            *(f32x4 *)(xs + jr * XLD + 4 * (idx % XPC)) = jb + jr < q ? xr[k] * w_s[jb + jr] : z;
+        }
+#pragma unroll
+        for (int k = 0; k < BPT; ++k) {
+            const int idx = tid + 256 * k, jr = idx / BPC;
+            *(f32x4 *)(bs + jr * BLD + 4 * (idx % BPC)) = jb + jr < q ? br[k] : z;
+        }
+    };
+
+    f32x4 acc[NTW][PT];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[t][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    load(0);
+    __syncthreads();  // w_s
+    for (int jb = 0; jb < q; jb += SL) {
+        write(jb);
+        lds_barrier();
+        load(jb + SL);  // past the end: clamped rows, never written
+#pragma unroll
+        for (int j0 = 0; j0 < SL; j0 += 16) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int jr = j0 + 4 * grp + e;
+                float xa[PT];
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) xa[pt] = xs[jr * XLD + pt * 16 + r];
+#pragma unroll
+                for (int t = 0; t < NTW; ++t) {
+                    const int nt = wave + 4 * t;
+                    if (nt < NT) {
+                        const float bv = bs[jr * BLD + nt * 16 + r];
+#pragma unroll
+                        for (int pt = 0; pt < PT; ++pt) acc[t][pt] = mfma_f32(bv, xa[pt], acc[t][pt]);
+                    }
+                }
+            }
+        }
+        lds_barrier();
+    }
+    // acc[t][pt][e] = S^T[n = nt*16 + 4 grp + e][p = pt*16 + r]
+    float *So = S + (((b * nc + c) * H + h) * (int64_t)P) * N;
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+        const int nt = wave + 4 * t;
+        if (nt < NT) {
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt)
+                *(f32x4 *)(So + (int64_t)(pt * 16 + r) * N + nt * 16 + 4 * grp) = acc[t][pt];
+        }
+    }
+}
+
+// Output of a chunk, transposed as in k_chunk_scan: Y^T[p][i] per 16-row
+// tile, the waves' tiles dealt in the same snake order.  The state term runs
+// first for all four of a wave's tiles, so h_{c-1} is read once per wave;
+// each tile's C B^T row pieces load in one round (buffer loads, the blocks
+// past the diagonal switched off) before its intra product.  Every tile is
+// computed, a tile past q on clamped rows; its stores fall outside the
+// buffer resource over y and are dropped.  The caller keeps the byte span
+// of a chunk's y rows below 2^31.
+template <int P, int N>
+__global__ __launch_bounds__(256) void k_chunk_scan_f32(const float *__restrict__ x,
+                                                        const float *__restrict__ C,
+                                                        const float *__restrict__ cb,
+                                                        const float *__restrict__ cs,
+                                                        const float *__restrict__ hprev,
+                                                        const float *__restrict__ D,
+                                                        float *__restrict__ y, int64_t L, int H,
+                                                        int G, int Q, int nc,
+                                                        const float *__restrict__ sc) {
+    constexpr int PT = P / 16, XLD = P + 4, PC = P / 4, KB = PC < 8 ? PC : 8;
+    const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = (int)(wid % H);
+    const int64_t bc = wid / H;
+    const int c = (int)(bc % nc);
+    const int64_t b = bc / nc;
+    const int g = h / (H / G);
+    const int64_t s = (int64_t)c * Q;
+    const int q = (int)min<int64_t>(Q, L - s);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, grp = lane >> 4;
+
+    __shared__ float cs_s[256], sc_s[256];
+    __shared__ float xs[256 * XLD];
+    const float *csc = cs + (((int64_t)b * H + h) * nc + c) * Q;
+    const float *scc = sc ? sc + (((int64_t)b * H + h) * nc + c) * Q : nullptr;
+    cs_s[tid] = csc[min(tid, Q - 1)];
+    sc_s[tid] = scc ? scc[min(tid, Q - 1)] : 1.f;
+    const int64_t row0 = (b * L + s) * H + h;  // (row of step s, head h) in x / y
+    const int64_t HP = (int64_t)H * P;
+    const float *xb = x + row0 * P;
+    // the chunk's x rows, rows q .. 255 as zero
+#pragma unroll
+    for (int k0 = 0; k0 < PC; k0 += KB) {
+        f32x4 v[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const int idx = tid + 256 * (k0 + k);
+            v[k] = *(const f32x4 *)(xb + min(idx / PC, q - 1) * HP + 4 * (idx % PC));
+        }
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const int idx = tid + 256 * (k0 + k), j = idx / PC;
+            *(f32x4 *)(xs + j * XLD + 4 * (idx % PC)) = j < q ? v[k] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    __syncthreads();
+
+    const float *cbc = cb + (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
+    const float *hp = hprev ? hprev + (((b * nc + c) * H + h) * (int64_t)P) * N : nullptr;
+    const float *Cb = C + ((b * L + s) * G + g) * N;
+    const int64_t GN = (int64_t)G * N;
+    const float Dh = D ? D[h] : 0.f;
+    int tI[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) tI[t] = 4 * t + ((t & 1) ? 3 - wave : wave);
+    // tiles past Q (Q < 256) are computed on clamped rows and never stored
+    f32x4 acc[4][PT];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[t][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // state term exp(cs_i) C_i h_{c-1}: A = h rows, B = C rows
+    if (hp) {
+#pragma unroll 2
+        for (int k0 = 0; k0 < N; k0 += 16) {
+            const int kk = k0 + 4 * grp;
+            f32x4 h4[PT], c4[4];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) h4[pt] = *(const f32x4 *)(hp + (int64_t)(pt * 16 + r) * N + kk);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) c4[t] = *(const f32x4 *)(Cb + min(tI[t] * 16 + r, q - 1) * GN + kk);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[t][pt] = mfma_f32(h4[pt][e], c4[t][e], acc[t][pt]);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float ei = __expf(cs_s[tI[t] * 16 + r]);
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) acc[t][pt] *= ei;
+        }
+    }
+
+    const auto rsG = buf_rsrc(cbc, (uint32_t)Q * (uint32_t)Q * 4u);
+    const auto rsY = buf_rsrc(y + row0 * P, (uint32_t)(((int64_t)(q - 1) * HP + P) * 4));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int I = tI[t];
+        const int il = I * 16 + r;  // this lane's output row inside the chunk
+        const int ilc = min(il, q - 1);
+        const float csi = cs_s[il];
+        // C B^T row pieces of blocks 0..I (the rest read as zero)
+        f32x4 g4[16];
+#pragma unroll
+        for (int jb = 0; jb < 16; ++jb)
+            g4[jb] = __builtin_bit_cast(
+                f32x4, buf_ld16(rsG, jb <= I && jb * 16 < Q ? (uint32_t)(ilc * Q + jb * 16 + 4 * grp) * 4u : kBufOff));
+#pragma unroll
+        for (int jb = 0; jb < 16; ++jb) {
+            if (jb <= I) {
+                const int jl = jb * 16 + 4 * grp;
+                const f32x4 csj = *(const f32x4 *)(cs_s + jl), scj = *(const f32x4 *)(sc_s + jl);
+                float m[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    m[e] = (jl + e <= il) ? __expf(csi - csj[e]) * g4[jb][e] * scj[e] : 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt)
+                        acc[t][pt] = mfma_f32(xs[(jl + e) * XLD + pt * 16 + r], m[e], acc[t][pt]);
+                }
+            }
+        }
+        // + D x_i; lane holds row il, channels p0 .. p0 + 3
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const int p0 = pt * 16 + 4 * grp;
+            const f32x4 o = acc[t][pt] + Dh * *(const f32x4 *)(xs + il * XLD + p0);
+            const uint32_t off = il < q ? (uint32_t)((il * HP + p0) * 4) : kBufOff;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rsY, (int)off, 0, 0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Decode step: one workgroup per (b, h).  N / 4 lanes share a state row (one
 // float4 each); rows are processed 8 deep so 8 loads per lane are in flight.
 // The row dot product with C is a butterfly over the row's lanes.
@@ -981,7 +1240,7 @@ hipError_t launch_chunk_state(const Dims &d, const void *x, const void *B, const
                 (const bf16 *)x, (const bf16 *)B, cs, S, d.L, (int)d.H, (int)d.G, (int)d.Q,       \
                 (int)d.nc, sc);                                                                   \
         else                                                                                      \
-            k_chunk_state<float, PP, NN, FS><<<grid, 256, 0, st>>>(                               \
+            k_chunk_state_f32<PP, NN, FS><<<grid, 256, 0, st>>>(                                  \
                 (const float *)x, (const float *)B, cs, S, d.L, (int)d.H, (int)d.G, (int)d.Q,     \
                 (int)d.nc, sc);                                                                   \
     })
@@ -1019,11 +1278,17 @@ hipError_t launch_chunk_scan(const Dims &d, const void *x, const void *C, const 
                              hipStream_t st, const float *sc) {
     if (d.b == 0 || d.nc == 0) return hipSuccess;
     const unsigned grid = (unsigned)(d.b * d.nc * d.H);
+    // k_chunk_scan_f32 addresses a chunk's y rows through one buffer resource
+    const bool f32_span_ok = d.Q * d.H * d.P * 4 < ((int64_t)1 << 31);
     SSD_DISPATCH_PN(d.P, d.N, {
         if (d.dtype == 1)
             k_chunk_scan<bf16, PP, NN><<<grid, 256, 0, st>>>(
                 (const bf16 *)x, (const bf16 *)C, (const bf16 *)cb, cs, hprev, D, (bf16 *)y, d.L,
                 (int)d.H, (int)d.G, (int)d.Q, (int)d.nc, sc);
+        else if (f32_span_ok)
+            k_chunk_scan_f32<PP, NN><<<grid, 256, 0, st>>>(
+                (const float *)x, (const float *)C, (const float *)cb, cs, hprev, D, (float *)y,
+                d.L, (int)d.H, (int)d.G, (int)d.Q, (int)d.nc, sc);
         else
             k_chunk_scan<float, PP, NN><<<grid, 256, 0, st>>>(
                 (const float *)x, (const float *)C, (const float *)cb, cs, hprev, D, (float *)y,

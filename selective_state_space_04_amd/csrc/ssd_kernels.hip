@@ -186,8 +186,8 @@ __global__ __launch_bounds__(256) void k_chunk_cb(const T *__restrict__ B, const
 // start), which with (x, B) -> (dy, C) gives the gradient that a chunk's
 // outputs send back to the state entering it.  bf16: 64-step slabs of x (pre-scaled by w_j) and B are staged
 // in LDS transposed (step index contiguous) so each MFMA fragment is one
-// 16-byte LDS read.  f32: fragments come straight from global memory (one
-// element per lane per MFMA).  Wave w owns n-tiles w, w + 4, ...
+// 16-byte LDS read (float32 inputs: k_chunk_state_f32).  Wave w owns
+// n-tiles w, w + 4, ...
 // ---------------------------------------------------------------------------
 // One thread's share of a [64 x COLS] bf16 slab in registers: blocks of 4
 // rows x 8 columns, block tid + 256 i, as four 16-byte row pieces; rows at
@@ -287,7 +287,8 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T *__restrict__ x,
 
     const T *xb = x + ((b * L + s) * H + h) * P;
     const T *Bb = B + ((b * L + s) * G + g) * N;
-    if constexpr (sizeof(T) == 2) {
+    static_assert(sizeof(T) == 2, "float32 inputs use k_chunk_state_f32");
+    {
         constexpr int SL = 64, LD = SL + 8;
         __shared__ bf16 xs[P * LD];
         __shared__ bf16 bs[N * LD];
@@ -323,36 +324,6 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T *__restrict__ x,
                 }
             }
             lds_barrier();
-        }
-    } else {
-        for (int j0 = 0; j0 < q; j0 += 16) {
-            float xv[PT][4];
-            bool valid[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = j0 + 4 * grp + e;
-                valid[e] = j < q;
-                const float w = valid[e] ? w_s[j] : 0.f;
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
-                    xv[pt][e] = valid[e] ? to_f32(xb[(int64_t)j * H * P + pt * 16 + r]) * w : 0.f;
-            }
-#pragma unroll
-            for (int t = 0; t < NTW; ++t) {
-                const int nt = wave + 4 * t;
-                if (nt < NT) {
-                    float bv[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int j = j0 + 4 * grp + e;
-                        bv[e] = valid[e] ? to_f32(Bb[(int64_t)j * G * N + nt * 16 + r]) : 0.f;
-                    }
-#pragma unroll
-                    for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[t][pt] = mfma_f32(bv[e], xv[pt][e], acc[t][pt]);
-                }
-            }
         }
     }
     // acc[t][pt][e] = S^T[n = nt*16 + 4 grp + e][p = pt*16 + r]
@@ -647,7 +618,9 @@ __global__ __launch_bounds__(256) void k_copy_state(const float *init, float *fi
 //   skip:      Y^T[p][i] += D_h x[i][p]
 // The 16-wide output tiles are dealt to the four waves in a snake order so
 // the triangular work is balanced.  bf16: x^T and the state (as bf16) are
-// staged in LDS; f32: operands come from global memory.
+// staged in LDS.  float32 inputs run k_chunk_scan_f32; this kernel's f32
+// branch, with operands read from global memory, serves only chunks whose y
+// rows span 2^31 bytes or more (beyond one buffer resource).
 // ---------------------------------------------------------------------------
 template <typename T, int P, int N>
 __global__ __launch_bounds__(256) void k_chunk_scan(const T *__restrict__ x, const T *__restrict__ C,

@@ -560,9 +560,12 @@ __global__ __launch_bounds__(64 * (N / 16)) void k_chunk_state_mh(const bf16 *__
 
 // ---------------------------------------------------------------------------
 // Inter-chunk recurrence, in place: S[c] -> hprev[c].  Each thread owns four
-// consecutive state elements of one (b, h) and walks the chunks in order,
-// with the next 8 chunk states loaded ahead (they do not depend on the
-// running state).
+// consecutive state elements of one (b, h) and walks the chunks in order.
+// The chunk states do not depend on the running state, so they load in
+// batches of U, one batch ahead of the one being combined (two batches in
+// flight).  The loads are unconditional (a batch past the end repeats the
+// last chunk) and so are the full batches' stores; only the last partial
+// batch branches.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_state_passing(float *__restrict__ S,
                                                        const float *__restrict__ cs,
@@ -575,27 +578,53 @@ __global__ __launch_bounds__(256) void k_state_passing(float *__restrict__ S,
     const int64_t bh = b * H + h;
     f32x4 hv = init ? *(const f32x4 *)(init + bh * PN + e0) : f32x4{0.f, 0.f, 0.f, 0.f};
     const float *csb = cs + bh * (int64_t)nc * Q;
+    auto at = [&](int c) { return S + (((b * nc + c) * H + h) * (int64_t)PN) + e0; };
     constexpr int U = 8;
-    for (int c0 = 0; c0 < nc; c0 += U) {
-        f32x4 sv[U];
-        float lam[U];
+    f32x4 sa[U], sb[U];
+    float la[U], lb[U];
+    auto load = [&](int c0, f32x4(&v)[U], float(&l)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int c = c0 + u;
-            if (c < nc) {
-                const int last = (int)min<int64_t>(Q, L - (int64_t)c * Q) - 1;
-                lam[u] = __expf(csb[(int64_t)c * Q + last]);
-                sv[u] = *(const f32x4 *)(S + (((b * nc + c) * H + h) * (int64_t)PN) + e0);
-            }
+            const int c = min(c0 + u, nc - 1);
+            const int last = (int)min<int64_t>(Q, L - (int64_t)c * Q) - 1;
+            l[u] = __expf(csb[(int64_t)c * Q + last]);
+            v[u] = *(const f32x4 *)at(c);
         }
+    };
+    auto step = [&](int c0, const f32x4(&v)[U], const float(&l)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int c = c0 + u;
-            if (c < nc) {
-                *(f32x4 *)(S + (((b * nc + c) * H + h) * (int64_t)PN) + e0) = hv;
-                hv = lam[u] * hv + sv[u];
+            *(f32x4 *)at(c0 + u) = hv;
+            hv = l[u] * hv + v[u];
+        }
+    };
+    auto tail = [&](int c0, const f32x4(&v)[U], const float(&l)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (c0 + u < nc) {
+                *(f32x4 *)at(c0 + u) = hv;
+                hv = l[u] * hv + v[u];
             }
         }
+    };
+    // two register batches used in turn (a copy from one to the other would
+    // wait for the batch in flight)
+    load(0, sa, la);
+    for (int c0 = 0;;) {
+        if (c0 + U > nc) {
+            tail(c0, sa, la);
+            break;
+        }
+        load(c0 + U, sb, lb);
+        step(c0, sa, la);
+        c0 += U;
+        if (c0 + U > nc) {
+            tail(c0, sb, lb);
+            break;
+        }
+        load(c0 + U, sa, la);
+        step(c0, sb, lb);
+        c0 += U;
     }
     if (fin) *(f32x4 *)(fin + bh * PN + e0) = hv;
 }

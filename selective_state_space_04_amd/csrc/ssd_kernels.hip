@@ -947,10 +947,11 @@ __global__ __launch_bounds__(256) void k_chunk_state_f32(const float *__restrict
 // each tile's C B^T row pieces load in one round (buffer loads, the blocks
 // past the diagonal switched off) before its intra product.  Every tile is
 // computed, a tile past q on clamped rows; its stores fall outside the
-// buffer resource over y and are dropped.  The caller keeps the byte span
+// buffer resource over y and are dropped.  The next tile's C B^T pieces load
+// while a tile computes.  The caller keeps the byte span
 // of a chunk's y rows below 2^31.
 template <int P, int N>
-__global__ __launch_bounds__(256) void k_chunk_scan_f32(const float *__restrict__ x,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_chunk_scan_f32(const float *__restrict__ x,
                                                         const float *__restrict__ C,
                                                         const float *__restrict__ cb,
                                                         const float *__restrict__ cs,
@@ -1012,9 +1013,22 @@ __global__ __launch_bounds__(256) void k_chunk_scan_f32(const float *__restrict_
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) acc[t][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // C B^T row pieces of tile t's blocks 0..I (the rest read as zero), in two
+    // register sets used in turn: tile t + 1's load while tile t computes
+    const auto rsG = buf_rsrc(cbc, (uint32_t)Q * (uint32_t)Q * 4u);
+    f32x4 gA[16], gB[16];
+    auto load_g = [&](int t, f32x4(&g4)[16]) {
+        const int I = tI[t], ilc = min(I * 16 + r, q - 1);
+#pragma unroll
+        for (int jb = 0; jb < 16; ++jb)
+            g4[jb] = __builtin_bit_cast(
+                f32x4, buf_ld16(rsG, jb <= I && jb * 16 < Q ? (uint32_t)(ilc * Q + jb * 16 + 4 * grp) * 4u : kBufOff));
+    };
+    load_g(0, gA);
+
     // state term exp(cs_i) C_i h_{c-1}: A = h rows, B = C rows
     if (hp) {
-#pragma unroll 2
+#pragma unroll 1
         for (int k0 = 0; k0 < N; k0 += 16) {
             const int kk = k0 + 4 * grp;
             f32x4 h4[PT], c4[4];
@@ -1037,20 +1051,14 @@ __global__ __launch_bounds__(256) void k_chunk_scan_f32(const float *__restrict_
         }
     }
 
-    const auto rsG = buf_rsrc(cbc, (uint32_t)Q * (uint32_t)Q * 4u);
     const auto rsY = buf_rsrc(y + row0 * P, (uint32_t)(((int64_t)(q - 1) * HP + P) * 4));
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+        f32x4(&g4)[16] = (t & 1) ? gB : gA;
+        if (t + 1 < 4) load_g(t + 1, (t & 1) ? gA : gB);  // the next tile's, in flight meanwhile
         const int I = tI[t];
         const int il = I * 16 + r;  // this lane's output row inside the chunk
-        const int ilc = min(il, q - 1);
         const float csi = cs_s[il];
-        // C B^T row pieces of blocks 0..I (the rest read as zero)
-        f32x4 g4[16];
-#pragma unroll
-        for (int jb = 0; jb < 16; ++jb)
-            g4[jb] = __builtin_bit_cast(
-                f32x4, buf_ld16(rsG, jb <= I && jb * 16 < Q ? (uint32_t)(ilc * Q + jb * 16 + 4 * grp) * 4u : kBufOff));
 #pragma unroll
         for (int jb = 0; jb < 16; ++jb) {
             if (jb <= I) {

@@ -1026,22 +1026,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
     load_g(0, gA);
 
-    // state term exp(cs_i) C_i h_{c-1}: A = h rows, B = C rows
+    // state term exp(cs_i) C_i h_{c-1}: A = h rows, B = C rows; the pieces of
+    // step k + 1 load while step k multiplies (two register sets)
     if (hp) {
-#pragma unroll 1
-        for (int k0 = 0; k0 < N; k0 += 16) {
-            const int kk = k0 + 4 * grp;
-            f32x4 h4[PT], c4[4];
+        constexpr int NK = N / 16;
+        f32x4 h4[2][PT], c4[2][4];
+        auto load_hc = [&](int k, f32x4(&hv)[PT], f32x4(&cv)[4]) {
+            const int kk = k * 16 + 4 * grp;
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) h4[pt] = *(const f32x4 *)(hp + (int64_t)(pt * 16 + r) * N + kk);
+            for (int pt = 0; pt < PT; ++pt) hv[pt] = *(const f32x4 *)(hp + (int64_t)(pt * 16 + r) * N + kk);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) c4[t] = *(const f32x4 *)(Cb + min(tI[t] * 16 + r, q - 1) * GN + kk);
+            for (int t = 0; t < 4; ++t) cv[t] = *(const f32x4 *)(Cb + min(tI[t] * 16 + r, q - 1) * GN + kk);
+        };
+        load_hc(0, h4[0], c4[0]);
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+            if (k + 1 < NK) load_hc(k + 1, h4[(k + 1) & 1], c4[(k + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);  // the prefetch stays ahead of the MFMAs
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[t][pt] = mfma_f32(h4[pt][e], c4[t][e], acc[t][pt]);
+                    for (int e = 0; e < 4; ++e)
+                        acc[t][pt] = mfma_f32(h4[k & 1][pt][e], c4[k & 1][t][e], acc[t][pt]);
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -1056,6 +1064,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int t = 0; t < 4; ++t) {
         f32x4(&g4)[16] = (t & 1) ? gB : gA;
         if (t + 1 < 4) load_g(t + 1, (t & 1) ? gA : gB);  // the next tile's, in flight meanwhile
+        __builtin_amdgcn_sched_barrier(0);
         const int I = tI[t];
         const int il = I * 16 + r;  // this lane's output row inside the chunk
         const float csi = cs_s[il];

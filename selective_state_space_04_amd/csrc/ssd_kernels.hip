@@ -918,7 +918,9 @@ __global__ __launch_bounds__(256) void k_chunk_state_f32(const float *__restrict
 #pragma unroll
                 for (int t = 0; t < NTW; ++t) {
                     const int nt = wave + 4 * t;
-                    if (nt < NT) {
+                    // (no branch when every wave has NTW tiles: the LDS reads then
+                    // run ahead of the MFMAs instead of waiting in each branch)
+                    if (NT % 4 == 0 || nt < NT) {
                         const float bv = bs[jr * BLD + nt * 16 + r];
 #pragma unroll
                         for (int pt = 0; pt < PT; ++pt) acc[t][pt] = mfma_f32(bv, xa[pt], acc[t][pt]);

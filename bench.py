@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+F32_PEAK_TFLOPS = 157.3
 METRIC = "SSD fwd tokens/s at H=80,P=64,N=128,L=4096; % of MFMA/HBM roofline"
 
 
@@ -42,6 +43,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=["forward", "backward", "decode", "gated_norm", "scan", "copy"],
                     default="forward")
+    ap.add_argument("--shape", choices=["2.7B-layer", "long-fp32"], default="2.7B-layer",
+                    help="forward: the workload (long-fp32: batch 1, L 65536, H 32, P 64, N 128, "
+                         "float32, carried state; a parity workload, timed on request)")
     ap.add_argument("--ngroups", type=int, default=0,
                     help="forward: B/C groups (0 = the workload's own, 1)")
     ap.add_argument("--path", choices=["fused", "staged"], default="fused")
@@ -64,6 +68,14 @@ def forward_bytes(w) -> int:
     n = 2 * b * L * H * P * e + b * L * H * e + 2 * b * L * G * N * e + 2 * H * 4
     n += b * H * P * N * 4 * (2 if w.init_mode == "normal" else 1)
     return n
+
+
+def chunk_scan_flops(w) -> int:
+    """Algorithmic flops of the output step: the masked intra-chunk product
+    over lower-triangular pairs and the state term C h."""
+    b, L, H, P, N, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.chunk
+    tri = sum(min(Q, L - c * Q) * (min(Q, L - c * Q) + 1) // 2 for c in range((L + Q - 1) // Q))
+    return b * H * 2 * (P * tri + L * N * P)
 
 
 def forward_flops(w) -> int:
@@ -310,7 +322,8 @@ def run_forward_bench(args):
     import selective_state_space_04_amd as ssd
     import ssd_inputs as si
 
-    w = si.WORKLOADS[2]
+    long32 = args.shape == "long-fp32"
+    w = si.WORKLOADS[3 if long32 else 2]
     if args.ngroups:
         w = w.with_(ngroups=args.ngroups)
     dev = torch.device("cuda:0")
@@ -358,17 +371,24 @@ def run_forward_bench(args):
     ms_per_step = statistics.mean(ms)
     tokens = w.batch * w.seqlen
     value = tokens / (ms_per_step * 1e-3)
-    t_roof_us = max(forward_bytes(w) / (HBM_PEAK_GBS * 1e3), forward_flops(w) / (BF16_PEAK_TFLOPS * 1e6))
+    t_hbm = forward_bytes(w) / (HBM_PEAK_GBS * 1e3)
+    t_mfma = forward_flops(w) / ((F32_PEAK_TFLOPS if long32 else BF16_PEAK_TFLOPS) * 1e6)
+    t_roof_us = max(t_hbm, t_mfma)
 
     result = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": ("SSD fwd tokens/s at H=32,P=64,N=128,L=65536 fp32, carried state; % of fp32-MFMA roofline"
+                   if long32 else METRIC),
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded; distributions of the workload)",
-        "config": {"workload": "2.7B-layer-shaped SSD forward", "batch": w.batch, "seqlen": w.seqlen,
+        "vs_baseline": None, "dtype": "f32" if long32 else "bf16",
+        "data": "synthetic (seeded; distributions of the workload)",
+        "config": {"workload": ("long-sequence SSD forward with carried state" if long32
+                                else "2.7B-layer-shaped SSD forward"), "batch": w.batch, "seqlen": w.seqlen,
                    "nheads": w.nheads, "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
-                   "chunk": w.chunk, "inputs": "bf16", "accumulate": "fp32", "path": args.path,
+                   "chunk": w.chunk, "inputs": w.dtype, "accumulate": "fp32", "path": args.path,
                    "dt_options": args.options, "mall_flushed": flush is not None},
-        "forward_roofline": {"bound": "hbm", "t_roof_us": t_roof_us, "frac": t_roof_us / (ms_per_step * 1e3),
+        "forward_roofline": {"bound": "mfma" if t_mfma > t_hbm else "hbm", "t_roof_us": t_roof_us,
+                             "frac": t_roof_us / (ms_per_step * 1e3),
                              "alg_bytes": forward_bytes(w), "alg_flops": forward_flops(w)},
         "ms_min": min(ms), "ms_median": statistics.median(ms), "wall_s": wall,
     }
@@ -441,6 +461,14 @@ def kernel_roofline(ssd, w, x, dt, A, B, C, D, init, ws, y, fin, flush, args):
                 times[n].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)
     avg = {n: statistics.mean(v) for n, v in times.items()}
     dom = max(avg, key=avg.get)
+    if w.dtype == "f32" and dom == "chunk_scan":
+        # float32: the output kernel is bound by the fp32 MFMA rate
+        fl = chunk_scan_flops(w)
+        achieved = fl / (avg[dom] * 1e-6) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": F32_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / F32_PEAK_TFLOPS, "traffic": None,
+                "alg_flops_per_launch": fl, "avg_launch_us": avg[dom]}
+        return roof, avg
     kb = kernel_bytes(w)[dom]
     achieved = kb / (avg[dom] * 1e-6) / 1e9
     roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

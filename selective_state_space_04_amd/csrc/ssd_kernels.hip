@@ -1129,34 +1129,42 @@ __global__ __launch_bounds__(256) void k_decode(float *__restrict__ state, const
     float *st = state + bh * (int64_t)P * N;
     const T *xp = x + bh * P;
     T *yp = y + bh * P;
+    // Loads are unconditional (rows past P clamped to row P - 1) and stores go
+    // through buffer resources whose switched-off lanes point past the end, so
+    // no branch makes the compiler wait for each load, or each store, in turn.
+    // The state streams through once per step: non-temporal accesses.
+    const auto rsS = buf_rsrc(st, (uint32_t)P * N * 4u);
+    const auto rsY = buf_rsrc(yp, (uint32_t)P * (uint32_t)sizeof(T));
     for (int p0 = 0; p0 < P; p0 += RPI * U) {
         f32x4 hv[U];
-        float xv[U];
+        T xr[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int p = p0 + u * RPI + slot;
-            if (p < P) {
-                // the state streams through once per step: non-temporal
-                hv[u] = __builtin_nontemporal_load((const f32x4 *)(st + (int64_t)p * N + nl * 4));
-                xv[u] = to_f32(xp[p]);
-            }
+            const int pc = min(p0 + u * RPI + slot, P - 1);
+            hv[u] = __builtin_nontemporal_load((const f32x4 *)(st + (int64_t)pc * N + nl * 4));
+            xr[u] = xp[pc];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int p = p0 + u * RPI + slot;
+            const float xv = to_f32(xr[u]);
             float part = 0.f;
-            if (p < P) {
-                f32x4 nh;
+            f32x4 nh;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    nh[e] = a * hv[u][e] + (xsc * xv[u]) * bv[e];
-                    part += nh[e] * cv[e];
-                }
-                __builtin_nontemporal_store(nh, (f32x4 *)(st + (int64_t)p * N + nl * 4));
+            for (int e = 0; e < 4; ++e) {
+                nh[e] = a * hv[u][e] + (xsc * xv) * bv[e];
+                part += nh[e] * cv[e];
             }
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, nh), rsS,
+                                                   p < P ? (p * N + nl * 4) * 4 : (int)kBufOff, 0, 2);
 #pragma unroll
             for (int off = NL / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-            if (nl == 0 && p < P) yp[p] = from_f32<T>(part + Dh * xv[u]);
+            const int yo = (nl == 0 && p < P) ? p * (int)sizeof(T) : (int)kBufOff;
+            const T yv = from_f32<T>(part + Dh * xv);
+            if constexpr (sizeof(T) == 2)
+                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, yv), rsY, yo, 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, yv), rsY, yo, 0, 0);
         }
     }
 }

@@ -722,12 +722,32 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const T *__restrict__ x, con
         for (int pt = 0; pt < PT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         const T *crow = Cb + (int64_t)il * G * N;
+        // bf16: this tile's C row pieces and C B^T row pieces load in one round,
+        // unconditionally (rows past q clamped, values then zeroed), so no
+        // branch makes each wait for the one before
+        constexpr int NKC = (N + 31) / 32;
+        u32x4 cpc[NKC], gpc[8];
+        if constexpr (sizeof(T) == 2) {
+            const T *crc = Cb + (int64_t)min(il, q - 1) * G * N;
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+                const int kk = kc * 32 + grp * 8;
+                cpc[kc] = *(const u32x4 *)(crc + (kk < N ? kk : 0));
+            }
+            // il < Q: a row of this chunk's tiles; pieces past the row are
+            // clamped to its last 8 columns (only pieces with jl <= il are used,
+            // and those lie at or before Q - 8)
+            const T *grw = cbc + (int64_t)il * Q;
+#pragma unroll
+            for (int J = 0; J < 8; ++J) gpc[J] = *(const u32x4 *)(grw + min(32 * J + grp * 8, Q - 8));
+        }
         if (hp) {
             if constexpr (sizeof(T) == 2) {
-                for (int k0 = 0; k0 < N; k0 += 32) {
-                    const int kk = k0 + grp * 8;
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc) {
+                    const int kk = kc * 32 + grp * 8;
                     const u32x4 z = {0u, 0u, 0u, 0u};
-                    const bf16x8 bcv = as_bf16x8((vi && kk < N) ? *(const u32x4 *)(crow + kk) : z);
+                    const bf16x8 bcv = as_bf16x8((vi && kk < N) ? cpc[kc] : z);
 #pragma unroll
                     for (int pt = 0; pt < PT; ++pt) {
                         const bf16x8 ah =
@@ -756,11 +776,14 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const T *__restrict__ x, con
         const T *grow = cbc + (int64_t)il * Q;
         const int jend = I * 16 + 15;
         if constexpr (sizeof(T) == 2) {
-            for (int j0 = 0; j0 <= jend; j0 += 32) {
+#pragma unroll
+            for (int J = 0; J < 8; ++J) {
+                const int j0 = 32 * J;
+                if (j0 > jend) break;
                 const int jl = j0 + grp * 8;
                 bf16x8 bm;
                 if (jl <= il) {
-                    const bf16x8 gv = as_bf16x8(*(const u32x4 *)(grow + jl));
+                    const bf16x8 gv = as_bf16x8(gpc[J]);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int j = jl + e;

@@ -209,17 +209,31 @@ hipError_t launch_gated_rmsnorm(const Dims &d, int64_t ngroups, float eps, const
                                 const void *z, const float *w, void *out, hipStream_t st) {
     const int64_t rows = d.b * d.L, D = d.H * d.P;
     if (rows == 0 || D == 0) return hipSuccess;
-    constexpr int kMaxP = 4;  // 8-channel pieces per thread
-    if (ngroups <= 8 && D <= 256 * 8 * kMaxP) {
+    // 8-channel pieces per thread: 4, 5 or 8, whichever leaves the fewest lanes
+    // idle in one to four waves (5 at 5120 channels: 128 threads, none idle)
+    if (ngroups <= 8 && D <= 256 * 8 * 8) {
         const int Di = (int)D, Dg = (int)(D / ngroups), ng = (int)ngroups;
-        const int64_t per = (D / 8 + kMaxP - 1) / kMaxP;  // threads needed
-        const unsigned nthr = (unsigned)((per + 63) / 64 * 64);
-        if (d.dtype == 1)
-            k_gated_rmsnorm_reg<bf16, kMaxP><<<(unsigned)rows, nthr, 0, st>>>(
-                (const bf16 *)y, (const bf16 *)z, w, (bf16 *)out, Di, Dg, ng, eps);
-        else
-            k_gated_rmsnorm_reg<float, kMaxP><<<(unsigned)rows, nthr, 0, st>>>(
-                (const float *)y, (const float *)z, w, (float *)out, Di, Dg, ng, eps);
+        const int64_t npc = D / 8;
+        int best = 0;
+        int64_t best_idle = INT64_MAX;
+        for (int m : {4, 5, 8}) {
+            const int64_t nthr = ((npc + m - 1) / m + 63) / 64 * 64;
+            if (nthr > 256) continue;
+            const int64_t idle = nthr * m - npc;
+            if (idle < best_idle) best_idle = idle, best = m;
+        }
+        const unsigned nthr = (unsigned)(((npc + best - 1) / best + 63) / 64 * 64);
+#define SSD_GN_LAUNCH(M)                                                                               \
+    if (d.dtype == 1)                                                                                  \
+        k_gated_rmsnorm_reg<bf16, M><<<(unsigned)rows, nthr, 0, st>>>((const bf16 *)y, (const bf16 *)z, \
+                                                                    w, (bf16 *)out, Di, Dg, ng, eps);  \
+    else                                                                                               \
+        k_gated_rmsnorm_reg<float, M><<<(unsigned)rows, nthr, 0, st>>>(                              \
+            (const float *)y, (const float *)z, w, (float *)out, Di, Dg, ng, eps);
+        if (best == 4) { SSD_GN_LAUNCH(4) }
+        else if (best == 5) { SSD_GN_LAUNCH(5) }
+        else { SSD_GN_LAUNCH(8) }
+#undef SSD_GN_LAUNCH
         return hipGetLastError();
     }
     if (d.dtype == 1)

@@ -707,6 +707,24 @@ def test_gated_rmsnorm(ssd, dtype, groups):
     assert worst_rel(f64(o1)[:, None], ref[:, 5:6], "y") < TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("H,P", [(8, 64), (80, 64), (12, 16), (96, 128), (160, 128)])
+def test_gated_rmsnorm_widths(ssd, dtype, H, P):
+    """Row widths that pick each pieces-per-thread count of the one-pass
+    kernel (512: 4, 5120: 5, 192: 4 with one wave, 12288: 8) and the
+    two-pass kernel past 16384 channels (20480), with 1 and 8 groups."""
+    g = torch.Generator().manual_seed(H * 1000 + P)
+    dt_ = si.DTYPES[dtype]
+    y = torch.randn((2, 3, H, P), generator=g).to(dt_)
+    z = torch.randn((2, 3, H, P), generator=g).to(dt_)
+    wt = torch.randn(H * P, generator=g)
+    for groups in (1, 8):
+        out = ssd.gated_rmsnorm(dev(y), dev(z), dev(wt), norm_groups=groups, eps=1e-5)
+        torch.cuda.synchronize()
+        ref = oracle.gated_rmsnorm(y, z, wt, norm_groups=groups, eps=1e-5)
+        assert worst_rel(f64(out), ref, "y") < TOL[dtype]
+
+
 def test_gated_rmsnorm_2p7b_layer_rows(ssd):
     """The 2.7B-layer output shape ([4, 4096, 80, 64] bf16, H * P = 5120)."""
     g = torch.Generator().manual_seed(32)

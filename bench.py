@@ -422,7 +422,7 @@ def kernel_roofline(ssd, w, x, dt, A, B, C, D, init, ws, y, fin, flush, args):
     single = args.path == "fused" and ssd.lib.ssd_forward_is_single_pass(dp)
     if single:
         seq = [
-            ("forward_prep", lambda: ssd.lib.ssd_forward_prep(dp, p(B), p(C), p(ws), nbytes, stream)),
+            ("forward_prep", lambda: ssd.lib.ssd_forward_prep(dp, p(dt), p(A), p(B), p(C), p(ws), nbytes, stream)),
             ("forward_main", lambda: ssd.lib.ssd_forward_main(dp, p(x), p(dt), p(A), p(B), p(C), p(D), p(init),
                                                              p(y), p(fin), p(ws), nbytes, stream)),
         ]

@@ -118,24 +118,29 @@ ssd_status ssd_forward_staged(const ssd_dims *dims, const void *x, const void *d
 
 /*
  * The single-pass arrangement ssd_forward uses for bfloat16 inputs with
- * headdim 64, dstate 128 and chunk <= 256 (other shapes use the staged
- * one).  One workgroup per (batch, chunk, head) stages its chunk of x once,
- * computes the chunk state and the intra-chunk product, receives the state
- * entering its chunk from the workgroup of the previous chunk through a
- * two-slot ring in the workspace, hands its own end state on, and writes y:
- * x is read and y written once (review page, section "2つのルートを半分ずつ":
- * only the end-of-block state passes between blocks).  ssd_forward is exactly
- * ssd_forward_prep followed by ssd_forward_main on the same stream and
- * workspace; they are exposed so each launch can be timed on its own.
- *   ssd_forward_prep: C B^T tiles and B^T of every chunk into the workspace,
- *                     hand-off flags cleared.
+ * headdim 64 and dstate 128 (any chunk; other shapes use the staged one).
+ * One workgroup per (batch, head) walks the whole sequence in 32-step chunks
+ * and keeps the state in its registers: inside each chunk the masked
+ * attention form, across chunks the recurrence on the carried state (review
+ * page, section "2つのルートを半分ずつ": only the end-of-block state passes
+ * from block to block).  x is read and y written once, and no state goes
+ * through memory.  The chunked algorithm gives the same result for every
+ * chunk length (up to rounding), so this route ignores `chunk`.
+ * ssd_forward is exactly ssd_forward_prep followed by ssd_forward_main on
+ * the same stream and workspace; they are exposed so each launch can be
+ * timed on its own.
+ *   ssd_forward_prep: for every 32-step chunk, the C, B^T and causal C B^T
+ *                     operand tiles of each group and the decay prefix of
+ *                     each head (from dt and A) into the workspace.
  *   ssd_forward_main: everything else.  Must follow ssd_forward_prep on the
- *                     same workspace, with no other use of it in between.
+ *                     same workspace and the same dt, A, B, C, with no other
+ *                     use of the workspace in between; its dt, A, B, C
+ *                     arguments are validated but not read.
  * Both return SSD_ERR_UNSUPPORTED for shapes outside the single-pass set.
  * ssd_forward_is_single_pass tells whether ssd_forward takes this route. */
 int ssd_forward_is_single_pass(const ssd_dims *dims);
-ssd_status ssd_forward_prep(const ssd_dims *dims, const void *B, const void *C, void *workspace,
-                            size_t workspace_bytes, void *stream);
+ssd_status ssd_forward_prep(const ssd_dims *dims, const void *dt, const float *A, const void *B,
+                            const void *C, void *workspace, size_t workspace_bytes, void *stream);
 ssd_status ssd_forward_main(const ssd_dims *dims, const void *x, const void *dt, const float *A,
                             const void *B, const void *C, const float *D, const float *init_state,
                             void *y, float *final_state, void *workspace, size_t workspace_bytes,

@@ -56,7 +56,7 @@ _SIGS = {
     "ssd_forward_staged": (ctypes.c_int, [_dp] + [_vp] * 10 + [ctypes.c_size_t, _vp]),
     "ssd_decode_step": (ctypes.c_int, [_dp] + [_vp] * 9),
     "ssd_forward_is_single_pass": (ctypes.c_int, [_dp]),
-    "ssd_forward_prep": (ctypes.c_int, [_dp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "ssd_forward_prep": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "ssd_forward_main": (ctypes.c_int, [_dp] + [_vp] * 10 + [ctypes.c_size_t, _vp]),
     "ssd_chunk_cumsum": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp]),
     "ssd_chunk_cb": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp]),

@@ -17,15 +17,21 @@ OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libssd_mi355x.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["ssd_kernels.hip", "ssd_fused.hip", "ssd_backward.hip", "ssd_epilogue.hip", "ssd_scan.hip", "ssd_api.cpp"]
+SOURCES = ["ssd_kernels.hip", "ssd_walk.hip", "ssd_backward.hip", "ssd_epilogue.hip", "ssd_scan.hip", "ssd_api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-x", "hip",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# Per-file flags.  The walk keeps its state in MFMA accumulators that the
+# vector ALU also reads every chunk; the VGPR form of the MFMAs avoids copying
+# them between accumulation and vector registers.
+EXTRA = {"ssd_walk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

@@ -111,28 +111,25 @@ WsLayout ws_layout(const ssd::Dims &d) {
     return w;
 }
 
-// Workspace of the single-pass arrangement: fragment-ordered C B^T, B^T and
-// C of every chunk | state ring (2 slots) | hand-off flags.
-struct FusedLayout {
-    int64_t Gf = 0, Btf = 0, Cf = 0, ring = 0, flags = 0, total = 0;
+// Workspace of the single-pass arrangement: fragment-ordered operands of
+// every 32-step chunk and group | decay record of every chunk and head.
+struct WalkLayout {
+    int64_t ops = 0, rec = 0, total = 0;
 };
 
-FusedLayout fused_layout(const ssd::Dims &d) {
-    FusedLayout f;
-    const int64_t nbcg = d.b * d.nc * d.G, T16 = d.Q / 16, NJ = (d.Q + 31) / 32;
-    f.Gf = 0;
-    f.Btf = align256(f.Gf + nbcg * T16 * NJ * 1024);
-    f.Cf = align256(f.Btf + nbcg * d.N * NJ * 64);
-    f.ring = align256(f.Cf + nbcg * T16 * (d.N / 32) * 1024);
-    f.flags = align256(f.ring + 2 * d.b * d.H * d.P * d.N * 4);
-    f.total = align256(f.flags + d.b * d.H * 4 * 4);  // one flag per (b, h, wave)
-    if (d.b == 0 || d.nc == 0) f.total = 0;
-    return f;
+WalkLayout walk_layout(const ssd::Dims &d) {
+    WalkLayout w;
+    const ssd::WalkBytes wb = ssd::walk_bytes(d);
+    w.ops = 0;
+    w.rec = align256(wb.ops);
+    w.total = align256(w.rec + wb.rec);
+    if (d.b == 0 || d.L == 0) w.total = 0;
+    return w;
 }
 
 int64_t ws_total(const ssd::Dims &d) {
     int64_t t = ws_layout(d).total;
-    if (ssd::fused_supported(d)) t = std::max(t, fused_layout(d).total);
+    if (ssd::walk_supported(d)) t = std::max(t, walk_layout(d).total);
     return t;
 }
 
@@ -488,22 +485,19 @@ ssd_status run_backward(const ssd::Dims &d, const void *x, const void *dt, const
     return SSD_OK;
 }
 
-ssd_status run_fused_prep(const ssd::Dims &d, const void *B, const void *C, void *ws,
-                          hipStream_t st) {
-    const FusedLayout f = fused_layout(d);
+ssd_status run_walk_prep(const ssd::Dims &d, const void *dt, const float *A, const void *B, const void *C,
+                         void *ws, hipStream_t st, const ssd::DtOpts *o = nullptr) {
+    const WalkLayout w = walk_layout(d);
     char *base = (char *)ws;
-    return hip_status(ssd::launch_fused_prep(d, B, C, base + f.Gf, base + f.Btf, base + f.Cf,
-                                             (int *)(base + f.flags), st));
+    return hip_status(ssd::launch_walk_prep(d, dt, A, B, C, base + w.ops, (float *)(base + w.rec), st, o));
 }
 
-ssd_status run_fused_main(const ssd::Dims &d, const void *x, const void *dt, const float *A,
-                          const void *C, const float *D, const float *init, void *y, float *fin,
-                          void *ws, hipStream_t st, const ssd::DtOpts *o = nullptr) {
-    const FusedLayout f = fused_layout(d);
+ssd_status run_walk_main(const ssd::Dims &d, const void *x, const float *D, const float *init, void *y,
+                         float *fin, void *ws, hipStream_t st, bool opts = false) {
+    const WalkLayout w = walk_layout(d);
     char *base = (char *)ws;
-    return hip_status(ssd::launch_fused_main(d, x, dt, A, base + f.Btf, base + f.Cf, base + f.Gf, D,
-                                             init, y, fin, (float *)(base + f.ring),
-                                             (int *)(base + f.flags), st, o));
+    return hip_status(ssd::launch_walk_main(d, x, base + w.ops, (const float *)(base + w.rec), D, init, y, fin,
+                                            st, opts));
 }
 
 }  // namespace
@@ -584,9 +578,9 @@ static ssd_status forward_any(const ssd_dims *dims, const ssd_dt_options *opts, 
         o = &dev;
     }
     hipStream_t s = (hipStream_t)stream;
-    if (!staged_only && d.b > 0 && d.nc > 0 && ssd::fused_supported(d)) {
-        if ((st = run_fused_prep(d, B, C, workspace, s)) != SSD_OK) return st;
-        return run_fused_main(d, x, dt, A, C, D, init_state, y, final_state, workspace, s, o);
+    if (!staged_only && d.b > 0 && d.L > 0 && ssd::walk_supported(d)) {
+        if ((st = run_walk_prep(d, dt, A, B, C, workspace, s, o)) != SSD_OK) return st;
+        return run_walk_main(d, x, D, init_state, y, final_state, workspace, s, o != nullptr);
     }
     return run_staged(d, x, dt, A, B, C, D, init_state, y, final_state, workspace, s, o);
 }
@@ -636,21 +630,20 @@ ssd_status ssd_validate_forward_ex(const ssd_dims *dims, const ssd_dt_options *o
 int ssd_forward_is_single_pass(const ssd_dims *dims) {
     ssd::Dims d;
     if (check_dims(dims, false, &d) != SSD_OK) return 0;
-    return (d.b > 0 && d.nc > 0 && ssd::fused_supported(d)) ? 1 : 0;
+    return (d.b > 0 && d.L > 0 && ssd::walk_supported(d)) ? 1 : 0;
 }
 
-ssd_status ssd_forward_prep(const ssd_dims *dims, const void *B, const void *C, void *workspace,
-                            size_t workspace_bytes, void *stream) {
+ssd_status ssd_forward_prep(const ssd_dims *dims, const void *dt, const float *A, const void *B, const void *C,
+                            void *workspace, size_t workspace_bytes, void *stream) {
     ssd::Dims d;
     ssd_status st = check_dims(dims, false, &d);
     if (st != SSD_OK) return st;
-    if (!ssd::fused_supported(d)) return SSD_ERR_UNSUPPORTED;
-    if (d.b == 0 || d.nc == 0) return SSD_OK;
-    const void *req[] = {B, C, workspace};
-    if ((st = validate_ptrs(req, 3, nullptr, 0)) != SSD_OK) return st;
+    if (!ssd::walk_supported(d)) return SSD_ERR_UNSUPPORTED;
+    const void *req[] = {dt, A, B, C, workspace};
+    if ((st = validate_ptrs(req, 5, nullptr, 0)) != SSD_OK) return st;
     if (!aligned(workspace, 256)) return SSD_ERR_ALIGN;
     if ((int64_t)workspace_bytes < ws_total(d)) return SSD_ERR_WORKSPACE;
-    return run_fused_prep(d, B, C, workspace, (hipStream_t)stream);
+    return run_walk_prep(d, dt, A, B, C, workspace, (hipStream_t)stream);
 }
 
 ssd_status ssd_forward_main(const ssd_dims *dims, const void *x, const void *dt, const float *A,
@@ -661,10 +654,8 @@ ssd_status ssd_forward_main(const ssd_dims *dims, const void *x, const void *dt,
     ssd_status st = validate_forward(dims, x, dt, A, B, C, D, init_state, y, final_state,
                                      workspace, workspace_bytes, &d);
     if (st != SSD_OK) return st;
-    if (!ssd::fused_supported(d)) return SSD_ERR_UNSUPPORTED;
-    if (d.b == 0 || d.nc == 0) return SSD_OK;
-    return run_fused_main(d, x, dt, A, C, D, init_state, y, final_state, workspace,
-                          (hipStream_t)stream);
+    if (!ssd::walk_supported(d)) return SSD_ERR_UNSUPPORTED;
+    return run_walk_main(d, x, D, init_state, y, final_state, workspace, (hipStream_t)stream);
 }
 
 ssd_status ssd_gated_rmsnorm(const ssd_dims *dims, int64_t norm_groups, float eps, const void *y,

@@ -33,13 +33,19 @@ hipError_t launch_chunk_scan(const Dims &d, const void *x, const void *C, const 
 hipError_t launch_decode(const Dims &d, float *state, const void *x, const void *dt,
                          const float *A, const void *B, const void *C, const float *D, void *y,
                          hipStream_t st, const DtOpts *o = nullptr);
-bool fused_supported(const Dims &d);
-hipError_t launch_fused_prep(const Dims &d, const void *B, const void *C, void *Gf, void *Btf,
-                             void *Cf, int *flags, hipStream_t st);
-hipError_t launch_fused_main(const Dims &d, const void *x, const void *dt, const float *A,
-                             const void *Btf, const void *Cf, const void *Gf, const float *D,
-                             const float *init, void *y, float *fin, float *ring, int *flags,
-                             hipStream_t st, const DtOpts *o = nullptr);
+// Single-pass forward (ssd_walk.hip): bfloat16, P = 64, N = 128.  The
+// preparation writes every 32-step chunk's operands (per group) and decay
+// records (per head) into the workspace; the walk reads them.
+bool walk_supported(const Dims &d);
+struct WalkBytes {
+    int64_t ops;  // fragment-ordered C, B^T and causal C B^T of every chunk and group
+    int64_t rec;  // decay record of every chunk and head
+};
+WalkBytes walk_bytes(const Dims &d);
+hipError_t launch_walk_prep(const Dims &d, const void *dt, const float *A, const void *B, const void *C,
+                            void *ops, float *rec, hipStream_t st, const DtOpts *o = nullptr);
+hipError_t launch_walk_main(const Dims &d, const void *x, const void *ops, const float *rec, const float *D,
+                            const float *init, void *y, float *fin, hipStream_t st, bool opts);
 hipError_t launch_zero_state(const Dims &d, const float *init, float *fin, hipStream_t st);
 
 // Selective (Mamba-1) scan (ssd_scan.hip).  algo 1 = segments (seg steps per

@@ -377,7 +377,8 @@ def test_single_pass_launches_compose(ssd):
     ws = torch.empty(ssd.workspace_bytes(d), dtype=torch.uint8, device=DEV)
     y2, f2 = torch.empty_like(y1), torch.empty_like(f1)
     p, s = ssd._p, ssd._stream()
-    assert ssd.lib.ssd_forward_prep(ctypes.byref(d), p(t["B"]), p(t["C"]), p(ws), ws.numel(), s) == 0
+    assert ssd.lib.ssd_forward_prep(ctypes.byref(d), p(t["dt"]), p(t["A"]), p(t["B"]), p(t["C"]), p(ws),
+                                    ws.numel(), s) == 0
     assert ssd.lib.ssd_forward_main(ctypes.byref(d), p(t["x"]), p(t["dt"]), p(t["A"]), p(t["B"]), p(t["C"]),
                                     p(t["D"]), p(t["init"]), p(y2), p(f2), p(ws), ws.numel(), s) == 0
     torch.cuda.synchronize()

@@ -34,6 +34,13 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 F32_PEAK_TFLOPS = 157.3
 METRIC = "SSD fwd tokens/s at H=80,P=64,N=128,L=4096; % of MFMA/HBM roofline"
+# forward workloads: --shape -> index into ssd_inputs.WORKLOADS, description
+FORWARD_SHAPES = {
+    "tiny": (0, "tiny SSD forward (float32)"),
+    "370M-layer": (1, "370M-layer-shaped SSD forward"),
+    "2.7B-layer": (2, "2.7B-layer-shaped SSD forward"),
+    "long-fp32": (3, "long-sequence SSD forward with carried state"),
+}
 
 
 def parse():
@@ -43,9 +50,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=["forward", "backward", "decode", "gated_norm", "scan", "copy"],
                     default="forward")
-    ap.add_argument("--shape", choices=["2.7B-layer", "long-fp32"], default="2.7B-layer",
-                    help="forward: the workload (long-fp32: batch 1, L 65536, H 32, P 64, N 128, "
-                         "float32, carried state; a parity workload, timed on request)")
+    ap.add_argument("--shape", choices=list(FORWARD_SHAPES), default="2.7B-layer",
+                    help="forward: the workload (tiny: batch 1, L 256, H 4, P 16, N 16, float32; "
+                         "370M-layer: batch 8, L 2048, H 32; 2.7B-layer: batch 4, L 4096, H 80; "
+                         "long-fp32: batch 1, L 65536, H 32, float32, carried state)")
     ap.add_argument("--ngroups", type=int, default=0,
                     help="forward: B/C groups (0 = the workload's own, 1)")
     ap.add_argument("--path", choices=["fused", "staged"], default="fused")
@@ -107,12 +115,12 @@ def kernel_bytes(w) -> dict:
     init_b = st if w.init_mode == "normal" else 0
     Bt = b * nc * G * N * ((Q + 31) // 32 * 32) * e
     return {
-        # single-pass arrangement: prep reads B, C and writes the lower C B^T
-        # tiles and B^T; main reads x, dt, C, the tiles, B^T, A, D (+ init)
-        # and writes y and the final state (the state hand-off between chunks
-        # is not algorithmic traffic)
-        "forward_prep": 2 * BC + cb + Bt,
-        "forward_main": x + b * L * H * e + BC + cb + Bt + 2 * H * 4 + init_b + x + st,
+        # single-pass arrangement: the compulsory bytes of the forward split
+        # between its two launches (their sum is forward_bytes); the
+        # per-chunk fragments and decay records the preparation writes and
+        # the walk reads are intermediates and count for neither
+        "forward_prep": b * L * H * e + 2 * BC + H * 4,
+        "forward_main": 2 * x + H * 4 + init_b + st,
         "chunk_cumsum": b * L * H * e + H * 4 + cs,
         "chunk_cb": 2 * BC + cb,
         "chunk_state": x + BC + cs + S,
@@ -323,7 +331,8 @@ def run_forward_bench(args):
     import ssd_inputs as si
 
     long32 = args.shape == "long-fp32"
-    w = si.WORKLOADS[3 if long32 else 2]
+    widx, wdesc = FORWARD_SHAPES[args.shape]
+    w = si.WORKLOADS[widx]
     if args.ngroups:
         w = w.with_(ngroups=args.ngroups)
     dev = torch.device("cuda:0")
@@ -375,18 +384,19 @@ def run_forward_bench(args):
     t_mfma = forward_flops(w) / ((F32_PEAK_TFLOPS if long32 else BF16_PEAK_TFLOPS) * 1e6)
     t_roof_us = max(t_hbm, t_mfma)
 
+    metric = METRIC if args.shape == "2.7B-layer" else (
+        f"SSD fwd tokens/s at H={w.nheads},P={w.headdim},N={w.dstate},L={w.seqlen} {w.dtype}; "
+        "% of MFMA/HBM roofline")
     result = {
-        "metric": ("SSD fwd tokens/s at H=32,P=64,N=128,L=65536 fp32, carried state; % of fp32-MFMA roofline"
-                   if long32 else METRIC),
+        "metric": metric,
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32" if long32 else "bf16",
+        "vs_baseline": None, "dtype": "f32" if w.dtype == "f32" else "bf16",
         "data": "synthetic (seeded; distributions of the workload)",
-        "config": {"workload": ("long-sequence SSD forward with carried state" if long32
-                                else "2.7B-layer-shaped SSD forward"), "batch": w.batch, "seqlen": w.seqlen,
+        "config": {"workload": wdesc, "batch": w.batch, "seqlen": w.seqlen,
                    "nheads": w.nheads, "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
                    "chunk": w.chunk, "inputs": w.dtype, "accumulate": "fp32", "path": args.path,
-                   "dt_options": args.options, "mall_flushed": flush is not None},
+                   "dt_options": args.options, "mall_flushed": flush is not None, "seed": w.seed},
         "forward_roofline": {"bound": "mfma" if t_mfma > t_hbm else "hbm", "t_roof_us": t_roof_us,
                              "frac": t_roof_us / (ms_per_step * 1e3),
                              "alg_bytes": forward_bytes(w), "alg_flops": forward_flops(w)},
@@ -396,9 +406,54 @@ def run_forward_bench(args):
     if not args.no_kernel_timing and args.options == "none":
         result["roofline"], result["kernels_us"] = kernel_roofline(ssd, w, x, dt, A, B, C, D, init, ws,
                                                                   y, fin, flush, args)
+    result["env"] = environment(torch)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, inp)
+        result["cpu_baseline"], ref = cpu_baseline(w, inp)
+        if args.options == "none":
+            result["parity"] = parity(w, y, fin, ref)
     return result
+
+
+def environment(torch) -> dict:
+    """The machine the line was measured on: GPU, ROCm/HIP and host CPU."""
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    props = torch.cuda.get_device_properties(0)
+    return {"gpu": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hip": getattr(torch.version, "hip", None),
+            "torch": torch.__version__, "cpu_model": cpu, "host_cpus": os.cpu_count()}
+
+
+def parity(w, y, fin, ref) -> dict:
+    """Relative L2 error of the timed forward's y and final state against the
+    float64 oracle on the same inputs: the worst (batch, head) slice, the
+    bound the workload's dtype sets."""
+    import numpy as np
+
+    y_ref, f_ref = ref
+    yg = y.detach().float().cpu().double().numpy()
+    fg = fin.detach().cpu().double().numpy()
+
+    def worst(a, r, kind):
+        if kind == "y":
+            b, L, H, P = r.shape
+            a = a.transpose(0, 2, 1, 3).reshape(b * H, -1)
+            r = r.transpose(0, 2, 1, 3).reshape(b * H, -1)
+        else:
+            a = a.reshape(-1, a.shape[-2] * a.shape[-1])
+            r = r.reshape(-1, r.shape[-2] * r.shape[-1])
+        return float(np.max(np.linalg.norm(a - r, axis=1) / np.maximum(np.linalg.norm(r, axis=1), 1e-30)))
+
+    tol = 2e-2 if w.dtype == "bf16" else 1e-5
+    ey, ef = worst(yg, y_ref, "y"), worst(fg, f_ref, "state")
+    return {"y_rel_l2_worst_slice": ey, "final_rel_l2_worst_slice": ef, "tol": tol,
+            "ok": bool(ey <= tol and ef <= tol)}
 
 
 def kernel_roofline(ssd, w, x, dt, A, B, C, D, init, ws, y, fin, flush, args):
@@ -471,23 +526,25 @@ def kernel_roofline(ssd, w, x, dt, A, B, C, D, init, ws, y, fin, flush, args):
         return roof, avg
     kb = kernel_bytes(w)[dom]
     achieved = kb / (avg[dom] * 1e-6) / 1e9
+    tag = f"{args.shape}/G{w.ngroups}/{args.options}"
     roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(dom), "alg_bytes_per_launch": kb,
+            "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(dom, tag), "alg_bytes_per_launch": kb,
             "avg_launch_us": avg[dom]}
     return roof, avg
 
 
-def measured_traffic(key: str):
+def measured_traffic(key: str, tag: str = ""):
     """HBM bytes per launch from the committed rocprofv3 counters
     (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE, scaled by the copy
-    calibration), or None once the kernel source has changed since they were
-    taken."""
+    calibration) for this kernel on this workload (`tag`: shape, groups and
+    options, "" for the kernels with one workload), or None when no entry
+    matches or the kernel source has changed since they were taken."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get(key)
+    rec = json.load(open(path)).get(f"{key}@{tag}" if tag else key)
     if not rec:
         return None
     src = os.path.join(ROOT, rec["source"])
@@ -497,16 +554,18 @@ def measured_traffic(key: str):
 
 
 def cpu_baseline(w, inp):
+    """The float64 oracle on the same inputs, timed on the host cores; also
+    returns its (y, final_state) for the parity entry."""
     import oracle
 
     args = [inp[k] for k in ("x", "dt", "A", "B", "C", "D", "init")]
     f = [oracle._f64(a) for a in args]
     t0 = time.perf_counter()
-    oracle.forward(*f)
+    ref = oracle.forward(*f)
     t = time.perf_counter() - t0
     return {"value": w.batch * w.seqlen / t, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle", "sample": f"the full workload ({w.batch}x{w.seqlen} tokens, {w.nheads} heads), "
-            f"float64 sequential recurrence, {t:.2f} s"}
+            f"float64 sequential recurrence, {t:.2f} s"}, ref
 
 
 def run_gated_norm_bench(args):

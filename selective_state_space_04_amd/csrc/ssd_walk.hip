@@ -530,13 +530,13 @@ __global__ __launch_bounds__(64 * (4 / CT)) void k_ssd_walk(
         }
     };
 
-    while (k < nblk) {
-        const unsigned char *slot;
+    const unsigned char *slot;
+    begin_chunk(slot);
+    for (;;) {
+        // ---- fast path, chunk after chunk while the factors stay in range:
+        //   y = 2^(Ls + c_i) [C_i g + (C B^T) V],  V_j = 2^-(Ls + c_j) s_j x_j,
+        //   g' = g + B^T V,  Ls' = Ls + c_last
         for (;;) {
-            // ---- fast path:
-            //   y = 2^(Ls + c_i) [C_i g + (C B^T) V],  V_j = 2^-(Ls + c_j) s_j x_j,
-            //   g' = g + B^T V,  Ls' = Ls + c_last
-            begin_chunk(slot);
             const float *rc = (const float *)(slot + kRecOff);
             const f32x4 meta = *(const f32x4 *)(rc + 32);
             const float c_last = rfl(meta[0]), cmin = rfl(meta[1]), cmax = rfl(meta[2]);
@@ -594,8 +594,26 @@ __global__ __launch_bounds__(64 * (4 / CT)) void k_ssd_walk(
             Ls += c_last;
             store_y(xt, acc_y);
             if (++k >= nblk) break;
+            begin_chunk(slot);
         }
         if (k >= nblk) break;
+
+        // Chunk k is out of range with the current Ls.  If it is in range on
+        // its own, fold 2^Ls into the accumulators (Ls restarts at 0) and take
+        // the fast path for it; otherwise the per-element path below.
+        {
+            const float *rc = (const float *)(slot + kRecOff);
+            const float cmin = rfl(rc[33]), cmax = rfl(rc[34]);
+            if (__builtin_amdgcn_readfirstlane((int)(cmin >= -kRange && cmax <= kRange))) {
+                const float sc = exp2_raw(Ls);
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) acc_h[nt][ct] *= sc;
+                Ls = 0.f;
+                continue;
+            }
+        }
 
         // ---- per-element path for chunk k (its copies are in `slot`); every
         // exponent is <= 0 for a non-increasing prefix, and 2^Ls goes back
@@ -661,8 +679,9 @@ __global__ __launch_bounds__(64 * (4 / CT)) void k_ssd_walk(
             }
             Ls = 0.f;
             store_y(xt, acc_y);
-            ++k;
         }
+        if (++k >= nblk) break;
+        begin_chunk(slot);
     }
 
     wait_vm<0>();  // the repeated copies past the end still write this workgroup's LDS

@@ -37,6 +37,17 @@ bool overlap(const Range &a, const Range &b) {
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// The integer a C caller stored in an enum-typed field or argument.  A C
+// caller may pass any int there; reading it through the enum type is
+// undefined in C++ when the value lies outside the enumeration, so its bytes
+// are read as an int instead.
+template <typename E> int raw_enum(const E &e) {
+    static_assert(sizeof(E) == sizeof(int), "enums of the C ABI are int-sized");
+    int v;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
+
 bool is_pow2_in(int64_t v, int64_t lo, int64_t hi) {
     return v >= lo && v <= hi && (v & (v - 1)) == 0;
 }
@@ -51,7 +62,7 @@ bool mul_ok(int64_t &acc, int64_t v) {
 
 ssd_status check_dims(const ssd_dims *d, bool decode, ssd::Dims *out) {
     if (!d) return SSD_ERR_NULL;
-    if (d->dtype != SSD_F32 && d->dtype != SSD_BF16) return SSD_ERR_DTYPE;
+    if (raw_enum(d->dtype) != SSD_F32 && raw_enum(d->dtype) != SSD_BF16) return SSD_ERR_DTYPE;
     const int64_t L = decode ? 1 : d->seqlen;
     if (d->batch < 0 || L < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
         d->ngroups < 1 || (!decode && d->chunk < 1))
@@ -297,7 +308,7 @@ ssd_status validate_backward(const ssd_dims *dims, const void *x, const void *dt
 // Selective scan: shape checks, segment length and workspace.
 ssd_status check_scan(const ssd_scan_dims *sd, ssd::ScanDims *out) {
     if (!sd) return SSD_ERR_NULL;
-    if (sd->dtype != SSD_F32 && sd->dtype != SSD_BF16) return SSD_ERR_DTYPE;
+    if (raw_enum(sd->dtype) != SSD_F32 && raw_enum(sd->dtype) != SSD_BF16) return SSD_ERR_DTYPE;
     if (sd->batch < 0 || sd->seqlen < 0 || sd->channels < 1 || sd->ngroups < 1) return SSD_ERR_SHAPE;
     if (sd->channels % sd->ngroups != 0) return SSD_ERR_SHAPE;
     const int64_t N = sd->dstate;
@@ -505,7 +516,7 @@ ssd_status run_walk_main(const ssd::Dims &d, const void *x, const float *D, cons
 extern "C" {
 
 const char *ssd_status_string(ssd_status s) {
-    switch (s) {
+    switch (raw_enum(s)) {
     case SSD_OK: return "SSD_OK";
     case SSD_ERR_NULL: return "SSD_ERR_NULL: a required pointer is NULL";
     case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE: negative or inconsistent sizes";

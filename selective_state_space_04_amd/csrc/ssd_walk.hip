@@ -43,10 +43,6 @@ namespace {
 constexpr int kBlk = 32;                 // steps per chunk
 constexpr int kOpsBytes = 18432;         // C (8 KiB), B^T (8 KiB), causal C B^T (2 KiB) fragments
 constexpr int kOffBt = 8192, kOffG = 16384;
-constexpr int kXOff = kOpsBytes;         // x tile: 32 rows x 64 bf16, swizzled
-constexpr int kRecOff = kOpsBytes + 4096;
-constexpr int kSlotBytes = 24576;        // one prefetch slot
-constexpr int kSlots = 3;                // chunk k computes while k + 1, k + 2 load
 constexpr float kRange = 64.f;           // |log2| bound on every factor of the fast path
 
 template <bool OPTS> struct Rec {
@@ -200,43 +196,6 @@ __device__ __forceinline__ XOffsets x_offsets(int lane, int rowlim, int H) {
     return o;
 }
 
-// Where the copies of the next chunk come from (advanced one chunk per issue
-// until the last chunk, which later issues repeat) and go to.
-struct CopySrc {
-    const unsigned char *ops;  // this wave's first operand fragment of the chunk
-    const unsigned char *x;    // row t0 of this (b, h)
-    const unsigned char *rec;  // the chunk's decay record
-    uint32_t slot;             // LDS address of the chunk's slot
-};
-
-// Issue the copies of wave WV for one chunk: instructions [i0, i1).
-template <int WV, int NIW>
-__device__ __forceinline__ void walk_issue(const CopySrc &cs, const XOffsets &xo, uint32_t lane16,
-                                           uint32_t recoff) {
-    constexpr int i0 = WV * NIW, i1 = i0 + NIW;
-    constexpr int o1 = i1 < kInsOps ? i1 : kInsOps;
-#pragma unroll
-    for (int i = i0; i < o1; i += 4) {
-        const int n = o1 - i;
-        const unsigned char *src = cs.ops + 1024 * (i - i0);
-        const uint32_t dst = cs.slot + 1024 * i;
-        if (n >= 4) dma16<4>(lane16, src, dst);
-        else if (n == 3) dma16<3>(lane16, src, dst);
-        else if (n == 2) dma16<2>(lane16, src, dst);
-        else dma16<1>(lane16, src, dst);
-    }
-    static_assert(i0 <= kInsOps || i0 >= kInsAll, "the x tile is copied by one wave");
-    if constexpr (i0 <= kInsOps && i1 >= kInsOps + kInsX)
-        dma16_4v(xo.v[0], xo.v[1], xo.v[2], xo.v[3], cs.x - kXBias, cs.slot + 1024 * kInsOps);
-    if constexpr (i0 <= kInsOps + kInsX && i1 > kInsOps + kInsX)
-        dma16<1>(recoff, cs.rec, cs.slot + 1024 * (kInsOps + kInsX));
-    // a wave whose range runs past the last instruction repeats the record
-    // into the slot's padding, so every wave issues exactly NIW copies (its
-    // explicit vmcnt waits count them)
-    static_assert(i1 <= kInsAll + 1, "at most one padding copy");
-    if constexpr (i1 > kInsAll) dma16<1>(recoff, cs.rec, cs.slot + 1024 * kInsAll);
-}
-
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -367,144 +326,314 @@ __global__ __launch_bounds__(256) void k_walk_prep(const bf16 *__restrict__ B, c
 }
 
 // ---------------------------------------------------------------------------
-// The walk.  Workgroup = one (b, h); 4 / CT waves, wave w owns the CT column
-// tiles 16 (w CT + ct) .. + 15 of P = 64.  Each chunk's operands (its group's
-// fragments, the head's 32 x 64 x tile and decay record) are copied straight
-// into one of three LDS slots two chunks ahead (dma16), so the copies of
-// chunks k + 1 and k + 2 are in flight while chunk k computes.  Every wave
-// waits for its own copies with an explicit vmcnt (vector memory operations
-// retire in issue order; the only others in the loop are the y stores) and
-// meets the others at a barrier before the slot is read.
+// The walk.  Workgroup = NH heads of one batch (same group) and 2 NH + 1
+// waves: compute wave 2 hh + w owns columns 32 w .. 32 w + 31 of head h0 + hh
+// (two 16-column MFMA tiles), and the last wave only moves data.  That copy
+// wave streams each chunk's operands (its group's fragments), the heads' x
+// tiles and decay records straight into LDS rings (dma16) several chunks
+// ahead, waits for them itself (vector memory operations retire in issue
+// order), and turns each record into the factors the compute waves use
+// (below); one barrier per chunk hands a chunk over.  The compute waves
+// touch global memory only to store y, so they never wait on a copy, and
+// they overlap the state products of chunk k with the output of chunk k - 1
+// and the scaled x of chunk k + 1.
+//
+// Factors of chunk m and head hh (LDS, written two chunks ahead, in the
+// copy wave's per-head running scale Ls):
+//   fast chunk:  F0_j = 2^-(Ls + c_j) s_j, F1_i = 2^(Ls + c_i), then Ls += c_last;
+//     a chunk out of range with Ls but in range on its own first folds 2^Ls
+//     into the state (resc) and restarts Ls at 0;
+//   per-element chunk: F0_i = 2^(Ls + c_i), F1 = 1, lam = 2^(Ls + c_last),
+//     then Ls = 0;
+//   F2_j = c_j, F3_j = s_j; meta = {mode, resc, lam, Ls after the chunk}.
 // ---------------------------------------------------------------------------
-template <int CT, bool OPTS, bool HAS_D>
-__global__ __launch_bounds__(64 * (4 / CT)) void k_ssd_walk(
+template <int NH> struct WalkLds {
+    static constexpr int SO = 4;                         // operand slots (chunks k .. k + 3)
+    static constexpr int SX = 6;                         // x + record slots (k - 1 .. k + 4)
+    static constexpr int SF = 4;                         // factor slots (k - 1 .. k + 2)
+    static constexpr int kXHead = 5120;                  // per head: x tile (4 KiB) + record copy (1 KiB)
+    static constexpr int kFHead = 528;                   // per head: F0..F3 (32 floats each) + meta
+    static constexpr int kOps = 0;
+    static constexpr int kX = kOps + SO * kOpsBytes;
+    static constexpr int kF = kX + SX * NH * kXHead;
+    static constexpr int kBytes = kF + SF * NH * kFHead;
+    static_assert(kBytes <= 160 * 1024, "LDS");
+};
+constexpr int kModeFast = 0, kModeRescale = 1, kModeElem = 2;
+
+template <int NH, bool OPTS, bool HAS_D>
+__global__ __launch_bounds__(64 * (2 * NH + 1)) void k_ssd_walk(
     const bf16 *__restrict__ x, const unsigned char *__restrict__ ops, const float *__restrict__ rec,
     const float *__restrict__ D, const float *init, bf16 *__restrict__ y, float *fin, int L, int H, int G,
     int nblk) {
-    constexpr int W = 4 / CT;
+    using Lay = WalkLds<NH>;
+    constexpr int NW = 2 * NH;                            // compute waves
     constexpr int RF = Rec<OPTS>::kFloats, RP = Rec<OPTS>::kPieces;
-    constexpr int NIW = (kInsAll + W - 1) / W;  // copy instructions per wave and chunk
-    constexpr int NST = CT / 2;                  // y stores per wave, row tile and chunk
-    static_assert(NIW * W * 1024 <= kSlotBytes, "slot layout");
-    static_assert(CT == 2 || CT == 4, "column tiles per wave");
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kSlots * kSlotBytes];
+    constexpr int NI = kInsOps + NH * (kInsX + 1);        // copies per chunk
+    static_assert(2 * NI < 64, "vmcnt is 6 bits");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::kBytes];
 
-    const int nbh = (int)gridDim.x;
-    const int item = (int)xcd_remap(blockIdx.x, nbh);
-    const int b = item / H, h = item - b * H;
-    const int grp = h / (H / G);
+    const int nunits = H / NH;
+    const int item = (int)xcd_remap(blockIdx.x, gridDim.x);
+    const int b = item / nunits, h0 = (item - b * nunits) * NH;
+    const int grp = h0 / (H / G);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int r = lane & 15, gq = lane >> 4;
-    const int ct0 = wave * CT;  // first column tile of this wave
-
-    // copy sources of chunk 0 and their per-chunk strides
-    CopySrc cs;
-    cs.ops = ops + (((int64_t)b * nblk) * G + grp) * kOpsBytes + 1024 * (wave * NIW);
-    cs.x = (const unsigned char *)(x + ((int64_t)b * L * H + h) * 64);
-    cs.rec = (const unsigned char *)(rec + ((int64_t)b * nblk * H + h) * RF);
     const uint32_t smem_lds = lds_addr(smem);
-    cs.slot = smem_lds;
-    const int64_t ops_step = (int64_t)G * kOpsBytes, x_step = (int64_t)kBlk * H * 128,
-                  rec_step = (int64_t)H * RF * 4;
-    const XOffsets xo_full = x_offsets(lane, kBlk - 1, H);
-    const XOffsets xo_tail = x_offsets(lane, L - (nblk - 1) * kBlk - 1, H);
-    const uint32_t lane16 = 16u * (uint32_t)lane, recoff = 16u * (uint32_t)min(lane, RP - 1);
-    int kn = 0;  // chunk whose copies are issued next
-    auto issue = [&]() {
-        const XOffsets &xo = kn >= nblk - 1 ? xo_tail : xo_full;
-        if (W == 1 || wave == 0)
-            walk_issue<0, NIW>(cs, xo, lane16, recoff);
-        else
-            walk_issue<1, NIW>(cs, xo, lane16, recoff);
-        if (kn < nblk - 1) {  // past the last chunk the same copies repeat (unread)
-            cs.ops += ops_step;
-            cs.x += x_step;
-            cs.rec += rec_step;
-        }
-        cs.slot = cs.slot + kSlotBytes == smem_lds + kSlots * kSlotBytes ? smem_lds : cs.slot + kSlotBytes;
-        ++kn;
-    };
+    auto x_slot = [&](int m) { return Lay::kX + (m % Lay::SX) * NH * Lay::kXHead; };
+    auto f_slot = [&](int m) { return Lay::kF + (m & (Lay::SF - 1)) * NH * Lay::kFHead; };
+    auto o_slot = [&](int m) { return Lay::kOps + (m & (Lay::SO - 1)) * kOpsBytes; };
 
-    issue();
-    issue();
+    if (wave == NW) {
+        // ---------------- copy wave ----------------
+        const unsigned char *ops_b = ops + ((int64_t)b * nblk * G + grp) * kOpsBytes;
+        const int64_t ops_step = (int64_t)G * kOpsBytes, x_step = (int64_t)kBlk * H * 128,
+                      rec_step = (int64_t)H * RF * 4;
+        const unsigned char *x_b = (const unsigned char *)(x + ((int64_t)b * L * H + h0) * 64);
+        const unsigned char *rec_b = (const unsigned char *)(rec + ((int64_t)b * nblk * H + h0) * RF);
+        const XOffsets xo_full = x_offsets(lane, kBlk - 1, H);
+        const XOffsets xo_tail = x_offsets(lane, L - (nblk - 1) * kBlk - 1, H);
+        const uint32_t lane16 = 16u * (uint32_t)lane, recoff = 16u * (uint32_t)min(lane, RP - 1);
+        // chunk m's copies; past the last chunk the sources repeat it (into
+        // slots nobody reads) so every chunk issues exactly NI copies
+        auto issue_ops = [&](int m) {
+            const unsigned char *src = ops_b + (int64_t)min(m, nblk - 1) * ops_step;
+            const uint32_t dst = smem_lds + (uint32_t)o_slot(m);
+            dma16<4>(lane16, src, dst);
+            dma16<4>(lane16, src + 4096, dst + 4096);
+            dma16<4>(lane16, src + 8192, dst + 8192);
+            dma16<4>(lane16, src + 12288, dst + 12288);
+            dma16<2>(lane16, src + 16384, dst + 16384);
+            static_assert(kInsOps == 18, "operand copies");
+        };
+        auto issue_x = [&](int m) {
+            const int mc = min(m, nblk - 1);
+            const XOffsets &xo = mc == nblk - 1 ? xo_tail : xo_full;
+            const uint32_t dst = smem_lds + (uint32_t)x_slot(m);
+#pragma unroll
+            for (int hh = 0; hh < NH; ++hh)
+                dma16_4v(xo.v[0], xo.v[1], xo.v[2], xo.v[3], x_b + hh * 128 + mc * x_step - kXBias,
+                         dst + hh * Lay::kXHead);
+#pragma unroll
+            for (int hh = 0; hh < NH; ++hh)  // last: the waits below count from these
+                dma16<1>(recoff, rec_b + hh * RF * 4 + mc * rec_step, dst + hh * Lay::kXHead + 4096);
+        };
+        // lanes 32 hh + j: step j of head hh (NH = 1: lanes 32..63 repeat 0..31)
+        const int hh = NH == 2 ? lane >> 5 : 0, j = lane & 31;
+        const bool writer = NH == 2 || lane < 32;
+        float Ls = 0.f;
+        auto factors = [&](int m) {
+            const float *rc = (const float *)(smem + x_slot(m) + hh * Lay::kXHead + 4096);
+            const float c = rc[j];
+            const f32x4 meta = *(const f32x4 *)(rc + 32);
+            const float s = OPTS ? rc[36 + j] : 1.f;
+            const float cl = meta[0], cmin = meta[1], cmax = meta[2];
+            const bool inr = Ls + cmin >= -kRange && Ls + cmax <= kRange;
+            const bool alone = cmin >= -kRange && cmax <= kRange;
+            const bool fast = inr || alone;
+            const float Lb = fast && !inr ? 0.f : Ls;
+            const float e_dn = exp2_raw(-(Lb + c)), e_up = exp2_raw(Lb + c);
+            float *fd = (float *)(smem + f_slot(m) + hh * Lay::kFHead);
+            if (writer) {
+                fd[j] = fast ? e_dn * s : e_up;
+                fd[32 + j] = fast ? e_up : 1.f;
+                fd[64 + j] = c;
+                fd[96 + j] = s;
+                if (j == 0)
+                    *(f32x4 *)(fd + 128) = f32x4{(float)(fast ? (inr ? kModeFast : kModeRescale) : kModeElem),
+                                                 fast && !inr ? exp2_raw(Ls) : 1.f, exp2_raw(Ls + cl),
+                                                 fast ? Lb + cl : 0.f};
+            }
+            Ls = fast ? Lb + cl : 0.f;
+        };
+        // before the first barrier: operands of chunks 0 .. 2, x and records
+        // of 0 .. 3 (issued as the iterations -4 .. -1 of the loop below
+        // would), factors of chunks 0 and 1
+        issue_x(0);
+        issue_ops(0);
+        issue_x(1);
+        issue_ops(1);
+        issue_x(2);
+        issue_ops(2);
+        issue_x(3);
+        wait_vm<2 * NI>();  // the record of chunk 1 and everything before it
+        factors(0);
+        factors(1);
+        lds_barrier();
+        for (int k = 0; k < nblk; ++k) {
+            // slots of chunk k - 1 (operands) and k - 2 (x) are free now
+            issue_ops(k + 3);
+            issue_x(k + 4);
+            // the record of chunk k + 2 (and with it the operands of k + 1
+            // and the x tiles of k + 2) was issued two chunks ago
+            wait_vm<2 * NI>();
+            if (k + 2 < nblk) factors(k + 2);
+            if (k + 1 < nblk) lds_barrier();
+        }
+        wait_vm<0>();  // no copy may land after the workgroup ends
+        return;
+    }
+
+    // ---------------- compute waves ----------------
+    const int hh = wave >> 1, h = h0 + hh;
+    const int r = lane & 15, gq = lane >> 4;
+    const int ct0 = (wave & 1) * 2;  // first column tile of this wave
+    const int xh = hh * Lay::kXHead, fh = hh * Lay::kFHead;
 
     // g[n][p] with lane (r, gq) of acc_h[nt][ct] holding n = 16 nt + 4 gq + e,
     // p = 16 (ct0 + ct) + r
-    f32x4 acc_h[8][CT];
+    f32x4 acc_h[8][2];
     if (init) {
         const float *ib = init + ((int64_t)(b * H + h) * 64) * 128;
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
+            for (int ct = 0; ct < 2; ++ct)
                 acc_h[nt][ct] = *(const f32x4 *)(ib + (16 * (ct0 + ct) + r) * 128 + 16 * nt + 4 * gq);
     } else {
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) acc_h[nt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ct = 0; ct < 2; ++ct) acc_h[nt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const float Dh = HAS_D ? D[h] : 0.f;
-    float Ls = 0.f;  // accumulators hold h / 2^Ls
     const auto rsY = buf_rsrc(y + ((int64_t)b * L * H + h) * 64, (uint32_t)(((int64_t)(L - 1) * H + 1) * 64 * 2));
-    int soff = 0;    // byte offset of chunk k's slot
 
-    // Per chunk: wait for its copies, meet the other waves, issue the copies
-    // two chunks ahead, then compute.  Chunks whose factors stay in range run
-    // back to back in the inner loop, one straight-line body that updates the
-    // accumulators in place; a chunk out of range leaves it for the
-    // per-element path below and the walk re-enters.
-    int k = 0;
-    auto begin_chunk = [&](const unsigned char *&slot) {
-        // chunk k's copies were issued before those of chunk k + 1 (NIW) and
-        // the y stores of chunks k - 2, k - 1 (2 NST each), in that order
-        if (k >= 2) wait_vm<NIW + 4 * NST>();
-        else if (k == 1) wait_vm<NIW + 2 * NST>();
-        else wait_vm<NIW>();
-        lds_barrier();  // every wave's copies of slot k landed; slot k + 2 is free
-        issue();
-        slot = smem + soff;
-        soff = soff + kSlotBytes == kSlots * kSlotBytes ? 0 : soff + kSlotBytes;
-    };
-    // the state as the bf16 operand of the output product (before the update):
-    // hB[s][ct] = h[n in 32 s + kset(gq)][p = 16 (ct0 + ct) + r]
-    auto state_operand = [&](bf16x8 (&hB)[4][CT]) {
+    // the state as the bf16 operand of the output product:
+    // hB[s][ct] = g[n in 32 s + kset(gq)][p = 16 (ct0 + ct) + r]
+    auto state_operand = [&](bf16x8 (&hB)[4][2]) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     hB[s][ct][e] = (bf16)acc_h[2 * s][ct][e];
                     hB[s][ct][e + 4] = (bf16)acc_h[2 * s + 1][ct][e];
                 }
     };
-    // acc_y[ct][rt] = C_rt h: lane (r, gq) holds y[i = 16 rt + r][p = 16 (ct0 + ct) + 4 gq + e]
-    auto state_output = [&](const unsigned char *slot, const bf16x8 (&hB)[4][CT], f32x4 (&acc_y)[CT][2]) {
+    // acc_y[ct][rt] = C_rt g: lane (r, gq) holds y[i = 16 rt + r][p = 16 (ct0 + ct) + 4 gq + e]
+    auto state_output = [&](const unsigned char *os, const bf16x8 (&hB)[4][2], f32x4 (&acc_y)[2][2]) {
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) acc_y[ct][0] = acc_y[ct][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ct = 0; ct < 2; ++ct) acc_y[ct][0] = acc_y[ct][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const bf16x8 cf = *(const bf16x8 *)(slot + (rt * 4 + s) * 1024 + 16 * lane);
+                const bf16x8 cf = *(const bf16x8 *)(os + (rt * 4 + s) * 1024 + 16 * lane);
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) acc_y[ct][rt] = mfma_bf16(hB[s][ct], cf, acc_y[ct][rt]);
+                for (int ct = 0; ct < 2; ++ct) acc_y[ct][rt] = mfma_bf16(hB[s][ct], cf, acc_y[ct][rt]);
             }
     };
-    // + D x, to bf16; lane groups gq, gq ^ 1 swap one 8-byte piece (one
-    // permlane16 swap per dword) so each holds 8 consecutive columns of its
-    // row: one 16-byte store per row tile and column-tile pair
-    auto store_y = [&](const unsigned char *xt, const f32x4 (&acc_y)[CT][2]) {
-        const int t0 = k * kBlk;
+    // E = F0 x of chunk m (the fast path's scaled input), as the B operand
+    auto scaled_x = [&](int m, bf16x8 (&V)[2]) {
+        const float *F0 = (const float *)(smem + f_slot(m) + fh);
+        const f32x4 ea = *(const f32x4 *)(F0 + 4 * gq), eb = *(const f32x4 *)(F0 + 16 + 4 * gq);
+        const unsigned char *xt = smem + x_slot(m) + xh;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const bf16x8 X = x_frag(xt, 16 * (ct0 + ct), lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                V[ct][e] = (bf16)((float)X[e] * ea[e]);
+                V[ct][e + 4] = (bf16)((float)X[e + 4] * eb[e]);
+            }
+        }
+    };
+    // fast chunk: acc_y = C g + (C B^T) E, g += B^T E
+    auto chunk_fast = [&](int m, const bf16x8 (&V)[2], f32x4 (&acc_y)[2][2]) {
+        const unsigned char *os = smem + o_slot(m);
+        bf16x8 hB[4][2];
+        state_operand(hB);
+        state_output(os, hB, acc_y);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const bf16x8 gf = *(const bf16x8 *)(os + kOffG + rt * 1024 + 16 * lane);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) acc_y[ct][rt] = mfma_bf16(V[ct], gf, acc_y[ct][rt]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            const bf16x8 bt = *(const bf16x8 *)(os + kOffBt + nt * 1024 + 16 * lane);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) acc_h[nt][ct] = mfma_bf16(bt, V[ct], acc_h[nt][ct]);
+        }
+    };
+    // per-element chunk (every exponent <= 0 for a non-increasing prefix):
+    //   y = 2^(Ls + c_i) C_i g + (mask . C B^T) x,  mask_ij = 2^(c_i - c_j) s_j [j <= i],
+    //   g' = 2^(Ls + c_last) g + B^T U,  U_j = 2^(c_last - c_j) s_j x_j
+    auto chunk_elem = [&](int m, f32x4 (&acc_y)[2][2]) {
+        const unsigned char *os = smem + o_slot(m);
+        const float *fb = (const float *)(smem + f_slot(m) + fh);
+        const float *cc = fb + 64;
+        const f32x4 ca = *(const f32x4 *)(cc + 4 * gq), cb = *(const f32x4 *)(cc + 16 + 4 * gq);
+        const float ci[2] = {cc[r], cc[16 + r]};
+        const float pre[2] = {fb[r], fb[16 + r]};
+        const float c_last = cc[31];
+        const float lam = rfl(fb[130]);
+        f32x4 sa = {1.f, 1.f, 1.f, 1.f}, sb = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (OPTS) {
+            sa = *(const f32x4 *)(fb + 96 + 4 * gq);
+            sb = *(const f32x4 *)(fb + 112 + 4 * gq);
+        }
+        const unsigned char *xt = smem + x_slot(m) + xh;
+        bf16x8 hB[4][2];
+        state_operand(hB);
+        bf16x8 X[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) X[ct] = x_frag(xt, 16 * (ct0 + ct), lane);
+        state_output(os, hB, acc_y);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) acc_y[ct][rt] *= pre[rt];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             const int i = 16 * rt + r;
-            uint32_t pk[CT][2];
+            bf16x8 gm = *(const bf16x8 *)(os + kOffG + rt * 1024 + 16 * lane);
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                f32x4 v = acc_y[ct][rt];
+            for (int e = 0; e < 4; ++e) {
+                // above the diagonal the tile is zero; its exponent is replaced so
+                // that no factor overflows (a select, not a branch)
+                const int ja = 4 * gq + e, jb = 16 + 4 * gq + e;
+                const float fa = exp2_raw(ja <= i ? ci[rt] - ca[e] : -256.f) * sa[e];
+                const float fb2 = exp2_raw(jb <= i ? ci[rt] - cb[e] : -256.f) * sb[e];
+                gm[e] = (bf16)((float)gm[e] * fa);
+                gm[e + 4] = (bf16)((float)gm[e + 4] * fb2);
+            }
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) acc_y[ct][rt] = mfma_bf16(X[ct], gm, acc_y[ct][rt]);
+        }
+        bf16x8 U[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                U[ct][e] = (bf16)((float)X[ct][e] * exp2_raw(c_last - ca[e]) * sa[e]);
+                U[ct][e + 4] = (bf16)((float)X[ct][e + 4] * exp2_raw(c_last - cb[e]) * sb[e]);
+            }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            const bf16x8 bt = *(const bf16x8 *)(os + kOffBt + nt * 1024 + 16 * lane);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) acc_h[nt][ct] = mfma_bf16(bt, U[ct], acc_h[nt][ct] * lam);
+        }
+    };
+    // y of chunk m = F1_i acc_y + D x, to bf16; lane groups gq, gq ^ 1 swap one
+    // 8-byte piece (one permlane16 swap per dword) so each holds 8 consecutive
+    // columns of its row: one 16-byte store per row tile
+    auto store_y = [&](int m, const f32x4 (&acc_y)[2][2]) {
+        const float *F1 = (const float *)(smem + f_slot(m) + fh) + 32;
+        const float rs[2] = {F1[r], F1[16 + r]};
+        const unsigned char *xt = smem + x_slot(m) + xh;
+        const int t0 = m * kBlk;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int i = 16 * rt + r;
+            uint32_t pk[2][2];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                f32x4 v = acc_y[ct][rt] * rs[rt];
                 if constexpr (HAS_D) {
                     const u32x2 xr = x_row4(xt, i, 16 * (ct0 + ct) + 4 * gq);
                     v[0] += Dh * bf16_lo(xr[0]);
@@ -517,181 +646,54 @@ __global__ __launch_bounds__(64 * (4 / CT)) void k_ssd_walk(
             }
             const bool odd = gq & 1;
             const uint32_t off_row = (t0 + i < L) ? (uint32_t)(t0 + i) * (uint32_t)H * 128u : kBufOff;
-#pragma unroll
-            for (int m = 0; m < CT / 2; ++m) {
-                // lane group gq even ends with columns 16 (ct0 + 2m) + 8 (gq / 2) .. + 7,
-                // odd with 16 (ct0 + 2m + 1) + 8 (gq / 2) .. + 7
-                const auto s0 = __builtin_amdgcn_permlane16_swap(pk[2 * m][0], pk[2 * m + 1][0], false, false);
-                const auto s1 = __builtin_amdgcn_permlane16_swap(pk[2 * m][1], pk[2 * m + 1][1], false, false);
-                const u32x4 out = {s0[0], s1[0], s0[1], s1[1]};
-                const int col = 16 * (ct0 + 2 * m + (odd ? 1 : 0)) + 8 * (gq >> 1);
-                buf_st16(out, rsY, off_row == kBufOff ? kBufOff : off_row + (uint32_t)col * 2u);
-            }
+            // lane group gq even ends with columns 16 ct0 + 8 (gq / 2) .. + 7,
+            // odd with 16 (ct0 + 1) + 8 (gq / 2) .. + 7
+            const auto s0 = __builtin_amdgcn_permlane16_swap(pk[0][0], pk[1][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(pk[0][1], pk[1][1], false, false);
+            const u32x4 out = {s0[0], s1[0], s0[1], s1[1]};
+            const int col = 16 * (ct0 + (odd ? 1 : 0)) + 8 * (gq >> 1);
+            buf_st16(out, rsY, off_row == kBufOff ? kBufOff : off_row + (uint32_t)col * 2u);
         }
     };
 
-    const unsigned char *slot;
-    begin_chunk(slot);
-    for (;;) {
-        // ---- fast path, chunk after chunk while the factors stay in range:
-        //   y = 2^(Ls + c_i) [C_i g + (C B^T) V],  V_j = 2^-(Ls + c_j) s_j x_j,
-        //   g' = g + B^T V,  Ls' = Ls + c_last
-        for (;;) {
-            const float *rc = (const float *)(slot + kRecOff);
-            const f32x4 meta = *(const f32x4 *)(rc + 32);
-            const float c_last = rfl(meta[0]), cmin = rfl(meta[1]), cmax = rfl(meta[2]);
-            if (!__builtin_amdgcn_readfirstlane((int)(Ls + cmin >= -kRange && Ls + cmax <= kRange))) break;
-            const unsigned char *xt = slot + kXOff;
-            // c at this lane's steps kset(gq) and at its output rows r, 16 + r
-            const f32x4 ca = *(const f32x4 *)(rc + 4 * gq), cb = *(const f32x4 *)(rc + 16 + 4 * gq);
-            const float cr0 = rc[r], cr1 = rc[16 + r];
-            bf16x8 hB[4][CT];
-            state_operand(hB);
-            bf16x8 V[CT];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) V[ct] = x_frag(xt, 16 * (ct0 + ct), lane);
-            f32x4 acc_y[CT][2];
-            state_output(slot, hB, acc_y);
-            float ea[4], eb[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                ea[e] = exp2_raw(-(Ls + ca[e]));
-                eb[e] = exp2_raw(-(Ls + cb[e]));
-            }
-            if constexpr (OPTS) {
-                const f32x4 sa = *(const f32x4 *)(rc + 36 + 4 * gq), sb = *(const f32x4 *)(rc + 52 + 4 * gq);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    ea[e] *= sa[e];
-                    eb[e] *= sb[e];
-                }
-            }
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    V[ct][e] = (bf16)((float)V[ct][e] * ea[e]);
-                    V[ct][e + 4] = (bf16)((float)V[ct][e + 4] * eb[e]);
-                }
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const bf16x8 gf = *(const bf16x8 *)(slot + kOffG + rt * 1024 + 16 * lane);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) acc_y[ct][rt] = mfma_bf16(V[ct], gf, acc_y[ct][rt]);
-            }
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-                const bf16x8 bt = *(const bf16x8 *)(slot + kOffBt + nt * 1024 + 16 * lane);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) acc_h[nt][ct] = mfma_bf16(bt, V[ct], acc_h[nt][ct]);
-            }
-            const float rs0 = exp2_raw(Ls + cr0), rs1 = exp2_raw(Ls + cr1);
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                acc_y[ct][0] *= rs0;
-                acc_y[ct][1] *= rs1;
-            }
-            Ls += c_last;
-            store_y(xt, acc_y);
-            if (++k >= nblk) break;
-            begin_chunk(slot);
-        }
-        if (k >= nblk) break;
-
-        // Chunk k is out of range with the current Ls.  If it is in range on
-        // its own, fold 2^Ls into the accumulators (Ls restarts at 0) and take
-        // the fast path for it; otherwise the per-element path below.
-        {
-            const float *rc = (const float *)(slot + kRecOff);
-            const float cmin = rfl(rc[33]), cmax = rfl(rc[34]);
-            if (__builtin_amdgcn_readfirstlane((int)(cmin >= -kRange && cmax <= kRange))) {
-                const float sc = exp2_raw(Ls);
+    lds_barrier();  // operands of chunk 0, x and factors of chunks 0 and 1
+    bf16x8 Vc[2];
+    scaled_x(0, Vc);
+    // chunk k: its state products, its output (overlapping the state update)
+    // and the scaled x of chunk k + 1, which does not depend on them
+    for (int k = 0; k < nblk; ++k) {
+        const f32x4 meta = *(const f32x4 *)(smem + f_slot(k) + fh + 512);
+        const int mode = (int)rfl(meta[0]);
+        f32x4 acc_y[2][2];
+        // each branch is one straight-line block, so the output and the next
+        // scaled x (past the last chunk: unused values from a stale slot) can
+        // be scheduled between the state products
+        if (mode == kModeElem) {
+            chunk_elem(k, acc_y);
+            store_y(k, acc_y);
+            scaled_x(k + 1, Vc);
+        } else {
+            if (mode == kModeRescale) {
+                const float sc = rfl(meta[1]);
 #pragma unroll
                 for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) acc_h[nt][ct] *= sc;
-                Ls = 0.f;
-                continue;
+                    for (int ct = 0; ct < 2; ++ct) acc_h[nt][ct] *= sc;
             }
+            chunk_fast(k, Vc, acc_y);
+            store_y(k, acc_y);
+            scaled_x(k + 1, Vc);
         }
-
-        // ---- per-element path for chunk k (its copies are in `slot`); every
-        // exponent is <= 0 for a non-increasing prefix, and 2^Ls goes back
-        // into the accumulators (Ls restarts at 0):
-        //   y = 2^(Ls + c_i) C_i g + (mask . C B^T) x,  mask_ij = 2^(c_i - c_j) s_j [j <= i],
-        //   g' = 2^(Ls + c_last) g + B^T U,  U_j = 2^(c_last - c_j) s_j x_j
-        {
-            const float *rc = (const float *)(slot + kRecOff);
-            const unsigned char *xt = slot + kXOff;
-            const float c_last = rfl(rc[32]);
-            const f32x4 ca = *(const f32x4 *)(rc + 4 * gq), cb = *(const f32x4 *)(rc + 16 + 4 * gq);
-            const float ci[2] = {rc[r], rc[16 + r]};
-            f32x4 sa = {1.f, 1.f, 1.f, 1.f}, sb = {1.f, 1.f, 1.f, 1.f};
-            if constexpr (OPTS) {
-                sa = *(const f32x4 *)(rc + 36 + 4 * gq);
-                sb = *(const f32x4 *)(rc + 52 + 4 * gq);
-            }
-            bf16x8 hB[4][CT];
-            state_operand(hB);
-            bf16x8 X[CT];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) X[ct] = x_frag(xt, 16 * (ct0 + ct), lane);
-            f32x4 acc_y[CT][2];
-            state_output(slot, hB, acc_y);
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const float pre = exp2_raw(Ls + ci[rt]);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) acc_y[ct][rt] *= pre;
-            }
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const int i = 16 * rt + r;
-                bf16x8 gm = *(const bf16x8 *)(slot + kOffG + rt * 1024 + 16 * lane);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // above the diagonal the tile is zero; its exponent is replaced so
-                    // that no factor overflows (a select, not a branch)
-                    const int ja = 4 * gq + e, jb = 16 + 4 * gq + e;
-                    const float fa = exp2_raw(ja <= i ? ci[rt] - ca[e] : -256.f) * sa[e];
-                    const float fb = exp2_raw(jb <= i ? ci[rt] - cb[e] : -256.f) * sb[e];
-                    gm[e] = (bf16)((float)gm[e] * fa);
-                    gm[e + 4] = (bf16)((float)gm[e + 4] * fb);
-                }
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) acc_y[ct][rt] = mfma_bf16(X[ct], gm, acc_y[ct][rt]);
-            }
-            // (rows past L: zero B, no contribution)
-            bf16x8 U[CT];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    U[ct][e] = (bf16)((float)X[ct][e] * exp2_raw(c_last - ca[e]) * sa[e]);
-                    U[ct][e + 4] = (bf16)((float)X[ct][e + 4] * exp2_raw(c_last - cb[e]) * sb[e]);
-                }
-            const float lam = exp2_raw(Ls + c_last);
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-                const bf16x8 bt = *(const bf16x8 *)(slot + kOffBt + nt * 1024 + 16 * lane);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) acc_h[nt][ct] = mfma_bf16(bt, U[ct], acc_h[nt][ct] * lam);
-            }
-            Ls = 0.f;
-            store_y(xt, acc_y);
-        }
-        if (++k >= nblk) break;
-        begin_chunk(slot);
+        if (k + 1 < nblk) lds_barrier();
     }
 
-    wait_vm<0>();  // the repeated copies past the end still write this workgroup's LDS
     if (fin) {
-        const float sc = exp2_raw(Ls);
+        const float sc = exp2_raw(rfl(((const float *)(smem + f_slot(nblk - 1) + fh))[131]));
         float *fb = fin + ((int64_t)(b * H + h) * 64) * 128;
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
+            for (int ct = 0; ct < 2; ++ct)
                 *(f32x4 *)(fb + (16 * (ct0 + ct) + r) * 128 + 16 * nt + 4 * gq) = acc_h[nt][ct] * sc;
     }
 }
@@ -726,26 +728,33 @@ hipError_t launch_walk_prep(const Dims &d, const void *dt, const float *A, const
 }
 
 namespace {
-template <int CT, bool OPTS, bool HAS_D>
+template <int NH, bool OPTS, bool HAS_D>
 void launch_walk_t(const Dims &d, const void *x, const void *ops, const float *rec, const float *D,
                    const float *init, void *y, float *fin, hipStream_t st) {
     const int nblk = (int)((d.L + kBlk - 1) / kBlk);
-    k_ssd_walk<CT, OPTS, HAS_D><<<(unsigned)(d.b * d.H), 64 * (4 / CT), 0, st>>>(
+    k_ssd_walk<NH, OPTS, HAS_D><<<(unsigned)(d.b * (d.H / NH)), 64 * (2 * NH + 1), 0, st>>>(
         (const bf16 *)x, (const unsigned char *)ops, rec, D, init, (bf16 *)y, fin, (int)d.L, (int)d.H, (int)d.G,
         nblk);
+}
+template <int NH>
+void launch_walk_nh(const Dims &d, const void *x, const void *ops, const float *rec, const float *D,
+                    const float *init, void *y, float *fin, hipStream_t st, bool opts) {
+    if (opts) {
+        if (D) launch_walk_t<NH, true, true>(d, x, ops, rec, D, init, y, fin, st);
+        else launch_walk_t<NH, true, false>(d, x, ops, rec, D, init, y, fin, st);
+    } else {
+        if (D) launch_walk_t<NH, false, true>(d, x, ops, rec, D, init, y, fin, st);
+        else launch_walk_t<NH, false, false>(d, x, ops, rec, D, init, y, fin, st);
+    }
 }
 }  // namespace
 
 hipError_t launch_walk_main(const Dims &d, const void *x, const void *ops, const float *rec, const float *D,
                             const float *init, void *y, float *fin, hipStream_t st, bool opts) {
-    constexpr int CT = 2;
-    if (opts) {
-        if (D) launch_walk_t<CT, true, true>(d, x, ops, rec, D, init, y, fin, st);
-        else launch_walk_t<CT, true, false>(d, x, ops, rec, D, init, y, fin, st);
-    } else {
-        if (D) launch_walk_t<CT, false, true>(d, x, ops, rec, D, init, y, fin, st);
-        else launch_walk_t<CT, false, false>(d, x, ops, rec, D, init, y, fin, st);
-    }
+    // two heads per workgroup share each chunk's operand copies when both
+    // belong to one group
+    if ((d.H / d.G) % 2 == 0) launch_walk_nh<2>(d, x, ops, rec, D, init, y, fin, st, opts);
+    else launch_walk_nh<1>(d, x, ops, rec, D, init, y, fin, st, opts);
     return hipGetLastError();
 }
 

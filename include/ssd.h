@@ -147,6 +147,28 @@ ssd_status ssd_forward_main(const ssd_dims *dims, const void *x, const void *dt,
                             void *stream);
 
 /*
+ * ssd_forward for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same contract and
+ * result as ssd_forward except that there is no workspace argument: the
+ * workspace is a device array of SSD_NOALLOC_WORKSPACE_BYTES inside the
+ * library, one per GPU, held from the library's load to the end of the
+ * process.  The entry point makes no allocation (no hipMalloc, hipFree or
+ * allocating library call); the first call on a device looks up the array's
+ * address there (hipGetSymbolAddress, SSD_ERR_HIP if that fails).
+ *   Dims whose ssd_forward_workspace_bytes exceeds SSD_NOALLOC_WORKSPACE_BYTES
+ *   return SSD_ERR_WORKSPACE before any HIP call (as invalid dims return
+ *   their own status).  The array's contents on entry are ignored, as
+ *   ssd_forward ignores its workspace's.
+ *   All calls on one GPU share its array: calls that overlap in time on one
+ *   GPU (on different streams, or from different host threads without
+ *   ordering) race on it and must not be made.
+ */
+#define SSD_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)
+ssd_status ssd_forward_noalloc(const ssd_dims *dims, const void *x, const void *dt, const float *A,
+                               const void *B, const void *C, const float *D, const float *init_state,
+                               void *y, float *final_state, void *stream);
+
+/*
  * Step-size preprocessing and input scaling, the neighbours of the core in a
  * Mamba layer, applied inside the kernels.  For every step and head:
  *   dt_eff = softplus(dt + dt_bias)   if dt_softplus  (Mamba review page,

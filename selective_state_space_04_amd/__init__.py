@@ -58,6 +58,7 @@ _SIGS = {
     "ssd_forward_is_single_pass": (ctypes.c_int, [_dp]),
     "ssd_forward_prep": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "ssd_forward_main": (ctypes.c_int, [_dp] + [_vp] * 10 + [ctypes.c_size_t, _vp]),
+    "ssd_forward_noalloc": (ctypes.c_int, [_dp] + [_vp] * 10),
     "ssd_chunk_cumsum": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp]),
     "ssd_chunk_cb": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp]),
     "ssd_chunk_state": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp, _vp]),
@@ -209,6 +210,32 @@ def forward(x, dt, A, B, C, D=None, init_state=None, chunk: int = 256, *, staged
     else:
         fn = lib.ssd_forward_staged_ex if staged else lib.ssd_forward_ex
         _check(fn(ctypes.byref(dims), ctypes.byref(opts), *args))
+    return y, final_state
+
+
+NOALLOC_WORKSPACE_BYTES = 32 << 20  # SSD_NOALLOC_WORKSPACE_BYTES
+
+
+def forward_noalloc(x, dt, A, B, C, D=None, init_state=None, chunk: int = 256, *, y=None, final_state=None,
+                    want_final: bool = True):
+    """ssd_forward_noalloc: the forward with the library's own fixed device
+    workspace (no workspace argument, no allocation inside the library).
+    Returns (y, final_state); ``y`` / ``final_state`` may be preallocated so
+    that the call itself allocates nothing on the torch side either.
+    """
+    dims = _forward_dims(x, dt, A, B, C, D, init_state, chunk)
+    b, L, H, P = x.shape
+    N = B.shape[3]
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", x.shape, x.dtype, x.device)
+    if final_state is None and want_final:
+        final_state = torch.empty((b, H, P, N), dtype=torch.float32, device=x.device)
+    elif final_state is not None:
+        _need(final_state, "final_state", (b, H, P, N), torch.float32, x.device)
+    _check(lib.ssd_forward_noalloc(ctypes.byref(dims), _p(x), _p(dt), _p(A), _p(B), _p(C), _p(D),
+                                   _p(init_state), _p(y), _p(final_state), _stream()))
     return y, final_state
 
 

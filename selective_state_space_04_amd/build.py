@@ -17,7 +17,8 @@ OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libssd_mi355x.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["ssd_kernels.hip", "ssd_walk.hip", "ssd_backward.hip", "ssd_epilogue.hip", "ssd_scan.hip", "ssd_api.cpp"]
+SOURCES = ["ssd_kernels.hip", "ssd_walk.hip", "ssd_backward.hip", "ssd_epilogue.hip", "ssd_scan.hip", "ssd_noalloc.hip",
+           "ssd_api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-x", "hip",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"), "-I", CSRC]

@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cstring>
 
+#include "ssd_internal.h"
 #include "ssd_launch.h"
 
 namespace {
@@ -512,6 +513,19 @@ ssd_status run_walk_main(const ssd::Dims &d, const void *x, const float *D, cons
 }
 
 }  // namespace
+
+namespace ssd {
+
+ssd_status forward_dims_check(const ssd_dims *dims, size_t *ws_bytes) {
+    ssd::Dims d;
+    const ssd_status st = check_dims(dims, false, &d);
+    if (st == SSD_OK && ws_bytes) *ws_bytes = (size_t)ws_total(d);
+    return st;
+}
+
+ssd_status hip_error(hipError_t e) { return hip_status(e); }
+
+}  // namespace ssd
 
 extern "C" {
 

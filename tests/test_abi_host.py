@@ -200,6 +200,20 @@ def test_entry_points_reject_before_launch():
         "SSD_ERR_DTYPE"
 
 
+def test_noalloc_rejects_before_any_hip_call():
+    """The no-allocation forward rejects bad dims, and dims whose workspace
+    exceeds its fixed array, on the host (this machine has no GPU: any HIP
+    call would fail with SSD_ERR_HIP instead)."""
+    a = fwd_args(dims())
+    ptrs = [a[k] for k in ("x", "dt", "A", "B", "C", "D", "init", "y", "fin")]
+    bad = dims(headdim=48)
+    assert ssd.STATUS[LIB.ssd_forward_noalloc(ctypes.byref(bad), *ptrs, None)] == "SSD_ERR_UNSUPPORTED"
+    big = dims(batch=1, seqlen=65536, nheads=32, ngroups=1, chunk=256, dtype=ssd.F32)
+    assert ssd.workspace_bytes(big) > ssd.NOALLOC_WORKSPACE_BYTES
+    assert ssd.STATUS[LIB.ssd_forward_noalloc(ctypes.byref(big), *ptrs, None)] == "SSD_ERR_WORKSPACE"
+    assert ssd.STATUS[LIB.ssd_forward_noalloc(None, *ptrs, None)] == "SSD_ERR_NULL"
+
+
 # ------------------------------------------------------------------ backward
 BWD_NAMES = ["x", "dt", "A", "B", "C", "D", "init", "dy", "dfinal", "dx", "ddt", "dA", "dB", "dC", "dD",
              "dinit"]

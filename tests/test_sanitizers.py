@@ -23,7 +23,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "selective_state_space_04_amd", "csrc")
 OBJ = os.path.join(ROOT, "selective_state_space_04_amd", "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-KERNEL_OBJS = ["ssd_kernels.o", "ssd_walk.o", "ssd_backward.o", "ssd_epilogue.o", "ssd_scan.o"]
+KERNEL_OBJS = ["ssd_kernels.o", "ssd_walk.o", "ssd_backward.o", "ssd_epilogue.o", "ssd_scan.o", "ssd_noalloc.o"]
 SAN_OPTS = "detect_leaks=0:halt_on_error=1:abort_on_error=1"
 
 

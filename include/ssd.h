@@ -215,6 +215,7 @@ ssd_status ssd_decode_step_ex(const ssd_dims *dims, const ssd_dt_options *opts, 
  * "4つのトークンで計算してみる").  `state` [batch, H, P, N] float32 is read and
  * overwritten in place with a_t * state + x B^T; y [batch, H, P] receives
  * state C + D x.  dims->seqlen and dims->chunk are ignored.  D nullable.
+ * batch * H * P must stay below 2^31 - 4096 (else SSD_ERR_UNSUPPORTED).
  */
 ssd_status ssd_decode_step(const ssd_dims *dims, float *state, const void *x, const void *dt,
                            const float *A, const void *B, const void *C, const float *D,

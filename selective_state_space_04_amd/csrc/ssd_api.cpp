@@ -249,6 +249,7 @@ ssd_status validate_decode(const ssd_dims *dims, const float *state, const void 
     ssd::Dims d;
     ssd_status st = check_dims(dims, true, &d);
     if (st != SSD_OK) return st;
+    if (d.b * d.H * d.P > ssd::kDecodeMaxRows) return SSD_ERR_UNSUPPORTED;
     if (!A) return SSD_ERR_NULL;
     if (d.b > 0 && (!state || !x || !dt || !B || !C || !y)) return SSD_ERR_NULL;
     const void *ptrs[] = {state, x, dt, A, B, C, D, y};

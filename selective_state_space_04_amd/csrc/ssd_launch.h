@@ -30,6 +30,8 @@ hipError_t launch_state_passing(const Dims &d, float *S, const float *cs, const 
 hipError_t launch_chunk_scan(const Dims &d, const void *x, const void *C, const void *cb,
                              const float *cs, const float *hprev, const float *D, void *y,
                              hipStream_t st, const float *sc = nullptr);
+// Decode: batch * nheads * headdim state rows at most (32-bit row indices).
+constexpr int64_t kDecodeMaxRows = ((int64_t)1 << 31) - 4096;
 hipError_t launch_decode(const Dims &d, float *state, const void *x, const void *dt,
                          const float *A, const void *B, const void *C, const float *D, void *y,
                          hipStream_t st, const DtOpts *o = nullptr);

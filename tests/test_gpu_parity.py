@@ -371,6 +371,33 @@ def test_decode_steps_equal_forward(ssd, dtype, N):
     assert worst_rel(f64(state), f_ref, "state") < TOL[dtype]
 
 
+# The decode step has two launch shapes: pieces of RPI = 1024 / N rows of one
+# slice spread over a grid of at most 40960 workgroups (a multiple of 64 once
+# above 64, in an XCD-aware order, spare workgroups idle) when RPI divides P,
+# and one workgroup per (b, h) slice otherwise.  These shapes reach: a grid
+# rounded up with idle workgroups (37 x 12 x 128 rows at N = 64: 3552 pieces),
+# one piece per slice (P = RPI = 32), four pieces per slice at N = 256, a
+# grid under 64, and the per-slice path (RPI = 64 > P = 16), with groups.
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(37, 12, 128, 64, 3), (3, 5, 32, 32, 5), (2, 3, 16, 256, 1),
+                                   (1, 2, 16, 128, 2), (5, 6, 16, 16, 2)])
+def test_decode_launch_shapes(ssd, dtype, shape):
+    b, H, P, N, G = shape
+    w = small(dtype, batch=b, seqlen=3, nheads=H, headdim=P, dstate=N, ngroups=G, seed=31)
+    inp = si.make_forward_inputs(w)
+    state = dev(inp["init"]).clone()
+    st_ref = inp["init"].double().numpy().copy()
+    for t in range(w.seqlen):
+        y = ssd.decode_step(state, dev(inp["x"][:, t].contiguous()), dev(inp["dt"][:, t].contiguous()),
+                            dev(inp["A"]), dev(inp["B"][:, t].contiguous()), dev(inp["C"][:, t].contiguous()),
+                            dev(inp["D"]))
+        y_ref, st_ref = oracle.decode_step(st_ref, inp["x"][:, t], inp["dt"][:, t], inp["A"], inp["B"][:, t],
+                                           inp["C"][:, t], inp["D"])
+        torch.cuda.synchronize()
+        assert worst_rel(f64(y)[:, None], y_ref[:, None], "y") < TOL[dtype], t
+    assert worst_rel(f64(state), st_ref, "state") < TOL[dtype]
+
+
 # ------------------------------------------------------------------ full-size workloads
 @pytest.mark.parametrize("idx", [0, 1, 2, 3])
 def test_workload_forward_full(ssd, idx):

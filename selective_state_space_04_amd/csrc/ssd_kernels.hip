@@ -121,10 +121,10 @@ __global__ __launch_bounds__(64) void k_chunk_cumsum_opts(const T *__restrict__ 
 // transposed (cbT[j][i] = C_i . B_j), which the gradient kernels read with
 // the step index i contiguous.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int N>
 __global__ __launch_bounds__(256) void k_chunk_cb(const T *__restrict__ B, const T *__restrict__ C,
                                                   T *__restrict__ cb, T *__restrict__ cbT,
-                                                  int64_t L, int G, int N, int Q, int nc) {
+                                                  int64_t L, int G, int Q, int nc) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, grp = lane >> 4;
     const int T16 = Q / 16;
@@ -143,26 +143,41 @@ __global__ __launch_bounds__(256) void k_chunk_cb(const T *__restrict__ B, const
     const int64_t s = (int64_t)c * Q;
     const int64_t irow = s + ti * 16 + r, jrow = s + tj * 16 + r;
     const bool vi = irow < L, vj = jrow < L;
-    const T *Crow = C + ((b * L + irow) * G + g) * N;
-    const T *Brow = B + ((b * L + jrow) * G + g) * N;
+    // rows past L read row s (always present) and are zeroed after the load:
+    // all of a lane's loads issue before its first MFMA, with no branch
+    const T *Crow = C + ((b * L + (vi ? irow : s)) * G + g) * N;
+    const T *Brow = B + ((b * L + (vj ? jrow : s)) * G + g) * N;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (sizeof(T) == 2) {
-        for (int k0 = 0; k0 < N; k0 += 32) {
-            const int k = k0 + grp * 8;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            const u32x4 a = (vi && k < N) ? *(const u32x4 *)(Crow + k) : z;
-            const u32x4 bb = (vj && k < N) ? *(const u32x4 *)(Brow + k) : z;
-            acc = mfma_bf16(as_bf16x8(a), as_bf16x8(bb), acc);
-        }
-    } else {
-        for (int k0 = 0; k0 < N; k0 += 16) {
-            const int k = k0 + grp * 4;
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            const f32x4 a = vi ? *(const f32x4 *)(Crow + k) : z;
-            const f32x4 bb = vj ? *(const f32x4 *)(Brow + k) : z;
+        constexpr int NI = (N + 31) / 32;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        u32x4 a[NI], bb[NI];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc = mfma_f32(a[e], bb[e], acc);
+        for (int i = 0; i < NI; ++i) {
+            const int k = i * 32 + grp * 8;
+            a[i] = *(const u32x4 *)(Crow + min(k, N - 8));
+            bb[i] = *(const u32x4 *)(Brow + min(k, N - 8));
+            if (!vi || k >= N) a[i] = z;
+            if (!vj || k >= N) bb[i] = z;
         }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) acc = mfma_bf16(as_bf16x8(a[i]), as_bf16x8(bb[i]), acc);
+    } else {
+        constexpr int NI = N / 16;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 a[NI], bb[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int k = i * 16 + grp * 4;
+            a[i] = *(const f32x4 *)(Crow + k);
+            bb[i] = *(const f32x4 *)(Brow + k);
+            if (!vi) a[i] = z;
+            if (!vj) bb[i] = z;
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = mfma_f32(a[i][e], bb[i][e], acc);
     }
     const int64_t off = (((int64_t)b * nc + c) * G + g) * (int64_t)Q * Q;
     T *out = cb + off;
@@ -1335,14 +1350,14 @@ hipError_t launch_chunk_cb(const Dims &d, const void *B, const void *C, void *cb
     const int T16 = (int)(d.Q / 16);
     const int ntiles = T16 * (T16 + 1) / 2;
     dim3 grid((unsigned)(d.b * d.nc * d.G), (unsigned)((ntiles + 3) / 4));
-    if (d.dtype == 1)
-        k_chunk_cb<bf16><<<grid, 256, 0, st>>>((const bf16 *)B, (const bf16 *)C, (bf16 *)cb,
-                                               (bf16 *)cbT, d.L, (int)d.G, (int)d.N, (int)d.Q,
-                                               (int)d.nc);
-    else
-        k_chunk_cb<float><<<grid, 256, 0, st>>>((const float *)B, (const float *)C, (float *)cb,
-                                                (float *)cbT, d.L, (int)d.G, (int)d.N, (int)d.Q,
-                                                (int)d.nc);
+    SSD_DISPATCH_N(d.N, {
+        if (d.dtype == 1)
+            k_chunk_cb<bf16, NN><<<grid, 256, 0, st>>>((const bf16 *)B, (const bf16 *)C, (bf16 *)cb,
+                                                       (bf16 *)cbT, d.L, (int)d.G, (int)d.Q, (int)d.nc);
+        else
+            k_chunk_cb<float, NN><<<grid, 256, 0, st>>>((const float *)B, (const float *)C, (float *)cb,
+                                                        (float *)cbT, d.L, (int)d.G, (int)d.Q, (int)d.nc);
+    });
     return hipGetLastError();
 }
 

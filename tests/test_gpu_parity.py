@@ -472,6 +472,23 @@ def test_single_pass_forward(ssd, chunk, L):
     assert worst_rel(f64(fin), f_ref, "state") < 2e-2
 
 
+# The walk takes one head per workgroup while batch x heads <= 256 (a CU
+# each) and two heads per workgroup above that when heads per group is even:
+# both layouts at more than 256 walks, with a ragged length and an initial
+# state (the smaller shapes above take the one-head layout).
+@pytest.mark.parametrize("batch,nheads,ngroups,L", [(5, 64, 2, 333), (3, 90, 2, 161)])
+def test_single_pass_many_walks(ssd, batch, nheads, ngroups, L):
+    w = small("bf16", batch=batch, seqlen=L, nheads=nheads, headdim=64, dstate=128, ngroups=ngroups,
+              chunk=256, seed=batch * 100 + nheads)
+    assert single_pass(ssd, w)
+    inp = si.make_forward_inputs(w)
+    y, fin = run_forward(ssd, inp, 256)
+    y_ref, f_ref = oracle_forward(inp)
+    assert worst_rel(f64(y), y_ref, "y") < 2e-2
+    assert worst_rel(f64(fin), f_ref, "state") < 2e-2
+    assert worst_row_rel(f64(y), y_ref, "y") < ROW_TOL_BF16
+
+
 def test_single_pass_long_chain(ssd):
     """256 chunks of 16 steps per (b, h): a long hand-off chain, with the
     fast/slow decay split of the long workload."""

@@ -184,6 +184,16 @@ def test_decode_validation():
     p[1] += 2
     assert ssd.STATUS[v(d, p)] == "SSD_ERR_ALIGN"
     assert ssd.STATUS[v(dims(dstate=24), ptrs)] == "SSD_ERR_UNSUPPORTED"
+    # the decode kernels index state rows with 32 bits: batch * H * P must stay
+    # below 2^31 - 4096 (checked on the sizes alone, before any pointer)
+    lim = (1 << 31) - 4096
+    bmax, P = 65535, 64                     # batch at its own limit (the grid's)
+    h_ok = lim // (bmax * P)
+    assert bmax * h_ok * P <= lim < bmax * (h_ok + 1) * P
+    assert ssd.STATUS[v(dims(batch=bmax, seqlen=1, nheads=h_ok + 1, headdim=P, ngroups=1), [None] * 8)] == \
+        "SSD_ERR_UNSUPPORTED"
+    assert ssd.STATUS[v(dims(batch=bmax, seqlen=1, nheads=h_ok, headdim=P, ngroups=1), [None] * 8)] == \
+        "SSD_ERR_NULL"
 
 
 def test_entry_points_reject_before_launch():

@@ -398,6 +398,25 @@ def test_decode_launch_shapes(ssd, dtype, shape):
     assert worst_rel(f64(state), st_ref, "state") < TOL[dtype]
 
 
+@pytest.mark.parametrize("shape", [(37, 12, 128, 64, 3), (5, 6, 16, 16, 2)])
+def test_decode_without_skip(ssd, shape):
+    """D = NULL on both decode layouts (pieces; one workgroup per slice)."""
+    b, H, P, N, G = shape
+    w = small("bf16", batch=b, seqlen=2, nheads=H, headdim=P, dstate=N, ngroups=G, seed=41)
+    inp = si.make_forward_inputs(w)
+    state = dev(inp["init"]).clone()
+    st_ref = inp["init"].double().numpy().copy()
+    for t in range(w.seqlen):
+        y = ssd.decode_step(state, dev(inp["x"][:, t].contiguous()), dev(inp["dt"][:, t].contiguous()),
+                            dev(inp["A"]), dev(inp["B"][:, t].contiguous()), dev(inp["C"][:, t].contiguous()),
+                            None)
+        y_ref, st_ref = oracle.decode_step(st_ref, inp["x"][:, t], inp["dt"][:, t], inp["A"], inp["B"][:, t],
+                                           inp["C"][:, t], None)
+        torch.cuda.synchronize()
+        assert worst_rel(f64(y)[:, None], y_ref[:, None], "y") < TOL["bf16"], t
+    assert worst_rel(f64(state), st_ref, "state") < TOL["bf16"]
+
+
 # ------------------------------------------------------------------ full-size workloads
 @pytest.mark.parametrize("idx", [0, 1, 2, 3])
 def test_workload_forward_full(ssd, idx):

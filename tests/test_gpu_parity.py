@@ -301,6 +301,18 @@ def test_forward_empty(ssd):
     assert y.numel() == 0 and fin.numel() == 0
 
 
+def test_decode_empty(ssd):
+    """A decode step over an empty batch launches nothing and returns an empty y."""
+    w = small("bf16", batch=0, seqlen=1, nheads=8, headdim=64, dstate=128, ngroups=2)
+    inp = si.make_forward_inputs(w)
+    state = dev(inp["init"]).clone()
+    y = ssd.decode_step(state, dev(inp["x"][:, 0].contiguous()), dev(inp["dt"][:, 0].contiguous()),
+                        dev(inp["A"]), dev(inp["B"][:, 0].contiguous()), dev(inp["C"][:, 0].contiguous()),
+                        dev(inp["D"]))
+    torch.cuda.synchronize()
+    assert y.numel() == 0 and state.numel() == 0
+
+
 def test_worked_example_on_gpu(ssd):
     """The four-token example printed on the Mamba-2 review page, embedded in
     the smallest compiled shape (P = N = 16) by zero padding."""
